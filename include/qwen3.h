@@ -1,0 +1,185 @@
+/*
+ * qwen3.h -- C ABI of the MI355X (gfx950) Qwen3 decoder-stack forward over a
+ * static per-seat KV cache, with the Qwen3-MoE block and 8-bit affine group
+ * quantised projections.
+ *
+ * What is computed (the pages):
+ *  - "maya2_mlx/backbone.py", module docstring and Backbone.forward(): per
+ *    layer h = h + pend (one rounding); y = RMSNorm(h) (two roundings);
+ *    qkv = y [Wq;Wk;Wv]^T; per-head RMSNorm of q and k (two roundings); RoPE in
+ *    fp32 on the model-dtype cos/sin table (one rounding); attention over keys
+ *    0..pos with an fp32 softmax (one rounding); h = h + o_proj(attn);
+ *    y2 = RMSNorm(h); pend = down(silu(g) * u) with silu in fp32 rounded once.
+ *    After the last layer h = h + pend and the result is RMSNorm(h, norm).
+ *    bf16 is the production dtype, fp32 the strict one.
+ *  - "@mlx-bun/inference" qwen3-moe.ts, Qwen3MoeSparseMoeBlock.forward: router
+ *    linear, softmax over all experts, top-k, renormalise, per-expert SwiGLU,
+ *    weighted sum.
+ *  - "rlx_flow/blocks/qwen3_decoder.rs", emit(): GQA, q head h reads kv head
+ *    h / (n_heads / n_kv_heads).
+ *
+ * Rounding: "rho" below is round-to-nearest-even to bf16 in QWEN3_BF16 mode and
+ * the identity in QWEN3_FP32 mode; the kernels accumulate in fp32.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked "host".  The library never
+ *    allocates device memory: weights, the KV cache and the workspace are
+ *    provided by the caller and BORROWED for the handle's lifetime; inputs are
+ *    borrowed for the call; outputs are written into caller buffers.
+ *  - All work is enqueued asynchronously on the handle's HIP stream; no call
+ *    synchronises.  The caller synchronises the stream before reading outputs.
+ *  - Every call returns QWEN3_OK (0) or a negative QWEN3_ERR_* code.  All
+ *    argument checks run on the host before anything is enqueued, so a failed
+ *    call leaves the cache, the seat length and all outputs unchanged (the
+ *    capacity check of Backbone.forward raises before any state change).
+ *    qwen3_last_error() then describes the failure.  A QWEN3_ERR_HIP from a
+ *    launch can leave work partly enqueued.
+ *  - A handle is one seat and is not thread-safe.
+ *
+ * Layouts (row-major, model dtype = bf16 or fp32 unless stated):
+ *  - projection weights are [out][in]: q|k|v fused as [(H+2KV)*D][hidden]
+ *    (q rows, then k rows, then v rows), o as [hidden][H*D], gate|up fused as
+ *    [2*I][hidden] (gate rows first), down as [hidden][I] ("fuse_proj" of
+ *    Backbone.__init__);
+ *  - 8-bit projections (quant_bits == 8): u8 codes [out][in], plus bf16 scale
+ *    and bias [out][in/quant_group]; w = scale * code + bias per group along
+ *    the input axis; q|k|v and gate|up are quantised as the fused rows;
+ *  - MoE: router [E][hidden], expert gate|up [E][2*Ie][hidden], expert down
+ *    [E][hidden][Ie];
+ *  - KV cache: K and V each [n_layers][n_kv_heads][capacity][head_dim]; the
+ *    cache holds post-norm, post-RoPE keys and raw values (Backbone.reset and
+ *    forward).  Entries at positions >= the seat length are never read;
+ *  - RoPE table: cos and sin each [capacity][head_dim], halves duplicated.
+ */
+#ifndef QWEN3_H
+#define QWEN3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QWEN3_BF16 = 0, QWEN3_FP32 = 1 } qwen3_dtype;
+
+enum {
+    QWEN3_OK = 0,
+    QWEN3_ERR_ARG = -1,         /* bad argument: null pointer, T < 1, bad layer index, ... */
+    QWEN3_ERR_DTYPE = -2,       /* dtype neither bf16 nor fp32 (Backbone.__init__ dtype gate) */
+    QWEN3_ERR_CAPACITY = -3,    /* length + T exceeds capacity (Backbone.forward) */
+    QWEN3_ERR_NULL_WEIGHT = -4, /* a weight the configuration needs is NULL */
+    QWEN3_ERR_UNSUPPORTED = -5, /* a shape the kernels do not handle (see qwen3_init) */
+    QWEN3_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+    QWEN3_ERR_WORKSPACE = -7    /* workspace missing or smaller than qwen3_workspace_bytes() */
+};
+
+typedef struct {
+    int n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, capacity;
+    float rms_eps;
+    double rope_theta;
+    int dtype;                 /* qwen3_dtype */
+    int n_experts, top_k, moe_intermediate, norm_topk_prob; /* n_experts == 0: dense MLP */
+    int quant_bits, quant_group; /* 0 (plain weights) or 8 with quant_group 64 */
+    int max_tokens;            /* largest T per call; sizes the workspace */
+} qwen3_config;
+
+typedef struct {
+    const void *in_norm, *post_norm, *q_norm, *k_norm; /* [hidden], [hidden], [D], [D] */
+    const void *qkv, *o, *gate_up, *down;               /* plain weights, or u8 codes if quantised */
+    const void *qkv_s, *qkv_b, *o_s, *o_b;              /* bf16 per-group scale and bias (quantised) */
+    const void *gate_up_s, *gate_up_b, *down_s, *down_b;
+    const void *router, *exp_gate_up, *exp_down;        /* MoE layers */
+} qwen3_layer_weights;
+
+typedef struct {
+    const void *embed;        /* [vocab][hidden]; may be NULL when only qwen3_forward_hidden is used */
+    const void *final_norm;   /* [hidden] */
+    const void *rope_cos, *rope_sin; /* [capacity][D] each, or both NULL: built by qwen3_init */
+    const qwen3_layer_weights *layers; /* HOST array [n_layers]; copied by qwen3_init */
+} qwen3_weights;
+
+typedef struct qwen3_handle qwen3_handle;
+
+/* Bytes of device workspace qwen3_init needs for this configuration (0 when
+ * the configuration is invalid).  The workspace holds activations, attention
+ * partials, MoE routing buffers and, when not supplied, the RoPE table. */
+size_t qwen3_workspace_bytes(const qwen3_config *cfg);
+
+/* Create a seat (Backbone.__init__ + reset without the zeroing: the caller's
+ * cache is used as is and the seat length starts at 0).
+ *   cfg, w: host structs, copied; the device buffers they point to are borrowed.
+ *   k_cache, v_cache: [n_layers][n_kv_heads][capacity][head_dim] each.
+ *   workspace: ws_bytes >= qwen3_workspace_bytes(cfg), 256-byte aligned.
+ *   stream: hipStream_t for every enqueue (NULL = the null stream).
+ * Supported: head_dim 64 or 128; n_heads a multiple of n_kv_heads; hidden,
+ * intermediate and moe_intermediate multiples of 64; quant_group 64.  Returns
+ * QWEN3_ERR_UNSUPPORTED otherwise, QWEN3_ERR_DTYPE for another dtype,
+ * QWEN3_ERR_NULL_WEIGHT for a missing weight.  *out is set only on success. */
+int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, void *v_cache,
+               void *workspace, size_t ws_bytes, void *stream, qwen3_handle **out);
+
+/* Zero the K/V cache of every layer and set the length to 0 (Backbone.reset). */
+int qwen3_reset(qwen3_handle *h);
+
+/* Forward T token ids (device int32 [T], each in [0, vocab)) at positions
+ * length..length+T-1: embedding gather (Backbone.embed_tokens), then
+ * qwen3_forward_hidden.  out: [T][hidden] final-norm hidden states.
+ * QWEN3_ERR_NULL_WEIGHT when the handle has no embedding table.  Ids are not
+ * range-checked on the host (they live on the device); the gather clamps an
+ * out-of-range id to 0 and sets the handle's device error flag, which
+ * qwen3_check_device_errors reports. */
+int qwen3_forward(qwen3_handle *h, const int32_t *tokens, int T, void *out);
+
+/* Forward hidden states x [T][hidden] (model dtype) at positions
+ * length..length+T-1 through every layer (Backbone.forward): writes the new
+ * K/V entries, advances the length by T and writes the final-norm hidden
+ * states to out [T][hidden].  T == 1 takes the decode kernels (split-K
+ * attention), T > 1 the prefill kernels (causal attention: the query at
+ * position p sees keys 0..p).  Errors: QWEN3_ERR_ARG (T < 1 or T > max_tokens),
+ * QWEN3_ERR_CAPACITY (length + T > capacity). */
+int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out);
+
+/* The MoE block of layer `layer` on already-normalised rows x [T][hidden]
+ * (Qwen3MoeSparseMoeBlock.forward): out [T][hidden].  topk_idx (int32 [T][top_k])
+ * and topk_w (model dtype [T][top_k]) receive the routing when not NULL: the
+ * selected experts in slot order of descending probability, ties to the lower
+ * expert index.  Does not touch the cache or the length.  Errors:
+ * QWEN3_ERR_ARG (not an MoE configuration, layer out of range, T < 1 or
+ * T > max_tokens). */
+int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out, int32_t *topk_idx,
+                    void *topk_w);
+
+/* Set the seat length (0 <= length <= capacity): a pre-filled cache, or a
+ * rewind.  Entries at positions >= length are never read and are overwritten
+ * by the next forward. */
+int qwen3_set_length(qwen3_handle *h, int length);
+int qwen3_get_length(const qwen3_handle *h);
+
+/* Use another HIP stream for later calls. */
+int qwen3_set_stream(qwen3_handle *h, void *stream);
+
+/* Synchronise the handle's stream and report device-side errors raised since
+ * the last check (an out-of-range token id): QWEN3_ERR_ARG if any, then
+ * cleared.  The only entry point that synchronises. */
+int qwen3_check_device_errors(qwen3_handle *h);
+
+/* Text of the last failure on this handle ("" when none); valid until the
+ * next call on the handle.  qwen3_status_string names a return code. */
+const char *qwen3_last_error(const qwen3_handle *h);
+const char *qwen3_status_string(int code);
+
+/* Free the handle (host memory only; borrowed buffers stay the caller's). */
+void qwen3_destroy(qwen3_handle *h);
+
+/* Build the RoPE table (Backbone.__init__ table comment, _rope):
+ * inv_j = fp32(theta^(-2j/D)), rounded to bf16 in bf16 mode;
+ * angle = fp32(p * inv_j); cos[p][j] = cos[p][j + D/2] = rho(fp32(cos(angle))),
+ * sin likewise.  cos, sin: [capacity][head_dim] in `dtype`. */
+int qwen3_rope_table(int capacity, int head_dim, double theta, int dtype, void *cos_out, void *sin_out,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,95 @@
+// common.h -- shared device helpers of the gfx950 kernels: storage types,
+// bf16 round-to-nearest-even, wave64 reductions, 128-bit vector loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+enum Dt { DT_BF16 = 0, DT_FP32 = 1 };
+
+// bf16 storage: the upper half of a binary32 pattern.
+struct bf16 {
+    uint16_t u;
+};
+
+__device__ __forceinline__ float to_f(bf16 x) { return __uint_as_float((uint32_t)x.u << 16); }
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even of binary32 to bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf_bits(lo) | (f2bf_bits(hi) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f(float f);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float f) { return bf16{(uint16_t)f2bf_bits(f)}; }
+template <> __device__ __forceinline__ float from_f<float>(float f) { return f; }
+
+// rho: round to the storage type and back (identity for fp32).
+template <typename T> __device__ __forceinline__ float rho(float f) { return to_f(from_f<T>(f)); }
+
+template <typename T> struct DtOf;
+template <> struct DtOf<bf16> { static constexpr Dt value = DT_BF16; };
+template <> struct DtOf<float> { static constexpr Dt value = DT_FP32; };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 16-byte global loads: streamed (non-temporal) for weights read once, plain otherwise.
+__device__ __forceinline__ u32x4 ld_stream(const void *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+
+// Expand 16 bytes of storage type T into fp32 values: 8 for bf16, 4 for fp32.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ void expand(u32x4 v, float *o) {
+        o[0] = bf_lo(v.x); o[1] = bf_hi(v.x); o[2] = bf_lo(v.y); o[3] = bf_hi(v.y);
+        o[4] = bf_lo(v.z); o[5] = bf_hi(v.z); o[6] = bf_lo(v.w); o[7] = bf_hi(v.w);
+    }
+};
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ void expand(u32x4 v, float *o) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Sum over a block of nwaves wave64s; every thread gets the total.  red: LDS of >= nwaves floats.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; ++i) t += red[i];
+    return t;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace q3

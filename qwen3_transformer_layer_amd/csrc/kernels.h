@@ -1,0 +1,60 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to libqwen3).
+// Every launcher validates nothing the host layer already checked; it returns
+// the hipError_t of the launch.  Pointers are device pointers; `dt` selects
+// bf16 or fp32 storage for every model-dtype buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q3 {
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+// out[t] = E[ids[t]] (ids outside [0, vocab) read row 0 and set *err).
+hipError_t launch_embed(int dt, const int32_t *ids, int T, const void *E, int vocab, int hid, void *out,
+                        int *err, hipStream_t s);
+
+// Per row t < T: h = res ? rho(h_in + res) : h_in (written to h_out when res and h_out);
+// y = rho(w * rho(h * r)), r = 1/sqrt(mean(h^2) + eps).
+hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const void *w, void *h_out, void *y,
+                              int T, int n, float eps, hipStream_t s);
+
+// RoPE table [cap][D] (cos, sin) in storage dt.
+hipError_t launch_rope_table(int dt, int cap, int D, double theta, void *cos_t, void *sin_t, hipStream_t s);
+
+// Per token t and head: per-head RMSNorm (q_norm / k_norm weights), RoPE at p0 + t,
+// q to q_out [T][H][D]; k and v written to the cache at position p0 + t.
+hipError_t launch_qknorm_rope_kv(int dt, const void *qkv, int T, int H, int KV, int D, const void *q_norm,
+                                 const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
+                                 int cap, void *q_out, void *k_cache, void *v_cache, hipStream_t s);
+
+// out = epilogue(x [M][K] . W^T), W [rows][K] row-major.
+//  EPI_STORE:  out[m][n] = rho(acc), n < N (W has N rows)
+//  EPI_RESID:  out[m][n] = rho(res[m][n] + rho(acc))
+//  EPI_SWIGLU: W has 2N rows (gate rows then up rows);
+//              out[m][n] = rho(rho(silu(rho(g))) * rho(u))
+hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int N, int epi, const void *res,
+                         void *out, hipStream_t s);
+
+// Same with 8-bit affine group weights: codes u8 [rows][K], scale/bias bf16 [rows][K/64]
+// (group must be 64); x, res and out are bf16.  Dequantised weights stay fp32.
+hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, const void *scale,
+                            const void *bias, int group, int N, int epi, const void *res, void *out, hipStream_t s);
+
+// Causal GQA attention of T queries at positions p0..p0+T-1 against cache entries
+// 0..p0+T-1: q [T][H][D] -> out [T][H*D].  ws: fp32 scratch of attention_workspace() bytes.
+hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,
+                            int D, int cap, int p0, void *out, float *ws, size_t ws_bytes, hipStream_t s);
+size_t attention_workspace(int T, int H, int KV, int D, int cap);
+
+// ---- MoE block: router logits rho(x . Wr^T), rho(softmax) over all E experts, top-k
+// (ties to the lower index, slot order descending probability), renormalised weights
+// w [T][k] (storage dt), expert SwiGLU FFNs and out [T][hid] = rho(sum_s rho(y_s * w_s)).
+// idx: int32 [T][k].  ws: moe_workspace() bytes.  Requires E <= 256, k <= 16.
+size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
+hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
+                      const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
+
+}  // namespace q3

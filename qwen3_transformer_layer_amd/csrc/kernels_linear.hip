@@ -1,0 +1,332 @@
+// kernels_linear.hip -- projections y = x . W^T with fused epilogues.
+//
+// The four projections of a layer ("maya2_mlx/backbone.py", forward: Q.mm with
+// the fused q|k|v rows, o_proj, fused gate|up rows, down) all take x [M][K] and a
+// row-major weight [rows][K].  Epilogues apply the page's rounding points:
+// STORE rounds the product once; RESID adds the rounded product to the residual
+// and rounds once more (h = h + o_proj(attn)); SWIGLU takes gate row n and up
+// row N + n together and rounds silu (computed in fp32) once, then the product
+// with up once.
+//
+//  - gemv_kernel: M <= 16 (decode).  HBM-bound: each wave64 owns one output
+//    column (a gate/up pair for SWIGLU) and streams its weight row with
+//    128-bit non-temporal loads, 4 loads in flight per lane; x is read through
+//    the L1/L2 caches; one wave reduction per output.
+//  - gemm_bf16_kernel: M > 16 in bf16.  MFMA v_mfma_f32_32x32x16_bf16, block
+//    tile 128 x 128 (SWIGLU: 128 rows x 64 gate + 64 up columns), K step 64,
+//    register-staged double buffering through padded LDS.
+//  - gemm_f32_kernel: M > 16 in fp32 (strict mode), LDS-tiled FMA.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+template <typename T> __device__ __forceinline__ float epi_value(int epi, float a, float b, const T *res, size_t idx) {
+    if (epi == EPI_SWIGLU) {
+        const float g = rho<T>(a), u = rho<T>(b);
+        return rho<T>(silu_f32(g)) * u;
+    }
+    if (epi == EPI_RESID) return to_f(res[idx]) + rho<T>(a);
+    return a;
+}
+
+// ------------------------------------------------------------ GEMV (M <= 16)
+template <typename T, int EPI, int MR>
+__global__ void __launch_bounds__(256) gemv_kernel(const T *__restrict__ x, int M, int K, const T *__restrict__ W,
+                                                   int N, const T *__restrict__ res, T *__restrict__ out) {
+    constexpr int VN = Vec<T>::N;
+    constexpr int U = 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 4 + wave;
+    if (n >= N) return;
+    const T *w0 = W + (size_t)n * K;
+    const T *w1 = W + (size_t)(EPI == EPI_SWIGLU ? n + N : n) * K;
+    float a0[MR], a1[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) a0[m] = a1[m] = 0.f;
+    const int nc = K / VN;  // 16-byte chunks per row
+    int c = lane;
+    for (; c + 64 * (U - 1) < nc; c += 64 * U) {
+        u32x4 wv0[U], wv1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wv0[u] = ld_stream(w0 + (size_t)(c + 64 * u) * VN);
+            if (EPI == EPI_SWIGLU) wv1[u] = ld_stream(w1 + (size_t)(c + 64 * u) * VN);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float wf0[VN], wf1[VN];
+            Vec<T>::expand(wv0[u], wf0);
+            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                if (m < M) {
+                    float xf[VN];
+                    Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)(c + 64 * u) * VN), xf);
+#pragma unroll
+                    for (int e = 0; e < VN; ++e) {
+                        a0[m] += wf0[e] * xf[e];
+                        if (EPI == EPI_SWIGLU) a1[m] += wf1[e] * xf[e];
+                    }
+                }
+            }
+        }
+    }
+    for (; c < nc; c += 64) {
+        float wf0[VN], wf1[VN];
+        Vec<T>::expand(ld_stream(w0 + (size_t)c * VN), wf0);
+        if (EPI == EPI_SWIGLU) Vec<T>::expand(ld_stream(w1 + (size_t)c * VN), wf1);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m < M) {
+                float xf[VN];
+                Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)c * VN), xf);
+#pragma unroll
+                for (int e = 0; e < VN; ++e) {
+                    a0[m] += wf0[e] * xf[e];
+                    if (EPI == EPI_SWIGLU) a1[m] += wf1[e] * xf[e];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+            const float s0 = wave_sum(a0[m]);
+            const float s1 = EPI == EPI_SWIGLU ? wave_sum(a1[m]) : 0.f;
+            if (lane == 0) {
+                const size_t idx = (size_t)m * N + n;
+                out[idx] = from_f<T>(epi_value<T>(EPI, s0, s1, res, idx));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ bf16 MFMA GEMM
+namespace gemm {
+constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row pitch in elements (144 B)
+}
+
+// B-tile row r of block nb -> weight row.  SWIGLU tiles pair 64 gate rows with the same 64 up rows.
+template <int EPI> __device__ __forceinline__ int b_row(int nb, int r, int N) {
+    if (EPI == EPI_SWIGLU) return r < 64 ? nb * 64 + r : N + nb * 64 + (r - 64);
+    return nb * gemm::BN + r;
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16 *__restrict__ A, int M, int K,
+                                                        const bf16 *__restrict__ B, int N,
+                                                        const bf16 *__restrict__ res, bf16 *__restrict__ out) {
+    using namespace gemm;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * BM, nb = blockIdx.x;
+
+    // global -> register staging: 4 chunks of 16 B per thread for each operand
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cidx = tid + i * 256, row = cidx >> 3, col = (cidx & 7) * 8;
+            const int gm = m0 + row;
+            ra[i] = gm < M ? ld16(A + (size_t)gm * K + k0 + col) : u32x4{0, 0, 0, 0};
+            const bool bval = EPI == EPI_SWIGLU ? nb * 64 + (row & 63) < N : nb * BN + row < N;
+            rb[i] = bval ? ld_stream(B + (size_t)b_row<EPI>(nb, row, N) * K + k0 + col) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cidx = tid + i * 256, row = cidx >> 3, col = (cidx & 7) * 8;
+            *(u32x4 *)&As[buf][row * LDK + col] = ra[i];
+            *(u32x4 *)&Bs[buf][row * LDK + col] = rb[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    int brow[2];
+    if (EPI == EPI_SWIGLU) {
+        brow[0] = wn * 32;
+        brow[1] = 64 + wn * 32;
+    } else {
+        brow[0] = wn * 64;
+        brow[1] = wn * 64 + 32;
+    }
+
+    const int nk = K / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *(const bf16x8 *)&As[cur][(wm * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bfr[j] = *(const bf16x8 *)&Bs[cur][(brow[j] + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            sstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row >= M) continue;
+            if (EPI == EPI_SWIGLU) {
+                const int col = nb * 64 + wn * 32 + (lane & 31);
+                if (col >= N) continue;
+                const size_t idx = (size_t)row * N + col;
+                out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[i][0][v], acc[i][1][v], res, idx));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = nb * BN + brow[j] + (lane & 31);
+                    if (col >= N) continue;
+                    const size_t idx = (size_t)row * N + col;
+                    out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[i][j][v], 0.f, res, idx));
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ fp32 tiled GEMM (strict mode)
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const float *__restrict__ A, int M, int K,
+                                                       const float *__restrict__ B, int N,
+                                                       const float *__restrict__ res, float *__restrict__ out) {
+    // 64 x 64 output tile (SWIGLU: 64 x 32 outputs from 32 gate + 32 up rows), K step 16.
+    __shared__ float As[16][64 + 1];
+    __shared__ float Bs[16][64 + 1];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * 64, nb = blockIdx.x;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        for (int i = tid; i < 64 * 16; i += 256) {
+            const int r = i / 16, kk = i % 16;
+            const int gm = m0 + r, gk = k0 + kk;
+            As[kk][r] = (gm < M && gk < K) ? A[(size_t)gm * K + gk] : 0.f;
+            int wr;
+            if (EPI == EPI_SWIGLU) wr = r < 32 ? nb * 32 + r : N + nb * 32 + (r - 32);
+            else wr = nb * 64 + r;
+            const bool ok = (EPI == EPI_SWIGLU ? (nb * 32 + (r & 31)) < N : wr < N) && gk < K;
+            Bs[kk][r] = ok ? B[(size_t)wr * K + gk] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+        }
+        __syncthreads();
+    }
+    if (EPI == EPI_SWIGLU) {
+        // columns tx*4+j < 32 are gate, >= 32 up: exchange through LDS
+        __shared__ float Cs[64][64 + 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Cs[ty * 4 + i][tx * 4 + j] = acc[i][j];
+        __syncthreads();
+        for (int e = tid; e < 64 * 32; e += 256) {
+            const int r = e / 32, cc = e % 32;
+            const int row = m0 + r, col = nb * 32 + cc;
+            if (row < M && col < N) {
+                const size_t idx = (size_t)row * N + col;
+                out[idx] = epi_value<float>(EPI, Cs[r][cc], Cs[r][32 + cc], res, idx);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = m0 + ty * 4 + i, col = nb * 64 + tx * 4 + j;
+            if (row < M && col < N) {
+                const size_t idx = (size_t)row * N + col;
+                out[idx] = epi_value<float>(EPI, acc[i][j], 0.f, res, idx);
+            }
+        }
+}
+
+// ------------------------------------------------------------ dispatch
+template <typename T, int EPI>
+static void launch_gemv_t(const void *x, int M, int K, const void *W, int N, const void *res, void *out,
+                          hipStream_t s) {
+    const dim3 grid((N + 3) / 4);
+    const T *xx = (const T *)x, *ww = (const T *)W, *rr = (const T *)res;
+    T *oo = (T *)out;
+    if (M <= 1) gemv_kernel<T, EPI, 1><<<grid, 256, 0, s>>>(xx, M, K, ww, N, rr, oo);
+    else if (M <= 2) gemv_kernel<T, EPI, 2><<<grid, 256, 0, s>>>(xx, M, K, ww, N, rr, oo);
+    else if (M <= 4) gemv_kernel<T, EPI, 4><<<grid, 256, 0, s>>>(xx, M, K, ww, N, rr, oo);
+    else if (M <= 8) gemv_kernel<T, EPI, 8><<<grid, 256, 0, s>>>(xx, M, K, ww, N, rr, oo);
+    else gemv_kernel<T, EPI, 16><<<grid, 256, 0, s>>>(xx, M, K, ww, N, rr, oo);
+}
+
+template <typename T>
+static void launch_gemv(int epi, const void *x, int M, int K, const void *W, int N, const void *res, void *out,
+                        hipStream_t s) {
+    if (epi == EPI_SWIGLU) launch_gemv_t<T, EPI_SWIGLU>(x, M, K, W, N, res, out, s);
+    else if (epi == EPI_RESID) launch_gemv_t<T, EPI_RESID>(x, M, K, W, N, res, out, s);
+    else launch_gemv_t<T, EPI_STORE>(x, M, K, W, N, res, out, s);
+}
+
+hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int N, int epi, const void *res,
+                         void *out, hipStream_t s) {
+    if (M <= 16) {
+        if (dt == DT_BF16) launch_gemv<bf16>(epi, x, M, K, W, N, res, out, s);
+        else launch_gemv<float>(epi, x, M, K, W, N, res, out, s);
+        return hipGetLastError();
+    }
+    if (dt == DT_BF16) {
+        const dim3 grid(epi == EPI_SWIGLU ? (N + 63) / 64 : (N + gemm::BN - 1) / gemm::BN, (M + gemm::BM - 1) / gemm::BM);
+        const bf16 *a = (const bf16 *)x, *b = (const bf16 *)W, *r = (const bf16 *)res;
+        bf16 *o = (bf16 *)out;
+        if (epi == EPI_SWIGLU) gemm_bf16_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+        else if (epi == EPI_RESID) gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+        else gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+    } else {
+        const dim3 grid(epi == EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64, (M + 63) / 64);
+        const float *a = (const float *)x, *b = (const float *)W, *r = (const float *)res;
+        float *o = (float *)out;
+        if (epi == EPI_SWIGLU) gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+        else if (epi == EPI_RESID) gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+        else gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace q3

@@ -1,0 +1,264 @@
+// kernels_q8.hip -- projections with 8-bit affine group-quantised weights.
+//
+// Format (the quantised fused rows of "maya2_mlx/backbone.py" fuse_proj; groups
+// of 64 along the input axis): w[n][k] = s[n][g] * q[n][k] + b[n][g], g = k / 64,
+// q an unsigned 8-bit code, s and b bf16.  The dequantised weight is used in
+// fp32 and never rounded: for each group the kernels form sum_k x_k q_k and
+// sum_k x_k and fold them as s * (x . q) + b * sum(x), the same sum regrouped.
+//
+//  - gemv_q8_kernel (M <= 16): each wave64 owns one output column; a lane reads
+//    16 codes (one 128-bit load) and the matching 16 bf16 activations, so a
+//    group's 64 codes are 4 lanes; weight bytes per column are K * (1 + 4/64).
+//  - gemm_q8_kernel (M > 16): the bf16 MFMA GEMM tiling with K step = one group
+//    (64).  Codes are integers 0..255 and exact in bf16, so each group's MFMA
+//    partial sum is exact products summed in fp32; it is folded into the
+//    running accumulator with the column's scale and bias and the row's
+//    activation sum over the group.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+static __device__ __forceinline__ float epi_q8(int epi, float a, float b, const bf16 *res, size_t idx) {
+    if (epi == EPI_SWIGLU) return rho<bf16>(silu_f32(rho<bf16>(a))) * rho<bf16>(b);
+    if (epi == EPI_RESID) return to_f(res[idx]) + rho<bf16>(a);
+    return a;
+}
+
+// 16 codes of one 128-bit word against 16 activations: returns sum x*q, adds sum x to *xs.
+static __device__ __forceinline__ float dot16_q8(u32x4 c, const float *xf) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a += xf[4 * i + b] * (float)((w[i] >> (8 * b)) & 0xffu);
+    return a;
+}
+
+template <int EPI, int MR>
+__global__ void __launch_bounds__(256) gemv_q8_kernel(const bf16 *__restrict__ x, int M, int K,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const bf16 *__restrict__ scale, const bf16 *__restrict__ bias,
+                                                      int N, const bf16 *__restrict__ res, bf16 *__restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 4 + wave;
+    if (n >= N) return;
+    const int ng = K / 64;
+    const int n1 = EPI == EPI_SWIGLU ? n + N : n;
+    const uint8_t *c0 = codes + (size_t)n * K, *c1 = codes + (size_t)n1 * K;
+    float a0[MR], a1[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) a0[m] = a1[m] = 0.f;
+    const int nch = K / 16;  // 16-code chunks per row
+    for (int c = lane; c < nch; c += 64) {
+        const int g = c >> 2;
+        const u32x4 q0 = ld_stream(c0 + (size_t)c * 16);
+        u32x4 q1 = q0;
+        if (EPI == EPI_SWIGLU) q1 = ld_stream(c1 + (size_t)c * 16);
+        const float s0 = to_f(scale[(size_t)n * ng + g]), b0 = to_f(bias[(size_t)n * ng + g]);
+        float s1 = 0.f, b1 = 0.f;
+        if (EPI == EPI_SWIGLU) {
+            s1 = to_f(scale[(size_t)n1 * ng + g]);
+            b1 = to_f(bias[(size_t)n1 * ng + g]);
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m < M) {
+                float xf[16];
+                const bf16 *xp = x + (size_t)m * K + (size_t)c * 16;
+                Vec<bf16>::expand(ld16(xp), xf);
+                Vec<bf16>::expand(ld16(xp + 8), xf + 8);
+                float xs = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xs += xf[i];
+                a0[m] += s0 * dot16_q8(q0, xf) + b0 * xs;
+                if (EPI == EPI_SWIGLU) a1[m] += s1 * dot16_q8(q1, xf) + b1 * xs;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+            const float r0 = wave_sum(a0[m]);
+            const float r1 = EPI == EPI_SWIGLU ? wave_sum(a1[m]) : 0.f;
+            if (lane == 0) {
+                const size_t idx = (size_t)m * N + n;
+                out[idx] = from_f<bf16>(epi_q8(EPI, r0, r1, res, idx));
+            }
+        }
+    }
+}
+
+namespace gq8 {
+constexpr int BM = 128, BN = 128, BK = 64, LDA = BK + 8, LDB = BK + 16;  // pitches: A in bf16, B in bytes
+}
+
+template <int EPI> __device__ __forceinline__ int q8_b_row(int nb, int r, int N) {
+    if (EPI == EPI_SWIGLU) return r < 64 ? nb * 64 + r : N + nb * 64 + (r - 64);
+    return nb * gq8::BN + r;
+}
+
+static __device__ __forceinline__ bf16x8 codes_to_bf16x8(uint2 c) {
+    bf16x8 r;
+    uint32_t *rw = (uint32_t *)&r;
+    const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t lo = __float_as_uint((float)((w[i] >> (16 * b)) & 0xffu)) >> 16;
+            const uint32_t hi = __float_as_uint((float)((w[i] >> (16 * b + 8)) & 0xffu)) >> 16;
+            rw[2 * i + b] = lo | (hi << 16);
+        }
+    return r;
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_q8_kernel(const bf16 *__restrict__ A, int M, int K,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const bf16 *__restrict__ scale, const bf16 *__restrict__ bias,
+                                                      int N, const bf16 *__restrict__ res, bf16 *__restrict__ out) {
+    using namespace gq8;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * LDB];
+    __shared__ float Xs[BM];          // sum of the group's activations per row
+    __shared__ float Ss[BN], Bb[BN];  // scale and bias of the group per B-tile row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * BM, nb = blockIdx.x;
+    const int ng = K / 64;
+    int brow[2];
+    if (EPI == EPI_SWIGLU) {
+        brow[0] = wn * 32;
+        brow[1] = 64 + wn * 32;
+    } else {
+        brow[0] = wn * 64;
+        brow[1] = wn * 64 + 32;
+    }
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    for (int g = 0; g < ng; ++g) {
+        const int k0 = g * 64;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // A: 128 rows x 64 bf16 = 1024 chunks of 16 B
+            const int cidx = tid + i * 256, row = cidx >> 3, col = (cidx & 7) * 8;
+            const int gm = m0 + row;
+            *(u32x4 *)&As[row * LDA + col] = gm < M ? ld16(A + (size_t)gm * K + k0 + col) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {  // B: 128 rows x 64 codes = 512 chunks of 16 B
+            const int cidx = tid + i * 256, row = cidx >> 2, col = (cidx & 3) * 16;
+            const bool bval = EPI == EPI_SWIGLU ? nb * 64 + (row & 63) < N : nb * BN + row < N;
+            *(u32x4 *)&Bs[row * LDB + col] =
+                bval ? ld_stream(codes + (size_t)q8_b_row<EPI>(nb, row, N) * K + k0 + col) : u32x4{0, 0, 0, 0};
+        }
+        if (tid < BN) {
+            const bool bval = EPI == EPI_SWIGLU ? nb * 64 + (tid & 63) < N : nb * BN + tid < N;
+            const int wr = q8_b_row<EPI>(nb, tid, N);
+            Ss[tid] = bval ? to_f(scale[(size_t)wr * ng + g]) : 0.f;
+            Bb[tid] = bval ? to_f(bias[(size_t)wr * ng + g]) : 0.f;
+        }
+        __syncthreads();
+        if (tid < BM) {
+            float xs = 0.f;
+            for (int c = 0; c < 64; ++c) xs += to_f(bf16{As[tid * LDA + c]});
+            Xs[tid] = xs;
+        }
+        f32x16 part[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) part[i][j][v] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *(const bf16x8 *)&As[(wm * 64 + i * 32 + (lane & 31)) * LDA + kk * 16 + (lane >> 5) * 8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bfr[j] = codes_to_bf16x8(*(const uint2 *)&Bs[(brow[j] + (lane & 31)) * LDB + kk * 16 + (lane >> 5) * 8]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
+        }
+        __syncthreads();  // Xs ready
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float sc = Ss[brow[j] + (lane & 31)], bi = Bb[brow[j] + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    acc[i][j][v] += sc * part[i][j][v] + bi * Xs[r];
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row >= M) continue;
+            if (EPI == EPI_SWIGLU) {
+                const int col = nb * 64 + wn * 32 + (lane & 31);
+                if (col >= N) continue;
+                const size_t idx = (size_t)row * N + col;
+                out[idx] = from_f<bf16>(epi_q8(EPI, acc[i][0][v], acc[i][1][v], res, idx));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = nb * BN + brow[j] + (lane & 31);
+                    if (col >= N) continue;
+                    const size_t idx = (size_t)row * N + col;
+                    out[idx] = from_f<bf16>(epi_q8(EPI, acc[i][j][v], 0.f, res, idx));
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+static void gemv_q8_dispatch(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
+                             int N, const void *res, void *out, hipStream_t s) {
+    const dim3 grid((N + 3) / 4);
+    const bf16 *xx = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *rr = (const bf16 *)res;
+    bf16 *oo = (bf16 *)out;
+    if (M <= 1) gemv_q8_kernel<EPI, 1><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+    else if (M <= 4) gemv_q8_kernel<EPI, 4><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+    else if (M <= 8) gemv_q8_kernel<EPI, 8><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+    else gemv_q8_kernel<EPI, 16><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+}
+
+hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
+                            int group, int N, int epi, const void *res, void *out, hipStream_t s) {
+    if (group != 64) return hipErrorInvalidValue;
+    if (M <= 16) {
+        if (epi == EPI_SWIGLU) gemv_q8_dispatch<EPI_SWIGLU>(x, M, K, codes, scale, bias, N, res, out, s);
+        else if (epi == EPI_RESID) gemv_q8_dispatch<EPI_RESID>(x, M, K, codes, scale, bias, N, res, out, s);
+        else gemv_q8_dispatch<EPI_STORE>(x, M, K, codes, scale, bias, N, res, out, s);
+        return hipGetLastError();
+    }
+    const dim3 grid(epi == EPI_SWIGLU ? (N + 63) / 64 : (N + gq8::BN - 1) / gq8::BN, (M + gq8::BM - 1) / gq8::BM);
+    const bf16 *a = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *r = (const bf16 *)res;
+    bf16 *o = (bf16 *)out;
+    if (epi == EPI_SWIGLU) gemm_q8_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, codes, sc, bi, N, r, o);
+    else if (epi == EPI_RESID) gemm_q8_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, codes, sc, bi, N, r, o);
+    else gemm_q8_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, codes, sc, bi, N, r, o);
+    return hipGetLastError();
+}
+
+}  // namespace q3

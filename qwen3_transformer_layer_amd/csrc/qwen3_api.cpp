@@ -1,0 +1,446 @@
+// qwen3_api.cpp -- the C ABI (include/qwen3.h): seat handle, host-side argument
+// checks (all before the first enqueue), workspace layout and the per-layer
+// launch sequence.
+//
+// Launch sequence of one forward call of T tokens ("maya2_mlx/backbone.py",
+// Backbone.forward, with its deferred MLP residual `pend`):
+//   layer 0:   y = RMSNorm(x)                              add_rmsnorm
+//   layer l>0: h = rho(h + pend); y = RMSNorm(h)           add_rmsnorm (fused add)
+//              qkv = rho(y Wqkv^T)                         linear (GEMV / MFMA GEMM)
+//              q, K[p], V[p] = norm + RoPE + cache write    qknorm_rope_kv
+//              a = attention(q, K[0..p], V[0..p])           split-K decode | flash prefill
+//              h = rho(h + rho(a Wo^T))                    linear, residual epilogue
+//              y2 = RMSNorm(h)                             add_rmsnorm
+//              dense: m = swiglu(y2 Wgu^T)                 linear, SwiGLU epilogue
+//                     pend = rho(m Wdown^T)                linear
+//              MoE:   pend = moe(y2)                       router/top-k/sort/experts/combine
+//   after the last layer: out = RMSNorm(rho(h + pend))     add_rmsnorm
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/qwen3.h"
+#include "../../include/qwen3_ops.h"
+#include "kernels.h"
+
+using namespace q3;
+
+struct qwen3_handle {
+    qwen3_config cfg;
+    std::vector<qwen3_layer_weights> layers;
+    const void *embed = nullptr, *final_norm = nullptr, *cos_t = nullptr, *sin_t = nullptr;
+    char *kc = nullptr, *vc = nullptr;
+    char *ws = nullptr;
+    size_t ws_bytes = 0;
+    hipStream_t stream = nullptr;
+    int length = 0;
+    std::string err;
+    // workspace pieces
+    void *h = nullptr, *y = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *pend = nullptr;
+    void *tmp = nullptr;
+    float *attn_ws = nullptr;
+    int *dev_err = nullptr;
+    int32_t *moe_idx = nullptr;
+    void *moe_w = nullptr, *moe_ws = nullptr;
+    // measurement: event pairs around launches of one kernel kind
+    static constexpr int NKIND = 5;
+    bool timer_on[NKIND] = {};
+    int timer_used[NKIND] = {};
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> timer_ev[NKIND];
+    ~qwen3_handle() {
+        for (auto &v : timer_ev)
+            for (auto &p : v) {
+                (void)hipEventDestroy(p.first);
+                (void)hipEventDestroy(p.second);
+            }
+    }
+};
+
+namespace {
+
+size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t h, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, total;
+};
+
+size_t esize(const qwen3_config &c) { return c.dtype == QWEN3_BF16 ? 2 : 4; }
+
+Layout layout(const qwen3_config &c) {
+    Layout L{};
+    const size_t es = esize(c), Tm = (size_t)c.max_tokens, hid = (size_t)c.hidden;
+    const size_t HD = (size_t)c.n_heads * c.head_dim, nqkv = (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+    size_t o = 0;
+    auto take = [&](size_t b) {
+        const size_t r = o;
+        o += al256(b);
+        return r;
+    };
+    L.h = take(Tm * hid * es);
+    L.y = take(Tm * hid * es);
+    L.qkv = take(Tm * nqkv * es);
+    L.q = take(Tm * HD * es);
+    L.a = take(Tm * HD * es);
+    L.m = take(Tm * (size_t)(c.intermediate > 0 ? c.intermediate : 1) * es);
+    L.pend = take(Tm * hid * es);
+    L.tmp = take(Tm * hid * es);
+    L.attn = take(attention_workspace(c.max_tokens, c.n_heads, c.n_kv_heads, c.head_dim, c.capacity));
+    L.cos_t = take((size_t)c.capacity * c.head_dim * es);
+    L.sin_t = take((size_t)c.capacity * c.head_dim * es);
+    L.err = take(256);
+    if (c.n_experts > 0) {
+        L.moe_idx = take(Tm * c.top_k * 4);
+        L.moe_w = take(Tm * c.top_k * es);
+        L.moe_ws = take(moe_workspace(c.max_tokens, c.hidden, c.n_experts, c.top_k, c.moe_intermediate, c.dtype));
+    }
+    L.total = o;
+    return L;
+}
+
+int fail(qwen3_handle *h, int code, const char *fmt, ...) {
+    if (h) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        h->err = buf;
+    }
+    return code;
+}
+
+// Configuration checks shared by qwen3_workspace_bytes and qwen3_init.
+int check_config(const qwen3_config *c, std::string *why) {
+    auto bad = [&](int code, const char *msg) {
+        if (why) *why = msg;
+        return code;
+    };
+    if (!c) return bad(QWEN3_ERR_ARG, "null config");
+    if (c->dtype != QWEN3_BF16 && c->dtype != QWEN3_FP32)
+        return bad(QWEN3_ERR_DTYPE, "dtype must be bf16 (production) or fp32 (strict)");
+    if (c->n_layers < 1 || c->hidden < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->capacity < 1 ||
+        c->max_tokens < 1)
+        return bad(QWEN3_ERR_ARG, "layer count, sizes, capacity and max_tokens must be positive");
+    if (c->head_dim != 64 && c->head_dim != 128) return bad(QWEN3_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (c->n_heads % c->n_kv_heads) return bad(QWEN3_ERR_ARG, "n_heads must be a multiple of n_kv_heads");
+    const int G = c->n_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return bad(QWEN3_ERR_UNSUPPORTED, "n_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (c->hidden % 128) return bad(QWEN3_ERR_UNSUPPORTED, "hidden must be a multiple of 128");
+    if (!(c->rms_eps >= 0.0f)) return bad(QWEN3_ERR_ARG, "rms_eps must be >= 0");
+    if (!(c->rope_theta > 1.0)) return bad(QWEN3_ERR_ARG, "rope_theta must be > 1");
+    if (c->n_experts > 0) {
+        if (c->n_experts > 256 || c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
+            return bad(QWEN3_ERR_UNSUPPORTED, "MoE needs 1 <= top_k <= min(16, n_experts) and n_experts <= 256");
+        if (c->moe_intermediate < 64 || c->moe_intermediate % 64)
+            return bad(QWEN3_ERR_UNSUPPORTED, "moe_intermediate must be a positive multiple of 64");
+        if (c->quant_bits) return bad(QWEN3_ERR_UNSUPPORTED, "quantised MoE experts are not supported");
+    } else {
+        if (c->intermediate < 64 || c->intermediate % 64)
+            return bad(QWEN3_ERR_UNSUPPORTED, "intermediate must be a positive multiple of 64");
+    }
+    if (c->quant_bits != 0) {
+        if (c->quant_bits != 8 || c->quant_group != 64)
+            return bad(QWEN3_ERR_UNSUPPORTED, "quantised weights must be 8-bit in groups of 64");
+        if (c->dtype != QWEN3_BF16) return bad(QWEN3_ERR_UNSUPPORTED, "quantised weights need the bf16 dtype");
+    }
+    return QWEN3_OK;
+}
+
+bool is_q8(const qwen3_handle *h) { return h->cfg.quant_bits == 8; }
+
+hipError_t linear(qwen3_handle *h, const void *x, int M, int K, const void *W, const void *Ws, const void *Wb, int N,
+                  int epi, const void *res, void *out) {
+    if (is_q8(h))
+        return launch_linear_q8(x, M, K, (const uint8_t *)W, Ws, Wb, h->cfg.quant_group, N, epi, res, out, h->stream);
+    return launch_linear(h->cfg.dtype, x, M, K, W, N, epi, res, out, h->stream);
+}
+
+enum { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_ATTN = 4 };
+
+// Record the start (begin = true) or end event of a timed launch of `kind`.
+hipError_t mark(qwen3_handle *h, int kind, bool begin) {
+    if (!h->timer_on[kind]) return hipSuccess;
+    auto &v = h->timer_ev[kind];
+    int &used = h->timer_used[kind];
+    if (begin) {
+        if ((size_t)used == v.size()) {
+            hipEvent_t a, b;
+            hipError_t e = hipEventCreate(&a);
+            if (e != hipSuccess) return e;
+            e = hipEventCreate(&b);
+            if (e != hipSuccess) return e;
+            v.push_back({a, b});
+        }
+        return hipEventRecord(v[used].first, h->stream);
+    }
+    const hipError_t e = hipEventRecord(v[used].second, h->stream);
+    ++used;
+    return e;
+}
+
+#define HIPCHECK(h, call)                                                                                    \
+    do {                                                                                                     \
+        hipError_t e_ = (call);                                                                              \
+        if (e_ != hipSuccess) return fail(h, QWEN3_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));       \
+    } while (0)
+
+int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
+    const qwen3_config &c = h->cfg;
+    const int dt = c.dtype, hid = c.hidden, H = c.n_heads, KV = c.n_kv_heads, D = c.head_dim;
+    const int nqkv = (H + 2 * KV) * D, p0 = h->length;
+    const size_t es = esize(c), layer_kv = (size_t)KV * c.capacity * D * es;
+    hipStream_t s = h->stream;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const qwen3_layer_weights &L = h->layers[l];
+        // deferred residual + input norm; layer 0 normalises x directly
+        if (l == 0) HIPCHECK(h, launch_add_rmsnorm(dt, x, nullptr, L.in_norm, nullptr, h->y, T, hid, c.rms_eps, s));
+        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, L.in_norm, h->h, h->y, T, hid, c.rms_eps, s));
+        HIPCHECK(h, mark(h, K_QKV, true));
+        HIPCHECK(h, linear(h, h->y, T, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
+        HIPCHECK(h, mark(h, K_QKV, false));
+        HIPCHECK(h, launch_qknorm_rope_kv(dt, h->qkv, T, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t, h->sin_t,
+                                          p0, c.capacity, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv, s));
+        HIPCHECK(h, mark(h, K_ATTN, true));
+        HIPCHECK(h, launch_attention(dt, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv, T, H, KV, D, c.capacity, p0,
+                                     h->a, h->attn_ws, 0, s));
+        HIPCHECK(h, mark(h, K_ATTN, false));
+        HIPCHECK(h, mark(h, K_O, true));
+        HIPCHECK(h, linear(h, h->a, T, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
+        HIPCHECK(h, mark(h, K_O, false));
+        HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, T, hid, c.rms_eps, s));
+        if (c.n_experts > 0) {
+            HIPCHECK(h, launch_moe(dt, h->y, T, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
+                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
+                                   h->moe_ws, s));
+        } else {
+            HIPCHECK(h, mark(h, K_GU, true));
+            HIPCHECK(h, linear(h, h->y, T, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
+                               nullptr, h->m));
+            HIPCHECK(h, mark(h, K_GU, false));
+            HIPCHECK(h, mark(h, K_DOWN, true));
+            HIPCHECK(h, linear(h, h->m, T, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_STORE, nullptr,
+                               h->pend));
+            HIPCHECK(h, mark(h, K_DOWN, false));
+        }
+    }
+    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, h->final_norm, nullptr, out, T, hid, c.rms_eps, s));
+    return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qwen3_status_string(int code) {
+    switch (code) {
+    case QWEN3_OK: return "ok";
+    case QWEN3_ERR_ARG: return "invalid argument";
+    case QWEN3_ERR_DTYPE: return "unsupported dtype";
+    case QWEN3_ERR_CAPACITY: return "context exceeds capacity";
+    case QWEN3_ERR_NULL_WEIGHT: return "missing weight";
+    case QWEN3_ERR_UNSUPPORTED: return "unsupported shape";
+    case QWEN3_ERR_HIP: return "HIP error";
+    case QWEN3_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown error";
+    }
+}
+
+size_t qwen3_workspace_bytes(const qwen3_config *cfg) {
+    if (check_config(cfg, nullptr) != QWEN3_OK) return 0;
+    return layout(*cfg).total;
+}
+
+int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, void *v_cache, void *workspace,
+               size_t ws_bytes, void *stream, qwen3_handle **out) {
+    if (!out) return QWEN3_ERR_ARG;
+    std::string why;
+    int rc = check_config(cfg, &why);
+    if (rc != QWEN3_OK) return rc;
+    if (!w || !w->layers || !k_cache || !v_cache) return QWEN3_ERR_ARG;
+    const Layout L = layout(*cfg);
+    if (!workspace || ws_bytes < L.total || ((uintptr_t)workspace & 255)) return QWEN3_ERR_WORKSPACE;
+    if (!w->final_norm) return QWEN3_ERR_NULL_WEIGHT;
+    if ((w->rope_cos == nullptr) != (w->rope_sin == nullptr)) return QWEN3_ERR_ARG;
+    const bool q8 = cfg->quant_bits == 8, moe = cfg->n_experts > 0;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const qwen3_layer_weights &Lw = w->layers[l];
+        if (!Lw.in_norm || !Lw.post_norm || !Lw.q_norm || !Lw.k_norm || !Lw.qkv || !Lw.o) return QWEN3_ERR_NULL_WEIGHT;
+        if (q8 && (!Lw.qkv_s || !Lw.qkv_b || !Lw.o_s || !Lw.o_b)) return QWEN3_ERR_NULL_WEIGHT;
+        if (moe) {
+            if (!Lw.router || !Lw.exp_gate_up || !Lw.exp_down) return QWEN3_ERR_NULL_WEIGHT;
+        } else {
+            if (!Lw.gate_up || !Lw.down) return QWEN3_ERR_NULL_WEIGHT;
+            if (q8 && (!Lw.gate_up_s || !Lw.gate_up_b || !Lw.down_s || !Lw.down_b)) return QWEN3_ERR_NULL_WEIGHT;
+        }
+    }
+    qwen3_handle *h = new qwen3_handle();
+    h->cfg = *cfg;
+    h->layers.assign(w->layers, w->layers + cfg->n_layers);
+    h->embed = w->embed;
+    h->final_norm = w->final_norm;
+    h->kc = (char *)k_cache;
+    h->vc = (char *)v_cache;
+    h->ws = (char *)workspace;
+    h->ws_bytes = ws_bytes;
+    h->stream = (hipStream_t)stream;
+    char *b = h->ws;
+    h->h = b + L.h;
+    h->y = b + L.y;
+    h->qkv = b + L.qkv;
+    h->q = b + L.q;
+    h->a = b + L.a;
+    h->m = b + L.m;
+    h->pend = b + L.pend;
+    h->tmp = b + L.tmp;
+    h->attn_ws = (float *)(b + L.attn);
+    h->dev_err = (int *)(b + L.err);
+    if (moe) {
+        h->moe_idx = (int32_t *)(b + L.moe_idx);
+        h->moe_w = b + L.moe_w;
+        h->moe_ws = b + L.moe_ws;
+    }
+    hipError_t e = hipMemsetAsync(h->dev_err, 0, 256, h->stream);
+    if (e == hipSuccess) {
+        if (w->rope_cos) {
+            h->cos_t = w->rope_cos;
+            h->sin_t = w->rope_sin;
+        } else {
+            h->cos_t = b + L.cos_t;
+            h->sin_t = b + L.sin_t;
+            e = launch_rope_table(cfg->dtype, cfg->capacity, cfg->head_dim, cfg->rope_theta, (void *)h->cos_t,
+                                  (void *)h->sin_t, h->stream);
+        }
+    }
+    if (e != hipSuccess) {
+        delete h;
+        return QWEN3_ERR_HIP;
+    }
+    *out = h;
+    return QWEN3_OK;
+}
+
+int qwen3_reset(qwen3_handle *h) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    const qwen3_config &c = h->cfg;
+    const size_t bytes = (size_t)c.n_layers * c.n_kv_heads * c.capacity * c.head_dim * esize(c);
+    HIPCHECK(h, hipMemsetAsync(h->kc, 0, bytes, h->stream));
+    HIPCHECK(h, hipMemsetAsync(h->vc, 0, bytes, h->stream));
+    h->length = 0;
+    return QWEN3_OK;
+}
+
+int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
+    if (h->length + T > h->cfg.capacity)
+        return fail(h, QWEN3_ERR_CAPACITY, "context %d exceeds capacity %d", h->length + T, h->cfg.capacity);
+    const int rc = run_layers(h, x, T, out);
+    if (rc == QWEN3_OK) h->length += T;
+    return rc;
+}
+
+int qwen3_forward(qwen3_handle *h, const int32_t *tokens, int T, void *out) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    if (!tokens || !out) return fail(h, QWEN3_ERR_ARG, "null tokens or output");
+    if (!h->embed || h->cfg.vocab < 1) return fail(h, QWEN3_ERR_NULL_WEIGHT, "no embedding table");
+    if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
+    if (h->length + T > h->cfg.capacity)
+        return fail(h, QWEN3_ERR_CAPACITY, "context %d exceeds capacity %d", h->length + T, h->cfg.capacity);
+    HIPCHECK(h, launch_embed(h->cfg.dtype, tokens, T, h->embed, h->cfg.vocab, h->cfg.hidden, h->tmp, h->dev_err,
+                             h->stream));
+    const int rc = run_layers(h, h->tmp, T, out);
+    if (rc == QWEN3_OK) h->length += T;
+    return rc;
+}
+
+int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out, int32_t *topk_idx, void *topk_w) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    const qwen3_config &c = h->cfg;
+    if (c.n_experts <= 0) return fail(h, QWEN3_ERR_ARG, "not an MoE configuration");
+    if (layer < 0 || layer >= c.n_layers) return fail(h, QWEN3_ERR_ARG, "layer %d out of range", layer);
+    if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (T < 1 || T > c.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, c.max_tokens);
+    const qwen3_layer_weights &L = h->layers[layer];
+    int32_t *idx = topk_idx ? topk_idx : h->moe_idx;
+    void *w = topk_w ? topk_w : h->moe_w;
+    HIPCHECK(h, launch_moe(c.dtype, x, T, c.hidden, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
+                           c.moe_intermediate, L.exp_gate_up, L.exp_down, idx, w, out, h->moe_ws, h->stream));
+    return QWEN3_OK;
+}
+
+int qwen3_set_length(qwen3_handle *h, int length) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    if (length < 0 || length > h->cfg.capacity)
+        return fail(h, QWEN3_ERR_ARG, "length %d outside 0..capacity=%d", length, h->cfg.capacity);
+    h->length = length;
+    return QWEN3_OK;
+}
+
+int qwen3_get_length(const qwen3_handle *h) { return h ? h->length : QWEN3_ERR_ARG; }
+
+int qwen3_set_stream(qwen3_handle *h, void *stream) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->stream = (hipStream_t)stream;
+    return QWEN3_OK;
+}
+
+int qwen3_check_device_errors(qwen3_handle *h) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    int flag = 0;
+    HIPCHECK(h, hipMemcpyAsync(&flag, h->dev_err, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+    HIPCHECK(h, hipStreamSynchronize(h->stream));
+    if (flag) {
+        HIPCHECK(h, hipMemsetAsync(h->dev_err, 0, sizeof(int), h->stream));
+        return fail(h, QWEN3_ERR_ARG, "a token id was outside [0, vocab)");
+    }
+    return QWEN3_OK;
+}
+
+int qwen3_kernel_timer(qwen3_handle *h, int kind, int enable) {
+    if (!h || kind < 0 || kind >= qwen3_handle::NKIND) return QWEN3_ERR_ARG;
+    h->timer_on[kind] = enable != 0;
+    h->timer_used[kind] = 0;
+    return QWEN3_OK;
+}
+
+int qwen3_kernel_timer_read(qwen3_handle *h, int kind, double *total_ms, int *count) {
+    if (!h || kind < 0 || kind >= qwen3_handle::NKIND || !total_ms || !count) return QWEN3_ERR_ARG;
+    h->err.clear();
+    double tot = 0.0;
+    for (int i = 0; i < h->timer_used[kind]; ++i) {
+        const auto &p = h->timer_ev[kind][i];
+        HIPCHECK(h, hipEventSynchronize(p.second));
+        float ms = 0.f;
+        HIPCHECK(h, hipEventElapsedTime(&ms, p.first, p.second));
+        tot += ms;
+    }
+    *total_ms = tot;
+    *count = h->timer_used[kind];
+    return QWEN3_OK;
+}
+
+const char *qwen3_last_error(const qwen3_handle *h) { return h ? h->err.c_str() : "null handle"; }
+
+void qwen3_destroy(qwen3_handle *h) { delete h; }
+
+int qwen3_rope_table(int capacity, int head_dim, double theta, int dtype, void *cos_out, void *sin_out,
+                     void *stream) {
+    if (dtype != QWEN3_BF16 && dtype != QWEN3_FP32) return QWEN3_ERR_DTYPE;
+    if (capacity < 1 || (head_dim != 64 && head_dim != 128) || !(theta > 1.0) || !cos_out || !sin_out)
+        return QWEN3_ERR_ARG;
+    return launch_rope_table(dtype, capacity, head_dim, theta, cos_out, sin_out, (hipStream_t)stream) == hipSuccess
+               ? QWEN3_OK
+               : QWEN3_ERR_HIP;
+}
+
+}  // extern "C"
