@@ -43,6 +43,10 @@ def log(*a):
 
 
 def decode_bench(steps: int, warmup: int):
+    """Time `steps` replays of one captured decode step (HIP graph on a side stream), then
+    `steps` eager steps with HIP events around every gate|up launch for the roofline."""
+    import ctypes
+
     import torch
 
     import qwen3_transformer_layer_amd as q3
@@ -53,34 +57,50 @@ def decode_bench(steps: int, warmup: int):
     log(f"decode: building {cfg.n_layers}-layer weights and a {cfg.capacity}-position cache")
     w = synth.model_weights(cfg, dev)
     K, V = synth.kv_cache(cfg, 4095, dev)
-    seat = q3.Seat(cfg, w, max_tokens=1, k_cache=K, v_cache=V)
+    stream = torch.cuda.Stream()
+    seat = q3.Seat(cfg, w, max_tokens=1, k_cache=K, v_cache=V, stream=stream)
     x = synth.hidden_states(cfg, 1, dev)
     out = torch.empty((1, cfg.hidden), dtype=torch.bfloat16, device=dev)
     L = _lib.load()
+    torch.cuda.synchronize()
 
     def step():
         seat.length = 4095
         q3.qwen3_forward_hidden(seat.handle, x, out)
 
-    for _ in range(warmup):
-        step()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
-    L.qwen3_kernel_timer(seat.handle.ptr, 2, 1)  # time every gate|up launch of the timed steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    import ctypes
+    dt = (time.perf_counter() - t0) / steps
+
+    # eager pass with the kernel timer on the library's stream
+    L.qwen3_kernel_timer(seat.handle.ptr, 2, 1)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    dt_eager = (time.perf_counter() - t0) / steps
     tot, cnt = ctypes.c_double(), ctypes.c_int()
     _lib.check(L.qwen3_kernel_timer_read(seat.handle.ptr, 2, ctypes.byref(tot), ctypes.byref(cnt)))
     L.qwen3_kernel_timer(seat.handle.ptr, 2, 0)
-    dt = (t1 - t0) / steps
     gu_us = tot.value * 1e3 / max(cnt.value, 1)
-    log(f"decode: {dt * 1e6:.1f} us/step, gate|up {gu_us:.2f} us/launch over {cnt.value} launches")
-    res = {"ms_per_step": dt * 1e3, "tokens_per_s": 1.0 / dt, "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9,
-           "gu_us": gu_us, "gu_launches": cnt.value}
-    del seat, w, K, V
+    log(f"decode: graph {dt * 1e6:.1f} us/step, eager {dt_eager * 1e6:.1f} us/step, "
+        f"gate|up {gu_us:.2f} us/launch over {cnt.value} launches")
+    res = {"ms_per_step": dt * 1e3, "eager_ms_per_step": dt_eager * 1e3, "tokens_per_s": 1.0 / dt,
+           "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "gu_us": gu_us, "gu_launches": cnt.value}
+    del graph, seat, w, K, V
     torch.cuda.empty_cache()
     return res
 
@@ -156,6 +176,7 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -166,6 +187,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.prefill_only:
+        pre = prefill_bench(args.prefill_iters)
+        print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
+        return
     dec = decode_bench(args.steps, args.warmup)
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     cpu = None if args.no_cpu else cpu_baseline()
@@ -179,6 +204,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 4),
+        "eager_ms_per_step": round(dec["eager_ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

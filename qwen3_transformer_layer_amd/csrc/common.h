@@ -92,4 +92,41 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// Block-cooperative RMSNorm prologue of a decode projection (one row of K values):
+// h = res ? rho(h_in + res) : h_in; ys = rho(w * rho(h * r)), r = 1/sqrt(mean(h^2) + eps),
+// stored in LDS in the storage type (values are exactly representable there).  Block 0
+// also writes h to h_out when both res and h_out are given.  Ends with a barrier.
+template <typename T>
+__device__ __forceinline__ void norm_prologue(const T *__restrict__ h_in, const T *__restrict__ res,
+                                              const T *__restrict__ w, float eps, T *__restrict__ h_out, int K,
+                                              T *ys, float *red) {
+    constexpr int VN = Vec<T>::N;
+    const int nc = K / VN;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+        float hv[VN];
+        Vec<T>::expand(ld16(h_in + (size_t)c * VN), hv);
+        if (res) {
+            float rv[VN];
+            Vec<T>::expand(ld16(res + (size_t)c * VN), rv);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) hv[e] = rho<T>(hv[e] + rv[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+            ss += hv[e] * hv[e];
+            ys[c * VN + e] = from_f<T>(hv[e]);
+            if (res && h_out && blockIdx.x == 0) h_out[c * VN + e] = from_f<T>(hv[e]);
+        }
+    }
+    const float r = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
+    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+        float wv[VN];
+        Vec<T>::expand(ld16(w + (size_t)c * VN), wv);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) ys[c * VN + e] = from_f<T>(wv[e] * rho<T>(to_f(ys[c * VN + e]) * r));
+    }
+    __syncthreads();
+}
+
 }  // namespace q3

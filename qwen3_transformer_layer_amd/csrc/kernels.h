@@ -38,6 +38,16 @@ hipError_t launch_qknorm_rope_kv(int dt, const void *qkv, int T, int H, int KV, 
 hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int N, int epi, const void *res,
                          void *out, hipStream_t s);
 
+// Decode projection (M == 1) with the RMSNorm prologue:
+//   h = res ? rho(h_in + res) : h_in   (written to h_out by one block when res and h_out)
+//   y = rho(nw * rho(h * r)), out = epilogue(y . W^T) with EPI_STORE or EPI_SWIGLU.
+// h_out must not alias h_in or res.
+hipError_t launch_linear_norm(int dt, const void *h_in, const void *res, const void *nw, float eps, void *h_out,
+                              int K, const void *W, int N, int epi, void *out, hipStream_t s);
+hipError_t launch_linear_q8_norm(const void *h_in, const void *res, const void *nw, float eps, void *h_out, int K,
+                                 const uint8_t *codes, const void *scale, const void *bias, int group, int N,
+                                 int epi, void *out, hipStream_t s);
+
 // Same with 8-bit affine group weights: codes u8 [rows][K], scale/bias bf16 [rows][K/64]
 // (group must be 64); x, res and out are bf16.  Dequantised weights stay fp32.
 hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, const void *scale,
@@ -48,6 +58,11 @@ hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, c
 hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,
                             int D, int cap, int p0, void *out, float *ws, size_t ws_bytes, hipStream_t s);
 size_t attention_workspace(int T, int H, int KV, int D, int cap);
+// Decode step (T == 1) at position p0 fused with the per-head q/k RMSNorm, RoPE and the
+// cache write: qkv [(H+2KV)D] of the token -> out [H*D]; writes K/V at p0.
+hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV, int D, const void *q_norm,
+                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
+                                         int cap, void *k_cache, void *v_cache, void *out, float *ws, hipStream_t s);
 
 // ---- MoE block: router logits rho(x . Wr^T), rho(softmax) over all E experts, top-k
 // (ties to the lower index, slot order descending probability), renormalised weights

@@ -40,37 +40,61 @@ size_t attention_workspace(int T, int H, int KV, int D, int cap) {
 }
 
 // ------------------------------------------------------------ split-K decode
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ q, const T *__restrict__ Kc,
-                                                          const T *__restrict__ Vc, int cap, int nkeys, int chunk,
-                                                          float scale, float *__restrict__ part, int nsplit) {
-    constexpr int VN = Vec<T>::N;
-    constexpr int LPK = D / VN;    // lanes per key row
-    constexpr int KPW = 64 / LPK;  // keys per wave step
-    constexpr int KPB = KPW * 4;   // keys per block step
-    extern __shared__ float smem[];
-    float *sc = smem;                    // [G][chunk] scores, then exp(score - max)
-    float *red = smem + G * chunk;       // [4][G][D] per-wave partial outputs
-    __shared__ float mrow[G], lrow[G];
+// Lane geometry: a key row of D values is LPK lanes x 16 bytes; a wave covers KPW keys per
+// step and the block's 4 waves KPB keys.  The first DEC_PF steps of K and V are loaded into
+// registers before any other work of the block so HBM latency overlaps the q/k prologue.
+constexpr int DEC_PF = 4;
 
-    const int s = blockIdx.x, g = blockIdx.y;
+template <typename T, int D> struct DecGeo {
+    static constexpr int VN = Vec<T>::N, LPK = D / VN, KPW = 64 / LPK, KPB = KPW * 4;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void decode_prefetch(const T *__restrict__ Kg, const T *__restrict__ Vg, int j0, int j1,
+                                                u32x4 *kp, u32x4 *vp) {
+    using G_ = DecGeo<T, D>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % G_::LPK, kslot = lane / G_::LPK;
+#pragma unroll
+    for (int i = 0; i < DEC_PF; ++i) {
+        const int j = j0 + wave * G_::KPW + i * G_::KPB + kslot;
+        const bool ok = j < j1;
+        kp[i] = ok ? ld_stream(Kg + (size_t)j * D + sub * G_::VN) : u32x4{0, 0, 0, 0};
+        vp[i] = ok ? ld_stream(Vg + (size_t)j * D + sub * G_::VN) : u32x4{0, 0, 0, 0};
+    }
+}
+
+// Core of one (split, kv head) block: keys [j0, j1) of kv head g against the G query
+// heads in qs (LDS, fp32 values of the model-dtype q).  Key `jspec` (if in range) is taken
+// from kspec / vspec in LDS instead of the cache (the fused kernel's fresh entry).
+template <typename T, int D, int G>
+__device__ __forceinline__ void decode_core(const float *qs, const T *__restrict__ Kg, const T *__restrict__ Vg,
+                                            const u32x4 *kp, const u32x4 *vp, int j0, int j1, int jspec,
+                                            const float *kspec, const float *vspec, float scale, float *sc, int chunk,
+                                            float *red, float *mrow, float *lrow, float *__restrict__ part,
+                                            int nsplit, int g, int s) {
+    using G_ = DecGeo<T, D>;
+    constexpr int VN = G_::VN, LPK = G_::LPK, KPW = G_::KPW, KPB = G_::KPB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPK, kslot = lane / LPK;
-    const int j0 = s * chunk;
-    const int j1 = min(nkeys, j0 + chunk);
     const int nj = j1 - j0;
-    const T *Kg = Kc + (size_t)g * cap * D;
-    const T *Vg = Vc + (size_t)g * cap * D;
 
     float qf[G][VN];
 #pragma unroll
-    for (int i = 0; i < G; ++i) Vec<T>::expand(ld16(q + (size_t)(g * G + i) * D + sub * VN), qf[i]);
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int e = 0; e < VN; ++e) qf[i][e] = qs[i * D + sub * VN + e];
 
-    for (int jb = j0 + wave * KPW; jb < j1; jb += KPB) {
+    auto score_step = [&](int jb, u32x4 kraw) {
         const int j = jb + kslot;
         const bool valid = j < j1;
         float kf[VN];
-        Vec<T>::expand(valid ? ld16(Kg + (size_t)j * D + sub * VN) : u32x4{0, 0, 0, 0}, kf);
+        if (j == jspec) {
+#pragma unroll
+            for (int e = 0; e < VN; ++e) kf[e] = kspec[sub * VN + e];
+        } else {
+            Vec<T>::expand(kraw, kf);
+        }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             float p = 0.f;
@@ -80,6 +104,15 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
             for (int o = LPK / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
             if (sub == 0 && valid) sc[i * chunk + (j - j0)] = p * scale;
         }
+    };
+#pragma unroll
+    for (int i = 0; i < DEC_PF; ++i) {
+        const int jb = j0 + wave * KPW + i * KPB;
+        if (jb < j1) score_step(jb, kp[i]);
+    }
+    for (int jb = j0 + wave * KPW + DEC_PF * KPB; jb < j1; jb += KPB) {
+        const int j = jb + kslot;
+        score_step(jb, j < j1 ? ld_stream(Kg + (size_t)j * D + sub * VN) : u32x4{0, 0, 0, 0});
     }
     __syncthreads();
     for (int i = wave; i < G; i += 4) {
@@ -105,11 +138,16 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
     for (int i = 0; i < G; ++i)
 #pragma unroll
         for (int e = 0; e < VN; ++e) o[i][e] = 0.f;
-    for (int jb = j0 + wave * KPW; jb < j1; jb += KPB) {
+    auto pv_step = [&](int jb, u32x4 vraw) {
         const int j = jb + kslot;
         if (j < j1) {
             float vf[VN];
-            Vec<T>::expand(ld16(Vg + (size_t)j * D + sub * VN), vf);
+            if (j == jspec) {
+#pragma unroll
+                for (int e = 0; e < VN; ++e) vf[e] = vspec[sub * VN + e];
+            } else {
+                Vec<T>::expand(vraw, vf);
+            }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const float e = sc[i * chunk + (j - j0)];
@@ -117,6 +155,15 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
                 for (int x = 0; x < VN; ++x) o[i][x] += e * vf[x];
             }
         }
+    };
+#pragma unroll
+    for (int i = 0; i < DEC_PF; ++i) {
+        const int jb = j0 + wave * KPW + i * KPB;
+        if (jb < j1) pv_step(jb, vp[i]);
+    }
+    for (int jb = j0 + wave * KPW + DEC_PF * KPB; jb < j1; jb += KPB) {
+        const int j = jb + kslot;
+        pv_step(jb, j < j1 ? ld_stream(Vg + (size_t)j * D + sub * VN) : u32x4{0, 0, 0, 0});
     }
 #pragma unroll
     for (int i = 0; i < G; ++i)
@@ -147,20 +194,134 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
     }
 }
 
-template <typename T>
-__global__ void attn_combine_kernel(const float *__restrict__ part, int nsplit, int D, T *__restrict__ out) {
-    const int h = blockIdx.x, d = threadIdx.x;
+// q [H][D] already normalised and rotated; the cache already holds position nkeys - 1.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ q, const T *__restrict__ Kc,
+                                                          const T *__restrict__ Vc, int cap, int nkeys, int chunk,
+                                                          float scale, float *__restrict__ part, int nsplit) {
+    extern __shared__ float smem[];
+    float *sc = smem;                  // [G][chunk]
+    float *red = smem + G * chunk;     // [4][G][D]
+    __shared__ float qs[G * D];
+    __shared__ float mrow[G], lrow[G];
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int j0 = s * chunk, j1 = min(nkeys, j0 + chunk);
+    const T *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
+    u32x4 kp[DEC_PF], vp[DEC_PF];
+    decode_prefetch<T, D>(Kg, Vg, j0, j1, kp, vp);
+    for (int i = threadIdx.x; i < G * D; i += 256) qs[i] = to_f(q[(size_t)g * G * D + i]);
+    __syncthreads();
+    decode_core<T, D, G>(qs, Kg, Vg, kp, vp, j0, j1, -1, nullptr, nullptr, scale, sc, chunk, red, mrow, lrow, part,
+                         nsplit, g, s);
+}
+
+// Fused decode step at position p = nkeys - 1: per-head RMSNorm of the group's q heads and
+// (in the split holding p) of k, RoPE at p, and the cache write of k and v at p, then the
+// split's attention.  qkv: [(H+2KV)D] for the one token.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) attn_decode_fused_kernel(
+    const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm, float eps,
+    const T *__restrict__ cos_t, const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc, int cap,
+    int nkeys, int chunk, float scale, float *__restrict__ part, int nsplit) {
+    extern __shared__ float smem[];
+    float *sc = smem;
+    float *red = smem + G * chunk;
+    __shared__ float qs[G * D];
+    __shared__ float kvs[2 * D];
+    __shared__ float mrow[G], lrow[G];
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j0 = s * chunk, j1 = min(nkeys, j0 + chunk);
+    const int p = nkeys - 1;
+    const bool has_p = j1 == nkeys;
+    T *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
+    u32x4 kp[DEC_PF], vp[DEC_PF];
+    decode_prefetch<T, D>(Kg, Vg, j0, j1, kp, vp);  // entry p, if loaded here, is replaced by kvs below
+    constexpr int half = D / 2;
+    const int nheads = G + (has_p ? 1 : 0);
+    for (int hh = wave; hh < nheads; hh += 4) {
+        const bool is_q = hh < G;
+        const T *row = qkv + (size_t)(is_q ? g * G + hh : H + g) * D;
+        const T *wn = is_q ? q_norm : k_norm;
+        const bool on = lane < half;
+        float x1 = 0.f, x2 = 0.f;
+        if (on) {
+            x1 = to_f(row[lane]);
+            x2 = to_f(row[lane + half]);
+        }
+        const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + eps);
+        if (on) {
+            const float n1 = rho<T>(to_f(wn[lane]) * rho<T>(x1 * r));
+            const float n2 = rho<T>(to_f(wn[lane + half]) * rho<T>(x2 * r));
+            const float c1 = to_f(cos_t[(size_t)p * D + lane]), s1 = to_f(sin_t[(size_t)p * D + lane]);
+            const float c2 = to_f(cos_t[(size_t)p * D + lane + half]), s2 = to_f(sin_t[(size_t)p * D + lane + half]);
+            const float o1 = rho<T>(n1 * c1 - n2 * s1), o2 = rho<T>(n2 * c2 + n1 * s2);
+            if (is_q) {
+                qs[hh * D + lane] = o1;
+                qs[hh * D + lane + half] = o2;
+            } else {
+                kvs[lane] = o1;
+                kvs[lane + half] = o2;
+                T *kd = Kg + (size_t)p * D;
+                kd[lane] = from_f<T>(o1);
+                kd[lane + half] = from_f<T>(o2);
+                const T *vrow = qkv + (size_t)(H + KV + g) * D;
+                T *vd = Vg + (size_t)p * D;
+                const T v1 = vrow[lane], v2 = vrow[lane + half];
+                vd[lane] = v1;
+                vd[lane + half] = v2;
+                kvs[D + lane] = to_f(v1);
+                kvs[D + lane + half] = to_f(v2);
+            }
+        }
+    }
+    __syncthreads();
+    decode_core<T, D, G>(qs, Kg, Vg, kp, vp, j0, j1, has_p ? p : -1, kvs, kvs + D, scale, sc, chunk, red, mrow, lrow,
+                         part, nsplit, g, s);
+}
+
+// Merge the splits of one head: out = rho(sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M)).
+// Thread t owns 32 consecutive values of split t / (D/32) in each pass of 256/(D/32)
+// splits, so every load of a pass is issued at once.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ part, int nsplit,
+                                                           T *__restrict__ out) {
+    constexpr int TPS = D / 32;        // threads per split
+    constexpr int SPP = 256 / TPS;     // splits per pass
+    __shared__ float red[4];
+    __shared__ float accs[SPP][D + 1];
+    __shared__ float lsum[SPP];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int sl = tid / TPS, d0 = (tid % TPS) * 32;
     const float *ph = part + (size_t)h * nsplit * (D + 2);
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ph[(size_t)s * (D + 2)]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float *p = ph + (size_t)s * (D + 2);
-        const float f = __expf(p[0] - M);
-        L += p[1] * f;
-        acc += p[2 + d] * f;
+    for (int s = sl; s < nsplit; s += SPP) M = fmaxf(M, ph[(size_t)s * (D + 2)]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float acc[32], L = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+    for (int s = sl; s < nsplit; s += SPP) {
+        const float *pp = ph + (size_t)s * (D + 2);
+        const float f = __expf(pp[0] - M);
+        L += pp[1] * f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) acc[e] += pp[2 + d0 + e] * f;
     }
-    out[(size_t)h * D + d] = from_f<T>(acc / L);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) accs[sl][d0 + e] = acc[e];
+    if (d0 == 0) lsum[sl] = L;
+    __syncthreads();
+    if (tid < D) {
+        float a = 0.f, l = 0.f;
+        for (int k = 0; k < SPP; ++k) {
+            a += accs[k][tid];
+            l += lsum[k];
+        }
+        out[(size_t)h * D + tid] = from_f<T>(a / l);
+    }
 }
 
 // ------------------------------------------------------------ fp32 / fallback row-wise kernel
@@ -351,8 +512,22 @@ __global__ void __launch_bounds__(256) attn_prefill_mfma_kernel(const bf16 *__re
 }
 
 // ------------------------------------------------------------ dispatch
+template <typename T, int D, int G>
+static void decode_launch(bool fused, dim3 grid, size_t lds, hipStream_t s, const void *q, const void *qkv, int H,
+                          int KV, const void *qn, const void *kn, float eps, const void *cs, const void *sn, void *kc,
+                          void *vc, int cap, int nkeys, int chunk, float scale, float *ws, int nsplit) {
+    if (fused)
+        attn_decode_fused_kernel<T, D, G><<<grid, 256, lds, s>>>((const T *)qkv, H, KV, (const T *)qn, (const T *)kn,
+                                                                  eps, (const T *)cs, (const T *)sn, (T *)kc, (T *)vc,
+                                                                  cap, nkeys, chunk, scale, ws, nsplit);
+    else
+        attn_decode_kernel<T, D, G><<<grid, 256, lds, s>>>((const T *)q, (const T *)kc, (const T *)vc, cap, nkeys,
+                                                            chunk, scale, ws, nsplit);
+}
+
 template <typename T, int D>
-static hipError_t decode_t(const void *q, const void *kc, const void *vc, int H, int KV, int cap, int nkeys,
+static hipError_t decode_t(bool fused, const void *q, const void *qkv, int H, int KV, const void *qn, const void *kn,
+                           float eps, const void *cs, const void *sn, void *kc, void *vc, int cap, int nkeys,
                            void *out, float *ws, hipStream_t s) {
     const int G = H / KV;
     const int chunk = decode_chunk(nkeys, KV);
@@ -360,18 +535,33 @@ static hipError_t decode_t(const void *q, const void *kc, const void *vc, int H,
     const float scale = (float)(1.0 / sqrt((double)D));
     const size_t lds = ((size_t)G * chunk + 4 * (size_t)G * D) * sizeof(float);
     const dim3 grid(nsplit, KV);
-    const T *qq = (const T *)q, *kk = (const T *)kc, *vv = (const T *)vc;
     switch (G) {
-    case 1: attn_decode_kernel<T, D, 1><<<grid, 256, lds, s>>>(qq, kk, vv, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 2: attn_decode_kernel<T, D, 2><<<grid, 256, lds, s>>>(qq, kk, vv, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 4: attn_decode_kernel<T, D, 4><<<grid, 256, lds, s>>>(qq, kk, vv, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 8: attn_decode_kernel<T, D, 8><<<grid, 256, lds, s>>>(qq, kk, vv, cap, nkeys, chunk, scale, ws, nsplit); break;
+    case 1: decode_launch<T, D, 1>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
+    case 2: decode_launch<T, D, 2>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
+    case 4: decode_launch<T, D, 4>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
+    case 8: decode_launch<T, D, 8>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_combine_kernel<T><<<H, D, 0, s>>>(ws, nsplit, D, (T *)out);
+    attn_combine_kernel<T, D><<<H, 256, 0, s>>>(ws, nsplit, (T *)out);
     return hipGetLastError();
+}
+
+hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV, int D, const void *q_norm,
+                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
+                                         int cap, void *k_cache, void *v_cache, void *out, float *ws,
+                                         hipStream_t s) {
+    const int nkeys = p0 + 1;
+    if (dt == DT_BF16)
+        return D == 128 ? decode_t<bf16, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
+                                              v_cache, cap, nkeys, out, ws, s)
+                        : decode_t<bf16, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
+                                             v_cache, cap, nkeys, out, ws, s);
+    return D == 128 ? decode_t<float, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
+                                           v_cache, cap, nkeys, out, ws, s)
+                    : decode_t<float, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
+                                          v_cache, cap, nkeys, out, ws, s);
 }
 
 hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,
@@ -380,11 +570,16 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
     const float scale = (float)(1.0 / sqrt((double)D));
     if (T == 1) {
         const int nkeys = p0 + 1;
+        void *kc = (void *)k_cache, *vc = (void *)v_cache;
         if (dt == DT_BF16)
-            return D == 128 ? decode_t<bf16, 128>(q, k_cache, v_cache, H, KV, cap, nkeys, out, ws, s)
-                            : decode_t<bf16, 64>(q, k_cache, v_cache, H, KV, cap, nkeys, out, ws, s);
-        return D == 128 ? decode_t<float, 128>(q, k_cache, v_cache, H, KV, cap, nkeys, out, ws, s)
-                        : decode_t<float, 64>(q, k_cache, v_cache, H, KV, cap, nkeys, out, ws, s);
+            return D == 128 ? decode_t<bf16, 128>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc,
+                                                  vc, cap, nkeys, out, ws, s)
+                            : decode_t<bf16, 64>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc,
+                                                 vc, cap, nkeys, out, ws, s);
+        return D == 128 ? decode_t<float, 128>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc, vc,
+                                               cap, nkeys, out, ws, s)
+                        : decode_t<float, 64>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc, vc,
+                                              cap, nkeys, out, ws, s);
     }
     if (dt == DT_BF16) {
         const dim3 grid((T + 63) / 64, H);

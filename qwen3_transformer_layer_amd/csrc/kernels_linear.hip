@@ -102,6 +102,108 @@ __global__ void __launch_bounds__(256) gemv_kernel(const T *__restrict__ x, int 
     }
 }
 
+// ------------------------------------------------------------ GEMV with RMSNorm prologue (M == 1)
+// The decode projections that follow a norm (q|k|v after the input norm with the deferred
+// residual add; gate|up after the post-attention norm) normalise the row once per block
+// into LDS and stream the weights as gemv_kernel does.
+template <typename T, int EPI>
+__global__ void __launch_bounds__(256) gemv_norm_kernel(const T *__restrict__ h_in, const T *__restrict__ res,
+                                                        const T *__restrict__ nw, float eps, T *__restrict__ h_out,
+                                                        int K, const T *__restrict__ W, int N, T *__restrict__ out) {
+    constexpr int VN = Vec<T>::N;
+    constexpr int U = 4;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    T *ys = (T *)smem_raw;
+    __shared__ float red[8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 4 + wave;
+    const bool active = n < N;
+    const T *w0 = W + (size_t)(active ? n : 0) * K;
+    const T *w1 = W + (size_t)(active ? (EPI == EPI_SWIGLU ? n + N : n) : 0) * K;
+    const int nc = K / VN;
+    // the first U chunks of the weight row(s) are in flight while the block normalises
+    u32x4 wv0[U], wv1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        const bool ok = active && c < nc;
+        wv0[u] = ok ? ld_stream(w0 + (size_t)c * VN) : u32x4{0, 0, 0, 0};
+        if (EPI == EPI_SWIGLU) wv1[u] = ok ? ld_stream(w1 + (size_t)c * VN) : u32x4{0, 0, 0, 0};
+    }
+    norm_prologue<T>(h_in, res, nw, eps, h_out, K, ys, red);
+    if (!active) return;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        if (c < nc) {
+            float wf0[VN], wf1[VN], xf[VN];
+            Vec<T>::expand(wv0[u], wf0);
+            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
+            Vec<T>::expand(*(const u32x4 *)&ys[c * VN], xf);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                a0 += wf0[e] * xf[e];
+                if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
+            }
+        }
+    }
+    int c = lane + 64 * U;
+    for (; c + 64 * (U - 1) < nc; c += 64 * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wv0[u] = ld_stream(w0 + (size_t)(c + 64 * u) * VN);
+            if (EPI == EPI_SWIGLU) wv1[u] = ld_stream(w1 + (size_t)(c + 64 * u) * VN);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float wf0[VN], wf1[VN], xf[VN];
+            Vec<T>::expand(wv0[u], wf0);
+            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
+            Vec<T>::expand(*(const u32x4 *)&ys[(c + 64 * u) * VN], xf);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                a0 += wf0[e] * xf[e];
+                if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
+            }
+        }
+    }
+    for (; c < nc; c += 64) {
+        float wf0[VN], wf1[VN], xf[VN];
+        Vec<T>::expand(ld_stream(w0 + (size_t)c * VN), wf0);
+        if (EPI == EPI_SWIGLU) Vec<T>::expand(ld_stream(w1 + (size_t)c * VN), wf1);
+        Vec<T>::expand(*(const u32x4 *)&ys[c * VN], xf);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+            a0 += wf0[e] * xf[e];
+            if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
+        }
+    }
+    const float s0 = wave_sum(a0);
+    const float s1 = EPI == EPI_SWIGLU ? wave_sum(a1) : 0.f;
+    if (lane == 0) out[n] = from_f<T>(epi_value<T>(EPI, s0, s1, (const T *)nullptr, n));
+}
+
+template <typename T>
+static void launch_gemv_norm_t(int epi, const void *h_in, const void *res, const void *nw, float eps, void *h_out,
+                               int K, const void *W, int N, void *out, hipStream_t s) {
+    const dim3 grid((N + 3) / 4);
+    const size_t lds = (size_t)K * sizeof(T);
+    const T *hi = (const T *)h_in, *rr = (const T *)res, *ww = (const T *)nw, *WW = (const T *)W;
+    if (epi == EPI_SWIGLU)
+        gemv_norm_kernel<T, EPI_SWIGLU><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (T *)h_out, K, WW, N, (T *)out);
+    else
+        gemv_norm_kernel<T, EPI_STORE><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (T *)h_out, K, WW, N, (T *)out);
+}
+
+hipError_t launch_linear_norm(int dt, const void *h_in, const void *res, const void *nw, float eps, void *h_out,
+                              int K, const void *W, int N, int epi, void *out, hipStream_t s) {
+    if (epi == EPI_RESID) return hipErrorInvalidValue;
+    if (dt == DT_BF16) launch_gemv_norm_t<bf16>(epi, h_in, res, nw, eps, h_out, K, W, N, out, s);
+    else launch_gemv_norm_t<float>(epi, h_in, res, nw, eps, h_out, K, W, N, out, s);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ bf16 MFMA GEMM
 namespace gemm {
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row pitch in elements (144 B)

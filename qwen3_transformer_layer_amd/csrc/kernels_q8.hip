@@ -90,6 +90,81 @@ __global__ void __launch_bounds__(256) gemv_q8_kernel(const bf16 *__restrict__ x
     }
 }
 
+// M == 1 with the RMSNorm prologue (norm_prologue): activations come from LDS.
+template <int EPI>
+__global__ void __launch_bounds__(256) gemv_q8_norm_kernel(const bf16 *__restrict__ h_in, const bf16 *__restrict__ res,
+                                                           const bf16 *__restrict__ nw, float eps,
+                                                           bf16 *__restrict__ h_out, int K,
+                                                           const uint8_t *__restrict__ codes,
+                                                           const bf16 *__restrict__ scale,
+                                                           const bf16 *__restrict__ bias, int N,
+                                                           bf16 *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    bf16 *ys = (bf16 *)smem_raw;
+    __shared__ float red[8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 4 + wave;
+    const bool active = n < N;
+    const int ng = K / 64;
+    const int n1 = EPI == EPI_SWIGLU ? n + N : n;
+    const uint8_t *c0 = codes + (size_t)(active ? n : 0) * K, *c1 = codes + (size_t)(active ? n1 : 0) * K;
+    const int nch = K / 16;
+    constexpr int U = 4;
+    u32x4 pq0[U], pq1[U];  // first chunks in flight during the norm
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        const bool ok = active && c < nch;
+        pq0[u] = ok ? ld_stream(c0 + (size_t)c * 16) : u32x4{0, 0, 0, 0};
+        if (EPI == EPI_SWIGLU) pq1[u] = ok ? ld_stream(c1 + (size_t)c * 16) : u32x4{0, 0, 0, 0};
+    }
+    norm_prologue<bf16>(h_in, res, nw, eps, h_out, K, ys, red);
+    if (!active) return;
+    float a0 = 0.f, a1 = 0.f;
+    auto consume = [&](int c, u32x4 q0, u32x4 q1) {
+        const int g = c >> 2;
+        float xf[16];
+        Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16], xf);
+        Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16 + 8], xf + 8);
+        float xs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs += xf[i];
+        a0 += to_f(scale[(size_t)n * ng + g]) * dot16_q8(q0, xf) + to_f(bias[(size_t)n * ng + g]) * xs;
+        if (EPI == EPI_SWIGLU)
+            a1 += to_f(scale[(size_t)n1 * ng + g]) * dot16_q8(q1, xf) + to_f(bias[(size_t)n1 * ng + g]) * xs;
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        if (c < nch) consume(c, pq0[u], pq1[u]);
+    }
+    for (int c = lane + 64 * U; c < nch; c += 64) {
+        const u32x4 q0 = ld_stream(c0 + (size_t)c * 16);
+        const u32x4 q1 = EPI == EPI_SWIGLU ? ld_stream(c1 + (size_t)c * 16) : q0;
+        consume(c, q0, q1);
+    }
+    const float r0 = wave_sum(a0);
+    const float r1 = EPI == EPI_SWIGLU ? wave_sum(a1) : 0.f;
+    if (lane == 0) out[n] = from_f<bf16>(epi_q8(EPI, r0, r1, nullptr, n));
+}
+
+hipError_t launch_linear_q8_norm(const void *h_in, const void *res, const void *nw, float eps, void *h_out, int K,
+                                 const uint8_t *codes, const void *scale, const void *bias, int group, int N,
+                                 int epi, void *out, hipStream_t s) {
+    if (group != 64 || epi == EPI_RESID) return hipErrorInvalidValue;
+    const dim3 grid((N + 3) / 4);
+    const size_t lds = (size_t)K * sizeof(bf16);
+    const bf16 *hi = (const bf16 *)h_in, *rr = (const bf16 *)res, *ww = (const bf16 *)nw;
+    const bf16 *sc = (const bf16 *)scale, *bi = (const bf16 *)bias;
+    if (epi == EPI_SWIGLU)
+        gemv_q8_norm_kernel<EPI_SWIGLU><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (bf16 *)h_out, K, codes, sc, bi, N,
+                                                               (bf16 *)out);
+    else
+        gemv_q8_norm_kernel<EPI_STORE><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (bf16 *)h_out, K, codes, sc, bi, N,
+                                                              (bf16 *)out);
+    return hipGetLastError();
+}
+
 namespace gq8 {
 constexpr int BM = 128, BN = 128, BK = 64, LDA = BK + 8, LDB = BK + 16;  // pitches: A in bf16, B in bytes
 }

@@ -39,7 +39,7 @@ struct qwen3_handle {
     int length = 0;
     std::string err;
     // workspace pieces
-    void *h = nullptr, *y = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *pend = nullptr;
+    void *h = nullptr, *h2 = nullptr, *y = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *pend = nullptr;
     void *tmp = nullptr;
     float *attn_ws = nullptr;
     int *dev_err = nullptr;
@@ -64,7 +64,7 @@ namespace {
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t h, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, total;
+    size_t h, h2, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, total;
 };
 
 size_t esize(const qwen3_config &c) { return c.dtype == QWEN3_BF16 ? 2 : 4; }
@@ -80,6 +80,7 @@ Layout layout(const qwen3_config &c) {
         return r;
     };
     L.h = take(Tm * hid * es);
+    L.h2 = take(Tm * hid * es);
     L.y = take(Tm * hid * es);
     L.qkv = take(Tm * nqkv * es);
     L.q = take(Tm * HD * es);
@@ -187,7 +188,67 @@ hipError_t mark(qwen3_handle *h, int kind, bool begin) {
         if (e_ != hipSuccess) return fail(h, QWEN3_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));       \
     } while (0)
 
+hipError_t linear_norm(qwen3_handle *h, const void *h_in, const void *res, const void *nw, void *h_out, int K,
+                       const void *W, const void *Ws, const void *Wb, int N, int epi, void *out) {
+    if (is_q8(h))
+        return launch_linear_q8_norm(h_in, res, nw, h->cfg.rms_eps, h_out, K, (const uint8_t *)W, Ws, Wb,
+                                     h->cfg.quant_group, N, epi, out, h->stream);
+    return launch_linear_norm(h->cfg.dtype, h_in, res, nw, h->cfg.rms_eps, h_out, K, W, N, epi, out, h->stream);
+}
+
+// T == 1: the norms ride in the projections' prologues and the per-head q/k norm, RoPE
+// and cache write in the split-K attention kernel; two hidden-state buffers alternate so
+// the block that writes h = rho(h + pend) never overwrites a row other blocks still read.
+int run_decode(qwen3_handle *h, const void *x, void *out) {
+    const qwen3_config &c = h->cfg;
+    const int dt = c.dtype, hid = c.hidden, H = c.n_heads, KV = c.n_kv_heads, D = c.head_dim;
+    const int nqkv = (H + 2 * KV) * D, p0 = h->length;
+    const size_t es = esize(c), layer_kv = (size_t)KV * c.capacity * D * es;
+    hipStream_t s = h->stream;
+    void *hb[2] = {h->h, h->h2};
+    void *hcur = nullptr;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const qwen3_layer_weights &L = h->layers[l];
+        void *hnext = l == 0 ? hb[0] : (hcur == hb[0] ? hb[1] : hb[0]);
+        HIPCHECK(h, mark(h, K_QKV, true));
+        if (l == 0)
+            HIPCHECK(h, linear_norm(h, x, nullptr, L.in_norm, nullptr, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE,
+                                    h->qkv));
+        else
+            HIPCHECK(h, linear_norm(h, hcur, h->pend, L.in_norm, hnext, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE,
+                                    h->qkv));
+        HIPCHECK(h, mark(h, K_QKV, false));
+        HIPCHECK(h, mark(h, K_ATTN, true));
+        HIPCHECK(h, launch_attention_decode_fused(dt, h->qkv, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t,
+                                                  h->sin_t, p0, c.capacity, h->kc + l * layer_kv,
+                                                  h->vc + l * layer_kv, h->a, h->attn_ws, s));
+        HIPCHECK(h, mark(h, K_ATTN, false));
+        HIPCHECK(h, mark(h, K_O, true));
+        HIPCHECK(h, linear(h, h->a, 1, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : hnext, hnext));
+        HIPCHECK(h, mark(h, K_O, false));
+        hcur = hnext;
+        if (c.n_experts > 0) {
+            HIPCHECK(h, launch_add_rmsnorm(dt, hcur, nullptr, L.post_norm, nullptr, h->y, 1, hid, c.rms_eps, s));
+            HIPCHECK(h, launch_moe(dt, h->y, 1, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
+                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
+                                   h->moe_ws, s));
+        } else {
+            HIPCHECK(h, mark(h, K_GU, true));
+            HIPCHECK(h, linear_norm(h, hcur, nullptr, L.post_norm, nullptr, hid, L.gate_up, L.gate_up_s, L.gate_up_b,
+                                    c.intermediate, EPI_SWIGLU, h->m));
+            HIPCHECK(h, mark(h, K_GU, false));
+            HIPCHECK(h, mark(h, K_DOWN, true));
+            HIPCHECK(h, linear(h, h->m, 1, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_STORE, nullptr,
+                               h->pend));
+            HIPCHECK(h, mark(h, K_DOWN, false));
+        }
+    }
+    HIPCHECK(h, launch_add_rmsnorm(dt, hcur, h->pend, h->final_norm, nullptr, out, 1, hid, c.rms_eps, s));
+    return QWEN3_OK;
+}
+
 int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
+    if (T == 1) return run_decode(h, x, out);
     const qwen3_config &c = h->cfg;
     const int dt = c.dtype, hid = c.hidden, H = c.n_heads, KV = c.n_kv_heads, D = c.head_dim;
     const int nqkv = (H + 2 * KV) * D, p0 = h->length;
@@ -288,6 +349,7 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
     h->stream = (hipStream_t)stream;
     char *b = h->ws;
     h->h = b + L.h;
+    h->h2 = b + L.h2;
     h->y = b + L.y;
     h->qkv = b + L.qkv;
     h->q = b + L.q;
