@@ -44,7 +44,9 @@ def log(*a):
 
 def decode_bench(steps: int, warmup: int):
     """Time `steps` replays of one captured decode step (HIP graph on a side stream), then
-    `steps` eager steps with HIP events around every gate|up launch for the roofline."""
+    `steps` eager steps with HIP events around the dominant kernel's launches on the
+    library's stream.  Done for the default T = 1 path (the persistent decode kernel) and,
+    for comparison, for the one-kernel-per-step path."""
     import ctypes
 
     import torch
@@ -68,39 +70,50 @@ def decode_bench(steps: int, warmup: int):
         seat.length = 4095
         q3.qwen3_forward_hidden(seat.handle, x, out)
 
-    with torch.cuda.stream(stream):
+    def run(path):
+        q3.qwen3_set_decode_path(seat.handle, path)
+        used = q3.qwen3_get_decode_path(seat.handle)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
         for _ in range(warmup):
-            step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        step()
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-
-    # eager pass with the kernel timer on the library's stream
-    L.qwen3_kernel_timer(seat.handle.ptr, 2, 1)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for _ in range(steps):
-            step()
-    torch.cuda.synchronize()
-    dt_eager = (time.perf_counter() - t0) / steps
-    tot, cnt = ctypes.c_double(), ctypes.c_int()
-    _lib.check(L.qwen3_kernel_timer_read(seat.handle.ptr, 2, ctypes.byref(tot), ctypes.byref(cnt)))
-    L.qwen3_kernel_timer(seat.handle.ptr, 2, 0)
-    gu_us = tot.value * 1e3 / max(cnt.value, 1)
-    log(f"decode: graph {dt * 1e6:.1f} us/step, eager {dt_eager * 1e6:.1f} us/step, "
-        f"gate|up {gu_us:.2f} us/launch over {cnt.value} launches")
-    res = {"ms_per_step": dt * 1e3, "eager_ms_per_step": dt_eager * 1e3, "tokens_per_s": 1.0 / dt,
-           "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "gu_us": gu_us, "gu_launches": cnt.value}
-    del graph, seat, w, K, V
+            graph.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        del graph
+        # eager pass with the timer on the dominant kernel: the whole-step kernel on the
+        # persistent path, the gate|up projection otherwise
+        kind = 5 if used == 2 else 2
+        L.qwen3_kernel_timer(seat.handle.ptr, kind, 1)
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for _ in range(steps):
+                step()
+        torch.cuda.synchronize()
+        dt_eager = (time.perf_counter() - t0) / steps
+        tot, cnt = ctypes.c_double(), ctypes.c_int()
+        _lib.check(L.qwen3_kernel_timer_read(seat.handle.ptr, kind, ctypes.byref(tot), ctypes.byref(cnt)))
+        L.qwen3_kernel_timer(seat.handle.ptr, kind, 0)
+        q3.qwen3_check_device_errors(seat.handle)
+        k_us = tot.value * 1e3 / max(cnt.value, 1)
+        log(f"decode path {used}: graph {dt * 1e6:.1f} us/step, eager {dt_eager * 1e6:.1f} us/step, "
+            f"timed kernel {k_us:.2f} us/launch over {cnt.value} launches")
+        return {"path": used, "ms_per_step": dt * 1e3, "eager_ms_per_step": dt_eager * 1e3,
+                "tokens_per_s": 1.0 / dt, "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "kernel_us": k_us,
+                "launches": cnt.value}
+
+    res = run(0)
+    res["kernels_path"] = run(1) if res["path"] == 2 else None
+    q3.qwen3_set_decode_path(seat.handle, 0)
+    del seat, w, K, V
     torch.cuda.empty_cache()
     return res
 
@@ -195,7 +208,14 @@ def main():
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     cpu = None if args.no_cpu else cpu_baseline()
 
-    gu_achieved = GU_LAUNCH_BYTES / (dec["gu_us"] * 1e-6) / 1e9
+    if dec["path"] == 2:
+        rl_kernel = "persistent decode kernel (all 28 layers of a T=1 step, final norm)"
+        rl_bytes = DECODE_STEP_BYTES
+    else:
+        rl_kernel = "gate|up projection GEMV with SwiGLU epilogue (T=1)"
+        rl_bytes = GU_LAUNCH_BYTES
+    achieved = rl_bytes / (dec["kernel_us"] * 1e-6) / 1e9
+    kp = dec["kernels_path"]
     line = {
         "metric": "decode tokens/s + HBM GB/s (T=1, ctx 4096); prefill TFLOP/s at T=2048",
         "value": round(dec["tokens_per_s"], 2),
@@ -213,15 +233,17 @@ def main():
         "config": {"workload": "Qwen3-1.7B-shaped bf16 decode, T=1 at position 4095 (ctx 4096), 28 layers, "
                                "hidden 2048, 16 q / 8 kv heads, head_dim 128, intermediate 6144",
                    "global_batch": 1, "seq_len": 4096, "parallelism": "single GPU"},
+        "decode_path": "persistent kernel" if dec["path"] == 2 else "one kernel per step",
         "hbm_gbps": round(dec["hbm_gbps"], 1),
         "hbm_frac": round(dec["hbm_gbps"] / HBM_PEAK_GBPS, 4),
+        "kernels_path_ms_per_step": None if kp is None else round(kp["ms_per_step"], 4),
         "prefill_tflops": None if pre is None else round(pre["tflops"], 1),
         "prefill_mfma_frac": None if pre is None else round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
         "prefill_ms": None if pre is None else round(pre["ms"], 3),
-        "roofline": {"kernel": "gate|up projection GEMV with SwiGLU epilogue (T=1)", "bound": "hbm",
-                     "achieved": round(gu_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "avg_launch_us": round(dec["gu_us"], 3), "launches": dec["gu_launches"]},
+        "roofline": {"kernel": rl_kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": rl_bytes, "avg_launch_us": round(dec["kernel_us"], 3),
+                     "launches": dec["launches"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

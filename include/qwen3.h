@@ -159,9 +159,22 @@ int qwen3_get_length(const qwen3_handle *h);
 /* Use another HIP stream for later calls. */
 int qwen3_set_stream(qwen3_handle *h, void *stream);
 
+/* Kernel structure of T == 1 steps.  path 0: automatic (default) -- the persistent decode
+ * kernel when the configuration and device support it (dense bf16 stacks with head_dim 128,
+ * hidden 2048 = n_heads * head_dim, intermediate 6144, 2 query heads per kv head, capacity
+ * <= 8192, on a device that holds 256 co-resident blocks of 512 threads), else one kernel per
+ * step of the layer; 1: always one kernel per step; 2: require the persistent kernel
+ * (QWEN3_ERR_UNSUPPORTED when unavailable).  Both compute the same values up to fp32
+ * summation order.  qwen3_get_decode_path returns the path T == 1 calls take (1 or 2). */
+int qwen3_set_decode_path(qwen3_handle *h, int path);
+int qwen3_get_decode_path(const qwen3_handle *h);
+
 /* Synchronise the handle's stream and report device-side errors raised since
- * the last check (an out-of-range token id): QWEN3_ERR_ARG if any, then
- * cleared.  The only entry point that synchronises. */
+ * the last check: an out-of-range token id (QWEN3_ERR_ARG) or a persistent decode
+ * step that timed out waiting for another block's results (QWEN3_ERR_HIP; the
+ * step's outputs are invalid).  The flags are then cleared.  Together with
+ * qwen3_init (which synchronises once to upload the persistent kernel's layer
+ * table), the only entry points that synchronise. */
 int qwen3_check_device_errors(qwen3_handle *h);
 
 /* Text of the last failure on this handle ("" when none); valid until the

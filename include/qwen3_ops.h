@@ -65,7 +65,8 @@ int qwen3_op_moe(int dtype, const void *x, int T, int hid, const void *router, i
                  size_t ws_bytes, void *stream);
 
 /* Kernel timing for measurement.  While enabled for a kind (0 q|k|v projection,
- * 1 o_proj, 2 gate|up projection, 3 down projection, 4 attention), every launch of
+ * 1 o_proj, 2 gate|up projection, 3 down projection, 4 attention, 5 the persistent
+ * decode kernel of a whole T == 1 step), every launch of
  * that kind by qwen3_forward / qwen3_forward_hidden on handle h is bracketed by two
  * HIP events recorded on the handle's stream.  qwen3_kernel_timer_read synchronises
  * on those events and returns the summed duration in ms and the launch count since

@@ -124,6 +124,15 @@ def qwen3_check_device_errors(h: _Handle) -> None:
     _lib.check(_lib.load().qwen3_check_device_errors(h.ptr), h.ptr)
 
 
+def qwen3_set_decode_path(h: _Handle, path: int) -> None:
+    """0: automatic, 1: one kernel per step of the layer, 2: the persistent decode kernel."""
+    _lib.check(_lib.load().qwen3_set_decode_path(h.ptr, path), h.ptr)
+
+
+def qwen3_get_decode_path(h: _Handle) -> int:
+    return _lib.load().qwen3_get_decode_path(h.ptr)
+
+
 def qwen3_destroy(h: _Handle) -> None:
     if h.ptr:
         _lib.load().qwen3_destroy(h.ptr)

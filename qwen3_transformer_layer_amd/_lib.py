@@ -68,6 +68,8 @@ def load():
         "qwen3_get_length": (_I, [H]),
         "qwen3_set_stream": (_I, [H, _P]),
         "qwen3_check_device_errors": (_I, [H]),
+        "qwen3_set_decode_path": (_I, [H, _I]),
+        "qwen3_get_decode_path": (_I, [H]),
         "qwen3_last_error": (ctypes.c_char_p, [H]),
         "qwen3_status_string": (ctypes.c_char_p, [_I]),
         "qwen3_destroy": (None, [H]),

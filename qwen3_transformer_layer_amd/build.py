@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqwen3.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["kernels_elem.hip", "kernels_linear.hip", "kernels_attn.hip", "kernels_moe.hip", "kernels_q8.hip",
+SOURCES = ["kernels_elem.hip", "kernels_linear.hip", "kernels_attn.hip", "kernels_moe.hip", "kernels_q8.hip", "kernels_decode_mk.hip",
            "qwen3_api.cpp", "qwen3_ops.cpp"]
 ARCH = os.environ.get("QWEN3_OFFLOAD_ARCH", "gfx950")
 
@@ -53,7 +53,7 @@ def build(jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}{r.stderr}")

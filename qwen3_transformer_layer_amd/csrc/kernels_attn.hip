@@ -19,6 +19,7 @@
 //    online softmax over key blocks of 64.
 #include <math.h>
 
+#include "attn_core.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -40,152 +41,16 @@ size_t attention_workspace(int T, int H, int KV, int D, int cap) {
 }
 
 // ------------------------------------------------------------ split-K decode
-// Lane geometry: a key row of D values is LPK lanes x 16 bytes; a wave covers KPW keys per
-// step and the block's 4 waves KPB keys.  The first DEC_PF steps of K and V are loaded into
-// registers before any other work of the block so HBM latency overlaps the q/k prologue.
-constexpr int DEC_PF = 4;
-
-template <typename T, int D> struct DecGeo {
-    static constexpr int VN = Vec<T>::N, LPK = D / VN, KPW = 64 / LPK, KPB = KPW * 4;
-};
-
-template <typename T, int D>
-__device__ __forceinline__ void decode_prefetch(const T *__restrict__ Kg, const T *__restrict__ Vg, int j0, int j1,
-                                                u32x4 *kp, u32x4 *vp) {
-    using G_ = DecGeo<T, D>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane % G_::LPK, kslot = lane / G_::LPK;
-#pragma unroll
-    for (int i = 0; i < DEC_PF; ++i) {
-        const int j = j0 + wave * G_::KPW + i * G_::KPB + kslot;
-        const bool ok = j < j1;
-        kp[i] = ok ? ld_stream(Kg + (size_t)j * D + sub * G_::VN) : u32x4{0, 0, 0, 0};
-        vp[i] = ok ? ld_stream(Vg + (size_t)j * D + sub * G_::VN) : u32x4{0, 0, 0, 0};
-    }
-}
-
-// Core of one (split, kv head) block: keys [j0, j1) of kv head g against the G query
-// heads in qs (LDS, fp32 values of the model-dtype q).  Key `jspec` (if in range) is taken
-// from kspec / vspec in LDS instead of the cache (the fused kernel's fresh entry).
 template <typename T, int D, int G>
 __device__ __forceinline__ void decode_core(const float *qs, const T *__restrict__ Kg, const T *__restrict__ Vg,
                                             const u32x4 *kp, const u32x4 *vp, int j0, int j1, int jspec,
                                             const float *kspec, const float *vspec, float scale, float *sc, int chunk,
                                             float *red, float *mrow, float *lrow, float *__restrict__ part,
                                             int nsplit, int g, int s) {
-    using G_ = DecGeo<T, D>;
-    constexpr int VN = G_::VN, LPK = G_::LPK, KPW = G_::KPW, KPB = G_::KPB;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane % LPK, kslot = lane / LPK;
-    const int nj = j1 - j0;
-
-    float qf[G][VN];
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int e = 0; e < VN; ++e) qf[i][e] = qs[i * D + sub * VN + e];
-
-    auto score_step = [&](int jb, u32x4 kraw) {
-        const int j = jb + kslot;
-        const bool valid = j < j1;
-        float kf[VN];
-        if (j == jspec) {
-#pragma unroll
-            for (int e = 0; e < VN; ++e) kf[e] = kspec[sub * VN + e];
-        } else {
-            Vec<T>::expand(kraw, kf);
-        }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            float p = 0.f;
-#pragma unroll
-            for (int e = 0; e < VN; ++e) p += qf[i][e] * kf[e];
-#pragma unroll
-            for (int o = LPK / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
-            if (sub == 0 && valid) sc[i * chunk + (j - j0)] = p * scale;
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < DEC_PF; ++i) {
-        const int jb = j0 + wave * KPW + i * KPB;
-        if (jb < j1) score_step(jb, kp[i]);
-    }
-    for (int jb = j0 + wave * KPW + DEC_PF * KPB; jb < j1; jb += KPB) {
-        const int j = jb + kslot;
-        score_step(jb, j < j1 ? ld_stream(Kg + (size_t)j * D + sub * VN) : u32x4{0, 0, 0, 0});
-    }
-    __syncthreads();
-    for (int i = wave; i < G; i += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < nj; j += 64) m = fmaxf(m, sc[i * chunk + j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < nj; j += 64) {
-            const float e = __expf(sc[i * chunk + j] - m);
-            sc[i * chunk + j] = e;
-            l += e;
-        }
-        l = wave_sum(l);
-        if (lane == 0) {
-            mrow[i] = m;
-            lrow[i] = l;
-        }
-    }
-    __syncthreads();
-
-    float o[G][VN];
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int e = 0; e < VN; ++e) o[i][e] = 0.f;
-    auto pv_step = [&](int jb, u32x4 vraw) {
-        const int j = jb + kslot;
-        if (j < j1) {
-            float vf[VN];
-            if (j == jspec) {
-#pragma unroll
-                for (int e = 0; e < VN; ++e) vf[e] = vspec[sub * VN + e];
-            } else {
-                Vec<T>::expand(vraw, vf);
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const float e = sc[i * chunk + (j - j0)];
-#pragma unroll
-                for (int x = 0; x < VN; ++x) o[i][x] += e * vf[x];
-            }
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < DEC_PF; ++i) {
-        const int jb = j0 + wave * KPW + i * KPB;
-        if (jb < j1) pv_step(jb, vp[i]);
-    }
-    for (int jb = j0 + wave * KPW + DEC_PF * KPB; jb < j1; jb += KPB) {
-        const int j = jb + kslot;
-        pv_step(jb, j < j1 ? ld_stream(Vg + (size_t)j * D + sub * VN) : u32x4{0, 0, 0, 0});
-    }
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int x = 0; x < VN; ++x) {
-            float v = o[i][x];
-#pragma unroll
-            for (int off = LPK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-            o[i][x] = v;
-        }
-    if (kslot == 0) {
-#pragma unroll
-        for (int i = 0; i < G; ++i)
-#pragma unroll
-            for (int x = 0; x < VN; ++x) red[(wave * G + i) * D + sub * VN + x] = o[i][x];
-    }
-    __syncthreads();
+    decode_core_lds<T, D, G, 4>(qs, Kg, Vg, kp, vp, j0, j1, jspec, kspec, vspec, scale, sc, chunk, red, mrow, lrow);
     for (int idx = threadIdx.x; idx < G * D; idx += 256) {
         const int i = idx / D, d = idx % D;
-        const float v = red[(0 * G + i) * D + d] + red[(1 * G + i) * D + d] + red[(2 * G + i) * D + d] +
-                        red[(3 * G + i) * D + d];
-        part[((size_t)(g * G + i) * nsplit + s) * (D + 2) + 2 + d] = v;
+        part[((size_t)(g * G + i) * nsplit + s) * (D + 2) + 2 + d] = decode_core_reduce<D, G, 4>(red, i, d);
     }
     if (threadIdx.x < G) {
         float *pp = part + ((size_t)(g * G + threadIdx.x) * nsplit + s) * (D + 2);
@@ -369,26 +234,46 @@ __global__ void __launch_bounds__(64) attn_rowwise_kernel(const T *__restrict__ 
 }
 
 // ------------------------------------------------------------ bf16 MFMA causal flash prefill
-// Block: 64 queries (4 waves x 16) of one query head, over key tiles of 64.
-template <int D>
-__global__ void __launch_bounds__(256) attn_prefill_mfma_kernel(const bf16 *__restrict__ q,
-                                                                const bf16 *__restrict__ Kc,
-                                                                const bf16 *__restrict__ Vc, int T, int H, int KV,
-                                                                int cap, int p0, float scale,
-                                                                bf16 *__restrict__ out) {
-    constexpr int KP = D + 8;   // K tile pitch (elements)
-    constexpr int VP = 64 + 8;  // V^T tile pitch
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-    const int ntiles = (T + 63) / 64;
-    const int qt = ntiles - 1 - blockIdx.x;  // heaviest (latest) query tiles first
-    const int h = blockIdx.y, g = h / (H / KV);
+// Block: QB queries of all G query heads of one kv head (so every K/V tile read serves G
+// heads); wave w owns 16 queries of one head.  K/V tiles of 64 keys are double-buffered in
+// LDS (next tile's global loads in registers while the current tile is computed).
+//   S^T (keys x queries) = K Q^T with v_mfma_f32_16x16x32_bf16: lane l holds query l%16 and
+//   keys 4*(l/16) + a of each 16-key sub-tile, so its softmax statistics are per query;
+//   O^T (d x queries) += V^T P^T: the V^T operand comes straight from the row-major V tile
+//   with the gfx950 LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, source
+//   lane s points at V[k + s/4][d + 4*(s%4)], and lane r receives V[k + v][d + r], v = 0..3;
+//   P (fp32) enters as bf16 hi + bf16 lo.  Scores are kept in base 2 (log2 e folded into
+//   the scale) and exponentiated with v_exp_f32.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_tr_b64(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ Kc, const bf16 *__restrict__ Vc, int T, int H, int KV,
+    int cap, int p0, float scale_log2, bf16 *__restrict__ out) {
+    constexpr int QB = G >= 4 ? 16 : 64 / G;   // queries per block
+    constexpr int QG = QB / 16;                // 16-query groups per head
+    constexpr int NW = G * QG;                 // waves
+    constexpr int NT = 64 * NW;
+    constexpr int P = D + 8;                   // LDS row pitch (elements)
+    constexpr int CH = 64 * (D / 8);           // 16-byte chunks per 64-key tile
+    constexpr int CPT = (CH + NT - 1) / NT;    // chunks per thread per operand
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * P];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * P];
+    const int ntiles = (T + QB - 1) / QB;
+    const int qt = ntiles - 1 - blockIdx.x;  // latest (heaviest) query tiles first
+    const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = qt * 64, wq0 = t0 + wave * 16;
+    const int h = g * G + wave / QG;
+    const int t0 = qt * QB, wq0 = t0 + (wave % QG) * 16;
     const int col = lane & 15, quad = lane >> 4;
-    const int tq = wq0 + col;                          // this lane's query (B-operand column)
-    const int qpos = p0 + min(tq, T - 1);              // padded queries behave like the last one
-    const int kmax = p0 + min(t0 + 63, T - 1);         // last key any query of the block sees
+    const int tq = wq0 + col;
+    const int qpos = p0 + min(tq, T - 1);
+    const int kmax = p0 + min(t0 + QB - 1, T - 1);
+    const int wlast = p0 + min(wq0 + 15, T - 1);  // last query position of this wave
     const bf16 *Kg = Kc + (size_t)g * cap * D;
     const bf16 *Vg = Vc + (size_t)g * cap * D;
 
@@ -406,97 +291,104 @@ __global__ void __launch_bounds__(256) attn_prefill_mfma_kernel(const bf16 *__re
     for (int i = 0; i < D / 16; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int nkt = kmax / 64 + 1;
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int k0 = kt * 64;
-        __syncthreads();
-        // stage K (row-major) and V (transposed) for keys k0..k0+63; rows past kmax are zero
-        for (int c = tid; c < 64 * (D / 8); c += 256) {
+    u32x4 rk[CPT], rv[CPT];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
             const int r = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const int kp = k0 + r;
-            u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
-            if (kp <= kmax) {
-                kv = ld16(Kg + (size_t)kp * D + d8);
-                vv = ld16(Vg + (size_t)kp * D + d8);
-            }
-            *(u32x4 *)&Ks[r * KP + d8] = kv;
-            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+            const bool ok = c < CH && k0 + r <= kmax;
+            rk[i] = ok ? ld16(Kg + (size_t)(k0 + r) * D + d8) : u32x4{0, 0, 0, 0};
+            rv[i] = ok ? ld16(Vg + (size_t)(k0 + r) * D + d8) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto sstore = [&](int buf) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Vt[(d8 + 2 * e) * VP + r] = (uint16_t)(w4[e] & 0xffffu);
-                Vt[(d8 + 2 * e + 1) * VP + r] = (uint16_t)(w4[e] >> 16);
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            if (c < CH) {
+                const int r = c / (D / 8), d8 = (c % (D / 8)) * 8;
+                *(u32x4 *)&Ks[buf][r * P + d8] = rk[i];
+                *(u32x4 *)&Vs[buf][r * P + d8] = rv[i];
             }
         }
-        __syncthreads();
-        if (k0 > p0 + min(wq0 + 15, T - 1)) continue;  // whole tile is in this wave's future
+    };
 
-        // S^T (16 keys x 16 queries per sub-tile): row key = 4*quad + a, column query = col
-        f32x4 sacc[4];
+    const int nkt = kmax / 64 + 1;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int k0 = kt * 64, buf = kt & 1;
+        if (kt + 1 < nkt) gload(k0 + 64);
+        if (k0 <= wlast) {
+            const uint16_t *Kt = Ks[buf], *Vt = Vs[buf];
+            f32x4 sacc[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < 4; ++kb) {
+                sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)&Ks[(kb * 16 + col) * KP + ks * 32 + quad * 8];
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    const bf16x8 kf = *(const bf16x8 *)&Kt[(kb * 16 + col) * P + ks * 32 + quad * 8];
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+                }
             }
-        }
-        float tmax = -INFINITY;
+            const bool need_mask = k0 + 63 > p0 + wq0;
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int kp = k0 + kb * 16 + quad * 4 + a;
-                const float sv = kp <= qpos ? sacc[kb][a] * scale : -INFINITY;
-                sacc[kb][a] = sv;
-                tmax = fmaxf(tmax, sv);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __expf(m_run - m_new);
-        float psum = 0.f;
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const float pv = __expf(sacc[2 * kc + half][a] - m_new);
-                    psum += pv;
-                    const uint32_t hb = f2bf_bits(pv);
-                    const float hf = __uint_as_float(hb << 16);
-                    const uint32_t lb = f2bf_bits(pv - hf);
-                    uint16_t hs = (uint16_t)hb, ls = (uint16_t)lb;
-                    phi[kc][half * 4 + a] = *(__bf16 *)&hs;
-                    plo[kc][half * 4 + a] = *(__bf16 *)&ls;
+                    float sv = sacc[kb][a] * scale_log2;
+                    if (need_mask && k0 + kb * 16 + quad * 4 + a > qpos) sv = -INFINITY;
+                    sacc[kb][a] = sv;
+                    tmax = fmaxf(tmax, sv);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float psum = 0.f;
+            bf16x8 phi[2], plo[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float pv = __builtin_amdgcn_exp2f(sacc[2 * kc + hf][a] - m_new);
+                        psum += pv;
+                        const __bf16 hb = (__bf16)pv;
+                        phi[kc][hf * 4 + a] = hb;
+                        plo[kc][hf * 4 + a] = (__bf16)(pv - (float)hb);
+                    }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) acc_o[dt][a] *= alpha;
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const uint16_t *src = &Vt[(kc * 32 + quad * 4 + (col >> 2)) * P + dt * 16 + 4 * (col & 3)];
+                    const s16x4 lo4 = lds_tr_b64(src);
+                    const s16x4 hi4 = lds_tr_b64(src + 16 * P);
+                    bf16x8 vf;
+                    short *vs = (short *)&vf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vs[e] = lo4[e];
+                        vs[4 + e] = hi4[e];
+                    }
+                    acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kc], acc_o[dt], 0, 0, 0);
+                    acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kc], acc_o[dt], 0, 0, 0);
                 }
             }
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) acc_o[dt][a] *= alpha;
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const uint16_t *vr = &Vt[(dt * 16 + col) * VP + kc * 32 + quad * 4];
-                bf16x8 vf;
-                const uint2 lo4 = *(const uint2 *)vr;
-                const uint2 hi4 = *(const uint2 *)(vr + 16);
-                uint32_t *vw = (uint32_t *)&vf;
-                vw[0] = lo4.x;
-                vw[1] = lo4.y;
-                vw[2] = hi4.x;
-                vw[3] = hi4.y;
-                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kc], acc_o[dt], 0, 0, 0);
-                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kc], acc_o[dt], 0, 0, 0);
-            }
-        }
+        if (kt + 1 < nkt) sstore(buf ^ 1);
+        __syncthreads();
     }
     if (tq < T) {
         const float inv = 1.0f / l_run;
@@ -582,13 +474,21 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
                                               cap, nkeys, out, ws, s);
     }
     if (dt == DT_BF16) {
-        const dim3 grid((T + 63) / 64, H);
+        const float sl2 = scale * 1.4426950408889634f;
         const bf16 *qq = (const bf16 *)q, *kk = (const bf16 *)k_cache, *vv = (const bf16 *)v_cache;
-        if (D == 128)
-            attn_prefill_mfma_kernel<128><<<grid, 256, 0, s>>>(qq, kk, vv, T, H, KV, cap, p0, scale, (bf16 *)out);
-        else
-            attn_prefill_mfma_kernel<64><<<grid, 256, 0, s>>>(qq, kk, vv, T, H, KV, cap, p0, scale, (bf16 *)out);
-        return hipGetLastError();
+        bf16 *oo = (bf16 *)out;
+        const int G = H / KV;
+        const int QB = G >= 4 ? 16 : 64 / G, NT = 64 * (G >= 8 ? 8 : 4);
+        const dim3 grid((T + QB - 1) / QB, KV);
+#define PREFILL_CASE(DD, GG)                                                                                   \
+    if (D == DD && G == GG) {                                                                                  \
+        attn_prefill_mfma_kernel<DD, GG><<<grid, NT, 0, s>>>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo);          \
+        return hipGetLastError();                                                                              \
+    }
+        PREFILL_CASE(128, 1) PREFILL_CASE(128, 2) PREFILL_CASE(128, 4) PREFILL_CASE(128, 8)
+        PREFILL_CASE(64, 1) PREFILL_CASE(64, 2) PREFILL_CASE(64, 4) PREFILL_CASE(64, 8)
+#undef PREFILL_CASE
+        return hipErrorInvalidValue;
     }
     attn_rowwise_kernel<float><<<dim3(T, H), 64, 0, s>>>((const float *)q, (const float *)k_cache,
                                                           (const float *)v_cache, H, KV, D, cap, p0, scale,

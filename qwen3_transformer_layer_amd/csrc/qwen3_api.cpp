@@ -45,8 +45,12 @@ struct qwen3_handle {
     int *dev_err = nullptr;
     int32_t *moe_idx = nullptr;
     void *moe_w = nullptr, *moe_ws = nullptr;
+    // persistent decode step (dense bf16 shapes it supports)
+    void *mk_ws = nullptr;
+    bool mk_ready = false;
+    int decode_path = 0;  // 0 auto, 1 separate kernels, 2 persistent kernel
     // measurement: event pairs around launches of one kernel kind
-    static constexpr int NKIND = 5;
+    static constexpr int NKIND = 6;
     bool timer_on[NKIND] = {};
     int timer_used[NKIND] = {};
     std::vector<std::pair<hipEvent_t, hipEvent_t>> timer_ev[NKIND];
@@ -64,7 +68,7 @@ namespace {
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t h, h2, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, total;
+    size_t h, h2, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, mk, total;
 };
 
 size_t esize(const qwen3_config &c) { return c.dtype == QWEN3_BF16 ? 2 : 4; }
@@ -97,6 +101,9 @@ Layout layout(const qwen3_config &c) {
         L.moe_w = take(Tm * c.top_k * es);
         L.moe_ws = take(moe_workspace(c.max_tokens, c.hidden, c.n_experts, c.top_k, c.moe_intermediate, c.dtype));
     }
+    if (decode_mk_supported(c.n_layers, c.dtype, c.n_experts, c.quant_bits, c.hidden, c.n_heads, c.n_kv_heads, c.head_dim,
+                            c.intermediate, c.capacity))
+        L.mk = take(decode_mk_workspace(c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate));
     L.total = o;
     return L;
 }
@@ -159,7 +166,7 @@ hipError_t linear(qwen3_handle *h, const void *x, int M, int K, const void *W, c
     return launch_linear(h->cfg.dtype, x, M, K, W, N, epi, res, out, h->stream);
 }
 
-enum { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_ATTN = 4 };
+enum { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_ATTN = 4, K_STEP = 5 };
 
 // Record the start (begin = true) or end event of a timed launch of `kind`.
 hipError_t mark(qwen3_handle *h, int kind, bool begin) {
@@ -201,6 +208,14 @@ hipError_t linear_norm(qwen3_handle *h, const void *h_in, const void *res, const
 // the block that writes h = rho(h + pend) never overwrites a row other blocks still read.
 int run_decode(qwen3_handle *h, const void *x, void *out) {
     const qwen3_config &c = h->cfg;
+    if (h->mk_ready && h->decode_path != 1) {
+        HIPCHECK(h, mark(h, K_STEP, true));
+        HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate,
+                                     c.capacity, h->length, c.rms_eps, x, out, h->final_norm, h->cos_t, h->sin_t, h->kc,
+                                     h->vc, h->dev_err, h->stream));
+        HIPCHECK(h, mark(h, K_STEP, false));
+        return QWEN3_OK;
+    }
     const int dt = c.dtype, hid = c.hidden, H = c.n_heads, KV = c.n_kv_heads, D = c.head_dim;
     const int nqkv = (H + 2 * KV) * D, p0 = h->length;
     const size_t es = esize(c), layer_kv = (size_t)KV * c.capacity * D * es;
@@ -376,6 +391,21 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
                                   (void *)h->sin_t, h->stream);
         }
     }
+    if (e == hipSuccess && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
+                                               cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->intermediate,
+                                               cfg->capacity) &&
+        decode_mk_max_blocks(cfg->hidden, cfg->intermediate, cfg->n_heads, cfg->n_kv_heads) >= decode_mk_blocks()) {
+        std::vector<const void *> ptrs;
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            const qwen3_layer_weights &Lw = w->layers[l];
+            const void *row[8] = {Lw.in_norm, Lw.post_norm, Lw.q_norm, Lw.k_norm, Lw.qkv, Lw.o, Lw.gate_up, Lw.down};
+            ptrs.insert(ptrs.end(), row, row + 8);
+        }
+        h->mk_ws = b + L.mk;
+        e = decode_mk_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, cfg->hidden, cfg->intermediate,
+                           ptrs.data(), h->stream);
+        h->mk_ready = e == hipSuccess;
+    }
     if (e != hipSuccess) {
         delete h;
         return QWEN3_ERR_HIP;
@@ -463,9 +493,25 @@ int qwen3_check_device_errors(qwen3_handle *h) {
     HIPCHECK(h, hipStreamSynchronize(h->stream));
     if (flag) {
         HIPCHECK(h, hipMemsetAsync(h->dev_err, 0, sizeof(int), h->stream));
+        if (flag & 2) return fail(h, QWEN3_ERR_HIP, "the persistent decode step timed out waiting for an exchange");
         return fail(h, QWEN3_ERR_ARG, "a token id was outside [0, vocab)");
     }
     return QWEN3_OK;
+}
+
+int qwen3_set_decode_path(qwen3_handle *h, int path) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    if (path < 0 || path > 2) return fail(h, QWEN3_ERR_ARG, "decode path must be 0, 1 or 2");
+    if (path == 2 && !h->mk_ready)
+        return fail(h, QWEN3_ERR_UNSUPPORTED, "no persistent decode kernel for this configuration or device");
+    h->decode_path = path;
+    return QWEN3_OK;
+}
+
+int qwen3_get_decode_path(const qwen3_handle *h) {
+    if (!h) return QWEN3_ERR_ARG;
+    return (h->mk_ready && h->decode_path != 1) ? 2 : 1;
 }
 
 int qwen3_kernel_timer(qwen3_handle *h, int kind, int enable) {
