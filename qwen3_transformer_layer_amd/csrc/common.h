@@ -19,12 +19,13 @@ __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round-to-nearest-even of binary32 to bf16 (NaN stays a quiet NaN).
+// Round-to-nearest-even of binary32 to bf16, ties to even (NaN stays a quiet NaN).  Integer
+// arithmetic rather than the conversion instruction, whose results differ on some inputs
+// (measured against the oracle's rounding on the RoPE table).
 __device__ __forceinline__ uint32_t f2bf_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7fffffffu) > 0x7f800000u ? (((u >> 16) | 0x40u) & 0xffffu) : r;
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf_bits(lo) | (f2bf_bits(hi) << 16); }
 
@@ -67,15 +68,36 @@ template <> struct Vec<float> {
     }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane reductions on DPP lane moves (VALU; no trip through the LDS crossbar).  The
+// wave must be fully active.  DPP controls: quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1,
+// lane ^ 2), row_half_mirror (lane 7-i within 8), row_mirror (lane 15-i within 16).
+#define Q3_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), (ctrl), 0xf, 0xf, false))
+// Sum over each 16-lane row; every lane of the row gets the row's total.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += Q3_DPP(v, 0xb1);
+    v += Q3_DPP(v, 0x4e);
+    v += Q3_DPP(v, 0x141);
+    v += Q3_DPP(v, 0x140);
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, Q3_DPP(v, 0xb1));
+    v = fmaxf(v, Q3_DPP(v, 0x4e));
+    v = fmaxf(v, Q3_DPP(v, 0x141));
+    v = fmaxf(v, Q3_DPP(v, 0x140));
     return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Sum / max over the wave (64 lanes); the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = row16_max(v);
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Sum over a block of nwaves wave64s; every thread gets the total.  red: LDS of >= nwaves floats.

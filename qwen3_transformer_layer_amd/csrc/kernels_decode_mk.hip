@@ -7,11 +7,26 @@
 //
 // Why one kernel.  A decode layer is six dependent steps (q|k|v projection, split-K
 // attention, split merge, o_proj + residual, gate|up + SwiGLU, down) whose weight streams are
-// 1 - 50 MB each.  As separate kernels every step pays launch, ramp-up and drain (~3-5 us on
-// gfx950), which is more than the 1.3 - 2.6 us the small steps need at HBM speed.  Here 256
-// blocks of 8 waves (one block per CU, co-resident) run all steps of all layers; each wave
-// issues its next steps' weight loads (registers, 128-bit non-temporal) before it waits for
-// the current step's inputs, so HBM streams while the exchange completes.
+// 8 - 50 MB each.  As separate kernels every step pays launch, ramp-up and drain (~3-5 us on
+// gfx950), more than the 1 - 8 us the steps need at HBM speed.  Here 256 blocks (one per CU,
+// co-resident) run all steps of all layers.
+//
+// Roles inside a block.  Waves 0-7 compute; waves 8-9 only stream.  The stream waves copy
+// every weight row (and the K/V rows of the block's attention split) that the block will
+// consume, in consumption order, from HBM straight into a ring of 4 KB LDS slots
+// (global_load_lds_dwordx4, 1 KB per instruction), keeping up to DL chunks in flight each
+// and running up to a full ring ahead of the compute waves, across step and layer
+// boundaries; when the ring is full a stream wave lands and publishes all its chunks in
+// flight before it waits for a slot, so the compute waves always see every landed chunk.
+// The compute waves never issue weight loads: a wave's vector-memory counter retires loads
+// in issue order, so a wave that polls another block's results while its own weight
+// prefetch is in flight waits for that prefetch as well.  With the roles split, the
+// compute waves' polls see a result as soon as it lands, and HBM streams while they wait.
+// Ring handshake (LDS only): slot s holds chunk g with s = g mod NS; the stream wave writes
+// ready[s] = g / NS + 1 after its counter shows the chunk landed, the consuming wave bumps
+// done[s] after its reads of the chunk; the stream wave waits for done[s] == g / NS before it
+// overwrites the slot.  Compute waves synchronise among themselves with an LDS counter
+// barrier (the stream waves take part in no barrier after the prologue).
 //
 // Exchange protocol between blocks (no grid barrier, no cache-maintenance fences): every
 // value handed to other blocks is written as one 32-bit word (tag << 16 | bf16 bits) or one
@@ -23,22 +38,38 @@
 // Every step's outputs go to a buffer that is rewritten only after all blocks have consumed
 // them: each full-vector exchange is a point every block passes only after every block has
 // finished the preceding steps.  Polls are bounded; a timeout sets bit 1 of the device
-// error word (the step's result is then invalid).
-#include "attn_core.h"
+// error word (the step's result is then invalid) and makes every other poll give up too.
 #include "common.h"
 #include "kernels.h"
 
 namespace q3 {
 namespace mk {
 
-constexpr int NB = 256;        // blocks
-constexpr int NWB = 8;         // waves per block
-constexpr int NT = 64 * NWB;   // threads per block
-constexpr int NW = NB * NWB;   // waves in the grid
-constexpr int D = 128;         // head dimension
-constexpr int CHUNK_MAX = 256; // keys per attention split
+constexpr int NB = 256;              // blocks, one per CU
+constexpr int NC = 8;                // compute waves per block
+constexpr int NL = 2;                // stream waves per block
+constexpr int NCT = 64 * NC;         // compute threads
+constexpr int NTH = 64 * (NC + NL);  // threads per block
+constexpr int D = 128;               // head dimension
+constexpr int HID = 2048;            // hidden size: one chunk is one weight row of HID bf16
+constexpr int CHB = HID * 2;         // chunk bytes
+constexpr int NS = 28;               // ring slots (112 KB)
+constexpr int DL = 8;                // chunks in flight per stream wave while the ring has room
+constexpr int KPC = CHB / (D * 2);   // keys per K or V chunk (16)
+constexpr int CHUNK_MAX = 256;       // keys per attention split
 constexpr int NSPLIT_MAX = 256;
-constexpr long SPIN = 1L << 21;  // poll rounds before a waiter gives up (order of a second)
+constexpr int MAXL = 63;             // layers (tags are call * 64 + layer)
+// Every block reads the whole of each exchanged vector.  Read from one copy, 256 blocks
+// would poll the same few KB, which sit in a few memory channels; producers therefore write
+// NREP copies, spaced so they fall in different channels, and block b reads copy b % NREP.
+constexpr int NREP = 8;
+__host__ __device__ constexpr int rep_stride(int words) {  // words between copies
+    return ((words * 4 + 4095) / 4096 * 4096 + 1280) / 4;
+}
+constexpr long SPIN = 1L << 21;      // global poll rounds before a waiter gives up (order of a second)
+constexpr long LSPIN = 1L << 22;     // LDS wait rounds before a waiter gives up (order of a second)
+static_assert(NS >= NL * DL, "the ring holds every stream wave's chunks in flight");
+static_assert(4 * (DL - 1) <= 63, "vector-memory counter range");
 
 struct DevLayer {
     const bf16 *in_norm, *post_norm, *q_norm, *k_norm, *qkv, *o, *gu, *down;
@@ -56,6 +87,16 @@ struct Args {
     int *err;
 };
 
+// The thread index behind an empty asm: every call yields a value the compiler cannot prove
+// equal to the last one, so per-thread addresses derived from it are recomputed inside the
+// layer loop instead of being hoisted out of it and kept live (or spilled) across all steps.
+__device__ __forceinline__ int tid_now() {
+    int z = 0;
+    __asm__ volatile("" : "+s"(z));
+    return (int)threadIdx.x + z;
+}
+
+// ---------------------------------------------------------------- cross-block exchange
 __device__ __forceinline__ void xstore(uint32_t *p, uint32_t w) {
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -70,26 +111,30 @@ __device__ __forceinline__ uint64_t xload64(const uint64_t *p) {
 }
 __device__ __forceinline__ uint32_t tagw(unsigned tag, float v) { return (tag << 16) | f2bf_bits(v); }
 
-// Poll bookkeeping: after SPIN rounds a waiter gives up and sets bit 1 of the error word;
-// every 256 rounds it also gives up when another waiter already has, so a step that cannot
-// complete (another block never ran) ends the whole grid after about one SPIN period
-// instead of one per remaining poll.
-__device__ __forceinline__ bool spin_out(long s, int *err) {
+// Every wait is bounded.  After SPIN rounds a waiter gives up, sets bit 1 of the error word
+// and the block's abort flag (LDS); every 256 rounds it also gives up when the error word or
+// the flag shows that another waiter already has, so a step that cannot complete ends the
+// whole grid after about one SPIN period instead of one per remaining wait.
+__device__ __forceinline__ bool spin_out(long s, int *err, unsigned *abt) {
     if (s > SPIN) {
         atomicOr(err, 2);
+        __hip_atomic_store(abt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return true;
     }
-    return (s & 255) == 0 && (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2);
+    return (s & 255) == 0 &&
+           ((__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2) ||
+            __hip_atomic_load(abt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 
 // Wait for words src[t], t < n, to carry `tag`; their bf16 payloads go to dst[t] (LDS).
-// Thread tid owns t = tid + NT * k; all its loads are in flight together.
+// Compute thread tid owns t = tid + NCT * k; all its loads are in flight together.
 template <int NPT>
-__device__ __forceinline__ void poll_bf16(const uint32_t *src, int n, unsigned tag, uint16_t *dst, int *err) {
+__device__ __forceinline__ void poll_bf16(const uint32_t *src, int n, unsigned tag, uint16_t *dst, int *err,
+                                          unsigned *abt, int tid) {
     uint32_t v[NPT];
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-        const int t = threadIdx.x + NT * k;
+        const int t = tid + NCT * k;
         v[k] = t < n ? xload(src + t) : (tag << 16);
     }
     long s = 0;
@@ -98,235 +143,522 @@ __device__ __forceinline__ void poll_bf16(const uint32_t *src, int n, unsigned t
 #pragma unroll
         for (int k = 0; k < NPT; ++k) ok &= (v[k] >> 16) == tag;
         if (ok) break;
-        if (spin_out(++s, err)) break;
+        if (spin_out(++s, err, abt)) break;
 #pragma unroll
         for (int k = 0; k < NPT; ++k) {
-            const int t = threadIdx.x + NT * k;
+            const int t = tid + NCT * k;
             if ((v[k] >> 16) != tag) v[k] = xload(src + t);
         }
     }
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-        const int t = threadIdx.x + NT * k;
+        const int t = tid + NCT * k;
         if (t < n) dst[t] = (uint16_t)(v[k] & 0xffffu);
     }
 }
 
-// Keeps the compiler from moving memory operations (the weight prefetches in particular)
-// across step boundaries, which would stretch their register live ranges.
-__device__ __forceinline__ void step_fence() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+// ---------------------------------------------------------------- LDS handshakes
+__device__ __forceinline__ unsigned lds_acquire(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until the LDS word *p reaches v (>= v).  Bounded like the global polls; on its own
+// time-out it raises the block's abort flag (and, where err is given, the error word).
+__device__ __forceinline__ void lds_wait_ge(const unsigned *p, unsigned v, unsigned *abt, int *err) {
+    long s = 0;
+    while (lds_acquire(p) < v) {
+        ++s;
+        if (s > LSPIN) {
+            __hip_atomic_store(abt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (err) atomicOr(err, 2);
+            return;
+        }
+        if ((s & 63) == 0 && __hip_atomic_load(abt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Barrier of the NC compute waves: a monotonic LDS counter; `ep` is the wave's running
+// target (NC per barrier passed).
+__device__ __forceinline__ void cbar(unsigned *ctr, unsigned &ep, unsigned *abt, int *err, int lane) {
+    ep += NC;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    lds_wait_ge(ctr, ep, abt, err);
+}
+
+// Wait until ring chunk g has landed; returns its slot.
+__device__ __forceinline__ const unsigned char *chunk_get(const unsigned char *ring, const unsigned *ready,
+                                                          unsigned g, unsigned *abt, int *err) {
+    const unsigned s = g % NS, gen = g / NS;
+    lds_wait_ge(ready + s, gen + 1u, abt, err);
+    return ring + (size_t)s * CHB;
+}
+// The wave's reads of chunk g are complete: its slot may be refilled.
+__device__ __forceinline__ void chunk_put(unsigned *done, unsigned g, int lane) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0)
+        __hip_atomic_fetch_add(done + g % NS, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// One 16-byte-per-lane copy from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane i's 16 bytes at g land at LDS byte address lds + 16 i.
+// Written as asm so the compiler does not see an LDS write it cannot place: with the
+// builtin it conservatively waits for every copy in flight before each later LDS access of
+// the stream wave (the ring flags), which would leave one chunk in flight.  The stream wave
+// tracks completion itself with wait_vm.  M0 carries the LDS address; the nop covers the
+// M0-write-to-LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt at maximum).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Returns p unchanged through an empty asm the compiler cannot see into: addresses derived
+// from it are then computed where they are used instead of being hoisted out of the layer
+// loop and kept live (in registers, or spilled) across every step.  The pointer is
+// wave-uniform (readfirstlane places it in scalar registers) and points to global memory:
+// going through a global-address-space pointer keeps the accesses global, not flat (flat
+// accesses also count against the LDS wait counter).
+template <typename T> __device__ __forceinline__ T *opaque(T *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    uint64_t q = ((uint64_t)hi << 32) | lo;
+    __asm__ volatile("" : "+s"(q));
+    typedef __attribute__((address_space(1))) T GT;
+    return (T *)(GT *)q;
 }
 
 __device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
-// Sum over the block (NT threads); every thread gets the total.
-__device__ __forceinline__ float bsum(float v, float *red) {
+// A lane's four 16-byte pieces of a 2048-element bf16 vector x in LDS (elements
+// (lane + 64 k) * 8 .. + 7, k < 4): loaded once per step, reused for every chunk.
+struct X4 {
+    u32x4 v[4];
+};
+__device__ __forceinline__ X4 load_x(const uint16_t *x, int lane) {
+    X4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.v[k] = *(const u32x4 *)(x + (lane + 64 * k) * 8);
+    return r;
+}
+// Per-lane partial dot of a 4 KB chunk (2048 bf16 in the same lane interleave) with x, added
+// to a; not summed over the wave.  All four LDS reads are issued before the arithmetic.
+__device__ __forceinline__ float dot_chunk(const unsigned char *c, const X4 &x, int lane, float a) {
+    u32x4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = *(const u32x4 *)(c + k * 1024 + lane * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float wf[8], xf[8];
+        Vec<bf16>::expand(w[k], wf);
+        Vec<bf16>::expand(x.v[k], xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += wf[e] * xf[e];
+    }
+    return a;
+}
+
+// Sum over the compute waves; every compute thread gets the total.  Two alternating
+// partial buffers, so one barrier per call suffices.
+__device__ __forceinline__ float csum(float v, float (*red)[NC], unsigned &par, unsigned *bar, unsigned &ep,
+                                     unsigned *abt, int *err, int tid) {
     v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    float *r = red[par];
+    par ^= 1u;
+    if ((tid & 63) == 0) r[tid >> 6] = v;
+    cbar(bar, ep, abt, err, tid & 63);
     float t = 0.f;
 #pragma unroll
-    for (int i = 0; i < NWB; ++i) t += red[i];
+    for (int i = 0; i < NC; ++i) t += r[i];
     return t;
 }
 
-// ys[i] = rho(w[i] * rho(hs[i] * r)), r = 1/sqrt(mean(hs^2) + eps), i < n (n = NT * NPT).
-template <int NPT>
-__device__ __forceinline__ void rmsnorm_lds(const float *hs, const bf16 *__restrict__ w, float eps, uint16_t *ys,
-                                            float *red) {
-    float ss = 0.f;
+// ---------------------------------------------------------------- per-block chunk sequence
+// Per layer the block consumes, in this order: QPB q|k|v rows, nK K chunks and nK V chunks
+// of its attention split (KPC keys each), OPB o rows, GPB gate/up row pairs (gate, then
+// up), OPB down rows of DCH chunks each.
+template <int QPB, int GPB, int DCH> struct Seq {
+    static constexpr int OPB = HID / NB;  // o rows (= down rows) per block
+    int nK, cpl;
+    __device__ explicit Seq(int nK_) : nK(nK_), cpl(QPB + 2 * nK_ + OPB + 2 * GPB + OPB * DCH) {}
+    __device__ int oK() const { return QPB; }
+    __device__ int oV() const { return QPB + nK; }
+    __device__ int oO() const { return QPB + 2 * nK; }
+    __device__ int oG() const { return QPB + 2 * nK + OPB; }
+    __device__ int oD() const { return QPB + 2 * nK + OPB + 2 * GPB; }
+};
+
+// Stream wave j (0 .. NL-1): chunks g = j, j + NL, ... of the whole step, in order.
+template <int QPB, int GPB, int DCH>
+__device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const DevLayer *lay, unsigned char *ring,
+                            unsigned *ready, const unsigned *done, unsigned *abt, int j, int ag, int j0, int j1) {
+    constexpr int IM = GPB * NB;
+    const int lane = tid_now() & 63, b = blockIdx.x;
+    const unsigned total = (unsigned)A.n_layers * (unsigned)S.cpl;
+    auto publish = [&](unsigned g) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(ready + g % NS, g / NS + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    // n: own chunks issued; pub: own chunks published (chunk k of this wave is g = j + NL k)
+    unsigned n = 0, pub = 0;
+    for (unsigned g = j; g < total; g += NL) {
+        const int l = (int)(g / (unsigned)S.cpl), idx = (int)(g - (unsigned)l * (unsigned)S.cpl);
+        const DevLayer &L = lay[l];
+        // the lane's source address for each of the chunk's four 1 KB pieces
+        const unsigned char *src[4];
+        if (idx < S.oK() || idx >= S.oO()) {
+            const unsigned char *base;
+            if (idx < S.oK()) {
+                base = (const unsigned char *)opaque(L.qkv) + ((size_t)b * QPB + idx) * CHB;
+            } else if (idx < S.oG()) {
+                base = (const unsigned char *)opaque(L.o) + ((size_t)b * S.OPB + (idx - S.oO())) * CHB;
+            } else if (idx < S.oD()) {
+                const int i = idx - S.oG();
+                base = (const unsigned char *)opaque(L.gu) + ((size_t)((i & 1) ? IM : 0) + (size_t)b * GPB + (i >> 1)) * CHB;
+            } else {
+                const int i = idx - S.oD();
+                base = (const unsigned char *)opaque(L.down) + ((size_t)b * S.OPB + i / DCH) * ((size_t)IM * 2) +
+                       (size_t)(i % DCH) * CHB;
+            }
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-        const float v = hs[threadIdx.x + NT * k];
-        ss += v * v;
-    }
-    const float r = 1.0f / sqrtf(bsum(ss, red) / (float)(NT * NPT) + eps);
+            for (int k = 0; k < 4; ++k) src[k] = base + k * 1024 + lane * 16;
+        } else {
+            const bool isV = idx >= S.oV();
+            const int i = idx - (isV ? S.oV() : S.oK());
+            const bf16 *cache = (isV ? opaque(A.vc) : opaque(A.kc)) + ((size_t)l * A.KV + ag) * A.cap * D;
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-        const int i = threadIdx.x + NT * k;
-        ys[i] = (uint16_t)f2bf_bits(to_f(w[i]) * rho<bf16>(hs[i] * r));
+            for (int k = 0; k < 4; ++k) {
+                // keys past the split's end (a partial last chunk) re-read its last key
+                const int key = min(j0 + i * KPC + 4 * k + lane / 16, j1 - 1);
+                src[k] = (const unsigned char *)(cache + (size_t)key * D) + (lane % 16) * 16;
+            }
+        }
+        const unsigned s = g % NS, gen = g / NS;
+        if (lds_acquire(done + s) < gen) {
+            // The ring is full: the compute waves still read the slot's previous chunk.  Land
+            // and publish everything in flight first (nothing else can be issued meanwhile),
+            // so the compute waves see the whole ring, then wait for the slot.
+            wait_vm<0>();
+            for (; pub < n; ++pub) publish(j + NL * pub);
+            lds_wait_ge(done + s, gen, abt, nullptr);
+        }
+        unsigned char *dst = ring + (size_t)s * CHB;
+        const unsigned dlds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dma16(src[k], dlds + k * 1024);
+        ++n;
+        if (n - pub >= DL) {
+            wait_vm<4 * (DL - 1)>();  // all but this wave's last DL-1 chunks have landed
+            for (; pub + (DL - 1) < n; ++pub) publish(j + NL * pub);
+        }
     }
+    wait_vm<0>();
+    for (; pub < n; ++pub) publish(j + NL * pub);
 }
 
-// Weight-row prefetch: row `row` of a [rows][64*8*CH] bf16 matrix, CH 16-byte chunks per lane.
-template <int CH>
-__device__ __forceinline__ void ld_row(const bf16 *__restrict__ W, size_t row, int K, u32x4 *r) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) r[c] = ld_stream(W + row * K + (size_t)(lane + 64 * c) * 8);
-}
-// Dot of a prefetched row with the LDS activation ys (bf16 bits), summed over the wave.
-template <int CH>
-__device__ __forceinline__ float dot_row(const u32x4 *r, const uint16_t *ys) {
-    const int lane = threadIdx.x & 63;
-    float a = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        float w[8], x[8];
-        Vec<bf16>::expand(r[c], w);
-        Vec<bf16>::expand(*(const u32x4 *)&ys[(lane + 64 * c) * 8], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a += w[e] * x[e];
-    }
-    return wave_sum(a);
-}
-
-// HCH: 16-byte chunks per lane of a hidden-size row (hidden = 512 * HCH); ICH likewise for
-// an intermediate-size row; QR q|k|v rows, UR gate/up pairs per wave; G query heads per kv head.
-template <int HCH, int ICH, int G, int QR, int UR>
-__global__ void __launch_bounds__(NT) decode_mk_kernel(Args A) {
-    constexpr int HID = 512 * HCH, IM = 512 * ICH;
-    constexpr int HPT = HID / NT, IPT = IM / NT;  // words per thread of a hidden / intermediate vector
-    constexpr int XMAX = HID > IM ? HID : IM;
-    __shared__ float hs[HID];                       // this block's copy of the residual stream h
-    __shared__ __attribute__((aligned(16))) uint16_t ys[XMAX];  // current projection input (bf16 bits)
+// ---------------------------------------------------------------- the kernel
+// QPB q|k|v rows and GPB gate/up pairs per block; DCH chunks per down row; G query heads
+// per kv head.
+template <int QPB, int GPB, int DCH, int G>
+__global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
+    constexpr int IM = GPB * NB;
+    constexpr int HPT = HID / NCT, IPT = IM / NCT;  // words per compute thread of a hidden / intermediate vector
+    constexpr int OPB = HID / NB;
+    constexpr int RSH = rep_stride(HID), RSM = rep_stride(IM);
+    static_assert(IM * 2 == DCH * CHB && HID % NCT == 0 && IM % NCT == 0 && OPB == NC, "shape");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[NS * CHB];
+    __shared__ unsigned ready[NS], done[NS], bar, abt;
+    __shared__ DevLayer lay[MAXL];
+    __shared__ float hs[HID];                                 // residual stream h (fp32 of bf16 values)
+    __shared__ __attribute__((aligned(16))) uint16_t ys[IM];  // current projection input (bf16 bits)
     __shared__ __attribute__((aligned(16))) uint16_t qraw[G * D + 2 * D];
     __shared__ float qs[G * D], kvs[2 * D];
     __shared__ float sc[G * CHUNK_MAX];
-    __shared__ float red[NWB * G * D];
-    __shared__ float mrow[G], lrow[G], rsum[NWB];
+    __shared__ float red[NC * G * D];
+    __shared__ float rsum[2][NC];
+    __shared__ float mrow[G], lrow[G];
     __shared__ float pm[NSPLIT_MAX], pl[NSPLIT_MAX];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
-    const int gw = b * NWB + wave;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), b = blockIdx.x;
     const int H = A.H, KV = A.KV;
     const int p = A.p, nkeys = p + 1;
-    const unsigned tag0 = A.ctr[0] * 64u;
-    const int bpg = NB / KV;                 // attention blocks per kv head (= splits)
-    const int ag = b / bpg, as = b % bpg;    // this block's (kv head, split)
+    const int bpg = NB / KV;               // attention blocks per kv head (= splits)
+    const int ag = b / bpg, as = b % bpg;  // this block's (kv head, split)
     const int j0 = as * A.chunk, j1 = min(nkeys, j0 + A.chunk);
+    const int nK = j0 < j1 ? (j1 - j0 + KPC - 1) / KPC : 0;
     const bool has_p = j0 < nkeys && j1 == nkeys;
-    const int dpb = H * D / NB;              // merged attention outputs per block
-    const int mh = b / (NB / H), md0 = (b % (NB / H)) * dpb;
+    const Seq<QPB, GPB, DCH> S(nK);
 
-    for (int k = 0; k < HPT; ++k) hs[tid + NT * k] = to_f(A.x[tid + NT * k]);
+    for (int i = tid; i < NS; i += NTH) {
+        ready[i] = 0;
+        done[i] = 0;
+    }
+    if (tid == 0) {
+        bar = 0;
+        abt = 0;
+    }
+    for (int i = tid; i < A.n_layers; i += NTH) lay[i] = A.layers[i];
+    const unsigned tag0 = A.ctr[0] * 64u;
+    __syncthreads();  // the only barrier of the whole block; the roles split here
 
-    u32x4 wq[QR][HCH];  // next q|k|v rows (loop-carried across layers)
-    {
-        const DevLayer L0 = A.layers[0];
-#pragma unroll
-        for (int r = 0; r < QR; ++r) ld_row<HCH>(L0.qkv, (size_t)gw * QR + r, HID, wq[r]);
+    if (wave >= NC) {
+        stream_wave<QPB, GPB, DCH>(A, S, lay, ring, ready, done, &abt, wave - NC, ag, j0, j1);
+        return;
     }
 
+    // ================================================================ compute waves
+    unsigned ep = 0, par = 0;
+    const int dpb = H * D / NB;  // merged attention outputs per block
+    const int mh = b / (NB / H), md0 = (b % (NB / H)) * dpb;
+    constexpr int half = D / 2;
+    const int jspec = has_p ? p : -1;              // the new key, taken from LDS
+
+    const int lane0 = tid & 63;
+    for (int k = 0; k < HPT; ++k) hs[tid + NCT * k] = to_f(opaque(A.x)[tid + NCT * k]);
+    // per-layer vectors of this thread, loaded a step ahead of their use
+    float w_in[HPT], w_post[HPT], w_qn[2], w_kn[2];
+    const float c1 = to_f(opaque(A.cos_t)[(size_t)p * D + lane0]), s1 = to_f(opaque(A.sin_t)[(size_t)p * D + lane0]);
+    const float c2 = to_f(opaque(A.cos_t)[(size_t)p * D + lane0 + half]);
+    const float s2 = to_f(opaque(A.sin_t)[(size_t)p * D + lane0 + half]);
+    auto load_small = [&](int l) {
+        const DevLayer &L = lay[l];
+        const int tid = tid_now(), lane = tid & 63;
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) {
+            w_in[k] = to_f(opaque(L.in_norm)[tid + NCT * k]);
+            w_post[k] = to_f(opaque(L.post_norm)[tid + NCT * k]);
+        }
+        w_qn[0] = to_f(opaque(L.q_norm)[lane]);
+        w_qn[1] = to_f(opaque(L.q_norm)[lane + half]);
+        w_kn[0] = to_f(opaque(L.k_norm)[lane]);
+        w_kn[1] = to_f(opaque(L.k_norm)[lane + half]);
+    };
+    load_small(0);
+
     for (int l = 0; l < A.n_layers; ++l) {
-        const DevLayer L = A.layers[l];
+        const int tid = tid_now(), lane = tid & 63;
+        const int sub = lane % 16, kslot = lane / 16;  // K/V pieces: 16 lanes per 128-dim key row
         const unsigned tag = (tag0 + (unsigned)l) & 0xffffu;
         const unsigned ptag = (tag0 + (unsigned)l - 1u) & 0xffffu;
-        bf16 *Kg = A.kc + ((size_t)l * KV + ag) * A.cap * D;
-        bf16 *Vg = A.vc + ((size_t)l * KV + ag) * A.cap * D;
+        const unsigned gb = (unsigned)l * (unsigned)S.cpl;
+        bf16 *Kg = opaque(A.kc) + ((size_t)l * KV + ag) * A.cap * D;
+        bf16 *Vg = opaque(A.vc) + ((size_t)l * KV + ag) * A.cap * D;
 
         // ---------------- step 1: h = rho(h + pend); y = RMSNorm(h); q|k|v rows
-        u32x4 kp[DEC_PF], vp[DEC_PF];
-        decode_prefetch<bf16, D, NWB>(Kg, Vg, j0, j1, kp, vp);
+        cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave is done reading ys (the previous layer's down rows)
         if (l > 0) {
-            poll_bf16<HPT>(A.x_pend, HID, ptag, ys, A.err);
-            __syncthreads();
-            for (int k = 0; k < HPT; ++k) {
-                const int i = tid + NT * k;
+            poll_bf16<HPT>(opaque(A.x_pend) + (b % NREP) * RSH, HID, ptag, ys, opaque(A.err), &abt, tid);
+#pragma unroll
+            for (int k = 0; k < HPT; ++k) {  // a thread's own elements only: no barrier needed
+                const int i = tid + NCT * k;
                 hs[i] = rho<bf16>(hs[i] + bfv(ys[i]));
             }
-            __syncthreads();
         }
-        rmsnorm_lds<HPT>(hs, L.in_norm, A.eps, ys, rsum);
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < QR; ++r) {
-            const float acc = dot_row<HCH>(wq[r], ys);
-            if (lane == 0) xstore(A.x_qkv + (size_t)gw * QR + r, tagw(tag, acc));
-        }
-
-        step_fence();
-        // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
-        u32x4 wo[HCH];
-        ld_row<HCH>(L.o, (size_t)gw, HID, wo);
-        poll_bf16<(G * D + NT - 1) / NT>(A.x_qkv + (size_t)ag * G * D, G * D, tag, qraw, A.err);
-        if (has_p) {
-            poll_bf16<1>(A.x_qkv + (size_t)(H + ag) * D, D, tag, qraw + G * D, A.err);
-            poll_bf16<1>(A.x_qkv + (size_t)(H + KV + ag) * D, D, tag, qraw + G * D + D, A.err);
-        }
-        __syncthreads();
         {
-            constexpr int half = D / 2;
-            const int nheads = G + (has_p ? 1 : 0);
-            for (int hh = wave; hh < nheads; hh += NWB) {
-                const bool is_q = hh < G;
-                const uint16_t *row = qraw + hh * D;
-                const bf16 *wn = is_q ? L.q_norm : L.k_norm;
-                const float x1 = bfv(row[lane]), x2 = bfv(row[lane + half]);
-                const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + A.eps);
-                const float n1 = rho<bf16>(to_f(wn[lane]) * rho<bf16>(x1 * r));
-                const float n2 = rho<bf16>(to_f(wn[lane + half]) * rho<bf16>(x2 * r));
-                const float c1 = to_f(A.cos_t[(size_t)p * D + lane]), s1 = to_f(A.sin_t[(size_t)p * D + lane]);
-                const float c2 = to_f(A.cos_t[(size_t)p * D + lane + half]);
-                const float s2 = to_f(A.sin_t[(size_t)p * D + lane + half]);
-                const float o1 = rho<bf16>(n1 * c1 - n2 * s1), o2 = rho<bf16>(n2 * c2 + n1 * s2);
-                if (is_q) {
-                    qs[hh * D + lane] = o1;
-                    qs[hh * D + lane + half] = o2;
-                } else {
-                    kvs[lane] = o1;
-                    kvs[lane + half] = o2;
-                    Kg[(size_t)p * D + lane] = from_f<bf16>(o1);
-                    Kg[(size_t)p * D + lane + half] = from_f<bf16>(o2);
-                    const uint16_t *vr = qraw + (G + 1) * D;
-                    Vg[(size_t)p * D + lane] = bf16{vr[lane]};
-                    Vg[(size_t)p * D + lane + half] = bf16{vr[lane + half]};
-                    kvs[D + lane] = bfv(vr[lane]);
-                    kvs[D + lane + half] = bfv(vr[lane + half]);
-                }
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < HPT; ++k) ss += hs[tid + NCT * k] * hs[tid + NCT * k];
+            const float r = 1.0f / sqrtf(csum(ss, rsum, par, &bar, ep, &abt, opaque(A.err), tid) / (float)HID + A.eps);
+#pragma unroll
+            for (int k = 0; k < HPT; ++k) {
+                const int i = tid + NCT * k;
+                ys[i] = (uint16_t)f2bf_bits(w_in[k] * rho<bf16>(hs[i] * r));
             }
         }
-        __syncthreads();
-        if (j0 < nkeys) {
-            decode_core_lds<bf16, D, G, NWB>(qs, Kg, Vg, kp, vp, j0, j1, has_p ? p : -1, kvs, kvs + D, A.scale, sc,
-                                             A.chunk, red, mrow, lrow);
-            for (int idx = tid; idx < G * D; idx += NT) {
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        const X4 xq = load_x(ys, lane);
+        for (int i = wave; i < QPB; i += NC) {
+            const unsigned g = gb + i;
+            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+            const float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
+            chunk_put(done, g, lane);
+            if (lane == 0) xstore(opaque(A.x_qkv) + (size_t)b * QPB + i, tagw(tag, acc));
+        }
+
+        // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
+        if (nK > 0) {
+            poll_bf16<(G * D + NCT - 1) / NCT>(opaque(A.x_qkv) + (size_t)ag * G * D, G * D, tag, qraw, opaque(A.err), &abt, tid);
+            if (has_p) {
+                poll_bf16<1>(opaque(A.x_qkv) + (size_t)(H + ag) * D, D, tag, qraw + G * D, opaque(A.err), &abt, tid);
+                poll_bf16<1>(opaque(A.x_qkv) + (size_t)(H + KV + ag) * D, D, tag, qraw + G * D + D, opaque(A.err), &abt, tid);
+            }
+        }
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        if (nK > 0 && wave < G + (has_p ? 1 : 0)) {
+            const int hh = wave;
+            const bool is_q = hh < G;
+            const uint16_t *row = qraw + hh * D;
+            const float x1 = bfv(row[lane]), x2 = bfv(row[lane + half]);
+            const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + A.eps);
+            const float wn1 = is_q ? w_qn[0] : w_kn[0], wn2 = is_q ? w_qn[1] : w_kn[1];
+            const float n1 = rho<bf16>(wn1 * rho<bf16>(x1 * r));
+            const float n2 = rho<bf16>(wn2 * rho<bf16>(x2 * r));
+            const float o1 = rho<bf16>(n1 * c1 - n2 * s1), o2 = rho<bf16>(n2 * c2 + n1 * s2);
+            if (is_q) {
+                qs[hh * D + lane] = o1;
+                qs[hh * D + lane + half] = o2;
+            } else {
+                kvs[lane] = o1;
+                kvs[lane + half] = o2;
+                Kg[(size_t)p * D + lane] = from_f<bf16>(o1);
+                Kg[(size_t)p * D + lane + half] = from_f<bf16>(o2);
+                const uint16_t *vr = qraw + (G + 1) * D;
+                Vg[(size_t)p * D + lane] = bf16{vr[lane]};
+                Vg[(size_t)p * D + lane + half] = bf16{vr[lane + half]};
+                kvs[D + lane] = bfv(vr[lane]);
+                kvs[D + lane + half] = bfv(vr[lane + half]);
+            }
+        }
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        if (nK > 0) {
+            // scores; K chunk i holds keys j0 + KPC*i ..; the lane's piece k is key 4k + kslot,
+            // dims sub*8 .. sub*8+7
+            float qf[G][8];
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[h][e] = qs[h * D + sub * 8 + e];
+            for (int i = wave; i < nK; i += NC) {
+                const unsigned g = gb + S.oK() + i;
+                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+                u32x4 kr[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) kr[k] = *(const u32x4 *)(c + k * 1024 + lane * 16);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = j0 + i * KPC + 4 * k + kslot;
+                    float kf[8];
+                    Vec<bf16>::expand(kr[k], kf);
+                    if (j == jspec) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) kf[e] = kvs[sub * 8 + e];
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s += qf[h][e] * kf[e];
+                        s = row16_sum(s);  // the key's 16 lanes form one DPP row
+                        if (sub == 0 && j < j1) sc[h * CHUNK_MAX + (j - j0)] = s * A.scale;
+                    }
+                }
+                chunk_put(done, g, lane);
+            }
+        }
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        const int nj = j1 - j0;
+        if (nK > 0 && wave < G) {
+            float m = -INFINITY;
+            for (int j = lane; j < nj; j += 64) m = fmaxf(m, sc[wave * CHUNK_MAX + j]);
+            m = wave_max(m);
+            float ls = 0.f;
+            for (int j = lane; j < nj; j += 64) {
+                const float e = __expf(sc[wave * CHUNK_MAX + j] - m);
+                sc[wave * CHUNK_MAX + j] = e;
+                ls += e;
+            }
+            ls = wave_sum(ls);
+            if (lane == 0) {
+                mrow[wave] = m;
+                lrow[wave] = ls;
+            }
+        }
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        if (nK > 0) {
+            // p . V: lane l owns dims 2l, 2l+1 of every key (no cross-lane reduction); the
+            // probabilities are LDS broadcasts
+            float o[G][2];
+#pragma unroll
+            for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
+            const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
+            for (int i = wave; i < nK; i += NC) {
+                const unsigned g = gb + S.oV() + i;
+                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+                const int jb = j0 + i * KPC;
+                // all KPC rows are read (rows past the split's end hold a copy of its last key
+                // and get probability 0); reads first, then the arithmetic
+                uint32_t vw[KPC];
+                float pe[G][KPC];
+#pragma unroll
+                for (int kk = 0; kk < KPC; ++kk) vw[kk] = *(const uint32_t *)(c + kk * (D * 2) + lane * 4);
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int kk = 0; kk < KPC; ++kk)
+                        pe[h][kk] = jb + kk < j1 ? sc[h * CHUNK_MAX + (jb + kk - j0)] : 0.f;
+#pragma unroll
+                for (int kk = 0; kk < KPC; ++kk) {
+                    float v0 = bf_lo(vw[kk]), v1 = bf_hi(vw[kk]);
+                    if (jb + kk == jspec) {
+                        v0 = vs0;
+                        v1 = vs1;
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        o[h][0] += pe[h][kk] * v0;
+                        o[h][1] += pe[h][kk] * v1;
+                    }
+                }
+                chunk_put(done, g, lane);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                red[(wave * G + h) * D + 2 * lane] = o[h][0];
+                red[(wave * G + h) * D + 2 * lane + 1] = o[h][1];
+            }
+        }
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        if (nK > 0) {
+            for (int idx = tid; idx < G * D; idx += NCT) {
                 const int i = idx / D, d = idx % D;
-                const float v = decode_core_reduce<D, G, NWB>(red, i, d);
-                xstore64(A.x_part + ((size_t)(ag * G + i) * A.nsplit + as) * (D + 2) + 2 + d,
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < NC; ++w) v += red[(w * G + i) * D + d];
+                xstore64(opaque(A.x_part) + ((size_t)(ag * G + i) * A.nsplit + as) * (D + 2) + 2 + d,
                          ((uint64_t)tag << 32) | __float_as_uint(v));
             }
             if (tid < G) {
-                uint64_t *pp = A.x_part + ((size_t)(ag * G + tid) * A.nsplit + as) * (D + 2);
+                uint64_t *pp = opaque(A.x_part) + ((size_t)(ag * G + tid) * A.nsplit + as) * (D + 2);
                 xstore64(pp, ((uint64_t)tag << 32) | __float_as_uint(mrow[tid]));
                 xstore64(pp + 1, ((uint64_t)tag << 32) | __float_as_uint(lrow[tid]));
             }
         } else {  // an empty split (fewer keys than splits): max -inf, sum 0
-            for (int idx = tid; idx < G * (D + 2); idx += NT) {
+            for (int idx = tid; idx < G * (D + 2); idx += NCT) {
                 const int i = idx / (D + 2), e = idx % (D + 2);
                 const float v = e == 0 ? -INFINITY : 0.f;
-                xstore64(A.x_part + ((size_t)(ag * G + i) * A.nsplit + as) * (D + 2) + e,
+                xstore64(opaque(A.x_part) + ((size_t)(ag * G + i) * A.nsplit + as) * (D + 2) + e,
                          ((uint64_t)tag << 32) | __float_as_uint(v));
             }
         }
 
-        step_fence();
         // ---------------- step 3: merge the splits of (head mh, dims md0 .. md0 + dpb)
-        u32x4 wg[UR][HCH], wu[UR][HCH];
-#pragma unroll
-        for (int r = 0; r < UR; ++r) {
-            ld_row<HCH>(L.gu, (size_t)gw * UR + r, HID, wg[r]);
-            ld_row<HCH>(L.gu, (size_t)IM + gw * UR + r, HID, wu[r]);
-        }
-        __syncthreads();  // step 2's reads of red are finished before it becomes the merge buffer
+        cbar(&bar, ep, &abt, opaque(A.err), lane);  // red has been read before it becomes the merge buffer
         {
             const int ns = A.nsplit;
             const int nwords = ns * (2 + dpb);
             float *po = red;  // [ns][dpb]
-            for (int t = tid; t < nwords; t += NT) {
+            for (int t = tid; t < nwords; t += NCT) {
                 const uint64_t *src;
-                if (t < 2 * ns) src = A.x_part + ((size_t)mh * ns + t / 2) * (D + 2) + (t % 2);
+                if (t < 2 * ns) src = opaque(A.x_part) + ((size_t)mh * ns + t / 2) * (D + 2) + (t % 2);
                 else {
                     const int u = t - 2 * ns;
-                    src = A.x_part + ((size_t)mh * ns + u / dpb) * (D + 2) + 2 + md0 + u % dpb;
+                    src = opaque(A.x_part) + ((size_t)mh * ns + u / dpb) * (D + 2) + 2 + md0 + u % dpb;
                 }
                 uint64_t v = xload64(src);
                 long sp = 0;
                 while ((unsigned)(v >> 32) != tag) {
-                    if (spin_out(++sp, A.err)) break;
+                    if (spin_out(++sp, opaque(A.err), &abt)) break;
                     v = xload64(src);
                 }
                 const float f = __uint_as_float((uint32_t)v);
@@ -337,7 +669,7 @@ __global__ void __launch_bounds__(NT) decode_mk_kernel(Args A) {
                     po[t - 2 * ns] = f;
                 }
             }
-            __syncthreads();
+            cbar(&bar, ep, &abt, opaque(A.err), lane);
             if (tid < dpb) {
                 float M = -INFINITY;
                 for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s]);
@@ -347,70 +679,94 @@ __global__ void __launch_bounds__(NT) decode_mk_kernel(Args A) {
                     Ls += pl[s] * f;
                     acc += po[s * dpb + tid] * f;
                 }
-                xstore(A.x_a + (size_t)mh * D + md0 + tid, tagw(tag, acc / Ls));
+                const uint32_t w = tagw(tag, acc / Ls);
+#pragma unroll
+                for (int r = 0; r < NREP; ++r) xstore(opaque(A.x_a) + r * RSH + mh * D + md0 + tid, w);
             }
         }
 
-        step_fence();
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row
-        poll_bf16<HPT>(A.x_a, HID, tag, ys, A.err);
-        __syncthreads();
+        poll_bf16<HPT>(opaque(A.x_a) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
         {
-            const float acc = dot_row<HCH>(wo, ys);
-            if (lane == 0) xstore(A.x_h2 + gw, tagw(tag, hs[gw] + rho<bf16>(acc)));
+            const unsigned g = gb + S.oO() + wave;
+            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+            const float acc = wave_sum(dot_chunk(c, load_x(ys, lane), lane, 0.f));
+            chunk_put(done, g, lane);
+            const int row = b * OPB + wave;
+            if (lane < NREP) xstore(opaque(A.x_h2) + lane * RSH + row, tagw(tag, hs[row] + rho<bf16>(acc)));
         }
 
-        step_fence();
-        // ---------------- step 5: y2 = RMSNorm(h); gate|up rows + SwiGLU
-        __syncthreads();  // every wave has read hs for its residual before it is replaced
-        poll_bf16<HPT>(A.x_h2, HID, tag, ys, A.err);
-        __syncthreads();
-        for (int k = 0; k < HPT; ++k) hs[tid + NT * k] = bfv(ys[tid + NT * k]);
-        __syncthreads();
-        rmsnorm_lds<HPT>(hs, L.post_norm, A.eps, ys, rsum);
-        __syncthreads();
+        // ---------------- step 5: y2 = RMSNorm(h); gate|up row pairs + SwiGLU
+        cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave has read ys and hs before they are replaced
+        poll_bf16<HPT>(opaque(A.x_h2) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
+        {
+            float ss = 0.f;
 #pragma unroll
-        for (int r = 0; r < UR; ++r) {
-            const float g = dot_row<HCH>(wg[r], ys);
-            const float u = dot_row<HCH>(wu[r], ys);
-            if (lane == 0)
-                xstore(A.x_m + (size_t)gw * UR + r, tagw(tag, rho<bf16>(silu_f32(rho<bf16>(g))) * rho<bf16>(u)));
+            for (int k = 0; k < HPT; ++k) {
+                const int i = tid + NCT * k;
+                const float v = bfv(ys[i]);
+                hs[i] = v;
+                ss += v * v;
+            }
+            const float r = 1.0f / sqrtf(csum(ss, rsum, par, &bar, ep, &abt, opaque(A.err), tid) / (float)HID + A.eps);
+#pragma unroll
+            for (int k = 0; k < HPT; ++k) {
+                const int i = tid + NCT * k;
+                ys[i] = (uint16_t)f2bf_bits(w_post[k] * rho<bf16>(hs[i] * r));
+            }
+        }
+        if (l + 1 < A.n_layers) load_small(l + 1);
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
+        const X4 xg = load_x(ys, lane);
+        for (int i = wave; i < GPB; i += NC) {
+            const unsigned g = gb + S.oG() + 2 * i;
+            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+            const float gs = wave_sum(dot_chunk(c, xg, lane, 0.f));
+            chunk_put(done, g, lane);
+            const unsigned char *cu = chunk_get(ring, ready, g + 1, &abt, opaque(A.err));
+            const float us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
+            chunk_put(done, g + 1, lane);
+            if (lane < NREP)
+                xstore(opaque(A.x_m) + lane * RSM + b * GPB + i,
+                       tagw(tag, rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us)));
         }
 
-        step_fence();
         // ---------------- step 6: pend = rho(m . Wdown^T) for this wave's row
-        u32x4 wd[ICH];
-        ld_row<ICH>(L.down, (size_t)gw, IM, wd);
-        if (l + 1 < A.n_layers) {
-            const DevLayer Ln = A.layers[l + 1];
-#pragma unroll
-            for (int r = 0; r < QR; ++r) ld_row<HCH>(Ln.qkv, (size_t)gw * QR + r, HID, wq[r]);
-        }
-        __syncthreads();  // ys (y2) fully consumed before it receives m
-        poll_bf16<IPT>(A.x_m, IM, tag, ys, A.err);
-        __syncthreads();
+        cbar(&bar, ep, &abt, opaque(A.err), lane);  // ys (y2) fully consumed before it receives m
+        poll_bf16<IPT>(opaque(A.x_m) + (b % NREP) * RSM, IM, tag, ys, opaque(A.err), &abt, tid);
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
         {
-            const float acc = dot_row<ICH>(wd, ys);
-            if (lane == 0) xstore(A.x_pend + gw, tagw(tag, acc));
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < DCH; ++q) {
+                const unsigned g = gb + S.oD() + wave * DCH + q;
+                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+                a = dot_chunk(c, load_x(ys + q * HID, lane), lane, a);
+                chunk_put(done, g, lane);
+            }
+            const float acc = wave_sum(a);
+            if (lane < NREP) xstore(opaque(A.x_pend) + lane * RSH + b * OPB + wave, tagw(tag, acc));
         }
-        __syncthreads();
     }
 
     // ---------------- out = RMSNorm(rho(h + pend), final_norm) (block 0), then advance the counter
     if (b == 0) {
         const unsigned ltag = (tag0 + (unsigned)A.n_layers - 1u) & 0xffffu;
-        poll_bf16<HPT>(A.x_pend, HID, ltag, ys, A.err);
-        __syncthreads();
+        cbar(&bar, ep, &abt, opaque(A.err), lane0);
+        poll_bf16<HPT>(opaque(A.x_pend) + (b % NREP) * RSH, HID, ltag, ys, opaque(A.err), &abt, tid);
+        float ss = 0.f;
+#pragma unroll
         for (int k = 0; k < HPT; ++k) {
-            const int i = tid + NT * k;
+            const int i = tid + NCT * k;
             hs[i] = rho<bf16>(hs[i] + bfv(ys[i]));
+            ss += hs[i] * hs[i];
         }
-        __syncthreads();
-        rmsnorm_lds<HPT>(hs, A.final_norm, A.eps, ys, rsum);
-        __syncthreads();
+        const float r = 1.0f / sqrtf(csum(ss, rsum, par, &bar, ep, &abt, opaque(A.err), tid) / (float)HID + A.eps);
+#pragma unroll
         for (int k = 0; k < HPT; ++k) {
-            const int i = tid + NT * k;
-            A.out[i] = bf16{ys[i]};
+            const int i = tid + NCT * k;
+            opaque(A.out)[i] = bf16{(uint16_t)f2bf_bits(to_f(opaque(A.final_norm)[i]) * rho<bf16>(hs[i] * r))};
         }
         if (tid == 0) __hip_atomic_store(A.ctr, tag0 / 64u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -423,8 +779,9 @@ size_t decode_mk_workspace(int n_layers, int H, int KV, int hid, int I) {
     const size_t nsplit = mk::NB / (KV > 0 ? KV : 1);
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const size_t nqkv = (size_t)(H + 2 * KV) * mk::D;
-    return al(sizeof(mk::DevLayer) * n_layers) + al(nqkv * 4) + al((size_t)H * mk::D * 4) + al((size_t)hid * 4) +
-           al((size_t)I * 4) + al((size_t)hid * 4) + al((size_t)H * nsplit * (mk::D + 2) * 8) + al(256);
+    const size_t rh = (size_t)mk::NREP * mk::rep_stride(hid) * 4, rm = (size_t)mk::NREP * mk::rep_stride(I) * 4;
+    return al(sizeof(mk::DevLayer) * n_layers) + al(nqkv * 4) + 3 * al(rh) + al(rm) +
+           al((size_t)H * nsplit * (mk::D + 2) * 8) + al(256);
 }
 
 namespace {
@@ -439,32 +796,39 @@ MkLayout mk_layout(int n_layers, int H, int KV, int hid, int I) {
     size_t o = 0;
     L.layers = o; o += al(sizeof(mk::DevLayer) * n_layers);
     L.qkv = o; o += al(nqkv * 4);
-    L.a = o; o += al((size_t)H * mk::D * 4);
-    L.h2 = o; o += al((size_t)hid * 4);
-    L.m = o; o += al((size_t)I * 4);
-    L.pend = o; o += al((size_t)hid * 4);
+    const size_t rh = (size_t)mk::NREP * mk::rep_stride(hid) * 4, rm = (size_t)mk::NREP * mk::rep_stride(I) * 4;
+    L.a = o; o += al(rh);
+    L.h2 = o; o += al(rh);
+    L.m = o; o += al(rm);
+    L.pend = o; o += al(rh);
     L.part = o; o += al((size_t)H * nsplit * (mk::D + 2) * 8);
     L.ctr = o;
     return L;
 }
 
-template <int HCH, int ICH, int G, int QR, int UR> const void *mk_fn() {
-    return (const void *)mk::decode_mk_kernel<HCH, ICH, G, QR, UR>;
+template <int QPB, int GPB, int DCH, int G> const void *mk_fn() {
+    return (const void *)mk::decode_mk_kernel<QPB, GPB, DCH, G>;
 }
 
 const void *mk_select(int hid, int I, int G, int nqkv) {
-    if (hid == 2048 && I == 6144 && nqkv == 4096 && G == 2) return mk_fn<4, 12, 2, 2, 3>();
+    if (hid == 2048 && I == 6144 && nqkv == 4096 && G == 2) return mk_fn<16, 24, 3, 2>();
     return nullptr;
+}
+
+int mk_chunk(int nkeys, int nsplit) {  // keys per split, a multiple of a K/V chunk's keys
+    const int c = (nkeys + nsplit - 1) / nsplit;
+    return (c + mk::KPC - 1) / mk::KPC * mk::KPC;
 }
 }  // namespace
 
-bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I, int cap) {
+bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I,
+                         int cap) {
     if (dt != DT_BF16 || n_experts > 0 || quant_bits != 0 || D != mk::D) return false;
-    if (n_layers < 1 || n_layers > 63) return false;  // tags are call * 64 + layer
-    if (H % KV || mk::NB % KV || (H * D) != hid || hid != mk::NW || (H * D) % mk::NB) return false;
+    if (n_layers < 1 || n_layers > mk::MAXL) return false;  // tags are call * 64 + layer
+    if (hid != mk::HID || H * D != hid || H % KV || mk::NB % KV || mk::NB % H) return false;
     const int nsplit = mk::NB / KV;
-    if (nsplit > mk::NSPLIT_MAX || (cap + nsplit - 1) / nsplit > mk::CHUNK_MAX) return false;
-    if (nsplit * (2 + H * D / mk::NB) > mk::NWB * (H / KV) * mk::D) return false;  // merge buffer fits in LDS
+    if (nsplit > mk::NSPLIT_MAX || mk_chunk(cap, nsplit) > mk::CHUNK_MAX) return false;
+    if (nsplit * (2 + H * D / mk::NB) > mk::NC * (H / KV) * mk::D) return false;  // merge buffer fits in LDS
     return mk_select(hid, I, H / KV, (H + 2 * KV) * D) != nullptr;
 }
 
@@ -487,6 +851,9 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
     const MkLayout L = mk_layout(n_layers, H, KV, hid, I);
     char *b = (char *)ws;
     const int nsplit = mk::NB / KV;
+    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
+    if (!fn || p < 0 || p >= cap || n_layers < 1 || n_layers > mk::MAXL || mk_chunk(p + 1, nsplit) > mk::CHUNK_MAX)
+        return hipErrorInvalidValue;
     mk::Args A;
     A.layers = (const mk::DevLayer *)(b + L.layers);
     A.n_layers = n_layers;
@@ -495,7 +862,7 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
     A.cap = cap;
     A.p = p;
     A.nsplit = nsplit;
-    A.chunk = (p + 1 + nsplit - 1) / nsplit;
+    A.chunk = mk_chunk(p + 1, nsplit);
     A.eps = eps;
     A.scale = (float)(1.0 / sqrt((double)mk::D));
     A.x = (const bf16 *)x;
@@ -513,23 +880,21 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
     A.x_part = (uint64_t *)(b + L.part);
     A.ctr = (unsigned *)(b + L.ctr);
     A.err = err;
-    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
-    if (!fn) return hipErrorInvalidValue;
     void *args[] = {&A};
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(s, &cs);
     if (e != hipSuccess) return e;
     if (cs == hipStreamCaptureStatusNone)
-        return hipLaunchCooperativeKernel(fn, dim3(mk::NB), dim3(mk::NT), args, 0, s);
+        return hipLaunchCooperativeKernel(fn, dim3(mk::NB), dim3(mk::NTH), args, 0, s);
     // graph capture: a plain launch (the grid is one block per CU and fits the device at once)
-    return hipLaunchKernel(fn, dim3(mk::NB), dim3(mk::NT), args, 0, s);
+    return hipLaunchKernel(fn, dim3(mk::NB), dim3(mk::NTH), args, 0, s);
 }
 
 int decode_mk_max_blocks(int hid, int I, int H, int KV) {
     const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
     if (!fn) return 0;
     int per_cu = 0, dev = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, mk::NT, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, mk::NTH, 0) != hipSuccess) return 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
