@@ -42,7 +42,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bench(steps: int, warmup: int):
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device-to-device copy of known size (torch's copy kernel), run before the
+    decode leg when hardware counters are collected: its FETCH_SIZE / WRITE_SIZE per dispatch
+    against nbytes gives the counters' scale."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def decode_bench(steps: int, warmup: int, compare: bool = True):
     """Time `steps` replays of one captured decode step (HIP graph on a side stream), then
     `steps` eager steps with HIP events around the dominant kernel's launches on the
     library's stream.  Done for the default T = 1 path (the persistent decode kernel) and,
@@ -111,7 +126,7 @@ def decode_bench(steps: int, warmup: int):
                 "launches": cnt.value}
 
     res = run(0)
-    res["kernels_path"] = run(1) if res["path"] == 2 else None
+    res["kernels_path"] = run(1) if res["path"] == 2 and compare else None
     q3.qwen3_set_decode_path(seat.handle, 0)
     del seat, w, K, V
     torch.cuda.empty_cache()
@@ -190,6 +205,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (for profiling)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the one-kernel-per-step decode path (for profiling)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run a 1 GiB device copy first (hardware-counter scale for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -204,7 +223,9 @@ def main():
         pre = prefill_bench(args.prefill_iters)
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
         return
-    dec = decode_bench(args.steps, args.warmup)
+    if args.copy_calib:
+        copy_calibration()
+    dec = decode_bench(args.steps, args.warmup, compare=not args.no_compare)
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     cpu = None if args.no_cpu else cpu_baseline()
 
