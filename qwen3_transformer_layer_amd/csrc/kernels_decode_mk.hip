@@ -488,10 +488,22 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 
         // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
         if (nK > 0) {
-            poll_bf16<(G * D + NCT - 1) / NCT>(opaque(A.x_qkv) + (size_t)ag * G * D, G * D, tag, qraw, opaque(A.err), &abt, tid);
-            if (has_p) {
-                poll_bf16<1>(opaque(A.x_qkv) + (size_t)(H + ag) * D, D, tag, qraw + G * D, opaque(A.err), &abt, tid);
-                poll_bf16<1>(opaque(A.x_qkv) + (size_t)(H + KV + ag) * D, D, tag, qraw + G * D + D, opaque(A.err), &abt, tid);
+            // the group's q heads, and for the block holding the new key its k and v heads, in
+            // one round of loads (thread t < G*D: q word t; then k words; then v words)
+            static_assert(G * D + 2 * D <= NCT, "one word per thread");
+            const int nw = G * D + (has_p ? 2 * D : 0);
+            if (tid < nw) {
+                const int src = tid < G * D ? ag * G * D + tid
+                                            : (tid < G * D + D ? (H + ag) * D + tid - G * D
+                                                               : (H + KV + ag) * D + tid - G * D - D);
+                const uint32_t *w = opaque(A.x_qkv) + src;
+                uint32_t v = xload(w);
+                long sp = 0;
+                while ((v >> 16) != tag) {
+                    if (spin_out(++sp, opaque(A.err), &abt)) break;
+                    v = xload(w);
+                }
+                qraw[tid] = (uint16_t)(v & 0xffffu);
             }
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
