@@ -72,6 +72,11 @@ size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
 hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
                       const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
+// ---- bf16 projections for M > 16 (kernels_gemm.hip): 3-stage LDS-DMA pipeline, K % 64 == 0
+bool gemm_dma_ok(int M, int K, int N);
+hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, int epi, const void *res, void *out,
+                           hipStream_t s);
+
 // ---- persistent decode step (kernels_decode_mk.hip): dense bf16 stacks of supported shape
 bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I, int cap);
 size_t decode_mk_workspace(int n_layers, int H, int KV, int hid, int I);

@@ -201,43 +201,6 @@ __device__ __forceinline__ void chunk_put(unsigned *done, unsigned g, int lane) 
         __hip_atomic_fetch_add(done + g % NS, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// One 16-byte-per-lane copy from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane i's 16 bytes at g land at LDS byte address lds + 16 i.
-// Written as asm so the compiler does not see an LDS write it cannot place: with the
-// builtin it conservatively waits for every copy in flight before each later LDS access of
-// the stream wave (the ring flags), which would leave one chunk in flight.  The stream wave
-// tracks completion itself with wait_vm.  M0 carries the LDS address; the nop covers the
-// M0-write-to-LDS-DMA hazard.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
-    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-                     : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt at maximum).
-template <int N> __device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Returns p unchanged through an empty asm the compiler cannot see into: addresses derived
-// from it are then computed where they are used instead of being hoisted out of the layer
-// loop and kept live (in registers, or spilled) across every step.  The pointer is
-// wave-uniform (readfirstlane places it in scalar registers) and points to global memory:
-// going through a global-address-space pointer keeps the accesses global, not flat (flat
-// accesses also count against the LDS wait counter).
-template <typename T> __device__ __forceinline__ T *opaque(T *p) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    uint64_t q = ((uint64_t)hi << 32) | lo;
-    __asm__ volatile("" : "+s"(q));
-    typedef __attribute__((address_space(1))) T GT;
-    return (T *)(GT *)q;
-}
-
 __device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
 // A lane's four 16-byte pieces of a 2048-element bf16 vector x in LDS (elements

@@ -12,9 +12,7 @@
 //    column (a gate/up pair for SWIGLU) and streams its weight row with
 //    128-bit non-temporal loads, 4 loads in flight per lane; x is read through
 //    the L1/L2 caches; one wave reduction per output.
-//  - gemm_bf16_kernel: M > 16 in bf16.  MFMA v_mfma_f32_32x32x16_bf16, block
-//    tile 128 x 128 (SWIGLU: 128 rows x 64 gate + 64 up columns), K step 64,
-//    register-staged double buffering through padded LDS.
+//  - M > 16 in bf16: the MFMA GEMM of kernels_gemm.hip.
 //  - gemm_f32_kernel: M > 16 in fp32 (strict mode), LDS-tiled FMA.
 #include "common.h"
 #include "kernels.h"
@@ -204,119 +202,6 @@ hipError_t launch_linear_norm(int dt, const void *h_in, const void *res, const v
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------ bf16 MFMA GEMM
-namespace gemm {
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row pitch in elements (144 B)
-}
-
-// B-tile row r of block nb -> weight row.  SWIGLU tiles pair 64 gate rows with the same 64 up rows.
-template <int EPI> __device__ __forceinline__ int b_row(int nb, int r, int N) {
-    if (EPI == EPI_SWIGLU) return r < 64 ? nb * 64 + r : N + nb * 64 + (r - 64);
-    return nb * gemm::BN + r;
-}
-
-template <int EPI>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16 *__restrict__ A, int M, int K,
-                                                        const bf16 *__restrict__ B, int N,
-                                                        const bf16 *__restrict__ res, bf16 *__restrict__ out) {
-    using namespace gemm;
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, nb = blockIdx.x;
-
-    // global -> register staging: 4 chunks of 16 B per thread for each operand
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * 256, row = cidx >> 3, col = (cidx & 7) * 8;
-            const int gm = m0 + row;
-            ra[i] = gm < M ? ld16(A + (size_t)gm * K + k0 + col) : u32x4{0, 0, 0, 0};
-            const bool bval = EPI == EPI_SWIGLU ? nb * 64 + (row & 63) < N : nb * BN + row < N;
-            rb[i] = bval ? ld_stream(B + (size_t)b_row<EPI>(nb, row, N) * K + k0 + col) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * 256, row = cidx >> 3, col = (cidx & 7) * 8;
-            *(u32x4 *)&As[buf][row * LDK + col] = ra[i];
-            *(u32x4 *)&Bs[buf][row * LDK + col] = rb[i];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    int brow[2];
-    if (EPI == EPI_SWIGLU) {
-        brow[0] = wn * 32;
-        brow[1] = 64 + wn * 32;
-    } else {
-        brow[0] = wn * 64;
-        brow[1] = wn * 64 + 32;
-    }
-
-    const int nk = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *(const bf16x8 *)&As[cur][(wm * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *(const bf16x8 *)&Bs[cur][(brow[j] + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            sstore(cur ^ 1);
-            __syncthreads();
-        }
-    }
-
-    // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row >= M) continue;
-            if (EPI == EPI_SWIGLU) {
-                const int col = nb * 64 + wn * 32 + (lane & 31);
-                if (col >= N) continue;
-                const size_t idx = (size_t)row * N + col;
-                out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[i][0][v], acc[i][1][v], res, idx));
-            } else {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = nb * BN + brow[j] + (lane & 31);
-                    if (col >= N) continue;
-                    const size_t idx = (size_t)row * N + col;
-                    out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[i][j][v], 0.f, res, idx));
-                }
-            }
-        }
-    }
-}
-
 // ------------------------------------------------------------ fp32 tiled GEMM (strict mode)
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float *__restrict__ A, int M, int K,
@@ -414,20 +299,15 @@ hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int
         return hipGetLastError();
     }
     if (dt == DT_BF16) {
-        const dim3 grid(epi == EPI_SWIGLU ? (N + 63) / 64 : (N + gemm::BN - 1) / gemm::BN, (M + gemm::BM - 1) / gemm::BM);
-        const bf16 *a = (const bf16 *)x, *b = (const bf16 *)W, *r = (const bf16 *)res;
-        bf16 *o = (bf16 *)out;
-        if (epi == EPI_SWIGLU) gemm_bf16_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
-        else if (epi == EPI_RESID) gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
-        else gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
-    } else {
-        const dim3 grid(epi == EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64, (M + 63) / 64);
-        const float *a = (const float *)x, *b = (const float *)W, *r = (const float *)res;
-        float *o = (float *)out;
-        if (epi == EPI_SWIGLU) gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
-        else if (epi == EPI_RESID) gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
-        else gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+        if (!gemm_dma_ok(M, K, N)) return hipErrorInvalidValue;
+        return launch_gemm_dma(x, M, K, W, N, epi, res, out, s);
     }
+    const dim3 grid(epi == EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64, (M + 63) / 64);
+    const float *a = (const float *)x, *b = (const float *)W, *r = (const float *)res;
+    float *o = (float *)out;
+    if (epi == EPI_SWIGLU) gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+    else if (epi == EPI_RESID) gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
+    else gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a, M, K, b, N, r, o);
     return hipGetLastError();
 }
 
