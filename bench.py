@@ -8,7 +8,10 @@ hidden-state input, final norm output); the seat length is rewound to 4095 befor
 step on the host.  Also reported: HBM GB/s of the step (algorithmic bytes / time), the
 2048-token causal prefill in TFLOP/s (algorithmic FLOPs / time), the dominant kernel's
 roofline fraction from HIP events on the library's stream, and the CPU oracle on a
-bounded sample of the same decode step.
+bounded sample of the same decode step.  Two more workloads are reported beside the
+headline: the Qwen3-MoE-shaped stack (48 layers, 128 experts, top-8; decode at ctx 2048,
+a 64-token call, the isolated MoE block) and the 1.7B shape with 8-bit group-quantised
+projections (decode at ctx 4096, a 512-token prefill), each against its roofline.
 """
 from __future__ import annotations
 
@@ -36,6 +39,25 @@ GU_LAUNCH_BYTES = 12288 * 2048 * 2 + 2048 * 2 + 6144 * 2
 PREFILL_T = 2048
 PREFILL_FLOPS = 28 * (2 * PREFILL_T * (4096 * 2048 + 2048 * 2048 + 12288 * 2048 + 2048 * 6144)
                       + 4 * 128 * 16 * PREFILL_T * (PREFILL_T + 1) // 2)
+
+
+# Qwen3-MoE shape (48 layers, hidden 2048, 32 q / 4 kv heads, 128 experts, top-8, expert
+# intermediate 768).  Per layer: q|k|v [5120][2048], o [2048][4096], router [128][2048], one
+# expert's gate|up [1536][2048] + down [2048][768], all bf16.
+MOE_QKV_O_ROUTER = (5120 * 2048 + 2048 * 4096 + 128 * 2048) * 2
+MOE_EXPERT_BYTES = (1536 * 2048 + 2048 * 768) * 2
+# Decode at position 2047: attention weights + router + the 8 routed experts + the K/V read
+# of 2048 positions (4 kv heads, head_dim 128, K and V).
+MOE_DECODE_STEP_BYTES = 48 * (MOE_QKV_O_ROUTER + 8 * MOE_EXPERT_BYTES + 4 * 2048 * 128 * 2 * 2)
+# q8 decode at ctx 4096: per layer u8 codes + bf16 scale and bias per 64 codes for the four
+# projections (50,331,648 weights), the K/V read, the norm vectors and the new K/V entries.
+Q8_WEIGHTS = 4096 * 2048 + 2048 * 2048 + 12288 * 2048 + 2048 * 6144
+Q8_DECODE_STEP_BYTES = 28 * (Q8_WEIGHTS + Q8_WEIGHTS // 64 * 4 + 8 * 4096 * 128 * 2 * 2 + (2 * 2048 + 2 * 128) * 2
+                             + 8 * 128 * 2 * 2)
+# q8 prefill at T = 512 from an empty cache: projections and causal attention, as for the
+# bf16 prefill.
+Q8_PREFILL_T = 512
+Q8_PREFILL_FLOPS = 28 * (2 * Q8_PREFILL_T * Q8_WEIGHTS + 4 * 128 * 16 * Q8_PREFILL_T * (Q8_PREFILL_T + 1) // 2)
 
 
 def log(*a):
@@ -74,6 +96,7 @@ def decode_bench(steps: int, warmup: int, compare: bool = True):
     log(f"decode: building {cfg.n_layers}-layer weights and a {cfg.capacity}-position cache")
     w = synth.model_weights(cfg, dev)
     K, V = synth.kv_cache(cfg, 4095, dev)
+    torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     seat = q3.Seat(cfg, w, max_tokens=1, k_cache=K, v_cache=V, stream=stream)
     x = synth.hidden_states(cfg, 1, dev)
@@ -164,6 +187,142 @@ def prefill_bench(iters: int):
     return {"ms": dt * 1e3, "tflops": PREFILL_FLOPS / dt / 1e12}
 
 
+def _graph_seconds(fn, stream, steps: int, warmup: int) -> float:
+    """Seconds per call of `fn` replayed as one captured HIP graph on `stream`."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    del graph
+    return dt
+
+
+def moe_bench(steps: int, warmup: int):
+    """The Qwen3-MoE-shaped stack: (a) a T = 1 step at position 2047 over a K/V pre-fill of
+    0..2046, (b) one 64-token call from an empty cache, (c) the isolated MoE block (router,
+    top-8, sort, experts, weighted sum) on x [64][2048] and [1][2048].  Bytes: (a) counts the
+    8 routed experts of every layer; (c) counts the distinct experts the block's own top-8
+    output names; (b) counts the expected number of distinct experts for 64 tokens routed
+    uniformly (128 * (1 - (120/128)^64) = 125.95 per layer), since the stack's per-layer
+    routing is not returned."""
+    import torch
+
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_MOE as cfg
+
+    dev = "cuda"
+    log(f"moe: building {cfg.n_layers}-layer weights ({cfg.n_experts} experts per layer)")
+    w = synth.model_weights(cfg, dev)
+    K, V = synth.kv_cache(cfg, 2047, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    seat = q3.Seat(cfg, w, max_tokens=64, k_cache=K, v_cache=V, stream=stream)
+    x1 = synth.hidden_states(cfg, 1, dev)
+    x64 = synth.hidden_states(cfg, 64, dev, name="x64")
+    o1 = torch.empty_like(x1)
+    o64 = torch.empty_like(x64)
+    torch.cuda.synchronize()
+
+    def dec():
+        seat.length = 2047
+        q3.qwen3_forward_hidden(seat.handle, x1, o1)
+
+    t_dec = _graph_seconds(dec, stream, steps, warmup)
+
+    def call64():  # positions 0..63; cache entries at and past the length are never read
+        seat.length = 0
+        q3.qwen3_forward_hidden(seat.handle, x64, o64)
+
+    t64 = _graph_seconds(call64, stream, max(steps // 4, 5), warmup)
+    idx = torch.empty((64, cfg.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((64, cfg.top_k), dtype=torch.bfloat16, device=dev)
+    blk = {}
+    for T, xb, ob in ((64, x64, o64), (1, x1, o1)):
+        def block():
+            q3.qwen3_moe_block(seat.handle, 0, xb, ob, idx[:T], wts[:T])
+        t = _graph_seconds(block, stream, steps, warmup)
+        distinct = int(torch.unique(idx[:T]).numel())
+        nbytes = 128 * 2048 * 2 + distinct * MOE_EXPERT_BYTES + 2 * T * 2048 * 2
+        blk[T] = {"us": round(t * 1e6, 2), "distinct_experts": distinct, "bytes": nbytes,
+                  "gbps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+    q3.qwen3_check_device_errors(seat.handle)
+    b64 = cfg.n_layers * (MOE_QKV_O_ROUTER + 125.95 * MOE_EXPERT_BYTES)
+    res = {"workload": "Qwen3-MoE-shaped bf16 stack: 48 layers, hidden 2048, 32 q / 4 kv heads, 128 experts, "
+                       "top-8 renormalised, expert intermediate 768",
+           "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
+           "decode_step_bytes": MOE_DECODE_STEP_BYTES, "decode_gbps": round(MOE_DECODE_STEP_BYTES / t_dec / 1e9, 1),
+           "decode_hbm_frac": round(MOE_DECODE_STEP_BYTES / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
+           "T64_ms": round(t64 * 1e3, 4), "T64_tokens_per_s": round(64 / t64, 1),
+           "T64_gbps_expected_experts": round(b64 / t64 / 1e9, 1),
+           "block_T64": blk[64], "block_T1": blk[1]}
+    log(f"moe: decode {t_dec * 1e3:.3f} ms/step ({res['decode_gbps']} GB/s), T=64 call {t64 * 1e3:.3f} ms, "
+        f"block T=64 {blk[64]['us']} us ({blk[64]['gbps']} GB/s), block T=1 {blk[1]['us']} us")
+    del seat, w, K, V
+    torch.cuda.empty_cache()
+    return res
+
+
+def q8_bench(steps: int, warmup: int, iters: int):
+    """The 1.7B shape with 8-bit group-quantised projections: a T = 1 step at position 4095
+    (ctx 4096) and one 512-token causal prefill from an empty cache."""
+    import torch
+
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8 as cfg
+
+    dev = "cuda"
+    log("q8: building 28-layer 8-bit weights and a 4096-position cache")
+    w = synth.model_weights(cfg, dev)
+    K, V = synth.kv_cache(cfg, 4095, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    seat = q3.Seat(cfg, w, max_tokens=Q8_PREFILL_T, k_cache=K, v_cache=V, stream=stream)
+    x1 = synth.hidden_states(cfg, 1, dev)
+    xp = synth.hidden_states(cfg, Q8_PREFILL_T, dev, name="xp")
+    o1 = torch.empty_like(x1)
+    op = torch.empty_like(xp)
+    torch.cuda.synchronize()
+
+    def dec():
+        seat.length = 4095
+        q3.qwen3_forward_hidden(seat.handle, x1, o1)
+
+    def pre():
+        seat.length = 0
+        q3.qwen3_forward_hidden(seat.handle, xp, op)
+
+    t_dec = _graph_seconds(dec, stream, steps, warmup)
+    t_pre = _graph_seconds(pre, stream, iters, 2)
+    q3.qwen3_check_device_errors(seat.handle)
+    res = {"workload": "Qwen3-1.7B shape, 8-bit affine group-quantised projections (u8 codes, bf16 scale and "
+                       "bias per 64 along K)",
+           "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
+           "decode_step_bytes": Q8_DECODE_STEP_BYTES, "decode_gbps": round(Q8_DECODE_STEP_BYTES / t_dec / 1e9, 1),
+           "decode_hbm_frac": round(Q8_DECODE_STEP_BYTES / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
+           "prefill_T": Q8_PREFILL_T, "prefill_ms": round(t_pre * 1e3, 3),
+           "prefill_tflops": round(Q8_PREFILL_FLOPS / t_pre / 1e12, 1),
+           "prefill_mfma_frac": round(Q8_PREFILL_FLOPS / t_pre / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    log(f"q8: decode {t_dec * 1e3:.3f} ms/step ({res['decode_gbps']} GB/s), prefill T=512 {t_pre * 1e3:.3f} ms "
+        f"({res['prefill_tflops']} TFLOP/s)")
+    del seat, w, K, V
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(sample_layers: int = 4):
     """The oracle on the host: a decode step of the same shape over `sample_layers` layers
     (same per-layer work as the 28-layer step), scaled to a 28-layer step."""
@@ -205,6 +364,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (for profiling)")
+    ap.add_argument("--no-variants", action="store_true", help="skip the MoE and 8-bit workloads")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="time only the MoE and 8-bit workloads (for profiling)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the one-kernel-per-step decode path (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -223,10 +385,15 @@ def main():
         pre = prefill_bench(args.prefill_iters)
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
         return
+    if args.variants_only:
+        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5)}), flush=True)
+        return
     if args.copy_calib:
         copy_calibration()
     dec = decode_bench(args.steps, args.warmup, compare=not args.no_compare)
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
+    moe = None if args.no_variants else moe_bench(30, 3)
+    q8 = None if args.no_variants else q8_bench(30, 3, 5)
     cpu = None if args.no_cpu else cpu_baseline()
 
     if dec["path"] == 2:
@@ -265,6 +432,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": rl_bytes, "avg_launch_us": round(dec["kernel_us"], 3),
                      "launches": dec["launches"]},
+        "moe": moe,
+        "q8": q8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -72,6 +72,12 @@ def qwen3_init(cfg: Qwen3Config, weights: dict, k_cache: torch.Tensor, v_cache: 
         raise Qwen3Error(_lib.ERR_ARG, "invalid configuration")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+        if stream is not None:
+            workspace.record_stream(stream)  # the library's kernels use it on that stream
+    if stream is not None and stream != torch.cuda.current_stream():
+        # weights, caches and the workspace block may still have writes queued on the current
+        # stream (torch reuses freed blocks in stream order); the library's stream waits for them
+        stream.wait_stream(torch.cuda.current_stream())
     arr = (_lib.LayerWeights * cfg.n_layers)()
     for i, lw in enumerate(weights["layers"]):
         for name in _lib.LAYER_FIELDS:

@@ -79,17 +79,24 @@ __global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logi
         const int e = lane + 64 * i;
         v[i] = e < E ? rho<T>(v[i] / z) : -INFINITY;  // probabilities in the model dtype
     }
-    // k rounds of (largest value, lowest index) selection
+    // k rounds of (largest value, lowest index) selection among the experts not taken yet.
+    // Only experts e < E are candidates and a NaN probability ranks as -inf, so every round
+    // picks a valid expert (k <= E) whatever the logits hold.
     float psel[16];
     int isel[16];
+    unsigned taken = 0;  // bit i: expert lane + 64 i is selected or does not exist
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i >= E) taken |= 1u << i;
     for (int s = 0; s < k; ++s) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
-            if (v[i] > bv || (v[i] == bv && e < bi)) {
-                bv = v[i];
+            const float x = v[i] == v[i] ? v[i] : -INFINITY;
+            if (!((taken >> i) & 1u) && (x > bv || (x == bv && e < bi))) {
+                bv = x;
                 bi = e;
             }
         }
@@ -106,7 +113,7 @@ __global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logi
         isel[s] = bi;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (lane + 64 * i == bi) v[i] = -INFINITY;
+            if (lane + 64 * i == bi) taken |= 1u << i;
     }
     if (lane == 0) {
         float den = 0.f;
@@ -230,8 +237,9 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ 
     for (int n = threadIdx.x; n < hid; n += blockDim.x) {
         float acc = 0.f;
         for (int s = 0; s < k; ++s) {
-            const int r = t * k + s;
-            acc += rho<T>(to_f(y[(size_t)inv[r] * hid + n]) * to_f(w[r]));
+            const int r = t * k + s, p = inv[r];
+            if ((unsigned)p >= (unsigned)(gridDim.x * k)) continue;  // never for indices the top-k kernel writes
+            acc += rho<T>(to_f(y[(size_t)p * hid + n]) * to_f(w[r]));
         }
         out[(size_t)t * hid + n] = from_f<T>(acc);
     }

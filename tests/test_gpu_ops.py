@@ -204,3 +204,25 @@ def test_moe_block_op(orc, ops, dtype, T, hid, E, k, Ie):
     assert np.array_equal(gidx, ridx)   # same slot order: descending probability, ties to the lower index
     np.testing.assert_allclose(np32(w), rw, rtol=1e-5 if dtype == "fp32" else 2 ** -7, atol=0)
     assert e < (2e-5 if dtype == "fp32" else BF16_TOL)
+
+
+def test_moe_nan_router_row_gets_valid_experts(orc, ops):
+    """A token whose router logits are all NaN still receives k distinct experts in [0, E):
+    NaN ranks as -inf, so ties go to the lowest indices 0..k-1.  The other tokens' routing and
+    outputs equal the oracle's on the same rows (no routed row is lost or misplaced)."""
+    T, hid, E, k, Ie = 6, 128, 16, 4, 64
+    dt = TDT["bf16"]
+    x = randn((T, hid), 90, 1.0, dt)
+    x[2, 5] = float("nan")
+    Wr = randn((E, hid), 91, 0.02, dt)
+    Wgu = randn((E, 2 * Ie, hid), 92, 0.02, dt)
+    Wd = randn((E, hid, Ie), 93, 0.02, dt)
+    out, idx, w = ops.moe(x, Wr, Wgu, Wd, k)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    assert ((gidx >= 0) & (gidx < E)).all()
+    assert list(gidx[2]) == list(range(k))
+    good = [0, 1, 3, 4, 5]
+    ref, ridx, _ = orc.moe_block(np32(x)[good], np32(Wr), np32(Wgu), np32(Wd), k, True, False, "bf16")
+    assert np.array_equal(gidx[good], ridx)
+    assert max_row_rel_l2(np32(out)[good], ref) < BF16_TOL
