@@ -72,10 +72,14 @@ size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
 hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
                       const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
-// ---- bf16 projections for M > 16 (kernels_gemm.hip): 3-stage LDS-DMA pipeline, K % 64 == 0
+// ---- MFMA projections for M > 16 (kernels_gemm.hip): LDS-DMA pipeline, K % 64 == 0 (bf16
+// weights) or K % 128 == 0 and 4-byte aligned scale/bias (8-bit weights)
 bool gemm_dma_ok(int M, int K, int N);
 hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, int epi, const void *res, void *out,
                            hipStream_t s);
+bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias);
+hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
+                              int N, int epi, const void *res, void *out, hipStream_t s);
 
 // ---- persistent decode step (kernels_decode_mk.hip): dense bf16 stacks of supported shape
 bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I, int cap);

@@ -1,38 +1,58 @@
-// kernels_gemm.hip -- the bf16 projections of prefill (M > 16 rows): y = x . W^T with the
+// kernels_gemm.hip -- the MFMA projections of prefill (M > 16 rows): y = x . W^T with the
 // fused epilogues of kernels_linear.hip ("maya2_mlx/backbone.py", forward: the fused q|k|v
 // rows, o_proj + residual, fused gate|up rows + SwiGLU, down; the rounding points are those
-// of epi_value there).
+// of epi_value there), for bf16 weights and for 8-bit affine group-quantised weights (codes
+// q, bf16 scale s and bias b per 64 along K; w = s * q + b used in fp32, never rounded).
 //
 // Design for gfx950:
-//  - v_mfma_f32_32x32x16_bf16; block tile 128 rows x BN weight rows (BN = 256 or 128),
-//    4 waves in a 2 x 2 layout, each wave 64 rows x BN/2 weight rows (2 x BN/64 MFMA tiles).
-//    For SWIGLU a tile holds BN/2 gate rows and the BN/2 up rows of the same outputs, and a
-//    wave holds the gate and up accumulators of the same output columns.
-//  - K steps of 64 flow through a 3-stage LDS pipeline filled by direct-to-LDS copies
-//    (global_load_lds_dwordx4, 1 KB per instruction): two stages are in flight while the
-//    third is consumed, with no register staging.  One barrier per K step.
-//  - LDS rows are 128 B (64 bf16) with the 16-byte chunks XOR-swizzled by the row index, so
-//    a fragment read (32 rows, one chunk each) hits distinct banks.  The copy's lane ->
-//    address mapping writes that layout directly: lane l of a copy fetches row l/8, chunk
-//    (l%8) ^ (row%8).
+//  - v_mfma_f32_32x32x16_bf16 on block tiles of BM rows x BN weight rows, WM x WN waves, each
+//    wave (BM/WM) x (BN/WN).  For SWIGLU a tile holds BN/2 gate rows and the BN/2 up rows of
+//    the same outputs, and a wave holds the gate and up accumulators of the same columns.
+//  - K steps of 64 flow through an ST-stage LDS ring filled by direct-to-LDS copies
+//    (global_load_lds_dwordx4, 1 KB per instruction; no register staging): ST-1 stages are in
+//    flight while one is consumed, one barrier per K step.
+//  - LDS rows are 128 B (64 bf16; 64 B for 64 codes) with the 16-byte chunks XOR-swizzled by
+//    the row (chunk ^ ((row >> 1) & 7) for 128-B rows, chunk ^ ((row >> 2) & 3) for 64-B rows),
+//    so 16 lanes reading 16 consecutive rows at one chunk hit distinct banks.  A copy's lane
+//    -> address map writes that layout directly.
+//  - Tile shapes: 256 x 128 with 8 waves when that still gives >= 192 tiles (gate|up and
+//    q|k|v at T = 2048), else 128 x 128 with 4 waves and 4 stages (o_proj and down, and
+//    small T).  Measured on the 2048-token projections against a 128 x 256 / 4-wave tiling:
+//    gate|up 148 -> 125 us, q|k|v 48 -> 40 us.
+//  - 8-bit weights (one K step = one group): the codes (64 B per row) are copied to LDS like
+//    the bf16 operand; the scale and bias words of the group arrive by 4-byte direct copies
+//    (the aligned word holding groups 2i and 2i+1).  K is interleaved per lane so one 16-byte
+//    read yields the codes of two MFMA steps; codes 0..255 are exact in bf16 (converted
+//    through fp32).  Per group the MFMAs form P = x . q, and one more MFMA against a ones
+//    operand forms S = sum of x over the group in the same register layout; the group then
+//    folds as acc += s * P + b * S (the same sum regrouped, all fp32).
 //  - Rows past M and weight rows past N are clamped to the last valid row on load and
-//    skipped on store.  K must be a multiple of 64.
+//    skipped on store.  K must be a multiple of 64 (of 128 for 8-bit weights).
 #include "common.h"
 #include "kernels.h"
 
 namespace q3 {
 namespace g2 {
 
-constexpr int BM = 128, BK = 64, STAGES = 3;
-constexpr int ROWB = BK * 2;  // bytes per LDS row
-
-template <int BN> struct Geo {
-    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
-    static constexpr int COPIES = STAGE / 1024;  // 1 KB copies per stage
-    static constexpr int PER_WAVE = COPIES / 4;
-    static constexpr int NT = BN / 64;           // MFMA tiles per wave along the weight rows
-    static_assert(COPIES % 4 == 0, "copies split evenly over the 4 waves");
+template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_> struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, ST = ST_, WM = WM_, WN = WN_;
+    static constexpr bool Q8 = Q8_;
+    static constexpr int BK = 64, NW = WM * WN, NTH = 64 * NW;
+    static constexpr int RBA = 128, RBB = Q8 ? 64 : 128;  // LDS row bytes of A and of the weights
+    static constexpr int A_BYTES = BM * RBA, B_BYTES = BN * RBB, SB_BYTES = Q8 ? BN * 8 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;
+    static constexpr int ACOP = A_BYTES / 1024, NBIG = (A_BYTES + B_BYTES) / 1024, NSMALL = SB_BYTES / 256;
+    static constexpr int OPS = NBIG + NSMALL, PW = OPS / NW, APW = ACOP / NW, BPW = NBIG / NW;
+    static constexpr int WTM = BM / WM, WTN = BN / WN, NI = WTM / 32, NT = WTN / 32;
+    static_assert(OPS % NW == 0 && ACOP % NW == 0 && NBIG % NW == 0, "copy kinds split evenly over the waves");
+    static_assert(NI >= 1 && NT >= 1 && NT % 2 == 0, "wave tile at least 32 x 64");
 };
+
+__device__ __forceinline__ int offA(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+template <bool Q8> __device__ __forceinline__ int offB(int row, int c) {
+    if (Q8) return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+    return offA(row, c);
+}
 
 // Weight row held by tile-local row r of weight block nb.
 template <int EPI, int BN> __device__ __forceinline__ int w_row(int nb, int r, int N) {
@@ -44,111 +64,182 @@ template <int EPI, int BN> __device__ __forceinline__ int w_row(int nb, int r, i
     return min(nb * BN + r, N - 1);
 }
 
-// Swizzled byte offset of (row, 16-byte chunk c) inside an operand tile.
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+// Eight codes (two words, little-endian bytes) as exact bf16 values: the integer through fp32,
+// whose low 16 bits are zero for 0..255, then the high halves packed.
+__device__ __forceinline__ bf16x8 codes8(uint32_t w0, uint32_t w1) {
+    u32x4 r;
+    const uint32_t w[2] = {w0, w1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float f0 = (float)(w[h] & 0xffu), f1 = (float)((w[h] >> 8) & 0xffu);
+        const float f2 = (float)((w[h] >> 16) & 0xffu), f3 = (float)(w[h] >> 24);
+        r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 4-byte direct-to-LDS copy: lane l's word lands at lds + 4 l.
+__device__ __forceinline__ void dma4(const void *g, unsigned lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace g2
 
-template <int EPI, int BN>
-__global__ void __launch_bounds__(256) gemm_bf16_dma_kernel(const bf16 *__restrict__ A, int M, int K,
-                                                            const bf16 *__restrict__ W, int N,
-                                                            const bf16 *__restrict__ res, bf16 *__restrict__ out) {
+// W: bf16 weight rows, or (Q8) the u8 codes with their scale and bias arrays [rows][K/64].
+template <int EPI, class C>
+__global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restrict__ A, int M, int K,
+                                                          const void *__restrict__ W, const bf16 *__restrict__ scale,
+                                                          const bf16 *__restrict__ bias, int N,
+                                                          const bf16 *__restrict__ res, bf16 *__restrict__ out) {
     using namespace g2;
-    using G = Geo<BN>;
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, nb = blockIdx.x;
-    const int nk = K / BK;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int m0 = blockIdx.y * C::BM, nb = blockIdx.x;
+    const int nk = K / C::BK, ng = K / 64;
     const unsigned lds0 = (unsigned)(uintptr_t)smem;
 
-    // this wave's copies of one stage: copy d covers 8 tile rows (A rows for d < 16)
+    // this wave's copies of one stage: op d = i * NW + wave, in the order A, weights, scale|bias
     auto issue = [&](int kt) {
-        const int st = kt % STAGES, k0 = kt * BK;
+        const int k0 = kt * C::BK;
+        const unsigned st = lds0 + (kt % C::ST) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < G::PER_WAVE; ++i) {
-            const int d = wave + 4 * i;
-            const int r = (d & 15) * 8 + (lane >> 3);  // row inside its operand tile (d < 16: A)
-            const int c = (lane & 7) ^ (r & 7);
-            const bf16 *src;
-            unsigned dst;
-            if (d < 16) {
-                src = A + (size_t)min(m0 + r, M - 1) * K + k0 + c * 8;
-                dst = lds0 + st * G::STAGE + d * 1024;
+        for (int i = 0; i < C::PW; ++i) {
+            const int d = i * C::NW + wave;
+            if (i < C::APW) {
+                const int r = d * 8 + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+                dma16(A + (size_t)min(m0 + r, M - 1) * K + k0 + c * 8, __builtin_amdgcn_readfirstlane(st + d * 1024));
+            } else if (i < C::BPW) {
+                const int db = d - C::ACOP;
+                if (C::Q8) {
+                    const int r = db * 16 + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+                    const uint8_t *src = (const uint8_t *)W + (size_t)w_row<EPI, C::BN>(nb, r, N) * K + k0 + c * 16;
+                    dma16(src, __builtin_amdgcn_readfirstlane(st + d * 1024));
+                } else {
+                    const int r = db * 8 + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+                    const bf16 *src = (const bf16 *)W + (size_t)w_row<EPI, C::BN>(nb, r, N) * K + k0 + c * 8;
+                    dma16(src, __builtin_amdgcn_readfirstlane(st + d * 1024));
+                }
             } else {
-                const int rb = (d - 16) * 8 + (lane >> 3);
-                const int cb = (lane & 7) ^ (rb & 7);
-                src = W + (size_t)w_row<EPI, BN>(nb, rb, N) * K + k0 + cb * 8;
-                dst = lds0 + st * G::STAGE + G::A_BYTES + (d - 16) * 1024;
+                const int sm = d - C::NBIG;  // 256-B word copies: scale, then bias
+                const int part = sm % (C::BN / 64), which = sm / (C::BN / 64);
+                const int wr = w_row<EPI, C::BN>(nb, part * 64 + lane, N);
+                const bf16 *arr = which ? bias : scale;
+                dma4(arr + (size_t)wr * ng + (kt & ~1),
+                     __builtin_amdgcn_readfirstlane(st + C::A_BYTES + C::B_BYTES + sm * 256));
             }
-            dma16(src, __builtin_amdgcn_readfirstlane(dst));
         }
     };
 
-    f32x16 acc[2][G::NT];
+    f32x16 acc[C::NI][C::NT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::NI; ++i)
 #pragma unroll
-        for (int j = 0; j < G::NT; ++j)
+        for (int j = 0; j < C::NT; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // tile-local weight rows of this wave's MFMA tiles
-    int brow[G::NT];
+    int brow[C::NT];  // tile-local weight rows of this wave's MFMA tiles
 #pragma unroll
-    for (int j = 0; j < G::NT; ++j) {
+    for (int j = 0; j < C::NT; ++j) {
         if (EPI == EPI_SWIGLU) {
-            constexpr int HJ = G::NT / 2;  // gate tiles, then the matching up tiles
-            brow[j] = (j < HJ ? 0 : BN / 2) + wn * (BN / 4) + 32 * (j % HJ);
+            constexpr int HJ = C::NT / 2;  // gate tiles, then the matching up tiles
+            brow[j] = (j < HJ ? 0 : C::BN / 2) + wn * (C::WTN / 2) + 32 * (j % HJ);
         } else {
-            brow[j] = wn * (BN / 2) + 32 * j;
+            brow[j] = wn * C::WTN + 32 * j;
         }
     }
 
-    issue(0);
-    if (nk > 1) issue(1);
+#pragma unroll
+    for (int s = 0; s < C::ST - 1; ++s)
+        if (s < nk) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) wait_vm<G::PER_WAVE>();  // this wave's copies of stage kt have landed
+        constexpr int AHEAD = C::ST - 2;  // stages in flight beyond the one consumed
+        const int rem = nk - 1 - kt;
+        if (AHEAD >= 2 && rem >= 2) wait_vm<(AHEAD >= 2 ? 2 : 0) * C::PW>();
+        else if (AHEAD >= 1 && rem >= 1) wait_vm<(AHEAD >= 1 ? 1 : 0) * C::PW>();
         else wait_vm<0>();
-        __syncthreads();  // everyone's copies landed; everyone finished stage kt-1
-        if (kt + 2 < nk) issue(kt + 2);
-        const unsigned char *As = smem + (kt % STAGES) * G::STAGE;
-        const unsigned char *Bs = As + G::A_BYTES;
+        __syncthreads();  // every wave's copies of stage kt landed; every wave finished kt-1
+        if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+        const unsigned char *As = smem + (kt % C::ST) * C::STAGE;
+        const unsigned char *Bs = As + C::A_BYTES;
+        if (!C::Q8) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
-            bf16x8 af[2], bfr[G::NT];
+            for (int kk = 0; kk < C::BK / 16; ++kk) {
+                const int c = 2 * kk + (lane >> 5);
+                bf16x8 af[C::NI], bfr[C::NT];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + (lane & 31);
-                af[i] = *(const bf16x8 *)(As + swz(r, c));
+                for (int i = 0; i < C::NI; ++i)
+                    af[i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), c));
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) bfr[j] = *(const bf16x8 *)(Bs + offB<false>(brow[j] + (lane & 31), c));
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
             }
+        } else {
+            // MFMA step kk = 2p + e, lane half h: k = (2p + h) * 16 + 8 e + 0..7 of the group
+            const int h = lane >> 5;
+            const f32x16 zero = {};
+            const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+            f32x16 part[C::NI][C::NT], xs[C::NI];
 #pragma unroll
-            for (int j = 0; j < G::NT; ++j) {
-                const int r = brow[j] + (lane & 31);
-                bfr[j] = *(const bf16x8 *)(Bs + swz(r, c));
+            for (int p = 0; p < 2; ++p) {
+                u32x4 cw[C::NT];
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) cw[j] = *(const u32x4 *)(Bs + offB<true>(brow[j] + (lane & 31), 2 * p + h));
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    bf16x8 af[C::NI], bfr[C::NT];
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i)
+                        af[i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), 2 * (2 * p + h) + e));
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j) bfr[j] = codes8(cw[j][2 * e], cw[j][2 * e + 1]);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) {
+#pragma unroll
+                        for (int j = 0; j < C::NT; ++j)
+                            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], (p | e) ? part[i][j] : zero,
+                                                                                 0, 0, 0);
+                        xs[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], ones, (p | e) ? xs[i] : zero, 0, 0, 0);
+                    }
+                }
             }
+            const uint32_t *sw = (const uint32_t *)(Bs + C::B_BYTES), *bw = sw + C::BN;
+            const int sh = (kt & 1) * 16;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < C::NT; ++j) {
+                const int col = brow[j] + (lane & 31);
+                const float sc = __uint_as_float((sw[col] >> sh) << 16), bi = __uint_as_float((bw[col] >> sh) << 16);
 #pragma unroll
-                for (int j = 0; j < G::NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] += sc * part[i][j][v] + bi * xs[i][v];
+            }
         }
     }
 
     // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::NI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int row = m0 + wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (row >= M) continue;
             if (EPI == EPI_SWIGLU) {
-                constexpr int HJ = G::NT / 2;
+                constexpr int HJ = C::NT / 2;
 #pragma unroll
                 for (int j = 0; j < HJ; ++j) {
-                    const int col = nb * (BN / 2) + wn * (BN / 4) + 32 * j + (lane & 31);
+                    const int col = nb * (C::BN / 2) + wn * (C::WTN / 2) + 32 * j + (lane & 31);
                     if (col >= N) continue;
                     const size_t idx = (size_t)row * N + col;
                     const float g = rho<bf16>(acc[i][j][v]), u = rho<bf16>(acc[i][j + HJ][v]);
@@ -156,8 +247,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma_kernel(const bf16 *__restri
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < G::NT; ++j) {
-                    const int col = nb * BN + brow[j] + (lane & 31);
+                for (int j = 0; j < C::NT; ++j) {
+                    const int col = nb * C::BN + brow[j] + (lane & 31);
                     if (col >= N) continue;
                     const size_t idx = (size_t)row * N + col;
                     const float a = acc[i][j][v];
@@ -169,38 +260,56 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma_kernel(const bf16 *__restri
 }
 
 namespace {
-template <int EPI, int BN>
-hipError_t launch_g2(const bf16 *x, int M, int K, const bf16 *W, int N, const bf16 *res, bf16 *out, hipStream_t s) {
-    using G = g2::Geo<BN>;
-    const int cols = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    const dim3 grid((N + cols - 1) / cols, (M + g2::BM - 1) / g2::BM);
-    const size_t lds = (size_t)g2::STAGES * G::STAGE;
-    static bool attr = false;  // the kernel needs more than the default 64 KB of dynamic LDS
+typedef g2::Cfg<256, 128, 3, 4, 2, false> Wide;    // 8 waves, 64 x 64 per wave, 144 KB LDS
+typedef g2::Cfg<128, 128, 4, 2, 2, false> Narrow;  // 4 waves, 64 x 64 per wave, 128 KB LDS
+typedef g2::Cfg<128, 128, 4, 2, 2, true> Quant;    // 4 waves, 100 KB LDS
+
+template <int EPI, class C>
+hipError_t launch_c(const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N, const bf16 *res,
+                    bf16 *out, hipStream_t s) {
+    const int cols = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;
+    const dim3 grid((N + cols - 1) / cols, (M + C::BM - 1) / C::BM);
+    const size_t lds = (size_t)C::ST * C::STAGE;
+    static bool attr = false;  // more than the default 64 KB of dynamic LDS
     if (!attr) {
-        const hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_dma_kernel<EPI, BN>,
+        const hipError_t e = hipFuncSetAttribute((const void *)gemm_mfma_kernel<EPI, C>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    gemm_bf16_dma_kernel<EPI, BN><<<grid, 256, lds, s>>>(x, M, K, W, N, res, out);
+    gemm_mfma_kernel<EPI, C><<<grid, C::NTH, lds, s>>>(x, M, K, W, sc, bi, N, res, out);
     return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_e(int epi, const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N,
+                    const bf16 *r, bf16 *o, hipStream_t s) {
+    if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, C>(x, M, K, W, sc, bi, N, r, o, s);
+    if (epi == EPI_RESID) return launch_c<EPI_RESID, C>(x, M, K, W, sc, bi, N, r, o, s);
+    return launch_c<EPI_STORE, C>(x, M, K, W, sc, bi, N, r, o, s);
 }
 }  // namespace
 
-bool gemm_dma_ok(int M, int K, int N) { return M > 16 && K % g2::BK == 0 && K > 0 && N > 0; }
+bool gemm_dma_ok(int M, int K, int N) { return M > 16 && K % 64 == 0 && K > 0 && N > 0; }
 
 hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, int epi, const void *res, void *out,
                            hipStream_t s) {
-    const bf16 *a = (const bf16 *)x, *w = (const bf16 *)W, *r = (const bf16 *)res;
+    const bf16 *a = (const bf16 *)x, *r = (const bf16 *)res;
     bf16 *o = (bf16 *)out;
-    // 128 x 256 tiles when they still fill the 256 CUs, else 128 x 128
-    const int mblocks = (M + g2::BM - 1) / g2::BM;
-    const bool wide = (long)mblocks * ((epi == EPI_SWIGLU ? N / 128 : N / 256)) >= 256;
-    if (epi == EPI_SWIGLU) return wide ? launch_g2<EPI_SWIGLU, 256>(a, M, K, w, N, r, o, s)
-                                       : launch_g2<EPI_SWIGLU, 128>(a, M, K, w, N, r, o, s);
-    if (epi == EPI_RESID) return wide ? launch_g2<EPI_RESID, 256>(a, M, K, w, N, r, o, s)
-                                      : launch_g2<EPI_RESID, 128>(a, M, K, w, N, r, o, s);
-    return wide ? launch_g2<EPI_STORE, 256>(a, M, K, w, N, r, o, s) : launch_g2<EPI_STORE, 128>(a, M, K, w, N, r, o, s);
+    const long cols = epi == EPI_SWIGLU ? Wide::BN / 2 : Wide::BN;
+    const long wide_tiles = (long)((M + Wide::BM - 1) / Wide::BM) * ((N + cols - 1) / cols);
+    if (wide_tiles >= 192) return launch_e<Wide>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+    return launch_e<Narrow>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+}
+
+bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias) {
+    return M > 16 && K % 128 == 0 && K > 0 && N > 0 && ((uintptr_t)scale & 3) == 0 && ((uintptr_t)bias & 3) == 0;
+}
+
+hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
+                              int N, int epi, const void *res, void *out, hipStream_t s) {
+    return launch_e<Quant>(epi, (const bf16 *)x, M, K, codes, (const bf16 *)scale, (const bf16 *)bias, N,
+                           (const bf16 *)res, (bf16 *)out, s);
 }
 
 }  // namespace q3

@@ -9,7 +9,9 @@
 //  - gemv_q8_kernel (M <= 16): each wave64 owns one output column; a lane reads
 //    16 codes (one 128-bit load) and the matching 16 bf16 activations, so a
 //    group's 64 codes are 4 lanes; weight bytes per column are K * (1 + 4/64).
-//  - gemm_q8_kernel (M > 16): the bf16 MFMA GEMM tiling with K step = one group
+//  - M > 16: the MFMA GEMM of kernels_gemm.hip when K % 128 == 0 and the scale and bias
+//    arrays are 4-byte aligned; otherwise gemm_q8_kernel: the bf16 MFMA GEMM tiling with K
+//    step = one group
 //    (64).  Codes are integers 0..255 and exact in bf16, so each group's MFMA
 //    partial sum is exact products summed in fp32; it is folded into the
 //    running accumulator with the column's scale and bias and the row's
@@ -327,6 +329,8 @@ hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, c
         else gemv_q8_dispatch<EPI_STORE>(x, M, K, codes, scale, bias, N, res, out, s);
         return hipGetLastError();
     }
+    if (gemm_q8_dma_ok(M, K, N, scale, bias))
+        return launch_gemm_q8_dma(x, M, K, codes, scale, bias, N, epi, res, out, s);
     const dim3 grid(epi == EPI_SWIGLU ? (N + 63) / 64 : (N + gq8::BN - 1) / gq8::BN, (M + gq8::BM - 1) / gq8::BM);
     const bf16 *a = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *r = (const bf16 *)res;
     bf16 *o = (bf16 *)out;

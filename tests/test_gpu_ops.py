@@ -67,7 +67,9 @@ def test_add_rmsnorm(orc, dtype, n, ops):
             assert np.mean(got == rf) > 0.99 and max_row_rel_l2(got, rf) < 4e-3
 
 
-LIN_CASES = [(1, 2048, 4096), (3, 2048, 384), (16, 256, 512), (40, 512, 384), (300, 2048, 640), (130, 6144, 256)]
+# (520, 128, 8200) takes the 256 x 128 / 8-wave MFMA tiling (>= 192 tiles) with ragged M and N
+LIN_CASES = [(1, 2048, 4096), (3, 2048, 384), (16, 256, 512), (40, 512, 384), (300, 2048, 640), (130, 6144, 256),
+             (520, 128, 8200)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -95,7 +97,10 @@ def test_linear(orc, ops, dtype, epi, M, K, N):
 
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
-@pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (5, 6144, 256), (40, 2048, 384), (512, 2048, 640)])
+# K = 320 (an odd number of groups) takes the register-staged 8-bit GEMM; the other M > 16
+# cases the LDS-DMA one
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (5, 6144, 256), (40, 2048, 384), (512, 2048, 640),
+                                   (200, 6144, 136), (40, 320, 96)])
 def test_linear_q8(orc, ops, epi, M, K, N):
     from qwen3_transformer_layer_amd import synth
     from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8
