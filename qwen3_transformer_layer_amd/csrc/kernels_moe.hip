@@ -9,17 +9,21 @@
 //
 // Layout of the work:
 //  1. router logits: the shared projection kernels (GEMV / MFMA GEMM);
-//  2. moe_topk_kernel: one wave per token does softmax, k arg-max rounds and the
-//     renormalisation;
+//  2. moe_topk_kernel: one wave per token does softmax, k selection rounds (a DPP
+//     maximum, then ballots in expert order for the lowest index holding it) and
+//     the renormalisation;
 //  3. moe_sort_kernel: stable counting sort of the T*k (token, slot) rows by
-//     expert (one thread per expert scans the rows in order), giving per-expert
-//     row ranges, the sorted-to-row permutation, its inverse and the list of
-//     experts that received rows;
-//  4. moe_expert_kernel: grid (output column block, active expert); each wave
-//     streams one weight row (a gate/up pair in the first pass) of its expert
-//     once per group of 8 routed rows, so every hit expert's weights are read
-//     from HBM once for up to 8 tokens;
-//  5. moe_combine_kernel: out[t] = rho(sum_s rho(y[t,s] * w[t,s])), slot order.
+//     expert in one block (LDS counts, a wave scan, then each chunk of 256 rows
+//     ranked against the rows before it), giving per-expert row ranges, the
+//     sorted-to-row permutation, its inverse and the list of experts that received
+//     rows.  For T == 1, moe_route1_kernel does steps 2 and 3 in one wave: the k
+//     selected experts are distinct, so the sorted layout is their ascending order;
+//  4. moe_expert_kernel: grid (wave group, active expert); each wave streams
+//     weight rows of its expert (the gate/up pair of one output in the first
+//     pass, four output rows in the second) once per group of 8 routed rows, so
+//     every hit expert's weights are read from HBM once for up to 8 tokens;
+//  5. moe_combine_kernel: out[t] = rho(sum_s rho(y[t,s] * w[t,s])), slot order,
+//     one thread per output element.
 #include <math.h>
 
 #include "common.h"
@@ -51,13 +55,44 @@ MoeWs moe_layout(int T, int hid, int E, int k, int Ie, int dt) {
 size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt) { return moe_layout(T, hid, E, k, Ie, dt).total; }
 
 // ------------------------------------------------------------ softmax + top-k + renormalise
-template <typename T>
-__global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logits, int E, int k, int norm,
-                                                      int32_t *__restrict__ idx, T *__restrict__ wout) {
-    constexpr int EPL = 4;  // experts per lane (E <= 256)
-    const int t = blockIdx.x, lane = threadIdx.x;
-    const T *l = logits + (size_t)t * E;
-    float v[EPL];
+// The k largest of the wave's values (lane l holds experts l + 64 i), ties to the lower
+// expert index: each round takes the maximum over the experts not taken yet (DPP) and the
+// lowest index holding it (ballots in index order).  A NaN ranks as -inf and experts e >= E
+// are never candidates, so every round picks a valid, new expert (k <= E).
+template <int EPL>
+__device__ __forceinline__ void select_topk(const float (&v)[EPL], int E, int k, int lane, float *psel, int *isel) {
+    float x[EPL];
+    unsigned taken = 0;  // bit i: expert lane + 64 i is selected or does not exist
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        x[i] = v[i] == v[i] ? v[i] : -INFINITY;
+        if (lane + 64 * i >= E) taken |= 1u << i;
+    }
+    for (int s = 0; s < k; ++s) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (!((taken >> i) & 1u)) lm = fmaxf(lm, x[i]);
+        const float m = wave_max(lm);
+        int bi = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const unsigned long long msk = __ballot(!((taken >> i) & 1u) && x[i] == m);
+            if (msk) {
+                bi = 64 * i + (int)__builtin_ctzll(msk);
+                break;
+            }
+        }
+        psel[s] = m;
+        isel[s] = bi;
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
+}
+
+// Softmax over the token's E logits in fp32, probabilities rounded to the model dtype
+// (v[i] for expert lane + 64 i; -inf past E).
+template <typename T, int EPL>
+__device__ __forceinline__ void softmax_probs(const T *l, int E, int lane, float (&v)[EPL]) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -77,94 +112,142 @@ __global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logi
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? rho<T>(v[i] / z) : -INFINITY;  // probabilities in the model dtype
+        v[i] = e < E ? rho<T>(v[i] / z) : -INFINITY;
     }
-    // k rounds of (largest value, lowest index) selection among the experts not taken yet.
-    // Only experts e < E are candidates and a NaN probability ranks as -inf, so every round
-    // picks a valid expert (k <= E) whatever the logits hold.
+}
+
+template <typename T>
+__device__ __forceinline__ void write_routing(int t, int k, int norm, const float *psel, const int *isel,
+                                              int32_t *__restrict__ idx, T *__restrict__ wout) {
+    float den = 0.f;
+    for (int s = 0; s < k; ++s) den += psel[s];
+    const float denr = rho<T>(den);
+    for (int s = 0; s < k; ++s) {
+        idx[(size_t)t * k + s] = isel[s];
+        wout[(size_t)t * k + s] = from_f<T>(norm ? psel[s] / denr : psel[s]);
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logits, int E, int k, int norm,
+                                                      int32_t *__restrict__ idx, T *__restrict__ wout) {
+    constexpr int EPL = 4;  // experts per lane (E <= 256)
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float v[EPL];
+    softmax_probs<T, EPL>(logits + (size_t)t * E, E, lane, v);
     float psel[16];
     int isel[16];
-    unsigned taken = 0;  // bit i: expert lane + 64 i is selected or does not exist
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        if (lane + 64 * i >= E) taken |= 1u << i;
-    for (int s = 0; s < k; ++s) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
-            const float x = v[i] == v[i] ? v[i] : -INFINITY;
-            if (!((taken >> i) & 1u) && (x > bv || (x == bv && e < bi))) {
-                bv = x;
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        psel[s] = bv;
-        isel[s] = bi;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (lane + 64 * i == bi) taken |= 1u << i;
-    }
+    select_topk<EPL>(v, E, k, lane, psel, isel);
+    if (lane == 0) write_routing<T>(t, k, norm, psel, isel, idx, wout);
+}
+
+// T == 1: routing plus the sorted layout the expert kernels read.  The k selected experts are
+// distinct, so the row of slot s goes to position rank(s) = #{s' : e_s' < e_s}; the expert
+// of rank r owns rows [r, r + 1).  offsets is written only at the selected experts and their
+// successors (offsets[e + 1] = rank + 1 is also the start of expert e + 1 when that one is
+// selected); the expert kernels read no other entry.
+template <typename T>
+__global__ void __launch_bounds__(64) moe_route1_kernel(const T *__restrict__ logits, int E, int k, int norm,
+                                                        int32_t *__restrict__ idx, T *__restrict__ wout,
+                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                        int32_t *__restrict__ inv, int32_t *__restrict__ active) {
+    constexpr int EPL = 4;
+    const int lane = threadIdx.x;
+    float v[EPL];
+    softmax_probs<T, EPL>(logits, E, lane, v);
+    float psel[16];
+    int isel[16];
+    select_topk<EPL>(v, E, k, lane, psel, isel);
     if (lane == 0) {
-        float den = 0.f;
-        for (int s = 0; s < k; ++s) den += psel[s];
-        const float denr = rho<T>(den);
-        for (int s = 0; s < k; ++s) {
-            idx[(size_t)t * k + s] = isel[s];
-            wout[(size_t)t * k + s] = from_f<T>(norm ? psel[s] / denr : psel[s]);
-        }
+        write_routing<T>(0, k, norm, psel, isel, idx, wout);
+        active[0] = k;
+    }
+    if (lane < k) {
+        int e = 0, rank = 0;
+        for (int s = 0; s < k; ++s)
+            if (s == lane) e = isel[s];
+        for (int s = 0; s < k; ++s) rank += isel[s] < e;
+        perm[rank] = lane;
+        inv[lane] = rank;
+        active[1 + rank] = e;
+        offsets[e] = rank;
+        offsets[e + 1] = rank + 1;
     }
 }
 
 // ------------------------------------------------------------ stable counting sort by expert
+// One block of 256 threads, E <= 256.  Rows keep their order within an expert.
 __global__ void __launch_bounds__(256) moe_sort_kernel(const int32_t *__restrict__ idx, int rows, int E,
                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                        int32_t *__restrict__ inv, int32_t *__restrict__ active) {
-    __shared__ int cnt[257];
-    __shared__ int start[257];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int c = 0;
-        for (int r = 0; r < rows; ++r) c += idx[r] == e;
-        cnt[e] = c;
-    }
+    __shared__ int cnt[256], run[256], ch[256];
+    const int tid = threadIdx.x;
+    cnt[tid] = 0;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0, na = 0;
-        for (int e = 0; e < E; ++e) {
-            start[e] = acc;
-            offsets[e] = acc;
-            acc += cnt[e];
-            if (cnt[e] > 0) active[1 + na++] = e;
+    for (int r = tid; r < rows; r += 256) atomicAdd(&cnt[idx[r]], 1);
+    __syncthreads();
+    if (tid < 64) {  // exclusive scans of the counts and of the hit flags, four experts per lane
+        int c[4], f[4], sc = 0, sf = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            c[q] = e < E ? cnt[e] : 0;
+            f[q] = c[q] > 0;
+            sc += c[q];
+            sf += f[q];
         }
-        offsets[E] = acc;
-        active[0] = na;
+        int ic = sc, jf = sf;  // inclusive prefix over lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int uc = __shfl_up(ic, o, 64), uf = __shfl_up(jf, o, 64);
+            if (tid >= o) {
+                ic += uc;
+                jf += uf;
+            }
+        }
+        int pc = ic - sc, pf = jf - sf;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            if (e < E) {
+                run[e] = pc;
+                offsets[e] = pc;
+                if (f[q]) active[1 + pf] = e;
+            }
+            pc += c[q];
+            pf += f[q];
+        }
+        if (tid == 63) {
+            offsets[E] = ic;
+            active[0] = jf;
+        }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int pos = start[e];
-        for (int r = 0; r < rows; ++r)
-            if (idx[r] == e) {
-                perm[pos] = r;
-                inv[r] = pos;
-                ++pos;
-            }
+    for (int base = 0; base < rows; base += 256) {
+        const int r = base + tid;
+        const int e = r < rows ? idx[r] : -1;
+        ch[tid] = e;
+        __syncthreads();
+        int pos = 0;
+        if (r < rows) {
+            int rank = 0;
+            for (int j = 0; j < tid; ++j) rank += ch[j] == e;
+            pos = run[e] + rank;
+            perm[pos] = r;
+            inv[r] = pos;
+        }
+        __syncthreads();  // every row of the chunk has read run[]
+        if (r < rows) atomicAdd(&run[e], 1);
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------ grouped expert projections
 // PASS 0: m[i] = swiglu(x[row(i)] . Wgu_e^T)  (Wgu_e [2*Ie][hid], output Ie columns)
 // PASS 1: y[i] = rho(m[i] . Wd_e^T)           (Wd_e [hid][Ie], output hid columns)
-// i runs over the sorted rows of expert e; row(i) = perm[i] / k for PASS 0.
+// i runs over the sorted rows of expert e; row(i) = perm[i] / k for PASS 0.  A wave streams
+// NR weight rows together: the gate and up rows of one output (PASS 0), or four outputs
+// (PASS 1, whose rows are short: Ie values).
 template <typename T, int PASS>
 __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ xin, const T *__restrict__ W,
                                                          int K, int N, int k, const int32_t *__restrict__ offsets,
@@ -172,17 +255,19 @@ __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ x
                                                          const int32_t *__restrict__ active, T *__restrict__ out) {
     constexpr int VN = Vec<T>::N;
     constexpr int MR = 8;
+    constexpr int NR = PASS == 0 ? 2 : 4;
     const int slot = blockIdx.y;
     if (slot >= active[0]) return;
     const int e = active[1 + slot];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = blockIdx.x * 4 + wave;
-    if (n >= N) return;
+    const int n0 = PASS == 0 ? blockIdx.x * 4 + wave : (blockIdx.x * 4 + wave) * NR;
+    if (n0 >= N) return;
     const int r0 = offsets[e], r1 = offsets[e + 1];
     const size_t wrows = PASS == 0 ? 2 * (size_t)N : (size_t)N;
     const T *We = W + (size_t)e * wrows * K;
-    const T *w0 = We + (size_t)n * K;
-    const T *w1 = We + (size_t)(PASS == 0 ? n + N : n) * K;
+    const T *wr[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) wr[q] = We + (size_t)(PASS == 0 ? n0 + q * N : min(n0 + q, N - 1)) * K;
     const int nc = K / VN;
     for (int rb = r0; rb < r1; rb += MR) {
         const int nr = min(MR, r1 - rb);
@@ -192,36 +277,39 @@ __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ x
             const int i = rb + min(m, nr - 1);
             xr[m] = PASS == 0 ? xin + (size_t)(perm[i] / k) * K : xin + (size_t)i * K;
         }
-        float a0[MR], a1[MR];
+        float a[NR][MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) a0[m] = a1[m] = 0.f;
+        for (int q = 0; q < NR; ++q)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) a[q][m] = 0.f;
         for (int c = lane; c < nc; c += 64) {
-            float wf0[VN], wf1[VN];
-            Vec<T>::expand(ld_stream(w0 + (size_t)c * VN), wf0);
-            if (PASS == 0) Vec<T>::expand(ld_stream(w1 + (size_t)c * VN), wf1);
+            float wf[NR][VN];
+#pragma unroll
+            for (int q = 0; q < NR; ++q) Vec<T>::expand(ld_stream(wr[q] + (size_t)c * VN), wf[q]);
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 if (m < nr) {
                     float xf[VN];
                     Vec<T>::expand(ld16(xr[m] + (size_t)c * VN), xf);
 #pragma unroll
-                    for (int x = 0; x < VN; ++x) {
-                        a0[m] += wf0[x] * xf[x];
-                        if (PASS == 0) a1[m] += wf1[x] * xf[x];
-                    }
+                    for (int q = 0; q < NR; ++q)
+#pragma unroll
+                        for (int x = 0; x < VN; ++x) a[q][m] += wf[q][x] * xf[x];
                 }
             }
         }
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m < nr) {
-                const float s0 = wave_sum(a0[m]);
-                const float s1 = PASS == 0 ? wave_sum(a1[m]) : 0.f;
-                if (lane == 0) {
-                    float v;
-                    if (PASS == 0) v = rho<T>(silu_f32(rho<T>(s0))) * rho<T>(s1);
-                    else v = s0;
-                    out[(size_t)(rb + m) * N + n] = from_f<T>(v);
+                if (PASS == 0) {
+                    const float s0 = wave_sum(a[0][m]), s1 = wave_sum(a[1][m]);
+                    if (lane == 0) out[(size_t)(rb + m) * N + n0] = from_f<T>(rho<T>(silu_f32(rho<T>(s0))) * rho<T>(s1));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NR; ++q) {
+                        const float sq = wave_sum(a[q][m]);
+                        if (lane == 0 && n0 + q < N) out[(size_t)(rb + m) * N + n0 + q] = from_f<T>(sq);
+                    }
                 }
             }
         }
@@ -229,20 +317,28 @@ __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ x
 }
 
 // ------------------------------------------------------------ weighted slot sum
+// grid (hid / 256, T): one thread per output element; the token's k sorted positions and
+// weights are loaded first, so the k row reads are in flight together.
 template <typename T>
 __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ y, const T *__restrict__ w,
-                                                          const int32_t *__restrict__ inv, int hid, int k,
+                                                          const int32_t *__restrict__ inv, int hid, int k, int rows,
                                                           T *__restrict__ out) {
-    const int t = blockIdx.x;
-    for (int n = threadIdx.x; n < hid; n += blockDim.x) {
-        float acc = 0.f;
-        for (int s = 0; s < k; ++s) {
-            const int r = t * k + s, p = inv[r];
-            if ((unsigned)p >= (unsigned)(gridDim.x * k)) continue;  // never for indices the top-k kernel writes
-            acc += rho<T>(to_f(y[(size_t)p * hid + n]) * to_f(w[r]));
+    const int t = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+    int p[16];
+    float ws[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < k) {
+            p[s] = inv[t * k + s];
+            ws[s] = to_f(w[t * k + s]);
         }
-        out[(size_t)t * hid + n] = from_f<T>(acc);
-    }
+    if (n >= hid) return;
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < k && (unsigned)p[s] < (unsigned)rows)  // always, for positions the sort writes
+            acc += rho<T>(to_f(y[(size_t)p[s] * hid + n]) * ws[s]);
+    out[(size_t)t * hid + n] = from_f<T>(acc);
 }
 
 // ------------------------------------------------------------ dispatch
@@ -259,14 +355,18 @@ static hipError_t moe_t(const void *x, int T_, int hid, const void *Wr, int E, i
     const int rows = T_ * k;
     hipError_t e = launch_linear(dt, x, T_, hid, Wr, E, EPI_STORE, nullptr, logits, s);
     if (e != hipSuccess) return e;
-    moe_topk_kernel<T><<<T_, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w);
-    moe_sort_kernel<<<1, 256, 0, s>>>(idx, rows, E, offsets, perm, inv, active);
+    if (T_ == 1) {
+        moe_route1_kernel<T><<<1, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w, offsets, perm, inv, active);
+    } else {
+        moe_topk_kernel<T><<<T_, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w);
+        moe_sort_kernel<<<1, 256, 0, s>>>(idx, rows, E, offsets, perm, inv, active);
+    }
     const int na_max = rows < E ? rows : E;
     moe_expert_kernel<T, 0><<<dim3((Ie + 3) / 4, na_max), 256, 0, s>>>((const T *)x, (const T *)Wgu, hid, Ie, k,
                                                                        offsets, perm, active, mbuf);
-    moe_expert_kernel<T, 1><<<dim3((hid + 3) / 4, na_max), 256, 0, s>>>(mbuf, (const T *)Wd, Ie, hid, k, offsets,
-                                                                        perm, active, ybuf);
-    moe_combine_kernel<T><<<T_, 256, 0, s>>>(ybuf, (const T *)w, inv, hid, k, (T *)out);
+    moe_expert_kernel<T, 1><<<dim3((hid + 15) / 16, na_max), 256, 0, s>>>(mbuf, (const T *)Wd, Ie, hid, k, offsets,
+                                                                          perm, active, ybuf);
+    moe_combine_kernel<T><<<dim3((hid + 255) / 256, T_), 256, 0, s>>>(ybuf, (const T *)w, inv, hid, k, rows, (T *)out);
     return hipGetLastError();
 }
 
