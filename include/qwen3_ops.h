@@ -34,7 +34,8 @@ int qwen3_op_linear(int dtype, const void *x, int M, int K, const void *W, int N
                     void *out, void *stream);
 
 /* The same with 8-bit affine group weights (bf16 activations): codes u8 [rows][K],
- * scale and bias bf16 [rows][K/64]; w = scale * code + bias, kept in fp32. */
+ * scale and bias bf16 [rows][K/64]; w = scale * code + bias, kept in fp32.
+ * QWEN3_ERR_UNSUPPORTED for M <= 16 with K > 8192. */
 int qwen3_op_linear_q8(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                        int N, int epilogue, const void *res, void *out, void *stream);
 

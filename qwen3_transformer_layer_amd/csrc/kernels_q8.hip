@@ -9,6 +9,8 @@
 //  - gemv_q8_kernel (M <= 16): each wave64 owns one output column; a lane reads
 //    16 codes (one 128-bit load) and the matching 16 bf16 activations, so a
 //    group's 64 codes are 4 lanes; weight bytes per column are K * (1 + 4/64).
+//    All code, scale and bias loads of a lane (up to 8 chunks: K <= 8192) are
+//    issued before any arithmetic (and, with the norm prologue, before the norm).
 //  - M > 16: the MFMA GEMM of kernels_gemm.hip when K % 128 == 0 and the scale and bias
 //    arrays are 4-byte aligned; otherwise gemm_q8_kernel: the bf16 MFMA GEMM tiling with K
 //    step = one group
@@ -16,6 +18,8 @@
 //    partial sum is exact products summed in fp32; it is folded into the
 //    running accumulator with the column's scale and bias and the row's
 //    activation sum over the group.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,7 +42,31 @@ static __device__ __forceinline__ float dot16_q8(u32x4 c, const float *xf) {
     return a;
 }
 
-template <int EPI, int MR>
+// Every code, scale and bias load of the lane's chunks (c = lane + 64 u, u < QU) is issued
+// before any arithmetic, so a wave keeps its whole row in flight; K <= 64 * 16 * QU, QU = 2, 4
+// or 8 picked from K (registers for unused chunks would lower the occupancy).
+constexpr int QU_MAX = 8;
+
+template <int QU> struct Q8Row {
+    u32x4 q[QU];
+    float s[QU], b[QU];
+};
+
+template <int QU>
+__device__ __forceinline__ void q8_row_load(Q8Row<QU> &r, const uint8_t *codes, const bf16 *scale, const bf16 *bias,
+                                            int row, int K, int ng, bool ok, int lane) {
+    const uint8_t *c0 = codes + (size_t)row * K;
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+        const int c = lane + 64 * u;
+        const bool v = ok && c < K / 16;
+        r.q[u] = v ? ld_stream(c0 + (size_t)c * 16) : u32x4{0, 0, 0, 0};
+        r.s[u] = v ? to_f(scale[(size_t)row * ng + (c >> 2)]) : 0.f;
+        r.b[u] = v ? to_f(bias[(size_t)row * ng + (c >> 2)]) : 0.f;
+    }
+}
+
+template <int EPI, int MR, int QU>
 __global__ void __launch_bounds__(256) gemv_q8_kernel(const bf16 *__restrict__ x, int M, int K,
                                                       const uint8_t *__restrict__ codes,
                                                       const bf16 *__restrict__ scale, const bf16 *__restrict__ bias,
@@ -46,54 +74,49 @@ __global__ void __launch_bounds__(256) gemv_q8_kernel(const bf16 *__restrict__ x
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = blockIdx.x * 4 + wave;
     if (n >= N) return;
-    const int ng = K / 64;
+    const int ng = K / 64, nch = K / 16;
     const int n1 = EPI == EPI_SWIGLU ? n + N : n;
-    const uint8_t *c0 = codes + (size_t)n * K, *c1 = codes + (size_t)n1 * K;
+    Q8Row<QU> r0, r1;
+    q8_row_load(r0, codes, scale, bias, n, K, ng, true, lane);
+    if (EPI == EPI_SWIGLU) q8_row_load(r1, codes, scale, bias, n1, K, ng, true, lane);
     float a0[MR], a1[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) a0[m] = a1[m] = 0.f;
-    const int nch = K / 16;  // 16-code chunks per row
-    for (int c = lane; c < nch; c += 64) {
-        const int g = c >> 2;
-        const u32x4 q0 = ld_stream(c0 + (size_t)c * 16);
-        u32x4 q1 = q0;
-        if (EPI == EPI_SWIGLU) q1 = ld_stream(c1 + (size_t)c * 16);
-        const float s0 = to_f(scale[(size_t)n * ng + g]), b0 = to_f(bias[(size_t)n * ng + g]);
-        float s1 = 0.f, b1 = 0.f;
-        if (EPI == EPI_SWIGLU) {
-            s1 = to_f(scale[(size_t)n1 * ng + g]);
-            b1 = to_f(bias[(size_t)n1 * ng + g]);
-        }
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m < M) {
-                float xf[16];
-                const bf16 *xp = x + (size_t)m * K + (size_t)c * 16;
-                Vec<bf16>::expand(ld16(xp), xf);
-                Vec<bf16>::expand(ld16(xp + 8), xf + 8);
-                float xs = 0.f;
+    for (int u = 0; u < QU; ++u) {
+        const int c = lane + 64 * u;
+        if (c < nch) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) xs += xf[i];
-                a0[m] += s0 * dot16_q8(q0, xf) + b0 * xs;
-                if (EPI == EPI_SWIGLU) a1[m] += s1 * dot16_q8(q1, xf) + b1 * xs;
+            for (int m = 0; m < MR; ++m) {
+                if (m < M) {
+                    float xf[16];
+                    const bf16 *xp = x + (size_t)m * K + (size_t)c * 16;
+                    Vec<bf16>::expand(ld16(xp), xf);
+                    Vec<bf16>::expand(ld16(xp + 8), xf + 8);
+                    float xs = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xs += xf[i];
+                    a0[m] += r0.s[u] * dot16_q8(r0.q[u], xf) + r0.b[u] * xs;
+                    if (EPI == EPI_SWIGLU) a1[m] += r1.s[u] * dot16_q8(r1.q[u], xf) + r1.b[u] * xs;
+                }
             }
         }
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         if (m < M) {
-            const float r0 = wave_sum(a0[m]);
-            const float r1 = EPI == EPI_SWIGLU ? wave_sum(a1[m]) : 0.f;
+            const float s0 = wave_sum(a0[m]);
+            const float s1 = EPI == EPI_SWIGLU ? wave_sum(a1[m]) : 0.f;
             if (lane == 0) {
                 const size_t idx = (size_t)m * N + n;
-                out[idx] = from_f<bf16>(epi_q8(EPI, r0, r1, res, idx));
+                out[idx] = from_f<bf16>(epi_q8(EPI, s0, s1, res, idx));
             }
         }
     }
 }
 
 // M == 1 with the RMSNorm prologue (norm_prologue): activations come from LDS.
-template <int EPI>
+template <int EPI, int QU>
 __global__ void __launch_bounds__(256) gemv_q8_norm_kernel(const bf16 *__restrict__ h_in, const bf16 *__restrict__ res,
                                                            const bf16 *__restrict__ nw, float eps,
                                                            bf16 *__restrict__ h_out, int K,
@@ -107,63 +130,59 @@ __global__ void __launch_bounds__(256) gemv_q8_norm_kernel(const bf16 *__restric
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = blockIdx.x * 4 + wave;
     const bool active = n < N;
-    const int ng = K / 64;
+    const int ng = K / 64, nch = K / 16;
     const int n1 = EPI == EPI_SWIGLU ? n + N : n;
-    const uint8_t *c0 = codes + (size_t)(active ? n : 0) * K, *c1 = codes + (size_t)(active ? n1 : 0) * K;
-    const int nch = K / 16;
-    constexpr int U = 4;
-    u32x4 pq0[U], pq1[U];  // first chunks in flight during the norm
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = lane + 64 * u;
-        const bool ok = active && c < nch;
-        pq0[u] = ok ? ld_stream(c0 + (size_t)c * 16) : u32x4{0, 0, 0, 0};
-        if (EPI == EPI_SWIGLU) pq1[u] = ok ? ld_stream(c1 + (size_t)c * 16) : u32x4{0, 0, 0, 0};
-    }
+    Q8Row<QU> r0, r1;  // the whole row in flight during the norm
+    q8_row_load(r0, codes, scale, bias, active ? n : 0, K, ng, active, lane);
+    if (EPI == EPI_SWIGLU) q8_row_load(r1, codes, scale, bias, active ? n1 : 0, K, ng, active, lane);
     norm_prologue<bf16>(h_in, res, nw, eps, h_out, K, ys, red);
     if (!active) return;
     float a0 = 0.f, a1 = 0.f;
-    auto consume = [&](int c, u32x4 q0, u32x4 q1) {
-        const int g = c >> 2;
-        float xf[16];
-        Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16], xf);
-        Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16 + 8], xf + 8);
-        float xs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xs += xf[i];
-        a0 += to_f(scale[(size_t)n * ng + g]) * dot16_q8(q0, xf) + to_f(bias[(size_t)n * ng + g]) * xs;
-        if (EPI == EPI_SWIGLU)
-            a1 += to_f(scale[(size_t)n1 * ng + g]) * dot16_q8(q1, xf) + to_f(bias[(size_t)n1 * ng + g]) * xs;
-    };
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < QU; ++u) {
         const int c = lane + 64 * u;
-        if (c < nch) consume(c, pq0[u], pq1[u]);
+        if (c < nch) {
+            float xf[16];
+            Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16], xf);
+            Vec<bf16>::expand(*(const u32x4 *)&ys[c * 16 + 8], xf + 8);
+            float xs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xs += xf[i];
+            a0 += r0.s[u] * dot16_q8(r0.q[u], xf) + r0.b[u] * xs;
+            if (EPI == EPI_SWIGLU) a1 += r1.s[u] * dot16_q8(r1.q[u], xf) + r1.b[u] * xs;
+        }
     }
-    for (int c = lane + 64 * U; c < nch; c += 64) {
-        const u32x4 q0 = ld_stream(c0 + (size_t)c * 16);
-        const u32x4 q1 = EPI == EPI_SWIGLU ? ld_stream(c1 + (size_t)c * 16) : q0;
-        consume(c, q0, q1);
-    }
-    const float r0 = wave_sum(a0);
-    const float r1 = EPI == EPI_SWIGLU ? wave_sum(a1) : 0.f;
-    if (lane == 0) out[n] = from_f<bf16>(epi_q8(EPI, r0, r1, nullptr, n));
+    const float s0 = wave_sum(a0);
+    const float s1 = EPI == EPI_SWIGLU ? wave_sum(a1) : 0.f;
+    if (lane == 0) out[n] = from_f<bf16>(epi_q8(EPI, s0, s1, nullptr, n));
 }
 
 hipError_t launch_linear_q8_norm(const void *h_in, const void *res, const void *nw, float eps, void *h_out, int K,
                                  const uint8_t *codes, const void *scale, const void *bias, int group, int N,
                                  int epi, void *out, hipStream_t s) {
-    if (group != 64 || epi == EPI_RESID) return hipErrorInvalidValue;
+    if (group != 64 || epi == EPI_RESID || K > 64 * 16 * QU_MAX) return hipErrorInvalidValue;
     const dim3 grid((N + 3) / 4);
     const size_t lds = (size_t)K * sizeof(bf16);
     const bf16 *hi = (const bf16 *)h_in, *rr = (const bf16 *)res, *ww = (const bf16 *)nw;
     const bf16 *sc = (const bf16 *)scale, *bi = (const bf16 *)bias;
-    if (epi == EPI_SWIGLU)
-        gemv_q8_norm_kernel<EPI_SWIGLU><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (bf16 *)h_out, K, codes, sc, bi, N,
-                                                               (bf16 *)out);
-    else
-        gemv_q8_norm_kernel<EPI_STORE><<<grid, 256, lds, s>>>(hi, rr, ww, eps, (bf16 *)h_out, K, codes, sc, bi, N,
-                                                              (bf16 *)out);
+    auto go = [&](auto epi_c, auto qu_c) {
+        gemv_q8_norm_kernel<decltype(epi_c)::value, decltype(qu_c)::value><<<grid, 256, lds, s>>>(
+            hi, rr, ww, eps, (bf16 *)h_out, K, codes, sc, bi, N, (bf16 *)out);
+    };
+    using I = std::integral_constant<int, EPI_STORE>;
+    using G = std::integral_constant<int, EPI_SWIGLU>;
+    using U2 = std::integral_constant<int, 2>;
+    using U4 = std::integral_constant<int, 4>;
+    using U8 = std::integral_constant<int, 8>;
+    if (epi == EPI_SWIGLU) {
+        if (K <= 2048) go(G{}, U2{});
+        else if (K <= 4096) go(G{}, U4{});
+        else go(G{}, U8{});
+    } else {
+        if (K <= 2048) go(I{}, U2{});
+        else if (K <= 4096) go(I{}, U4{});
+        else go(I{}, U8{});
+    }
     return hipGetLastError();
 }
 
@@ -314,16 +333,23 @@ static void gemv_q8_dispatch(const void *x, int M, int K, const uint8_t *codes, 
     const dim3 grid((N + 3) / 4);
     const bf16 *xx = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *rr = (const bf16 *)res;
     bf16 *oo = (bf16 *)out;
-    if (M <= 1) gemv_q8_kernel<EPI, 1><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
-    else if (M <= 4) gemv_q8_kernel<EPI, 4><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
-    else if (M <= 8) gemv_q8_kernel<EPI, 8><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
-    else gemv_q8_kernel<EPI, 16><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+    auto go = [&](auto mr_c) {
+        constexpr int MR = decltype(mr_c)::value;
+        if (K <= 2048) gemv_q8_kernel<EPI, MR, 2><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+        else if (K <= 4096) gemv_q8_kernel<EPI, MR, 4><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+        else gemv_q8_kernel<EPI, MR, 8><<<grid, 256, 0, s>>>(xx, M, K, codes, sc, bi, N, rr, oo);
+    };
+    if (M <= 1) go(std::integral_constant<int, 1>{});
+    else if (M <= 4) go(std::integral_constant<int, 4>{});
+    else if (M <= 8) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
 }
 
 hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                             int group, int N, int epi, const void *res, void *out, hipStream_t s) {
     if (group != 64) return hipErrorInvalidValue;
     if (M <= 16) {
+        if (K > 64 * 16 * QU_MAX) return hipErrorInvalidValue;
         if (epi == EPI_SWIGLU) gemv_q8_dispatch<EPI_SWIGLU>(x, M, K, codes, scale, bias, N, res, out, s);
         else if (epi == EPI_RESID) gemv_q8_dispatch<EPI_RESID>(x, M, K, codes, scale, bias, N, res, out, s);
         else gemv_q8_dispatch<EPI_STORE>(x, M, K, codes, scale, bias, N, res, out, s);

@@ -153,6 +153,8 @@ int check_config(const qwen3_config *c, std::string *why) {
         if (c->quant_bits != 8 || c->quant_group != 64)
             return bad(QWEN3_ERR_UNSUPPORTED, "quantised weights must be 8-bit in groups of 64");
         if (c->dtype != QWEN3_BF16) return bad(QWEN3_ERR_UNSUPPORTED, "quantised weights need the bf16 dtype");
+        if (c->hidden > 8192 || c->n_heads * c->head_dim > 8192 || c->intermediate > 8192)
+            return bad(QWEN3_ERR_UNSUPPORTED, "quantised projections need input widths <= 8192");
     }
     return QWEN3_OK;
 }

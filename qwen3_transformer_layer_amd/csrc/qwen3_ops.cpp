@@ -33,6 +33,7 @@ int qwen3_op_linear_q8(const void *x, int M, int K, const uint8_t *codes, const 
     if (!x || !codes || !scale || !bias || !out || M < 1 || K < 64 || K % 64 || N < 1 || epilogue < 0 || epilogue > 2)
         return QWEN3_ERR_ARG;
     if (epilogue == EPI_RESID && !res) return QWEN3_ERR_ARG;
+    if (M <= 16 && K > 8192) return QWEN3_ERR_UNSUPPORTED;  // the GEMV keeps a whole row in flight
     return hip_rc(launch_linear_q8(x, M, K, codes, scale, bias, 64, N, epilogue, res, out, (hipStream_t)stream));
 }
 
