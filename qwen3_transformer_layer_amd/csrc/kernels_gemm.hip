@@ -15,10 +15,12 @@
 //    the row (chunk ^ ((row >> 1) & 7) for 128-B rows, chunk ^ ((row >> 2) & 3) for 64-B rows),
 //    so 16 lanes reading 16 consecutive rows at one chunk hit distinct banks.  A copy's lane
 //    -> address map writes that layout directly.
-//  - Tile shapes: 256 x 128 with 8 waves when that still gives >= 192 tiles (gate|up and
-//    q|k|v at T = 2048), else 128 x 128 with 4 waves and 4 stages (o_proj and down, and
-//    small T).  Measured on the 2048-token projections against a 128 x 256 / 4-wave tiling:
-//    gate|up 148 -> 125 us, q|k|v 48 -> 40 us.
+//  - Tile shapes, the largest that still gives >= 192 tiles: 256 x 128 with 8 waves (gate|up
+//    and q|k|v at T = 2048), 128 x 128 with 8 waves (o_proj and down at T = 2048), else
+//    128 x 64 (64 x 128 for SWIGLU, whose waves hold gate/up pairs) with 4 waves.  Measured
+//    against one 128 x 256 / 4-wave tiling at T = 2048: gate|up 148 -> 125 us, q|k|v 48 -> 40,
+//    o_proj 40 -> 31; at T = 512 o_proj 54 -> 20 and down 101 -> 38.  8-bit weights: 128 x
+//    128 with 4 waves, else 64 x 128 (the copy kinds must split evenly over the waves).
 //  - 8-bit weights (one K step = one group): the codes (64 B per row) are copied to LDS like
 //    the bf16 operand; the scale and bias words of the group arrive by 4-byte direct copies
 //    (the aligned word holding groups 2i and 2i+1).  K is interleaved per lane so one 16-byte
@@ -45,7 +47,7 @@ template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_> struct Cfg {
     static constexpr int OPS = NBIG + NSMALL, PW = OPS / NW, APW = ACOP / NW, BPW = NBIG / NW;
     static constexpr int WTM = BM / WM, WTN = BN / WN, NI = WTM / 32, NT = WTN / 32;
     static_assert(OPS % NW == 0 && ACOP % NW == 0 && NBIG % NW == 0, "copy kinds split evenly over the waves");
-    static_assert(NI >= 1 && NT >= 1 && NT % 2 == 0, "wave tile at least 32 x 64");
+    static_assert(NI >= 1 && NT >= 1, "wave tile at least 32 x 32");
 };
 
 __device__ __forceinline__ int offA(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
@@ -97,6 +99,7 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
                                                           const bf16 *__restrict__ bias, int N,
                                                           const bf16 *__restrict__ res, bf16 *__restrict__ out) {
     using namespace g2;
+    static_assert(EPI != EPI_SWIGLU || C::NT % 2 == 0, "a SWIGLU wave holds gate and up tiles in pairs");
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,8 +264,17 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
 
 namespace {
 typedef g2::Cfg<256, 128, 3, 4, 2, false> Wide;    // 8 waves, 64 x 64 per wave, 144 KB LDS
-typedef g2::Cfg<128, 128, 4, 2, 2, false> Narrow;  // 4 waves, 64 x 64 per wave, 128 KB LDS
+typedef g2::Cfg<128, 128, 4, 4, 2, false> Mid;     // 8 waves, 32 x 64 per wave, 128 KB LDS
+typedef g2::Cfg<128, 64, 4, 2, 2, false> SmallN;   // 4 waves, 64 x 32 per wave, 96 KB LDS
+typedef g2::Cfg<64, 128, 4, 2, 2, false> SmallM;   // 4 waves, 32 x 64 per wave, 96 KB LDS
 typedef g2::Cfg<128, 128, 4, 2, 2, true> Quant;    // 4 waves, 100 KB LDS
+typedef g2::Cfg<64, 128, 4, 2, 2, true> QuantS;    // 4 waves, 68 KB LDS
+
+// Output tiles of a BM x BN weight-row tiling (a SWIGLU tile covers BN/2 outputs).
+template <class C> long tiles(int M, int N, int epi) {
+    const long cols = epi == EPI_SWIGLU ? C::BN / 2 : C::BN;
+    return (long)((M + C::BM - 1) / C::BM) * ((N + cols - 1) / cols);
+}
 
 template <int EPI, class C>
 hipError_t launch_c(const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N, const bf16 *res,
@@ -296,10 +308,11 @@ hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, in
                            hipStream_t s) {
     const bf16 *a = (const bf16 *)x, *r = (const bf16 *)res;
     bf16 *o = (bf16 *)out;
-    const long cols = epi == EPI_SWIGLU ? Wide::BN / 2 : Wide::BN;
-    const long wide_tiles = (long)((M + Wide::BM - 1) / Wide::BM) * ((N + cols - 1) / cols);
-    if (wide_tiles >= 192) return launch_e<Wide>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
-    return launch_e<Narrow>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+    if (tiles<Wide>(M, N, epi) >= 192) return launch_e<Wide>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+    if (tiles<Mid>(M, N, epi) >= 192) return launch_e<Mid>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+    if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, SmallM>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+    if (epi == EPI_RESID) return launch_c<EPI_RESID, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+    return launch_c<EPI_STORE, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
 }
 
 bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias) {
@@ -308,8 +321,9 @@ bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias) {
 
 hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                               int N, int epi, const void *res, void *out, hipStream_t s) {
-    return launch_e<Quant>(epi, (const bf16 *)x, M, K, codes, (const bf16 *)scale, (const bf16 *)bias, N,
-                           (const bf16 *)res, (bf16 *)out, s);
+    const bf16 *a = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *r = (const bf16 *)res;
+    if (tiles<Quant>(M, N, epi) >= 192) return launch_e<Quant>(epi, a, M, K, codes, sc, bi, N, r, (bf16 *)out, s);
+    return launch_e<QuantS>(epi, a, M, K, codes, sc, bi, N, r, (bf16 *)out, s);
 }
 
 }  // namespace q3
