@@ -10,7 +10,15 @@
 //    of the group (each K/V row is read from HBM once per step), keeps
 //    un-normalised partial sums (max, sum of exp, exp-weighted V) in fp32,
 //    and a combine kernel merges the splits with the usual log-sum-exp scaling.
-//  - attn_prefill_mfma_kernel (T > 1, bf16): causal flash attention on MFMA.
+//  - attn_prefill_fa_kernel (T > 1, bf16, head_dim 128): causal flash attention on
+//    v_mfma_f32_32x32x16_bf16.  Block = 32 queries x the G heads of one kv head (two waves
+//    per head, each taking one 32-key half of every tile; all waves share one causal key
+//    range); K/V tiles of 64 keys arrive by direct-to-LDS copies in a 2-stage ring.  S^T = K Q^T leaves each lane one query and
+//    32 of the tile's keys, which is exactly the P^T operand layout of O^T += V^T P^T once
+//    the keys of each 16-key MFMA step are taken in the order {4h..4h+3, 8+4h..8+4h+3}
+//    (h = lane / 32); V^T comes from the LDS transpose read.  The grid is 1-D with kv head
+//    b % KV (one kv head per XCD when KV = 8) and the heaviest query tiles first.
+//  - attn_prefill_mfma_kernel (T > 1, bf16, head_dim 64): causal flash attention on MFMA.
 //    Computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (q and k are bf16
 //    values, so the products are exact and the sums fp32), an online fp32
 //    softmax, and O^T += V^T P^T where the fp32 P is split into bf16 hi + lo
@@ -403,6 +411,210 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
     }
 }
 
+// ------------------------------------------------------------ bf16 causal flash prefill, head_dim 128
+// Block: 32 queries x the G heads of one kv head; two waves per head, wave parity w splits
+// every 64-key tile into halves (keys 32 w .. 32 w + 31), so a CU holds 2 waves per SIMD and
+// one wave's softmax arithmetic overlaps another's MFMAs.  Each wave keeps its own running
+// maximum, sum and O; at the end the parity-1 wave hands them over through LDS and the
+// parity-0 wave merges (log-sum-exp scaling) and stores.  The running maximum is raised only
+// when a tile's maximum exceeds it by more than 8 (base 2), so probabilities stay <= 2^8 in
+// fp32 and the O rescale is rare; the normalised result is the same softmax.
+// LDS: per stage a K tile and a V tile of 64 rows x 256 B.  K rows: 16-byte chunk c at slot
+// c ^ (row & 15) (16 lanes reading 16 rows at one chunk hit distinct banks); V rows: chunk c
+// at slot c ^ (4 (row & 3)) (a transpose read covers 4 rows x 32 B per 16 lanes: distinct
+// banks for 32 lanes).
+template <int G>
+struct FaGeo {
+    static constexpr int D = 128, RB = 256, KT = 64, ST = 2, NW = 2 * G;
+    static constexpr int TILE = KT * RB, STAGE = 2 * TILE;
+    static constexpr int COPIES = STAGE / 1024, PW = COPIES / NW, HALF = PW / 2;
+    static constexpr int MERGE = D * 32 * 4 + 2 * 32 * 4;  // O, then m and l of 32 queries (fp32)
+    static constexpr int LDS = (ST * STAGE > G * MERGE) ? ST * STAGE : G * MERGE;
+    static_assert(COPIES % (2 * NW) == 0, "K and V copies split evenly over the waves");
+};
+
+template <int G>
+__global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
+                                                                  const bf16 *__restrict__ Vc, int T, int H, int KV,
+                                                                  int cap, int p0, float scale_log2,
+                                                                  bf16 *__restrict__ out) {
+    using F = FaGeo<G>;
+    constexpr int D = F::D, RB = F::RB, KT = F::KT;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
+    const int ntiles = (T + 31) / 32;
+    const int g = blockIdx.x % KV, qt = ntiles - 1 - (int)(blockIdx.x / KV);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hw = wave >> 1, par = wave & 1;
+    const int h = g * G + hw, t0 = qt * 32;
+    const int qi = lane & 31, hh = lane >> 5;
+    const int tq = min(t0 + qi, T - 1), qpos = p0 + tq;
+    const int kmax = p0 + min(t0 + 31, T - 1);  // the block's queries see keys 0..kmax
+    const int nkt = kmax / KT + 1;
+    const bf16 *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
+    const unsigned lds0 = (unsigned)(uintptr_t)fa_smem;
+
+    bf16x8 qf[D / 16];  // Q^T operand: query qi, d = 16 ks + 8 hh + 0..7
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, ld16(q + ((size_t)tq * H + h) * D + 16 * ks + 8 * hh));
+
+    // copy i < HALF of this wave: K rows; i >= HALF: V rows (4 rows of 256 B per copy)
+    auto issue = [&](int kt) {
+        const unsigned st = lds0 + (kt % F::ST) * F::STAGE;
+        const int slot = lane & 15;
+#pragma unroll
+        for (int i = 0; i < F::PW; ++i) {
+            const bool isv = i >= F::HALF;
+            const int dl = (isv ? i - F::HALF : i) * F::NW + wave;
+            const int r = dl * 4 + (lane >> 4);
+            const int c = isv ? (slot ^ (4 * (r & 3))) : (slot ^ (r & 15));
+            const int key = min(kt * KT + r, kmax);  // rows past kmax are masked
+            dma16((isv ? Vg : Kg) + (size_t)key * D + c * 8,
+                  __builtin_amdgcn_readfirstlane(st + (isv ? F::TILE : 0) + dl * 1024));
+        }
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const int gi = lane >> 4, sl = lane & 15;  // transpose-read group and source lane
+
+    issue(0);
+    for (int kt = 0; kt < nkt; ++kt) {
+        wait_vm<0>();
+        __syncthreads();  // stage kt landed for every wave; every wave finished kt - 1
+        if (kt + 1 < nkt) issue(kt + 1);
+        const int kb0 = kt * KT + 32 * par;  // this wave's 32 keys
+        if (kb0 > kmax) continue;            // all masked for every query of the block
+        const unsigned char *Ks = fa_smem + (kt % F::ST) * F::STAGE, *Vs = Ks + F::TILE;
+        f32x16 sc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+        {
+            const int r = 32 * par + qi;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 kf = *(const bf16x8 *)(Ks + r * RB + (((2 * ks + hh) ^ (r & 15)) << 4));
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
+            }
+        }
+        // accumulator v of S^T: key kb0 + 8 (v / 4) + 4 hh + v % 4, query qi
+        const bool need_mask = kb0 + 31 > p0 + t0;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float sv = sc[v] * scale_log2;
+            if (need_mask && kb0 + 8 * (v >> 2) + 4 * hh + (v & 3) > qpos) sv = -INFINITY;
+            sc[v] = sv;
+            tmax = fmaxf(tmax, sv);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool up = tmax > m_run + 8.0f;  // also on the first tile with a visible key
+        const float m_use = up ? tmax : m_run;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
+        if (__ballot(up)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+        }
+        m_run = m_use;
+        const float m_exp = m_use == -INFINITY ? 0.f : m_use;  // no visible key yet: every p is 0
+        float psum = 0.f;
+        bf16x8 phi[2], plo[2];  // P^T operand of 16-key step cc: values 8 cc .. 8 cc + 7
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(sc[8 * cc + e] - m_exp);
+                psum += pv;
+                const __bf16 hb = (__bf16)pv;
+                phi[cc][e] = hb;
+                plo[cc][e] = (__bf16)(pv - (float)hb);
+            }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        // V^T operand: group gi reads rows 32 par + 16 cc + 4 (gi / 2) (+ 8) and columns
+        // 32 dt + 16 (gi % 2) + 0..15; lane r of the group receives 4 keys of column 16 (gi % 2) + r
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d0 = 32 * dt + 16 * (gi & 1) + 4 * (sl & 3);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int r0 = 32 * par + 16 * cc + 4 * (gi >> 1) + (sl >> 2), r1 = r0 + 8;
+                const s16x4 lo4 = lds_tr_b64((const uint16_t *)(Vs + r0 * RB + (((d0 >> 3) ^ (4 * (r0 & 3))) << 4) +
+                                                                ((d0 >> 2) & 1) * 8));
+                const s16x4 hi4 = lds_tr_b64((const uint16_t *)(Vs + r1 * RB + (((d0 >> 3) ^ (4 * (r1 & 3))) << 4) +
+                                                                ((d0 >> 2) & 1) * 8));
+                bf16x8 vf;
+                short *vs = (short *)&vf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vs[e] = lo4[e];
+                    vs[4 + e] = hi4[e];
+                }
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[cc], o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[cc], o[dt], 0, 0, 0);
+            }
+        }
+    }
+    // merge the two key halves of each head: parity 1 hands over (m, l, O) through LDS
+    __syncthreads();  // every wave is done with the K/V tiles
+    float *mb = (float *)(fa_smem + hw * F::MERGE);  // O as [dt][v][lane], then m[32], l[32]
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mb[(dt * 16 + v) * 64 + lane] = o[dt][v];
+        if (lane < 32) {
+            mb[D * 32 + lane] = m_run;
+            mb[D * 32 + 32 + lane] = l_run;
+        }
+    }
+    __syncthreads();
+    if (par == 0 && t0 + qi < T) {
+        const float m1 = mb[D * 32 + qi], l1 = mb[D * 32 + 32 + qi];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+        const float inv = 1.0f / (l_run * a0 + l1 * a1);
+        bf16 *dst = out + (size_t)tq * H * D + (size_t)h * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * v4 + e;
+                    r[e] = (o[dt][v] * a0 + mb[(dt * 16 + v) * 64 + lane] * a1) * inv;
+                }
+                uint2 w;
+                w.x = pack_bf2(r[0], r[1]);
+                w.y = pack_bf2(r[2], r[3]);
+                *(uint2 *)&dst[32 * dt + 8 * v4 + 4 * hh] = w;
+            }
+    }
+}
+
+template <int G>
+static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T, int H, int KV, int cap, int p0,
+                             float sl2, bf16 *out, hipStream_t s) {
+    const size_t lds = FaGeo<G>::LDS;
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute((const void *)attn_prefill_fa_kernel<G>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int ntiles = (T + 31) / 32;
+    attn_prefill_fa_kernel<G><<<ntiles * KV, 128 * G, lds, s>>>(q, k, v, T, H, KV, cap, p0, sl2, out);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ dispatch
 template <typename T, int D, int G>
 static void decode_launch(bool fused, dim3 grid, size_t lds, hipStream_t s, const void *q, const void *qkv, int H,
@@ -478,6 +690,13 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
         const bf16 *qq = (const bf16 *)q, *kk = (const bf16 *)k_cache, *vv = (const bf16 *)v_cache;
         bf16 *oo = (bf16 *)out;
         const int G = H / KV;
+        if (D == 128) {
+            if (G == 1) return prefill_fa<1>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
+            if (G == 2) return prefill_fa<2>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
+            if (G == 4) return prefill_fa<4>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
+            if (G == 8) return prefill_fa<8>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
+            return hipErrorInvalidValue;
+        }
         const int QB = G >= 4 ? 16 : 64 / G, NT = 64 * (G >= 8 ? 8 : 4);
         const dim3 grid((T + QB - 1) / QB, KV);
 #define PREFILL_CASE(DD, GG)                                                                                   \
