@@ -17,7 +17,8 @@
 //    32 of the tile's keys, which is exactly the P^T operand layout of O^T += V^T P^T once
 //    the keys of each 16-key MFMA step are taken in the order {4h..4h+3, 8+4h..8+4h+3}
 //    (h = lane / 32); V^T comes from the LDS transpose read.  The grid is 1-D with kv head
-//    b % KV (one kv head per XCD when KV = 8) and the heaviest query tiles first.
+//    b % KV (one kv head per XCD when KV = 8); query tiles run heavy half descending, then
+//    light half ascending.
 //  - attn_prefill_mfma_kernel (T > 1, bf16, head_dim 64): causal flash attention on MFMA.
 //    Computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (q and k are bf16
 //    values, so the products are exact and the sums fp32), an online fp32
@@ -441,8 +442,11 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
     using F = FaGeo<G>;
     constexpr int D = F::D, RB = F::RB, KT = F::KT;
     extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
-    const int ntiles = (T + 31) / 32;
-    const int g = blockIdx.x % KV, qt = ntiles - 1 - (int)(blockIdx.x / KV);
+    const int ntiles = (T + 31) / 32, heavy = (ntiles + 1) / 2;
+    // query tile order: the heavy half from the last tile down, then the light half from the
+    // first tile up, so the two blocks a CU holds at once carry about equal causal work
+    const int bi = (int)(blockIdx.x / KV), g = blockIdx.x % KV;
+    const int qt = bi < heavy ? ntiles - 1 - bi : bi - heavy;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = wave >> 1, par = wave & 1;
     const int h = g * G + hw, t0 = qt * 32;
