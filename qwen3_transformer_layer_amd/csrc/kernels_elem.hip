@@ -76,9 +76,70 @@ __global__ void __launch_bounds__(256) add_rmsnorm_kernel(const T *__restrict__ 
     }
 }
 
+// 16 bytes of type T from VN fp32 values (each rounded once).
+template <typename T> __device__ __forceinline__ void store_vec(T *dst, const float *v);
+template <> __device__ __forceinline__ void store_vec<bf16>(bf16 *dst, const float *v) {
+    *(u32x4 *)dst = u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+}
+template <> __device__ __forceinline__ void store_vec<float>(float *dst, const float *v) {
+    *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+// The same with the row held in registers (n <= 256 * VN * MAXC): each thread keeps its
+// chunks c = tid + 256 i, and every store is 16 bytes.  Same arithmetic and order as above.
+template <typename T, int MAXC>
+__global__ void __launch_bounds__(256) add_rmsnorm_reg_kernel(const T *__restrict__ h_in, const T *__restrict__ res,
+                                                              const T *__restrict__ w, T *__restrict__ h_out,
+                                                              T *__restrict__ y, int n, float eps) {
+    constexpr int VN = Vec<T>::N;
+    __shared__ float red[8];
+    const size_t row = blockIdx.x;
+    const int nc = n / VN;
+    float v[MAXC][VN];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < nc) {
+            Vec<T>::expand(ld16(h_in + row * n + (size_t)c * VN), v[i]);
+            if (res) {
+                float r[VN];
+                Vec<T>::expand(ld16(res + row * n + (size_t)c * VN), r);
+#pragma unroll
+                for (int e = 0; e < VN; ++e) v[i][e] = rho<T>(v[i][e] + r[e]);
+                if (h_out) store_vec<T>(h_out + row * n + (size_t)c * VN, v[i]);
+            }
+#pragma unroll
+            for (int e = 0; e < VN; ++e) ss += v[i][e] * v[i][e];
+        }
+    }
+    const float r = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < nc) {
+            float wv[VN], o[VN];
+            Vec<T>::expand(ld16(w + (size_t)c * VN), wv);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) o[e] = wv[e] * rho<T>(v[i][e] * r);
+            store_vec<T>(y + row * n + (size_t)c * VN, o);
+        }
+    }
+}
+
 hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const void *w, void *h_out, void *y,
                               int T, int n, float eps, hipStream_t s) {
     const size_t lds = (size_t)n * sizeof(float);
+    if (dt == DT_BF16 && n <= 256 * 8 * 4) {
+        add_rmsnorm_reg_kernel<bf16, 4><<<T, 256, 0, s>>>((const bf16 *)h_in, (const bf16 *)res, (const bf16 *)w,
+                                                         (bf16 *)h_out, (bf16 *)y, n, eps);
+        return hipGetLastError();
+    }
+    if (dt == DT_FP32 && n <= 256 * 4 * 4) {
+        add_rmsnorm_reg_kernel<float, 4><<<T, 256, 0, s>>>((const float *)h_in, (const float *)res,
+                                                          (const float *)w, (float *)h_out, (float *)y, n, eps);
+        return hipGetLastError();
+    }
     if (dt == DT_BF16)
         add_rmsnorm_kernel<bf16><<<T, 256, lds, s>>>((const bf16 *)h_in, (const bf16 *)res, (const bf16 *)w,
                                                      (bf16 *)h_out, (bf16 *)y, n, eps);
@@ -172,10 +233,91 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_kernel(
     }
 }
 
+// The same with D/8 lanes per head: lane li of a head owns elements 4 li .. 4 li + 3 and their
+// rotate-half partners 4 li + D/2 .., so every access is 8 bytes (bf16), a wave holds 512 / D
+// heads, and the norm's sum of squares is a butterfly over the head's lanes.  The table row
+// and the norm weights are read once per token.
+template <int D>
+__global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
+    const bf16 *__restrict__ qkv, int H, int KV, const bf16 *__restrict__ q_norm, const bf16 *__restrict__ k_norm,
+    float eps, const bf16 *__restrict__ cos_t, const bf16 *__restrict__ sin_t, int p0, int cap,
+    bf16 *__restrict__ q_out, bf16 *__restrict__ kc, bf16 *__restrict__ vc) {
+    constexpr int LPH = D / 8, HPW = 64 / LPH, half = D / 2;  // lanes per head, heads per wave
+    const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane % LPH, sub = lane / LPH, e1 = 4 * li, e2 = e1 + half;
+    const int nqkv = (H + 2 * KV) * D, p = p0 + t;
+    float c1[4], s1[4], c2[4], s2[4], wq1[4], wq2[4], wk1[4], wk2[4];
+    auto ld4 = [](const bf16 *src, float *o) {
+        const uint2 u = *(const uint2 *)src;
+        o[0] = bf_lo(u.x); o[1] = bf_hi(u.x); o[2] = bf_lo(u.y); o[3] = bf_hi(u.y);
+    };
+    ld4(cos_t + (size_t)p * D + e1, c1);
+    ld4(sin_t + (size_t)p * D + e1, s1);
+    ld4(cos_t + (size_t)p * D + e2, c2);
+    ld4(sin_t + (size_t)p * D + e2, s2);
+    ld4(q_norm + e1, wq1);
+    ld4(q_norm + e2, wq2);
+    ld4(k_norm + e1, wk1);
+    ld4(k_norm + e2, wk2);
+    const int nh = H + KV;
+    for (int hb = wave * HPW; hb < nh; hb += HPW * (blockDim.x >> 6)) {
+        const int hh = hb + sub;
+        const bool on = hh < nh;
+        float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
+        if (on) {
+            ld4(qkv + (size_t)t * nqkv + (size_t)hh * D + e1, x1);
+            ld4(qkv + (size_t)t * nqkv + (size_t)hh * D + e2, x2);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+#pragma unroll
+        for (int o = 1; o < LPH; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        const float r = 1.0f / sqrtf(ss / (float)D + eps);
+        if (!on) continue;
+        const bool isq = hh < H;
+        float o1[4], o2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float n1 = rho<bf16>((isq ? wq1[e] : wk1[e]) * rho<bf16>(x1[e] * r));
+            const float n2 = rho<bf16>((isq ? wq2[e] : wk2[e]) * rho<bf16>(x2[e] * r));
+            o1[e] = n1 * c1[e] - n2 * s1[e];
+            o2[e] = n2 * c2[e] + n1 * s2[e];
+        }
+        const uint2 w1 = {pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3])};
+        const uint2 w2 = {pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3])};
+        if (isq) {
+            bf16 *dst = q_out + ((size_t)t * H + hh) * D;
+            *(uint2 *)(dst + e1) = w1;
+            *(uint2 *)(dst + e2) = w2;
+        } else {
+            const int g = hh - H;
+            bf16 *kd = kc + ((size_t)g * cap + p) * D;
+            *(uint2 *)(kd + e1) = w1;
+            *(uint2 *)(kd + e2) = w2;
+            const bf16 *vrow = qkv + (size_t)t * nqkv + (size_t)(H + KV + g) * D;
+            bf16 *vd = vc + ((size_t)g * cap + p) * D;
+            *(uint2 *)(vd + e1) = *(const uint2 *)(vrow + e1);
+            *(uint2 *)(vd + e2) = *(const uint2 *)(vrow + e2);
+        }
+    }
+}
+
 hipError_t launch_qknorm_rope_kv(int dt, const void *qkv, int T, int H, int KV, int D, const void *q_norm,
                                  const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
                                  int cap, void *q_out, void *k_cache, void *v_cache, hipStream_t s) {
     const dim3 grid(T);
+    if (dt == DT_BF16 && (D == 128 || D == 64)) {
+        const bf16 *a = (const bf16 *)qkv, *qn = (const bf16 *)q_norm, *kn = (const bf16 *)k_norm;
+        const bf16 *ct = (const bf16 *)cos_t, *st = (const bf16 *)sin_t;
+        if (D == 128)
+            qknorm_rope_kv_vec_kernel<128><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, eps, ct, st, p0, cap, (bf16 *)q_out,
+                                                                 (bf16 *)k_cache, (bf16 *)v_cache);
+        else
+            qknorm_rope_kv_vec_kernel<64><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, eps, ct, st, p0, cap, (bf16 *)q_out,
+                                                                (bf16 *)k_cache, (bf16 *)v_cache);
+        return hipGetLastError();
+    }
     if (dt == DT_BF16)
         qknorm_rope_kv_kernel<bf16><<<grid, 256, 0, s>>>((const bf16 *)qkv, H, KV, D, (const bf16 *)q_norm,
                                                         (const bf16 *)k_norm, eps, (const bf16 *)cos_t,
