@@ -71,7 +71,7 @@ def test_add_rmsnorm(orc, dtype, n, ops):
 # (2000, 128, 1900) 128 x 128 / 8 waves (SWIGLU: 256 x 128); (300, 192, 4100) SWIGLU 128 x 128,
 # the others 128 x 64; the remaining M > 16 cases 128 x 64 (SWIGLU 64 x 128).  Ragged M and N.
 LIN_CASES = [(1, 2048, 4096), (3, 2048, 384), (16, 256, 512), (40, 512, 384), (300, 2048, 640), (130, 6144, 256),
-             (520, 128, 8200), (2000, 128, 1900), (300, 192, 4100)]
+             (520, 128, 8200), (2000, 128, 1900), (300, 192, 4100), (17, 64, 200)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -102,7 +102,7 @@ def test_linear(orc, ops, dtype, epi, M, K, N):
 # K = 320 (an odd number of groups) takes the register-staged 8-bit GEMM; the other M > 16
 # cases the LDS-DMA one: (1030, 256, 2800) its 128 x 128 tiling, the rest 64 x 128
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (5, 6144, 256), (40, 2048, 384), (512, 2048, 640),
-                                   (200, 6144, 136), (40, 320, 96), (1030, 256, 2800)])
+                                   (200, 6144, 136), (40, 320, 96), (1030, 256, 2800), (17, 128, 72)])
 def test_linear_q8(orc, ops, epi, M, K, N):
     from qwen3_transformer_layer_amd import synth
     from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8
