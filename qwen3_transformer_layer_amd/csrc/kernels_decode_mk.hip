@@ -53,7 +53,7 @@ constexpr int NTH = 64 * (NC + NL);  // threads per block
 constexpr int D = 128;               // head dimension
 constexpr int HID = 2048;            // hidden size: one chunk is one weight row of HID bf16
 constexpr int CHB = HID * 2;         // chunk bytes
-constexpr int NS = 28;               // ring slots (112 KB)
+constexpr int NS = 30;               // ring slots (120 KB)
 constexpr int DL = 4;                // chunks in flight per stream wave while the ring has room
 constexpr int KPC = CHB / (D * 2);   // keys per K or V chunk (16)
 constexpr int CHUNK_MAX = 256;       // keys per attention split
