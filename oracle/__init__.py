@@ -64,6 +64,7 @@ def lib():
         L.orc_round_array.argtypes = [p, ctypes.c_size_t, i]
         L.orc_rmsnorm.argtypes = [p, p, i, f, i, p]
         L.orc_linear.argtypes = [p, i, i, p, i, i, p]
+        L.orc_head.argtypes = [p, i, i, p, i, i, p, p]
         L.orc_rope_table.argtypes = [i, i, ctypes.c_double, i, p, p]
         L.orc_rope.argtypes = [p, i, p, p, i, p]
         L.orc_attention.argtypes = [p, p, p, i, i, i, i, i, i, i, p, p]
@@ -131,6 +132,19 @@ def linear(x, W, mode="bf16") -> np.ndarray:
     out = np.empty((T, N), np.float32)
     lib().orc_linear(_ptr(x), T, K, _ptr(W), N, _mode(mode), _ptr(out))
     return out.reshape(x.shape[:-1] + (N,))
+
+
+def head(hs, W, mode="bf16"):
+    """(logits fp32 [T][V] = rho(hs @ W^T), argmax int32 [T]: lowest index of the largest)."""
+    hs = _f32(hs)
+    W = _f32(W)
+    T, K = hs.reshape(-1, hs.shape[-1]).shape
+    V = W.shape[0]
+    assert W.shape[1] == K
+    logits = np.empty((T, V), np.float32)
+    am = np.empty(T, np.int32)
+    lib().orc_head(_ptr(hs), T, K, _ptr(W), V, _mode(mode), _ptr(logits), am.ctypes.data_as(ctypes.c_void_p))
+    return logits, am
 
 
 def rope_table(capacity, head_dim, theta, mode="bf16"):

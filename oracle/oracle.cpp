@@ -87,6 +87,21 @@ extern "C" void orc_linear(const float *x, int T, int K, const float *W, int N, 
             out[(size_t)t * N + j] = rho(dot(x + (size_t)t * K, W + (size_t)j * K, K), mode);
 }
 
+/* ---------------------------------------------------------------- output head */
+
+extern "C" void orc_head(const float *hs, int T, int K, const float *W, int V, int mode, float *logits, int *argmax) {
+    std::vector<float> row(V);
+    for (int t = 0; t < T; ++t) {
+        orc_linear(hs + (size_t)t * K, 1, K, W, V, mode, row.data());
+        int best = 0;
+        for (int v = 1; v < V; ++v)  /* strictly larger only: ties keep the lower index */
+            if (row[v] > row[best] || (row[best] != row[best] && row[v] == row[v])) best = v;
+        argmax[t] = best;
+        if (logits)
+            for (int v = 0; v < V; ++v) logits[(size_t)t * V + v] = row[v];
+    }
+}
+
 /* ---------------------------------------------------------------- RoPE */
 
 extern "C" void orc_rope_table(int capacity, int D, double theta, int mode, float *cos_out,

@@ -68,6 +68,13 @@ void orc_rmsnorm(const float *v, const float *w, int n, float eps, int mode, flo
  * [N][K] (the y @ W^T of [P1] Q.mm). */
 void orc_linear(const float *x, int T, int K, const float *W, int N, int mode, float *out);
 
+/* Output head and greedy token ([P1] Backbone.cb0_logits: the head projection in the model
+ * dtype, then fp32; [P3] lmHead / the tied embedding used as a linear, then the greedy pick):
+ * logits[t][v] = rho(sum_k hs[t][k] * W[v][k]) held in fp32, and argmax[t] = the lowest v
+ * whose logit is the largest (a NaN logit is never the pick unless every logit is NaN, then
+ * v = 0).  W row-major [V][K]; logits may be NULL. */
+void orc_head(const float *hs, int T, int K, const float *W, int V, int mode, float *logits, int *argmax);
+
 /* RoPE table, [P1] __init__ comment on the table and _rope():
  *   inv_j = fp32(theta^(-2j/D)) for j < D/2, rounded to bf16 in bf16 mode;
  *   angle = fp32(float(p) * inv_j);

@@ -140,6 +140,51 @@ def test_linear_matches_numpy_fp64(orc):
     assert np.array_equal(got_b, torch.from_numpy(got).to(torch.bfloat16).float().numpy())
 
 
+# ------------------------------------------------------------------ output head + greedy token
+
+def test_head_logits_and_argmax_brute_force(orc):
+    """Logits are the fp64 dot rounded to fp32 and then to bf16 (one rounding of the product,
+    held in fp32); the pick is a plain Python scan for the first maximum."""
+    rng = np.random.default_rng(11)
+    hs = torch.from_numpy(rng.standard_normal((4, 96)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    W = torch.from_numpy((0.05 * rng.standard_normal((300, 96))).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    logits, am = orc.head(hs, W, "bf16")
+    ref = (hs.astype(np.float64) @ W.astype(np.float64).T).astype(np.float32)
+    ref = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(logits, ref)
+    for t in range(4):
+        best = 0
+        for v in range(300):
+            if logits[t, v] > logits[t, best]:
+                best = v
+        assert am[t] == best
+
+
+def test_head_ties_go_to_the_lower_index(orc):
+    """Duplicate head rows give equal logits; the pick is the lower row."""
+    rng = np.random.default_rng(12)
+    hs = rng.standard_normal((3, 64)).astype(np.float32)
+    W = (0.1 * rng.standard_normal((50, 64))).astype(np.float32)
+    top = np.argmax(hs @ W.T, axis=1)
+    for t in range(3):
+        W2 = W.copy()
+        W2[:] = -np.abs(W2) * np.sign(hs[t])  # every row scores below the copies of row top[t]
+        W2[7] = W[top[t]]
+        W2[31] = W[top[t]]
+        W2[40] = W[top[t]]
+        _, am = orc.head(hs[t:t + 1], W2, "fp32")
+        assert am[0] == 7
+
+
+def test_head_nan_logits_are_never_picked(orc):
+    hs = np.ones((1, 8), np.float32)
+    W = np.zeros((6, 8), np.float32)
+    W[1] = np.nan
+    W[4] = 1.0
+    logits, am = orc.head(hs, W, "fp32")
+    assert np.isnan(logits[0, 1]) and am[0] == 4
+
+
 # ------------------------------------------------------------------ RoPE
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
