@@ -150,6 +150,19 @@ int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out);
 int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out, int32_t *topk_idx,
                     void *topk_w);
 
+/* Output head and greedy token ("maya2_mlx/backbone.py" Backbone.cb0_logits: the head
+ * projection in the model dtype, then fp32; "@mlx-bun/inference" qwen3.ts lmHead or the tied
+ * embedding used as a linear) on final-norm hidden states hs [T][hidden] (model dtype):
+ *   logits[t][v] = fp32(rho(hs[t] . head[v]))  (fp32 [T][V], may be NULL)
+ *   argmax[t]    = the lowest v with the largest logit; a NaN logit is never picked unless
+ *                  every logit is NaN (then 0)  (int32 [T], may be NULL)
+ * head: [V][hidden] in the model dtype, or NULL for the handle's embedding table (tied
+ * weights, V must equal vocab).  All pointers are device memory; the call enqueues on the
+ * handle's stream and does not touch the cache or the length.  Errors: QWEN3_ERR_ARG (null
+ * hs, neither output requested, T outside 1..max_tokens, V < 1 or V != vocab when tied),
+ * QWEN3_ERR_NULL_WEIGHT (no head and no embedding table). */
+int qwen3_head(qwen3_handle *h, const void *hs, int T, const void *head, int V, float *logits, int32_t *argmax);
+
 /* Set the seat length (0 <= length <= capacity): a pre-filled cache, or a
  * rewind.  Entries at positions >= length are never read and are overwritten
  * by the next forward. */

@@ -17,7 +17,7 @@ from ._lib import BF16, FP32, Qwen3Error
 from .config import PRESETS, Qwen3Config
 
 __all__ = ["Qwen3Config", "PRESETS", "Qwen3Error", "Seat", "qwen3_init", "qwen3_reset", "qwen3_forward",
-           "qwen3_forward_hidden", "qwen3_moe_block", "qwen3_set_length", "qwen3_get_length",
+           "qwen3_forward_hidden", "qwen3_moe_block", "qwen3_head", "qwen3_set_length", "qwen3_get_length",
            "qwen3_destroy", "qwen3_workspace_bytes", "qwen3_rope_table", "ops"]
 
 DTYPES = {"bf16": BF16, "fp32": FP32}
@@ -112,6 +112,16 @@ def qwen3_moe_block(h: _Handle, layer: int, x: torch.Tensor, out: torch.Tensor, 
     _lib.check(_lib.load().qwen3_moe_block(h.ptr, layer, _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx),
                                            _ptr(topk_w)), h.ptr)
     return out
+
+
+def qwen3_head(h: _Handle, hs: torch.Tensor, head: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+               argmax: torch.Tensor | None = None):
+    """Output head + greedy token on final-norm hidden states hs [T][hidden]: logits (fp32 [T][V])
+    and/or argmax (int32 [T]); head [V][hidden] or None for the tied embedding table."""
+    V = head.shape[0] if head is not None else h.cfg.vocab
+    _lib.check(_lib.load().qwen3_head(h.ptr, _ptr(hs), hs.shape[0], _ptr(head), V, _ptr(logits), _ptr(argmax)),
+               h.ptr)
+    return logits, argmax
 
 
 def qwen3_set_length(h: _Handle, length: int) -> None:

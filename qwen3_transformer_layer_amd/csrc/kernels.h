@@ -72,6 +72,11 @@ size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
 hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
                       const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
+// ---- output head + greedy token (kernels_head.hip): logits fp32 [T][V] and/or argmax int32 [T];
+// keys: T 64-bit words of scratch
+hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int V, float *logits, int32_t *argmax,
+                       unsigned long long *keys, hipStream_t s);
+
 // ---- MFMA projections for M > 16 (kernels_gemm.hip): LDS-DMA pipeline, K % 64 == 0 (bf16
 // weights) or K % 128 == 0 and 4-byte aligned scale/bias (8-bit weights)
 bool gemm_dma_ok(int M, int K, int N);

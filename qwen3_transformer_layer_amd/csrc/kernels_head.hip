@@ -1,0 +1,121 @@
+// kernels_head.hip -- output head and greedy token ("maya2_mlx/backbone.py", Backbone.cb0_logits:
+// the head projection in the model dtype, then fp32; "@mlx-bun/inference" qwen3.ts, lmHead or the
+// tied embedding used as a linear): logits[t][v] = fp32(rho(hs[t] . W[v])) and argmax[t] = the
+// lowest v whose logit is the largest.
+//
+// One HBM-bound pass over W [V][K] in the GEMV layout of kernels_linear.hip: each wave64 owns one
+// row v and streams it with 128-bit non-temporal loads, four in flight per lane, for up to 16
+// rows of hs at once.  The rounded logit is written when asked and becomes an order-preserving
+// 64-bit key: the value's bits mapped so unsigned order is numeric order (-0 as +0, a NaN below
+// every number), then the complement of v, so the largest key is the largest logit at the lowest
+// index.  The block's four keys per row are reduced in LDS and one 64-bit atomicMax per (block,
+// row) folds them into the row's key; head_final_kernel turns keys into indices.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+__device__ __forceinline__ unsigned long long head_key(float f, int v) {
+    uint32_t u = __float_as_uint(f);
+    if (f != f) u = 0u;                            // NaN: below every number
+    else if (f == 0.f) u = 0x80000000u;            // -0 ranks as +0
+    else u = (u >> 31) ? ~u : (u | 0x80000000u);   // negative: reversed; positive: above all negatives
+    return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)v);
+}
+
+__global__ void head_init_kernel(unsigned long long *__restrict__ keys, int T) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < T) keys[t] = 0ull;
+}
+
+__global__ void head_final_kernel(const unsigned long long *__restrict__ keys, int T, int32_t *__restrict__ argmax) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < T) argmax[t] = (int32_t)(0xffffffffu - (uint32_t)(keys[t] & 0xffffffffull));
+}
+
+template <typename T, int MR>
+__global__ void __launch_bounds__(256) head_kernel(const T *__restrict__ x, int M, int K, const T *__restrict__ W,
+                                                   int V, float *__restrict__ logits,
+                                                   unsigned long long *__restrict__ keys) {
+    constexpr int VN = Vec<T>::N;
+    constexpr int U = 4;
+    __shared__ unsigned long long kb[4][MR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 4 + wave;
+    const bool act = n < V;
+    const T *w0 = W + (size_t)(act ? n : 0) * K;
+    float a[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) a[m] = 0.f;
+    const int nc = K / VN;  // 16-byte chunks per row
+    for (int c0 = lane; c0 < nc; c0 += 64 * U) {
+        u32x4 wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 64 * u;
+            wv[u] = (act && c < nc) ? ld_stream(w0 + (size_t)c * VN) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 64 * u;
+            if (c < nc) {
+                float wf[VN];
+                Vec<T>::expand(wv[u], wf);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    if (m < M) {
+                        float xf[VN];
+                        Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)c * VN), xf);
+#pragma unroll
+                        for (int e = 0; e < VN; ++e) a[m] += wf[e] * xf[e];
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+            const float r = rho<T>(wave_sum(a[m]));
+            if (lane == 0) {
+                if (act && logits) logits[(size_t)m * V + n] = r;
+                kb[wave][m] = act ? head_key(r, n) : 0ull;
+            }
+        }
+    }
+    __syncthreads();
+    if (keys && threadIdx.x < MR && (int)threadIdx.x < M) {
+        unsigned long long best = kb[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) best = kb[w][threadIdx.x] > best ? kb[w][threadIdx.x] : best;
+        atomicMax(&keys[threadIdx.x], best);
+    }
+}
+
+template <typename T>
+static void head_rows(const T *x, int M, int K, const T *W, int V, float *logits, unsigned long long *keys,
+                      hipStream_t s) {
+    const dim3 grid((V + 3) / 4);
+    if (M <= 1) head_kernel<T, 1><<<grid, 256, 0, s>>>(x, M, K, W, V, logits, keys);
+    else if (M <= 4) head_kernel<T, 4><<<grid, 256, 0, s>>>(x, M, K, W, V, logits, keys);
+    else if (M <= 8) head_kernel<T, 8><<<grid, 256, 0, s>>>(x, M, K, W, V, logits, keys);
+    else head_kernel<T, 16><<<grid, 256, 0, s>>>(x, M, K, W, V, logits, keys);
+}
+
+hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int V, float *logits, int32_t *argmax,
+                       unsigned long long *keys, hipStream_t s) {
+    if (argmax) head_init_kernel<<<(T + 255) / 256, 256, 0, s>>>(keys, T);
+    const size_t es = dt == DT_BF16 ? 2 : 4;
+    for (int t0 = 0; t0 < T; t0 += 16) {
+        const int M = T - t0 < 16 ? T - t0 : 16;
+        const char *x = (const char *)hs + (size_t)t0 * K * es;
+        float *lg = logits ? logits + (size_t)t0 * V : nullptr;
+        unsigned long long *kk = argmax ? keys + t0 : nullptr;
+        if (dt == DT_BF16) head_rows<bf16>((const bf16 *)x, M, K, (const bf16 *)W, V, lg, kk, s);
+        else head_rows<float>((const float *)x, M, K, (const float *)W, V, lg, kk, s);
+    }
+    if (argmax) head_final_kernel<<<(T + 255) / 256, 256, 0, s>>>(keys, T, argmax);
+    return hipGetLastError();
+}
+
+}  // namespace q3

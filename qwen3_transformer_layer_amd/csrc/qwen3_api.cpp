@@ -43,6 +43,7 @@ struct qwen3_handle {
     void *tmp = nullptr;
     float *attn_ws = nullptr;
     int *dev_err = nullptr;
+    unsigned long long *head_keys = nullptr;  // greedy-token keys, one per row
     int32_t *moe_idx = nullptr;
     void *moe_w = nullptr, *moe_ws = nullptr;
     // persistent decode step (dense bf16 shapes it supports)
@@ -68,7 +69,7 @@ namespace {
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t h, h2, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, moe_idx, moe_w, moe_ws, mk, total;
+    size_t h, h2, y, qkv, q, a, m, pend, tmp, attn, cos_t, sin_t, err, head_keys, moe_idx, moe_w, moe_ws, mk, total;
 };
 
 size_t esize(const qwen3_config &c) { return c.dtype == QWEN3_BF16 ? 2 : 4; }
@@ -96,6 +97,7 @@ Layout layout(const qwen3_config &c) {
     L.cos_t = take((size_t)c.capacity * c.head_dim * es);
     L.sin_t = take((size_t)c.capacity * c.head_dim * es);
     L.err = take(256);
+    L.head_keys = take(Tm * 8);
     if (c.n_experts > 0) {
         L.moe_idx = take(Tm * c.top_k * 4);
         L.moe_w = take(Tm * c.top_k * es);
@@ -376,6 +378,7 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
     h->tmp = b + L.tmp;
     h->attn_ws = (float *)(b + L.attn);
     h->dev_err = (int *)(b + L.err);
+    h->head_keys = (unsigned long long *)(b + L.head_keys);
     if (moe) {
         h->moe_idx = (int32_t *)(b + L.moe_idx);
         h->moe_w = b + L.moe_w;
@@ -437,6 +440,22 @@ int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out) {
     const int rc = run_layers(h, x, T, out);
     if (rc == QWEN3_OK) h->length += T;
     return rc;
+}
+
+int qwen3_head(qwen3_handle *h, const void *hs, int T, const void *head, int V, float *logits, int32_t *argmax) {
+    if (!h) return QWEN3_ERR_ARG;
+    h->err.clear();
+    if (!hs) return fail(h, QWEN3_ERR_ARG, "null hidden states");
+    if (!logits && !argmax) return fail(h, QWEN3_ERR_ARG, "neither logits nor argmax requested");
+    if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
+    if (!head) {
+        if (!h->embed || h->cfg.vocab < 1) return fail(h, QWEN3_ERR_NULL_WEIGHT, "no head and no embedding table");
+        if (V != h->cfg.vocab) return fail(h, QWEN3_ERR_ARG, "V=%d differs from the tied embedding's vocab %d", V, h->cfg.vocab);
+        head = h->embed;
+    }
+    if (V < 1) return fail(h, QWEN3_ERR_ARG, "V=%d must be positive", V);
+    HIPCHECK(h, launch_head(h->cfg.dtype, hs, T, h->cfg.hidden, head, V, logits, argmax, h->head_keys, h->stream));
+    return QWEN3_OK;
 }
 
 int qwen3_forward(qwen3_handle *h, const int32_t *tokens, int T, void *out) {
