@@ -323,6 +323,42 @@ def q8_bench(steps: int, warmup: int, iters: int):
     return res
 
 
+HEAD_V = 151936  # Qwen3 vocabulary
+HEAD_BYTES = HEAD_V * 2048 * 2 + 2048 * 2 + 8
+
+
+def head_bench(steps: int, warmup: int):
+    """Output head + greedy token at T = 1: a bf16 head [151936][2048] over one final-norm
+    hidden state, argmax only (the decode-time use); bytes = the head rows + the input row."""
+    import torch
+
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE
+
+    cfg = QWEN3_1P7B_DECODE.replace(n_layers=1)
+    dev = "cuda"
+    w = synth.model_weights(cfg, dev)
+    W = synth.linear_weight(cfg, "head", (HEAD_V, cfg.hidden), dev)
+    hs = synth.hidden_states(cfg, 1, dev, name="hs")
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    seat = q3.Seat(cfg, w, max_tokens=1, stream=stream)
+
+    def call():
+        q3.qwen3_head(seat.handle, hs, W, None, am)
+
+    t = _graph_seconds(call, stream, steps, warmup)
+    res = {"workload": f"bf16 output head [{HEAD_V}][2048], T=1, greedy token", "us": round(t * 1e6, 2),
+           "bytes": HEAD_BYTES, "gbps": round(HEAD_BYTES / t / 1e9, 1),
+           "hbm_frac": round(HEAD_BYTES / t / 1e9 / HBM_PEAK_GBPS, 4)}
+    log(f"head: {res['us']} us per call ({res['gbps']} GB/s)")
+    del seat, w, W
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(sample_layers: int = 4):
     """The oracle on the host: a decode step of the same shape over `sample_layers` layers
     (same per-layer work as the 28-layer step), scaled to a 28-layer step."""
@@ -386,7 +422,7 @@ def main():
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
         return
     if args.variants_only:
-        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5)}), flush=True)
+        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5), "head": head_bench(50, 5)}), flush=True)
         return
     if args.copy_calib:
         copy_calibration()
@@ -394,6 +430,7 @@ def main():
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     moe = None if args.no_variants else moe_bench(30, 3)
     q8 = None if args.no_variants else q8_bench(30, 3, 5)
+    head = None if args.no_variants else head_bench(50, 5)
     cpu = None if args.no_cpu else cpu_baseline()
 
     if dec["path"] == 2:
@@ -434,6 +471,7 @@ def main():
                      "launches": dec["launches"]},
         "moe": moe,
         "q8": q8,
+        "head": head,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

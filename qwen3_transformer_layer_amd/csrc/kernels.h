@@ -73,7 +73,7 @@ hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int
                       const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
 // ---- output head + greedy token (kernels_head.hip): logits fp32 [T][V] and/or argmax int32 [T];
-// keys: T 64-bit words of scratch
+// keys: 64 T 64-bit words of scratch
 hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int V, float *logits, int32_t *argmax,
                        unsigned long long *keys, hipStream_t s);
 

@@ -97,7 +97,7 @@ Layout layout(const qwen3_config &c) {
     L.cos_t = take((size_t)c.capacity * c.head_dim * es);
     L.sin_t = take((size_t)c.capacity * c.head_dim * es);
     L.err = take(256);
-    L.head_keys = take(Tm * 8);
+    L.head_keys = take(Tm * 64 * 8);  // 64 key slots per row (kernels_head.hip)
     if (c.n_experts > 0) {
         L.moe_idx = take(Tm * c.top_k * 4);
         L.moe_w = take(Tm * c.top_k * es);
