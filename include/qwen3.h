@@ -150,6 +150,18 @@ int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out);
 int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out, int32_t *topk_idx,
                     void *topk_w);
 
+/* One decode step for B seats at once (page 3 "decode": one new token per sequence; page 2
+ * batch): row b of x [B][hidden] (model dtype) is seat b's next token at position
+ * seats[b]'s length; out [B][hidden] gets the final-norm hidden states and every seat's
+ * length advances by 1.  seats: host array of B distinct handles with the same configuration
+ * (all shape fields, capacity, eps, theta, dtype, MoE and quantisation fields) and the same
+ * weight pointers; each keeps its own cache and length.  The projections read each weight
+ * once for the B rows; attention runs per seat in one batched launch.  The activations and
+ * the stream are seats[0]'s (its max_tokens must be >= B).  1 <= B <= 16.  Errors:
+ * QWEN3_ERR_ARG (B out of range, a null or repeated seat, a seat of another model),
+ * QWEN3_ERR_CAPACITY (a seat is full); on error no seat changes. */
+int qwen3_forward_batch(qwen3_handle *const *seats, int B, const void *x, void *out);
+
 /* Output head and greedy token ("maya2_mlx/backbone.py" Backbone.cb0_logits: the head
  * projection in the model dtype, then fp32; "@mlx-bun/inference" qwen3.ts lmHead or the tied
  * embedding used as a linear) on final-norm hidden states hs [T][hidden] (model dtype):

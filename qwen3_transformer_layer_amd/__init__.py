@@ -17,7 +17,7 @@ from ._lib import BF16, FP32, Qwen3Error
 from .config import PRESETS, Qwen3Config
 
 __all__ = ["Qwen3Config", "PRESETS", "Qwen3Error", "Seat", "qwen3_init", "qwen3_reset", "qwen3_forward",
-           "qwen3_forward_hidden", "qwen3_moe_block", "qwen3_head", "qwen3_set_length", "qwen3_get_length",
+           "qwen3_forward_hidden", "qwen3_moe_block", "qwen3_forward_batch", "qwen3_head", "qwen3_set_length", "qwen3_get_length",
            "qwen3_destroy", "qwen3_workspace_bytes", "qwen3_rope_table", "ops"]
 
 DTYPES = {"bf16": BF16, "fp32": FP32}
@@ -111,6 +111,15 @@ def qwen3_forward_hidden(h: _Handle, x: torch.Tensor, out: torch.Tensor) -> torc
 def qwen3_moe_block(h: _Handle, layer: int, x: torch.Tensor, out: torch.Tensor, topk_idx=None, topk_w=None):
     _lib.check(_lib.load().qwen3_moe_block(h.ptr, layer, _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx),
                                            _ptr(topk_w)), h.ptr)
+    return out
+
+
+def qwen3_forward_batch(handles, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """One decode step for len(handles) seats of the same model: row b of x is seat b's token."""
+    arr = (ctypes.c_void_p * len(handles))(*[hd.ptr.value if isinstance(hd.ptr, ctypes.c_void_p) else hd.ptr
+                                               for hd in handles])
+    _lib.check(_lib.load().qwen3_forward_batch(ctypes.cast(arr, ctypes.c_void_p), len(handles), _ptr(x), _ptr(out)),
+               handles[0].ptr)
     return out
 
 

@@ -59,10 +59,23 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
                             int D, int cap, int p0, void *out, float *ws, size_t ws_bytes, hipStream_t s);
 size_t attention_workspace(int T, int H, int KV, int D, int cap);
 // Decode step (T == 1) at position p0 fused with the per-head q/k RMSNorm, RoPE and the
-// cache write: qkv [(H+2KV)D] of the token -> out [H*D]; writes K/V at p0.
+// cache write: qkv [(H+2KV)D] of the token -> out [H*D]; writes K/V at p0.  The scratch of
+// attention_workspace(T, ...) holds min(T, DECODE_MAXB) seats' partials.
 hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV, int D, const void *q_norm,
                                          const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
                                          int cap, void *k_cache, void *v_cache, void *out, float *ws, hipStream_t s);
+// The same for B <= DECODE_MAXB seats at once (one token each, the same weights): seat b's
+// q|k|v row b of qkv [B][(H+2KV)D], its layer cache kc[b] / vc[b] ([KV][cap][D]) and position
+// p[b]; out row b of [B][H*D].
+constexpr int DECODE_MAXB = 16;
+struct DecodeBatch {
+    void *kc[DECODE_MAXB], *vc[DECODE_MAXB];
+    int p[DECODE_MAXB], chunk[DECODE_MAXB], nsplit[DECODE_MAXB];
+};
+hipError_t launch_attention_decode_batch(int dt, const void *qkv, int B, int H, int KV, int D, const void *q_norm,
+                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t,
+                                         void *const *k_cache, void *const *v_cache, const int *p, int cap, void *out,
+                                         float *ws, hipStream_t s);
 
 // ---- MoE block: router logits rho(x . Wr^T), rho(softmax) over all E experts, top-k
 // (ties to the lower index, slot order descending probability), renormalised weights

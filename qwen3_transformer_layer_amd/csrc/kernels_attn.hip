@@ -34,7 +34,7 @@
 
 namespace q3 {
 
-static inline int decode_chunk(int nkeys, int KV) {
+static inline int decode_chunk(int nkeys, int KV) {  // keys per split of a T == 1 step
     int c = (nkeys * KV + 511) / 512;
     c = (c + 31) / 32 * 32;
     if (c < 32) c = 32;
@@ -42,11 +42,13 @@ static inline int decode_chunk(int nkeys, int KV) {
     return c;
 }
 
+// split partials of one seat (fp32 words): H heads x up to cap / 32 splits x (max, sum, D values)
+static size_t seat_part_words(int H, int D, int cap) { return (size_t)H * ((cap + 31) / 32) * (D + 2); }
+
 size_t attention_workspace(int T, int H, int KV, int D, int cap) {
-    (void)T;
     (void)KV;
-    const size_t nsplit_max = (size_t)(cap + 31) / 32;
-    return (size_t)H * nsplit_max * (D + 2) * sizeof(float);
+    const int seats = T < DECODE_MAXB ? (T < 1 ? 1 : T) : DECODE_MAXB;
+    return (size_t)seats * seat_part_words(H, D, cap) * sizeof(float);
 }
 
 // ------------------------------------------------------------ split-K decode
@@ -93,17 +95,17 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
 // (in the split holding p) of k, RoPE at p, and the cache write of k and v at p, then the
 // split's attention.  qkv: [(H+2KV)D] for the one token.
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) attn_decode_fused_kernel(
-    const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm, float eps,
-    const T *__restrict__ cos_t, const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc, int cap,
-    int nkeys, int chunk, float scale, float *__restrict__ part, int nsplit) {
+__device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm,
+                                                   const T *__restrict__ k_norm, float eps, const T *__restrict__ cos_t,
+                                                   const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc,
+                                                   int cap, int nkeys, int chunk, float scale, float *__restrict__ part,
+                                                   int nsplit, int s, int g) {
     extern __shared__ float smem[];
     float *sc = smem;
     float *red = smem + G * chunk;
     __shared__ float qs[G * D];
     __shared__ float kvs[2 * D];
     __shared__ float mrow[G], lrow[G];
-    const int s = blockIdx.x, g = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j0 = s * chunk, j1 = min(nkeys, j0 + chunk);
     const int p = nkeys - 1;
@@ -154,18 +156,40 @@ __global__ void __launch_bounds__(256) attn_decode_fused_kernel(
                          part, nsplit, g, s);
 }
 
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) attn_decode_fused_kernel(
+    const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm, float eps,
+    const T *__restrict__ cos_t, const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc, int cap,
+    int nkeys, int chunk, float scale, float *__restrict__ part, int nsplit) {
+    decode_fused_block<T, D, G>(qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, Kc, Vc, cap, nkeys, chunk, scale, part,
+                                nsplit, blockIdx.x, blockIdx.y);
+}
+
+// Several seats at once (blockIdx.z = seat b): seat b's q|k|v row, cache, position and split
+// come from the by-value batch; its partials go to part + b * part_stride.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) attn_decode_fused_batch_kernel(
+    const T *__restrict__ qkv, int nqkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm,
+    float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t, DecodeBatch bt, int cap, float scale,
+    float *__restrict__ part, size_t part_stride) {
+    const int b = blockIdx.z;
+    if ((int)blockIdx.x >= bt.nsplit[b]) return;  // uniform over the block
+    decode_fused_block<T, D, G>(qkv + (size_t)b * nqkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, (T *)bt.kc[b],
+                                (T *)bt.vc[b], cap, bt.p[b] + 1, bt.chunk[b], scale, part + (size_t)b * part_stride,
+                                bt.nsplit[b], blockIdx.x, blockIdx.y);
+}
+
 // Merge the splits of one head: out = rho(sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M)).
 // Thread t owns 32 consecutive values of split t / (D/32) in each pass of 256/(D/32)
 // splits, so every load of a pass is issued at once.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ part, int nsplit,
-                                                           T *__restrict__ out) {
+__device__ __forceinline__ void combine_block(const float *__restrict__ part, int nsplit, T *__restrict__ out, int h) {
     constexpr int TPS = D / 32;        // threads per split
     constexpr int SPP = 256 / TPS;     // splits per pass
     __shared__ float red[4];
     __shared__ float accs[SPP][D + 1];
     __shared__ float lsum[SPP];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     const int sl = tid / TPS, d0 = (tid % TPS) * 32;
     const float *ph = part + (size_t)h * nsplit * (D + 2);
     float M = -INFINITY;
@@ -196,6 +220,20 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
         }
         out[(size_t)h * D + tid] = from_f<T>(a / l);
     }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ part, int nsplit,
+                                                           T *__restrict__ out) {
+    combine_block<T, D>(part, nsplit, out, blockIdx.x);
+}
+
+// grid (H, seats): seat b's partials at part + b * part_stride, output row b of out [B][H*D]
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_combine_batch_kernel(const float *__restrict__ part, size_t part_stride,
+                                                                 DecodeBatch bt, int H, T *__restrict__ out) {
+    const int b = blockIdx.y;
+    combine_block<T, D>(part + (size_t)b * part_stride, bt.nsplit[b], out + (size_t)b * H * D, blockIdx.x);
 }
 
 // ------------------------------------------------------------ fp32 / fallback row-wise kernel
@@ -670,6 +708,65 @@ hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV,
                                            v_cache, cap, nkeys, out, ws, s)
                     : decode_t<float, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
                                           v_cache, cap, nkeys, out, ws, s);
+}
+
+template <typename T, int D, int G>
+static void batch_launch(dim3 grid, size_t lds, hipStream_t s, const T *qkv, int nqkv, int H, int KV, const T *qn,
+                         const T *kn, float eps, const T *cs, const T *sn, const DecodeBatch &bt, int cap, float scale,
+                         float *ws, size_t stride) {
+    attn_decode_fused_batch_kernel<T, D, G><<<grid, 256, lds, s>>>(qkv, nqkv, H, KV, qn, kn, eps, cs, sn, bt, cap, scale,
+                                                                   ws, stride);
+}
+
+template <typename T, int D>
+static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const void *qn, const void *kn, float eps,
+                                 const void *cs, const void *sn, void *const *kc, void *const *vc, const int *p,
+                                 int cap, void *out, float *ws, hipStream_t s) {
+    const int G = H / KV;
+    DecodeBatch bt{};
+    int maxsplit = 0, maxchunk = 0;
+    for (int b = 0; b < B; ++b) {
+        bt.kc[b] = kc[b];
+        bt.vc[b] = vc[b];
+        bt.p[b] = p[b];
+        bt.chunk[b] = decode_chunk(p[b] + 1, KV);
+        bt.nsplit[b] = (p[b] + bt.chunk[b]) / bt.chunk[b];
+        maxsplit = bt.nsplit[b] > maxsplit ? bt.nsplit[b] : maxsplit;
+        maxchunk = bt.chunk[b] > maxchunk ? bt.chunk[b] : maxchunk;
+    }
+    const float scale = (float)(1.0 / sqrt((double)D));
+    const size_t lds = ((size_t)G * maxchunk + 4 * (size_t)G * D) * sizeof(float);
+    const size_t stride = seat_part_words(H, D, cap);
+    const int nqkv = (H + 2 * KV) * D;
+    const dim3 grid(maxsplit, KV, B);
+    const T *q = (const T *)qkv, *qnn = (const T *)qn, *knn = (const T *)kn, *c = (const T *)cs, *sv = (const T *)sn;
+    switch (G) {
+    case 1: batch_launch<T, D, 1>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 2: batch_launch<T, D, 2>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 4: batch_launch<T, D, 4>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 8: batch_launch<T, D, 8>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_combine_batch_kernel<T, D><<<dim3(H, B), 256, 0, s>>>(ws, stride, bt, H, (T *)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_decode_batch(int dt, const void *qkv, int B, int H, int KV, int D, const void *q_norm,
+                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t,
+                                         void *const *k_cache, void *const *v_cache, const int *p, int cap, void *out,
+                                         float *ws, hipStream_t s) {
+    if (B < 1 || B > DECODE_MAXB) return hipErrorInvalidValue;
+    if (dt == DT_BF16)
+        return D == 128 ? decode_batch_t<bf16, 128>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
+                                                    p, cap, out, ws, s)
+                        : decode_batch_t<bf16, 64>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
+                                                   p, cap, out, ws, s);
+    return D == 128 ? decode_batch_t<float, 128>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
+                                                 p, cap, out, ws, s)
+                    : decode_batch_t<float, 64>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
+                                                p, cap, out, ws, s);
 }
 
 hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,

@@ -310,9 +310,87 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
     return QWEN3_OK;
 }
 
+// B seats, one token each (B <= DECODE_MAXB): the leader's workspace and stream carry the
+// activations [B][...]; the projections run once over the B rows; attention runs per seat on
+// its own cache at its own position in one batched launch.
+int run_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
+    qwen3_handle *h = seats[0];
+    const qwen3_config &c = h->cfg;
+    const int dt = c.dtype, hid = c.hidden, H = c.n_heads, KV = c.n_kv_heads, D = c.head_dim;
+    const int nqkv = (H + 2 * KV) * D;
+    const size_t es = esize(c), layer_kv = (size_t)KV * c.capacity * D * es;
+    hipStream_t s = h->stream;
+    int pos[DECODE_MAXB];
+    void *kc[DECODE_MAXB], *vc[DECODE_MAXB];
+    for (int b = 0; b < B; ++b) pos[b] = seats[b]->length;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const qwen3_layer_weights &L = h->layers[l];
+        if (l == 0) HIPCHECK(h, launch_add_rmsnorm(dt, x, nullptr, L.in_norm, nullptr, h->y, B, hid, c.rms_eps, s));
+        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, L.in_norm, h->h, h->y, B, hid, c.rms_eps, s));
+        HIPCHECK(h, linear(h, h->y, B, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
+        for (int b = 0; b < B; ++b) {
+            kc[b] = seats[b]->kc + l * layer_kv;
+            vc[b] = seats[b]->vc + l * layer_kv;
+        }
+        HIPCHECK(h, launch_attention_decode_batch(dt, h->qkv, B, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t,
+                                                  h->sin_t, kc, vc, pos, c.capacity, h->a, h->attn_ws, s));
+        HIPCHECK(h, linear(h, h->a, B, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
+        HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, B, hid, c.rms_eps, s));
+        if (c.n_experts > 0) {
+            HIPCHECK(h, launch_moe(dt, h->y, B, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
+                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
+                                   h->moe_ws, s));
+        } else {
+            HIPCHECK(h, linear(h, h->y, B, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
+                               nullptr, h->m));
+            HIPCHECK(h, linear(h, h->m, B, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_STORE, nullptr,
+                               h->pend));
+        }
+    }
+    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, h->final_norm, nullptr, out, B, hid, c.rms_eps, s));
+    return QWEN3_OK;
+}
+
+bool same_model(const qwen3_handle *a, const qwen3_handle *b) {
+    const qwen3_config &x = a->cfg, &y = b->cfg;
+    if (x.n_layers != y.n_layers || x.hidden != y.hidden || x.n_heads != y.n_heads || x.n_kv_heads != y.n_kv_heads ||
+        x.head_dim != y.head_dim || x.intermediate != y.intermediate || x.capacity != y.capacity ||
+        x.rms_eps != y.rms_eps || x.rope_theta != y.rope_theta || x.dtype != y.dtype || x.n_experts != y.n_experts ||
+        x.top_k != y.top_k || x.moe_intermediate != y.moe_intermediate || x.norm_topk_prob != y.norm_topk_prob ||
+        x.quant_bits != y.quant_bits || x.quant_group != y.quant_group)
+        return false;
+    if (a->final_norm != b->final_norm) return false;
+    for (int l = 0; l < x.n_layers; ++l)
+        if (memcmp(&a->layers[l], &b->layers[l], sizeof(qwen3_layer_weights)) != 0) return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+int qwen3_forward_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
+    if (!seats || !seats[0]) return QWEN3_ERR_ARG;
+    qwen3_handle *h = seats[0];
+    h->err.clear();
+    if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (B < 1 || B > DECODE_MAXB) return fail(h, QWEN3_ERR_ARG, "B=%d outside 1..%d", B, DECODE_MAXB);
+    if (B > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "B=%d exceeds the first seat's max_tokens=%d", B, h->cfg.max_tokens);
+    for (int b = 0; b < B; ++b) {
+        if (!seats[b]) return fail(h, QWEN3_ERR_ARG, "seat %d is null", b);
+        for (int q = 0; q < b; ++q)
+            if (seats[q] == seats[b]) return fail(h, QWEN3_ERR_ARG, "seat %d appears twice", b);
+        if (!same_model(h, seats[b])) return fail(h, QWEN3_ERR_ARG, "seat %d has another configuration or weights", b);
+        if (seats[b]->length + 1 > seats[b]->cfg.capacity)
+            return fail(h, QWEN3_ERR_CAPACITY, "seat %d: context %d exceeds capacity %d", b, seats[b]->length + 1,
+                        seats[b]->cfg.capacity);
+    }
+    const int rc = run_batch(seats, B, x, out);
+    if (rc == QWEN3_OK)
+        for (int b = 0; b < B; ++b) seats[b]->length += 1;
+    return rc;
+}
+
 
 const char *qwen3_status_string(int code) {
     switch (code) {
