@@ -323,6 +323,50 @@ def q8_bench(steps: int, warmup: int, iters: int):
     return res
 
 
+def batch_bench(Bs=(8, 16), steps: int = 30, warmup: int = 3):
+    """B seats of the 1.7B-shaped bf16 stack, each at position 4095 over its own ctx-4096 cache,
+    one token each per step (qwen3_forward_batch).  Bytes per step: the weights once, plus each
+    seat's K/V read and write and the norm vectors."""
+    import torch
+
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE as cfg
+
+    dev = "cuda"
+    w = synth.model_weights(cfg, dev)
+    K0, V0 = synth.kv_cache(cfg, 4095, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    res = {}
+    weights = 2_818_572_288 + 243_712
+    per_seat = 469_762_048 + 114_688
+    for B in Bs:
+        seats = [q3.Seat(cfg, w, max_tokens=B, k_cache=K0.clone(), v_cache=V0.clone(), stream=stream)
+                 for _ in range(B)]
+        x = synth.hidden_states(cfg, B, dev, name="xb")
+        out = torch.empty_like(x)
+        handles = [s.handle for s in seats]
+        torch.cuda.synchronize()
+
+        def step():
+            for s in seats:
+                s.length = 4095
+            q3.qwen3_forward_batch(handles, x, out)
+
+        t = _graph_seconds(step, stream, steps, warmup)
+        nbytes = weights + B * per_seat
+        res[f"B{B}"] = {"ms_per_step": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1), "bytes": nbytes,
+                        "gbps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"batched decode B={B}: {t * 1e3:.3f} ms/step, {B / t:.0f} tok/s, {nbytes / t / 1e9:.0f} GB/s")
+        del seats
+        torch.cuda.empty_cache()
+    res["workload"] = "B seats of the Qwen3-1.7B-shaped bf16 stack, each T=1 at position 4095 (own ctx-4096 cache)"
+    del w, K0, V0
+    torch.cuda.empty_cache()
+    return res
+
+
 HEAD_V = 151936  # Qwen3 vocabulary
 HEAD_BYTES = HEAD_V * 2048 * 2 + 2048 * 2 + 8
 
@@ -422,7 +466,8 @@ def main():
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
         return
     if args.variants_only:
-        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5), "head": head_bench(50, 5)}), flush=True)
+        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5), "head": head_bench(50, 5),
+                          "batch": batch_bench()}), flush=True)
         return
     if args.copy_calib:
         copy_calibration()
@@ -431,6 +476,7 @@ def main():
     moe = None if args.no_variants else moe_bench(30, 3)
     q8 = None if args.no_variants else q8_bench(30, 3, 5)
     head = None if args.no_variants else head_bench(50, 5)
+    batch = None if args.no_variants else batch_bench()
     cpu = None if args.no_cpu else cpu_baseline()
 
     if dec["path"] == 2:
@@ -472,6 +518,7 @@ def main():
         "moe": moe,
         "q8": q8,
         "head": head,
+        "batch_decode": batch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -13,6 +13,11 @@
 //    128-bit non-temporal loads, 4 loads in flight per lane; x is read through
 //    the L1/L2 caches; one wave reduction per output.
 //  - M > 16 in bf16: the MFMA GEMM of kernels_gemm.hip.
+//  - gemv_mfma_kernel: 2 <= M <= 16 in bf16 (several seats' decode steps): v_mfma_f32_16x16x32_bf16
+//    on 16 weight rows x the M activation rows (padded to 16), so every 16-byte weight load
+//    pairs with one activation load (the plain GEMV re-reads all M activation chunks per weight
+//    chunk).  Block = 8 waves on the same 16 outputs (32 weight rows for SWIGLU), each a K/8
+//    slice with 8 loads in flight per lane; the 8 partial tiles are summed in LDS in wave order.
 //  - gemm_f32_kernel: M > 16 in fp32 (strict mode), LDS-tiled FMA.
 #include "common.h"
 #include "kernels.h"
@@ -202,6 +207,65 @@ hipError_t launch_linear_norm(int dt, const void *h_in, const void *res, const v
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ skinny MFMA GEMV (2 <= M <= 16, bf16)
+// MFMA 16x16x32: lane i supplies A[i % 16][8 (i / 16) .. + 8] (activation row i % 16) and
+// B[8 (i / 16) .. + 8][i % 16] (weight row n0 + i % 16); accumulator j of lane i is
+// C[4 (i / 16) + j][i % 16].  K % 256 == 0.
+template <int EPI>
+__global__ void __launch_bounds__(512) gemv_mfma_kernel(const bf16 *__restrict__ x, int M, int K,
+                                                        const bf16 *__restrict__ W, int N, const bf16 *__restrict__ res,
+                                                        bf16 *__restrict__ out) {
+    constexpr int NWV = 8, U = 8;
+    constexpr int NT = EPI == EPI_SWIGLU ? 2 : 1;  // gate and up tiles
+    __shared__ f32x4 part[NWV - 1][NT][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16, r = lane & 15, h = lane >> 4;
+    const bf16 *xr = x + (size_t)min(r, M - 1) * K + 8 * h;
+    const bf16 *wr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wr[t] = W + (size_t)(t * N + min(n0 + r, N - 1)) * K + 8 * h;
+    const int ks = K / NWV, k0 = wave * ks;  // this wave's K slice, a multiple of 32
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = k0; kb < k0 + ks; kb += 32 * U) {
+        u32x4 wv[NT][U], xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kb + 32 * u;
+            const bool ok = k < k0 + ks;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) wv[t][u] = ok ? ld_stream(wr[t] + k) : u32x4{0, 0, 0, 0};
+            xv[u] = ok ? ld16(xr + k) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, xv[u]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wv[t][u]), acc[t], 0, 0, 0);
+        }
+    }
+    if (wave > 0)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) part[wave - 1][t][lane] = acc[t];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < NWV - 1; ++w)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] += part[w][t][lane];
+    const int n = n0 + r;
+    if (n >= N) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = 4 * h + j;
+        if (m >= M) continue;
+        const size_t idx = (size_t)m * N + n;
+        out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[0][j], NT > 1 ? acc[NT - 1][j] : 0.f, res, idx));
+    }
+}
+
 // ------------------------------------------------------------ fp32 tiled GEMM (strict mode)
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float *__restrict__ A, int M, int K,
@@ -293,6 +357,15 @@ static void launch_gemv(int epi, const void *x, int M, int K, const void *W, int
 
 hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int N, int epi, const void *res,
                          void *out, hipStream_t s) {
+    if (M <= 16 && M >= 2 && dt == DT_BF16 && K % 256 == 0) {
+        const dim3 grid((N + 15) / 16);
+        const bf16 *a = (const bf16 *)x, *b = (const bf16 *)W, *r = (const bf16 *)res;
+        bf16 *o = (bf16 *)out;
+        if (epi == EPI_SWIGLU) gemv_mfma_kernel<EPI_SWIGLU><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
+        else if (epi == EPI_RESID) gemv_mfma_kernel<EPI_RESID><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
+        else gemv_mfma_kernel<EPI_STORE><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
+        return hipGetLastError();
+    }
     if (M <= 16) {
         if (dt == DT_BF16) launch_gemv<bf16>(epi, x, M, K, W, N, res, out, s);
         else launch_gemv<float>(epi, x, M, K, W, N, res, out, s);

@@ -67,11 +67,12 @@ def test_add_rmsnorm(orc, dtype, n, ops):
             assert np.mean(got == rf) > 0.99 and max_row_rel_l2(got, rf) < 4e-3
 
 
-# MFMA tilings (the largest with >= 192 tiles): (520, 128, 8200) 256 x 128 for every epilogue;
+# 2 <= M <= 16 in bf16 with K % 256 == 0: the skinny MFMA GEMV ((3, 2048, 384), (16, 256, 512),
+# (7, 6144, 130)); M = 1 the plain GEMV.  MFMA tilings (the largest with >= 192 tiles): (520, 128, 8200) 256 x 128 for every epilogue;
 # (2000, 128, 1900) 128 x 128 / 8 waves (SWIGLU: 256 x 128); (300, 192, 4100) SWIGLU 128 x 128,
 # the others 128 x 64; the remaining M > 16 cases 128 x 64 (SWIGLU 64 x 128).  Ragged M and N.
 LIN_CASES = [(1, 2048, 4096), (3, 2048, 384), (16, 256, 512), (40, 512, 384), (300, 2048, 640), (130, 6144, 256),
-             (520, 128, 8200), (2000, 128, 1900), (300, 192, 4100), (17, 64, 200)]
+             (520, 128, 8200), (2000, 128, 1900), (300, 192, 4100), (17, 64, 200), (7, 6144, 130)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
