@@ -335,6 +335,13 @@ extern "C" int orc_forward(const orc_config *cfg, const orc_layer *layers, const
     const int I = cfg->intermediate, cap = cfg->capacity, mode = cfg->mode;
     const float eps = cfg->rms_eps;
     const int nqkv = (H + 2 * KV) * D;
+    for (int l = 0; l < cfg->n_layers; ++l) { /* every layer has the weights of its kind */
+        const orc_layer &L = layers[l];
+        const bool moe = cfg->n_experts > 0 && L.router;
+        if (moe ? (!L.exp_gate_up || !L.exp_down || cfg->top_k < 1 || cfg->top_k > cfg->n_experts)
+                : (!L.gate_up || !L.down || I < 1))
+            return ORC_ERR_ARG;
+    }
 
     std::vector<float> h(x, x + (size_t)T * hid), pend((size_t)T * hid), y((size_t)T * hid);
     std::vector<float> qkv((size_t)T * nqkv), q((size_t)T * H * D), a((size_t)T * H * D);
@@ -379,7 +386,7 @@ extern "C" int orc_forward(const orc_config *cfg, const orc_layer *layers, const
         for (int t = 0; t < T; ++t)
             orc_rmsnorm(&h[(size_t)t * hid], L.post_norm, hid, eps, mode, &y[(size_t)t * hid]);
 
-        if (cfg->n_experts > 0) {
+        if (cfg->n_experts > 0 && L.router) {
             orc_moe_block(y.data(), T, hid, L.router, cfg->n_experts, cfg->top_k, cfg->moe_intermediate,
                           cfg->norm_topk_prob, L.exp_gate_up, L.exp_down, 0, mode, pend.data(), NULL, NULL);
         } else {

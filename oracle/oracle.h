@@ -140,6 +140,11 @@ typedef struct {
     int mode;                 /* ORC_BF16 or ORC_FP32 */
     int n_experts, top_k, moe_intermediate, norm_topk_prob; /* n_experts == 0: dense MLP */
 } orc_config;
+/* Layer kind ([P3] Qwen3MoeDecoderLayer: a layer runs the sparse MoE block unless its index is
+ * in mlp_only_layers or (index + 1) is not a multiple of decoder_sparse_step, and the dense
+ * MLP otherwise): with n_experts > 0, a layer whose router is NULL runs the dense MLP of
+ * intermediate width from gate_up / down; the caller applies the index rule when it builds the
+ * layers. */
 
 typedef struct {
     const float *in_norm, *post_norm, *q_norm, *k_norm; /* [hid], [hid], [D], [D] */
@@ -147,7 +152,7 @@ typedef struct {
     const float *o;        /* [hid][H*D] */
     const float *gate_up;  /* [2I][hid]: gate rows, then up rows (dense layers) */
     const float *down;     /* [hid][I] */
-    const float *router;   /* [E][hid] (MoE layers) */
+    const float *router;   /* [E][hid] (MoE layers; NULL: dense layer of an MoE stack) */
     const float *exp_gate_up; /* [E][2Ie][hid] */
     const float *exp_down;    /* [E][hid][Ie] */
 } orc_layer;
@@ -157,7 +162,9 @@ typedef struct {
  * into kcache/vcache ([n_layers][KV][capacity][D]), advances *length by T and
  * returns the final-norm hidden states in out [T][hid].
  * cos/sin: the [capacity][D] table from orc_rope_table.
- * Returns ORC_ERR_ARG for T < 1, ORC_ERR_CAPACITY when *length + T exceeds
+ * Returns ORC_ERR_ARG for T < 1 or a layer without the weights of its kind
+ * (dense: gate_up, down and intermediate >= 1; MoE: exp_gate_up, exp_down and
+ * 1 <= top_k <= n_experts), ORC_ERR_CAPACITY when *length + T exceeds
  * capacity; then nothing is written. */
 int orc_forward(const orc_config *cfg, const orc_layer *layers, const float *final_norm,
                 const float *cos_tab, const float *sin_tab, float *kcache, float *vcache,

@@ -32,6 +32,8 @@ class Qwen3Config:
     quant_bits: int = 0            # 0: bf16/fp32 weights; 8: u8 codes + bf16 scale/bias per group
     quant_group: int = 64
     seed: int = 0
+    decoder_sparse_step: int = 1   # MoE layer selection ("@mlx-bun/inference" qwen3-moe.ts,
+    mlp_only_layers: tuple = ()    # Qwen3MoeDecoderLayer): see is_moe_layer
 
     @property
     def qkv_rows(self) -> int:
@@ -40,6 +42,11 @@ class Qwen3Config:
     @property
     def is_moe(self) -> bool:
         return self.n_experts > 0
+
+    def is_moe_layer(self, layer: int) -> bool:
+        """A layer runs the sparse MoE block unless its index is in mlp_only_layers or
+        (index + 1) is not a multiple of decoder_sparse_step; otherwise the dense MLP."""
+        return self.n_experts > 0 and layer not in self.mlp_only_layers and (layer + 1) % self.decoder_sparse_step == 0
 
     def replace(self, **kw) -> "Qwen3Config":
         return dataclasses.replace(self, **kw)

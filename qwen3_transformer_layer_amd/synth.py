@@ -88,18 +88,26 @@ def layer_weights(cfg: Qwen3Config, layer: int, device="cpu") -> dict:
         "q_norm": norm_weight(cfg, p + "q_norm", D, device),
         "k_norm": norm_weight(cfg, p + "k_norm", D, device),
     }
-    names = ("qkv", "o") if cfg.is_moe else PROJ_SHAPES
+    moe_layer = cfg.is_moe_layer(layer)
+    names = ("qkv", "o") if moe_layer else PROJ_SHAPES
     for n in names:
         rows, cols = proj_shape(cfg, n)
         if cfg.quant_bits == 8:
             w[n + "_q"], w[n + "_s"], w[n + "_b"] = q8_weight(cfg, p + n, rows, cols, device)
         else:
             w[n] = linear_weight(cfg, p + n, (rows, cols), device)
-    if cfg.is_moe:
+    if moe_layer:
         E, Ie = cfg.n_experts, cfg.moe_intermediate
-        w["router"] = linear_weight(cfg, p + "router", (E, hid), device)
-        w["exp_gate_up"] = linear_weight(cfg, p + "exp_gate_up", (E, 2 * Ie, hid), device)
-        w["exp_down"] = linear_weight(cfg, p + "exp_down", (E, hid, Ie), device)
+        shapes = {"router": (E, hid), "exp_gate_up": (E, 2 * Ie, hid), "exp_down": (E, hid, Ie)}
+        for n, shape in shapes.items():
+            if cfg.quant_bits == 8:  # stacked experts: groups of 64 along each row's input axis
+                rows = shape[0] * (shape[1] if len(shape) == 3 else 1)
+                q, sc, bi = q8_weight(cfg, p + n, rows, shape[-1], device)
+                w[n + "_q"] = q.reshape(shape)
+                w[n + "_s"] = sc.reshape(shape[:-1] + (shape[-1] // cfg.quant_group,))
+                w[n + "_b"] = bi.reshape(shape[:-1] + (shape[-1] // cfg.quant_group,))
+            else:
+                w[n] = linear_weight(cfg, p + n, shape, device)
     return w
 
 

@@ -61,9 +61,11 @@ def host_layers(orc, cfg, weights):
             if k.endswith(("_q", "_s", "_b")):
                 continue
             d[k] = np32(v)
-        for name in ("qkv", "o", "gate_up", "down"):
-            if name + "_q" in lw:
-                d[name] = orc.q8_dequant(lw[name + "_q"].cpu().numpy(), np32(lw[name + "_s"]), np32(lw[name + "_b"]),
-                                         cfg.quant_group)
+        for name in ("qkv", "o", "gate_up", "down", "router", "exp_gate_up", "exp_down"):
+            if name + "_q" in lw:  # stacked experts [E][rows][cols] dequantised as E*rows rows
+                q = lw[name + "_q"].cpu().numpy()
+                d[name] = orc.q8_dequant(q.reshape(-1, q.shape[-1]), np32(lw[name + "_s"]).reshape(-1, q.shape[-1] // cfg.quant_group),
+                                         np32(lw[name + "_b"]).reshape(-1, q.shape[-1] // cfg.quant_group),
+                                         cfg.quant_group).reshape(q.shape)
         out.append(d)
     return out

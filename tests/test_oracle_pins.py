@@ -551,3 +551,106 @@ def test_presets_match_page_constants():
     assert QWEN3_MOE.rope_theta == pc["moe_rope_theta"]["value"] == h["rope_theta"]
     assert QWEN3_1P7B_DECODE.rope_theta == pc["qwen3_default_rope_base"]["value"]
     assert math.ceil(pc["sorted_expert_threshold"]["rows_numerator"] / QWEN3_MOE.top_k) == 8
+
+
+# ------------------------------------------------------------------ MoE stacks with dense layers
+
+@pytest.mark.parametrize("step,only", [(1, ()), (2, ()), (1, (0, 3)), (3, (2,)), (2, (1, 5))])
+def test_moe_layer_rule_matches_transformers(step, only):
+    """The layer-kind rule (MoE unless listed in mlp_only_layers or (index+1) is not a multiple of
+    decoder_sparse_step) against transformers' own per-layer choice."""
+    from transformers import Qwen3MoeConfig
+    from transformers.models.qwen3_moe.modeling_qwen3_moe import Qwen3MoeDecoderLayer, Qwen3MoeSparseMoeBlock
+    from qwen3_transformer_layer_amd.config import TINY_FP32
+    cfg = TINY_FP32.replace(n_layers=6, n_experts=4, top_k=2, moe_intermediate=16, decoder_sparse_step=step,
+                            mlp_only_layers=only)
+    hc = Qwen3MoeConfig(hidden_size=32, num_attention_heads=2, num_key_value_heads=1, head_dim=16,
+                        intermediate_size=16, num_experts=4, num_experts_per_tok=2, moe_intermediate_size=16,
+                        num_hidden_layers=6, decoder_sparse_step=step, mlp_only_layers=list(only))
+    for l in range(6):
+        hf = isinstance(Qwen3MoeDecoderLayer(hc, l).mlp, Qwen3MoeSparseMoeBlock)
+        assert cfg.is_moe_layer(l) == hf, (step, only, l)
+    assert not any(cfg.replace(n_experts=0).is_moe_layer(l) for l in range(6))
+
+
+def _mixed_moe_cfg():
+    from qwen3_transformer_layer_amd.config import TINY_FP32
+    return TINY_FP32.replace(n_layers=4, n_experts=8, top_k=2, moe_intermediate=32, norm_topk_prob=1,
+                             decoder_sparse_step=2, mlp_only_layers=(3,))
+
+
+def _hf_qwen3_moe_from_synth(cfg, w, dtype=torch.float64):
+    from transformers import Qwen3MoeConfig, Qwen3MoeModel
+    hc = Qwen3MoeConfig(vocab_size=16, hidden_size=cfg.hidden, intermediate_size=cfg.intermediate,
+                        num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
+                        num_key_value_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, rms_norm_eps=cfg.rms_eps,
+                        rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta},
+                        max_position_embeddings=cfg.capacity, attention_bias=False, num_experts=cfg.n_experts,
+                        num_experts_per_tok=cfg.top_k, moe_intermediate_size=cfg.moe_intermediate,
+                        norm_topk_prob=bool(cfg.norm_topk_prob), decoder_sparse_step=cfg.decoder_sparse_step,
+                        mlp_only_layers=list(cfg.mlp_only_layers))
+    hc._attn_implementation = "eager"
+    hc._experts_implementation = "eager"  # per-expert loop (the grouped kernel takes no float64)
+    m = Qwen3MoeModel(hc).to(dtype).eval()
+    HD, KVD, I = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.intermediate
+    with torch.no_grad():
+        for l, L in enumerate(w["layers"]):
+            ml = m.layers[l]
+            t = {k: v.to(dtype) for k, v in L.items()}
+            ml.self_attn.q_proj.weight.copy_(t["qkv"][:HD])
+            ml.self_attn.k_proj.weight.copy_(t["qkv"][HD:HD + KVD])
+            ml.self_attn.v_proj.weight.copy_(t["qkv"][HD + KVD:])
+            ml.self_attn.o_proj.weight.copy_(t["o"])
+            ml.self_attn.q_norm.weight.copy_(t["q_norm"])
+            ml.self_attn.k_norm.weight.copy_(t["k_norm"])
+            if "router" in t:
+                ml.mlp.gate.weight.copy_(t["router"])
+                ml.mlp.experts.gate_up_proj.copy_(t["exp_gate_up"])
+                ml.mlp.experts.down_proj.copy_(t["exp_down"])
+            else:
+                ml.mlp.gate_proj.weight.copy_(t["gate_up"][:I])
+                ml.mlp.up_proj.weight.copy_(t["gate_up"][I:])
+                ml.mlp.down_proj.weight.copy_(t["down"])
+            ml.input_layernorm.weight.copy_(t["in_norm"])
+            ml.post_attention_layernorm.weight.copy_(t["post_norm"])
+        m.norm.weight.copy_(w["final_norm"].to(dtype))
+    return m
+
+
+def test_mixed_moe_stack_fp32_matches_transformers_fp64(orc):
+    """Four layers, decoder_sparse_step 2 and mlp_only_layers (3,): dense, MoE, dense, dense
+    (layer 3 is listed).  The synthetic builder gives each layer the weights of its kind; the
+    oracle's fp32 stack matches the float64 Qwen3-MoE model over a 12-token prefill and three
+    decode steps."""
+    from qwen3_transformer_layer_amd import synth
+    cfg = _mixed_moe_cfg()
+    assert [cfg.is_moe_layer(l) for l in range(4)] == [False, True, False, False]
+    w = synth.model_weights(cfg)
+    assert ["router" in L for L in w["layers"]] == [False, True, False, False]
+    assert ["gate_up" in L for L in w["layers"]] == [True, False, True, True]
+    x = synth.hidden_states(cfg, 15)
+    st = _oracle_stack(orc, cfg, w, "fp32")
+    got = np.concatenate([st.forward(x[:12].numpy())] + [st.forward(x[12 + i:13 + i].numpy()) for i in range(3)])
+    m = _hf_qwen3_moe_from_synth(cfg, w)
+    ref = _hf_run(m, [x[:12].double()] + [x[12 + i:13 + i].double() for i in range(3)], cfg)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(got - ref)) / rms < 2e-5
+
+
+def test_moe_stack_rejects_a_layer_without_its_weights(orc):
+    from qwen3_transformer_layer_amd import synth
+    cfg = _mixed_moe_cfg().replace(n_layers=2)
+    w = synth.model_weights(cfg)
+    layers = [{k: v.float().numpy() for k, v in L.items()} for L in w["layers"]]
+    x = synth.hidden_states(cfg, 2).numpy()
+    bad = [dict(layers[0]), layers[1]]
+    del bad[0]["gate_up"]                    # a dense layer without its MLP
+    with pytest.raises(ValueError):
+        orc.Stack(cfg, bad, w["final_norm"].float().numpy(), "fp32").forward(x)
+    bad = [layers[0], dict(layers[1])]
+    del bad[1]["exp_down"]                   # an MoE layer without its experts
+    with pytest.raises(ValueError):
+        orc.Stack(cfg, bad, w["final_norm"].float().numpy(), "fp32").forward(x)
+    st = orc.Stack(cfg, layers, w["final_norm"].float().numpy(), "fp32")
+    st.forward(x)
+    assert st.length == 2
