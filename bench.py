@@ -49,6 +49,12 @@ MOE_EXPERT_BYTES = (1536 * 2048 + 2048 * 768) * 2
 # Decode at position 2047: attention weights + router + the 8 routed experts + the K/V read
 # of 2048 positions (4 kv heads, head_dim 128, K and V).
 MOE_DECODE_STEP_BYTES = 48 * (MOE_QKV_O_ROUTER + 8 * MOE_EXPERT_BYTES + 4 * 2048 * 128 * 2 * 2)
+# The same stack with 8-bit weights everywhere (codes + bf16 scale and bias per 64 codes).
+def _q8b(n):
+    return n + n // 64 * 4
+MOE_Q8_QKV_O_ROUTER = _q8b(5120 * 2048) + _q8b(2048 * 4096) + _q8b(128 * 2048)
+MOE_Q8_EXPERT_BYTES = _q8b(1536 * 2048) + _q8b(2048 * 768)
+MOE_Q8_DECODE_STEP_BYTES = 48 * (MOE_Q8_QKV_O_ROUTER + 8 * MOE_Q8_EXPERT_BYTES + 4 * 2048 * 128 * 2 * 2)
 # q8 decode at ctx 4096: per layer u8 codes + bf16 scale and bias per 64 codes for the four
 # projections (50,331,648 weights), the K/V read, the norm vectors and the new K/V entries.
 Q8_WEIGHTS = 4096 * 2048 + 2048 * 2048 + 12288 * 2048 + 2048 * 6144
@@ -209,8 +215,9 @@ def _graph_seconds(fn, stream, steps: int, warmup: int) -> float:
     return dt
 
 
-def moe_bench(steps: int, warmup: int):
-    """The Qwen3-MoE-shaped stack: (a) a T = 1 step at position 2047 over a K/V pre-fill of
+def moe_bench(steps: int, warmup: int, q8: bool = False):
+    """The Qwen3-MoE-shaped stack (q8: every weight 8-bit, router and experts included):
+    (a) a T = 1 step at position 2047 over a K/V pre-fill of
     0..2046, (b) one 64-token call from an empty cache, (c) the isolated MoE block (router,
     top-8, sort, experts, weighted sum) on x [64][2048] and [1][2048].  Bytes: (a) counts the
     8 routed experts of every layer; (c) counts the distinct experts the block's own top-8
@@ -221,10 +228,14 @@ def moe_bench(steps: int, warmup: int):
 
     import qwen3_transformer_layer_amd as q3
     from qwen3_transformer_layer_amd import synth
-    from qwen3_transformer_layer_amd.config import QWEN3_MOE as cfg
+    from qwen3_transformer_layer_amd.config import QWEN3_MOE
 
+    cfg = QWEN3_MOE.replace(quant_bits=8, quant_group=64) if q8 else QWEN3_MOE
+    qkv_o_router = MOE_Q8_QKV_O_ROUTER if q8 else MOE_QKV_O_ROUTER
+    expert_bytes = MOE_Q8_EXPERT_BYTES if q8 else MOE_EXPERT_BYTES
+    step_bytes = MOE_Q8_DECODE_STEP_BYTES if q8 else MOE_DECODE_STEP_BYTES
     dev = "cuda"
-    log(f"moe: building {cfg.n_layers}-layer weights ({cfg.n_experts} experts per layer)")
+    log(f"moe{' q8' if q8 else ''}: building {cfg.n_layers}-layer weights ({cfg.n_experts} experts per layer)")
     w = synth.model_weights(cfg, dev)
     K, V = synth.kv_cache(cfg, 2047, dev)
     torch.cuda.synchronize()
@@ -255,20 +266,20 @@ def moe_bench(steps: int, warmup: int):
             q3.qwen3_moe_block(seat.handle, 0, xb, ob, idx[:T], wts[:T])
         t = _graph_seconds(block, stream, steps, warmup)
         distinct = int(torch.unique(idx[:T]).numel())
-        nbytes = 128 * 2048 * 2 + distinct * MOE_EXPERT_BYTES + 2 * T * 2048 * 2
+        nbytes = (_q8b(128 * 2048) if q8 else 128 * 2048 * 2) + distinct * expert_bytes + 2 * T * 2048 * 2
         blk[T] = {"us": round(t * 1e6, 2), "distinct_experts": distinct, "bytes": nbytes,
                   "gbps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
     q3.qwen3_check_device_errors(seat.handle)
-    b64 = cfg.n_layers * (MOE_QKV_O_ROUTER + 125.95 * MOE_EXPERT_BYTES)
-    res = {"workload": "Qwen3-MoE-shaped bf16 stack: 48 layers, hidden 2048, 32 q / 4 kv heads, 128 experts, "
-                       "top-8 renormalised, expert intermediate 768",
+    b64 = cfg.n_layers * (qkv_o_router + 125.95 * expert_bytes)
+    res = {"workload": f"Qwen3-MoE-shaped {'8-bit-weight (groups of 64) ' if q8 else ''}bf16 stack: 48 layers, "
+                       "hidden 2048, 32 q / 4 kv heads, 128 experts, top-8 renormalised, expert intermediate 768",
            "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
-           "decode_step_bytes": MOE_DECODE_STEP_BYTES, "decode_gbps": round(MOE_DECODE_STEP_BYTES / t_dec / 1e9, 1),
-           "decode_hbm_frac": round(MOE_DECODE_STEP_BYTES / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
+           "decode_step_bytes": step_bytes, "decode_gbps": round(step_bytes / t_dec / 1e9, 1),
+           "decode_hbm_frac": round(step_bytes / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
            "T64_ms": round(t64 * 1e3, 4), "T64_tokens_per_s": round(64 / t64, 1),
            "T64_gbps_expected_experts": round(b64 / t64 / 1e9, 1),
            "block_T64": blk[64], "block_T1": blk[1]}
-    log(f"moe: decode {t_dec * 1e3:.3f} ms/step ({res['decode_gbps']} GB/s), T=64 call {t64 * 1e3:.3f} ms, "
+    log(f"moe{' q8' if q8 else ''}: decode {t_dec * 1e3:.3f} ms/step ({res['decode_gbps']} GB/s), T=64 call {t64 * 1e3:.3f} ms, "
         f"block T=64 {blk[64]['us']} us ({blk[64]['gbps']} GB/s), block T=1 {blk[1]['us']} us")
     del seat, w, K, V
     torch.cuda.empty_cache()
@@ -466,14 +477,15 @@ def main():
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
         return
     if args.variants_only:
-        print(json.dumps({"moe": moe_bench(30, 3), "q8": q8_bench(30, 3, 5), "head": head_bench(50, 5),
-                          "batch": batch_bench()}), flush=True)
+        print(json.dumps({"moe": moe_bench(30, 3), "moe_q8": moe_bench(30, 3, q8=True), "q8": q8_bench(30, 3, 5),
+                          "head": head_bench(50, 5), "batch": batch_bench()}), flush=True)
         return
     if args.copy_calib:
         copy_calibration()
     dec = decode_bench(args.steps, args.warmup, compare=not args.no_compare)
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     moe = None if args.no_variants else moe_bench(30, 3)
+    moe_q8 = None if args.no_variants else moe_bench(30, 3, q8=True)
     q8 = None if args.no_variants else q8_bench(30, 3, 5)
     head = None if args.no_variants else head_bench(50, 5)
     batch = None if args.no_variants else batch_bench()
@@ -516,6 +528,7 @@ def main():
                      "bytes_per_launch": rl_bytes, "avg_launch_us": round(dec["kernel_us"], 3),
                      "launches": dec["launches"]},
         "moe": moe,
+        "moe_q8": moe_q8,
         "q8": q8,
         "head": head,
         "batch_decode": batch,

@@ -45,7 +45,16 @@
  *    and bias [out][in/quant_group]; w = scale * code + bias per group along
  *    the input axis; q|k|v and gate|up are quantised as the fused rows;
  *  - MoE: router [E][hidden], expert gate|up [E][2*Ie][hidden], expert down
- *    [E][hidden][Ie];
+ *    [E][hidden][Ie]; with quant_bits == 8 all three are u8 codes of those
+ *    shapes with bf16 scale and bias [E][hidden/64], [E][2*Ie][hidden/64] and
+ *    [E][hidden][Ie/64] ("@mlx-bun/inference" qwen3-moe.ts, the quantised gate
+ *    Linear and QuantizedSwitchLinear experts of Qwen3SwitchWeights);
+ *  - layer kind in an MoE configuration (n_experts > 0; qwen3-moe.ts,
+ *    Qwen3MoeDecoderLayer: a layer is sparse unless its index is in
+ *    mlp_only_layers or (index + 1) is not a multiple of decoder_sparse_step):
+ *    a layer with a router runs the MoE block, a layer whose router is NULL
+ *    runs the dense MLP (gate_up / down of width intermediate); the caller
+ *    applies the index rule when it fills the layer array;
  *  - KV cache: K and V each [n_layers][n_kv_heads][capacity][head_dim]; the
  *    cache holds post-norm, post-RoPE keys and raw values (Backbone.reset and
  *    forward).  Entries at positions >= the seat length are never read;
@@ -89,7 +98,10 @@ typedef struct {
     const void *qkv, *o, *gate_up, *down;               /* plain weights, or u8 codes if quantised */
     const void *qkv_s, *qkv_b, *o_s, *o_b;              /* bf16 per-group scale and bias (quantised) */
     const void *gate_up_s, *gate_up_b, *down_s, *down_b;
-    const void *router, *exp_gate_up, *exp_down;        /* MoE layers */
+    const void *router, *exp_gate_up, *exp_down;        /* MoE layers (u8 codes if quantised) */
+    const void *router_s, *router_b;                    /* bf16 per-group scale and bias of the */
+    const void *exp_gate_up_s, *exp_gate_up_b;          /* quantised MoE weights */
+    const void *exp_down_s, *exp_down_b;
 } qwen3_layer_weights;
 
 typedef struct {
@@ -113,7 +125,8 @@ size_t qwen3_workspace_bytes(const qwen3_config *cfg);
  *   workspace: ws_bytes >= qwen3_workspace_bytes(cfg), 256-byte aligned.
  *   stream: hipStream_t for every enqueue (NULL = the null stream).
  * Supported: head_dim 64 or 128; n_heads a multiple of n_kv_heads; hidden,
- * intermediate and moe_intermediate multiples of 64; quant_group 64.  Returns
+ * intermediate and moe_intermediate multiples of 64 (intermediate may be 0 in
+ * an MoE configuration without dense layers); quant_group 64.  Returns
  * QWEN3_ERR_UNSUPPORTED otherwise, QWEN3_ERR_DTYPE for another dtype,
  * QWEN3_ERR_NULL_WEIGHT for a missing weight.  *out is set only on success. */
 int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, void *v_cache,
@@ -145,8 +158,8 @@ int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out);
  * and topk_w (model dtype [T][top_k]) receive the routing when not NULL: the
  * selected experts in slot order of descending probability, ties to the lower
  * expert index.  Does not touch the cache or the length.  Errors:
- * QWEN3_ERR_ARG (not an MoE configuration, layer out of range, T < 1 or
- * T > max_tokens). */
+ * QWEN3_ERR_ARG (not an MoE configuration, layer out of range or a dense
+ * layer, T < 1 or T > max_tokens). */
 int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out, int32_t *topk_idx,
                     void *topk_w);
 

@@ -82,7 +82,7 @@ def qwen3_init(cfg: Qwen3Config, weights: dict, k_cache: torch.Tensor, v_cache: 
     for i, lw in enumerate(weights["layers"]):
         for name in _lib.LAYER_FIELDS:
             t = lw.get(name)
-            if t is None and name in ("qkv", "o", "gate_up", "down"):
+            if t is None and name in ("qkv", "o", "gate_up", "down", "router", "exp_gate_up", "exp_down"):
                 t = lw.get(name + "_q")
             setattr(arr[i], name, None if t is None else t.data_ptr())
     w = _lib.Weights(_ptr(weights.get("embed")), _ptr(weights["final_norm"]),

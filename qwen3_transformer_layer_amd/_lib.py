@@ -26,7 +26,8 @@ class Config(ctypes.Structure):
 
 
 LAYER_FIELDS = ("in_norm", "post_norm", "q_norm", "k_norm", "qkv", "o", "gate_up", "down", "qkv_s", "qkv_b", "o_s",
-                "o_b", "gate_up_s", "gate_up_b", "down_s", "down_b", "router", "exp_gate_up", "exp_down")
+                "o_b", "gate_up_s", "gate_up_b", "down_s", "down_b", "router", "exp_gate_up", "exp_down",
+                "router_s", "router_b", "exp_gate_up_s", "exp_gate_up_b", "exp_down_s", "exp_down_b")
 
 
 class LayerWeights(ctypes.Structure):

@@ -51,6 +51,18 @@ __device__ __forceinline__ u32x4 ld_stream(const void *p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 
+// 16 codes of one 128-bit word against 16 activations: sum_i x_i * q_i (8-bit
+// affine weights: kernels_q8.hip, kernels_moe.hip).
+__device__ __forceinline__ float dot16_q8(u32x4 c, const float *xf) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a += xf[4 * i + b] * (float)((w[i] >> (8 * b)) & 0xffu);
+    return a;
+}
+
 // Expand 16 bytes of storage type T into fp32 values: 8 for bf16, 4 for fp32.
 template <typename T> struct Vec;
 template <> struct Vec<bf16> {

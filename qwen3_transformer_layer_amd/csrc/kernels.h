@@ -81,9 +81,17 @@ hipError_t launch_attention_decode_batch(int dt, const void *qkv, int B, int H, 
 // (ties to the lower index, slot order descending probability), renormalised weights
 // w [T][k] (storage dt), expert SwiGLU FFNs and out [T][hid] = rho(sum_s rho(y_s * w_s)).
 // idx: int32 [T][k].  ws: moe_workspace() bytes.  Requires E <= 256, k <= 16.
+// Weights: router [E][hid], gate|up [E][2*Ie][hid], down [E][hid][Ie] in the model dtype, or
+// (q8, bf16 only) u8 codes of those shapes with bf16 scale and bias [rows][in/64] each.
+struct MoeWeights {
+    const void *router, *router_s, *router_b;
+    const void *gate_up, *gate_up_s, *gate_up_b;
+    const void *down, *down_s, *down_b;
+    bool q8;
+};
 size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
-hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
-                      const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
+hipError_t launch_moe(int dt, const void *x, int T, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,
+                      int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
 // ---- output head + greedy token (kernels_head.hip): logits fp32 [T][V] and/or argmax int32 [T];
 // keys: 64 T 64-bit words of scratch

@@ -24,7 +24,14 @@
 //     every hit expert's weights are read from HBM once for up to 8 tokens;
 //  5. moe_combine_kernel: out[t] = rho(sum_s rho(y[t,s] * w[t,s])), slot order,
 //     one thread per output element.
+// 8-bit weights (bf16 model; the quantised gate Linear and QuantizedSwitchLinear experts of
+// qwen3-moe.ts): the router goes through the 8-bit projection kernels and
+// moe_expert_q8_kernel replaces step 4 with the same work mapping, a lane taking 16 codes
+// per weight row per step and folding each group as s * (x . q) + b * sum(x) in fp32
+// (kernels_q8.hip's format: groups of 64 along the input axis).
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -316,6 +323,86 @@ __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ x
     }
 }
 
+// The 8-bit form of moe_expert_kernel (bf16 activations): codes [E][rows][K] u8, scale and
+// bias [E][rows][K/64] bf16; chunk c of a row is codes 16c..16c+15, in group c / 4.
+template <int PASS>
+__global__ void __launch_bounds__(256) moe_expert_q8_kernel(const bf16 *__restrict__ xin,
+                                                            const uint8_t *__restrict__ codes,
+                                                            const bf16 *__restrict__ scale,
+                                                            const bf16 *__restrict__ bias, int K, int N, int k,
+                                                            const int32_t *__restrict__ offsets,
+                                                            const int32_t *__restrict__ perm,
+                                                            const int32_t *__restrict__ active, bf16 *__restrict__ out) {
+    constexpr int MR = 8;
+    constexpr int NR = PASS == 0 ? 2 : 4;
+    const int slot = blockIdx.y;
+    if (slot >= active[0]) return;
+    const int e = active[1 + slot];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = PASS == 0 ? blockIdx.x * 4 + wave : (blockIdx.x * 4 + wave) * NR;
+    if (n0 >= N) return;
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    const size_t wrows = PASS == 0 ? 2 * (size_t)N : (size_t)N;
+    const int ng = K / 64, nc = K / 16;
+    size_t row[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) row[q] = (size_t)e * wrows + (PASS == 0 ? n0 + q * N : min(n0 + q, N - 1));
+    for (int rb = r0; rb < r1; rb += MR) {
+        const int nr = min(MR, r1 - rb);
+        const bf16 *xr[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const int i = rb + min(m, nr - 1);
+            xr[m] = PASS == 0 ? xin + (size_t)(perm[i] / k) * K : xin + (size_t)i * K;
+        }
+        float a[NR][MR];
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) a[q][m] = 0.f;
+        for (int c = lane; c < nc; c += 64) {
+            u32x4 cw[NR];
+            float sc[NR], bi[NR];
+#pragma unroll
+            for (int q = 0; q < NR; ++q) {
+                cw[q] = ld_stream(codes + row[q] * K + (size_t)c * 16);
+                sc[q] = to_f(scale[row[q] * ng + (c >> 2)]);
+                bi[q] = to_f(bias[row[q] * ng + (c >> 2)]);
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                if (m < nr) {
+                    float xf[16];
+                    const bf16 *xp = xr[m] + (size_t)c * 16;
+                    Vec<bf16>::expand(ld16(xp), xf);
+                    Vec<bf16>::expand(ld16(xp + 8), xf + 8);
+                    float xs = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xs += xf[i];
+#pragma unroll
+                    for (int q = 0; q < NR; ++q) a[q][m] += sc[q] * dot16_q8(cw[q], xf) + bi[q] * xs;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m < nr) {
+                if (PASS == 0) {
+                    const float s0 = wave_sum(a[0][m]), s1 = wave_sum(a[1][m]);
+                    if (lane == 0)
+                        out[(size_t)(rb + m) * N + n0] = from_f<bf16>(rho<bf16>(silu_f32(rho<bf16>(s0))) * rho<bf16>(s1));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NR; ++q) {
+                        const float sq = wave_sum(a[q][m]);
+                        if (lane == 0 && n0 + q < N) out[(size_t)(rb + m) * N + n0 + q] = from_f<bf16>(sq);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ weighted slot sum
 // grid (hid / 256, T): one thread per output element; the token's k sorted positions and
 // weights are loaded first, so the k row reads are in flight together.
@@ -343,8 +430,8 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ 
 
 // ------------------------------------------------------------ dispatch
 template <typename T>
-static hipError_t moe_t(const void *x, int T_, int hid, const void *Wr, int E, int k, int norm, int Ie,
-                        const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
+static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,
+                        int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
     const int dt = DtOf<T>::value;
     const MoeWs L = moe_layout(T_, hid, E, k, Ie, dt);
     char *base = (char *)ws;
@@ -353,7 +440,9 @@ static hipError_t moe_t(const void *x, int T_, int hid, const void *Wr, int E, i
     int32_t *inv = (int32_t *)(base + L.inv), *active = (int32_t *)(base + L.active);
     T *mbuf = (T *)(base + L.m), *ybuf = (T *)(base + L.y);
     const int rows = T_ * k;
-    hipError_t e = launch_linear(dt, x, T_, hid, Wr, E, EPI_STORE, nullptr, logits, s);
+    hipError_t e = W.q8 ? launch_linear_q8(x, T_, hid, (const uint8_t *)W.router, W.router_s, W.router_b, 64, E,
+                                           EPI_STORE, nullptr, logits, s)
+                        : launch_linear(dt, x, T_, hid, W.router, E, EPI_STORE, nullptr, logits, s);
     if (e != hipSuccess) return e;
     if (T_ == 1) {
         moe_route1_kernel<T><<<1, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w, offsets, perm, inv, active);
@@ -362,18 +451,31 @@ static hipError_t moe_t(const void *x, int T_, int hid, const void *Wr, int E, i
         moe_sort_kernel<<<1, 256, 0, s>>>(idx, rows, E, offsets, perm, inv, active);
     }
     const int na_max = rows < E ? rows : E;
-    moe_expert_kernel<T, 0><<<dim3((Ie + 3) / 4, na_max), 256, 0, s>>>((const T *)x, (const T *)Wgu, hid, Ie, k,
-                                                                       offsets, perm, active, mbuf);
-    moe_expert_kernel<T, 1><<<dim3((hid + 15) / 16, na_max), 256, 0, s>>>(mbuf, (const T *)Wd, Ie, hid, k, offsets,
-                                                                          perm, active, ybuf);
+    const dim3 g0((Ie + 3) / 4, na_max), g1((hid + 15) / 16, na_max);
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (W.q8) {
+            moe_expert_q8_kernel<0><<<g0, 256, 0, s>>>((const bf16 *)x, (const uint8_t *)W.gate_up,
+                                                       (const bf16 *)W.gate_up_s, (const bf16 *)W.gate_up_b, hid, Ie,
+                                                       k, offsets, perm, active, mbuf);
+            moe_expert_q8_kernel<1><<<g1, 256, 0, s>>>(mbuf, (const uint8_t *)W.down, (const bf16 *)W.down_s,
+                                                       (const bf16 *)W.down_b, Ie, hid, k, offsets, perm, active,
+                                                       ybuf);
+        }
+    }
+    if (!W.q8) {
+        moe_expert_kernel<T, 0><<<g0, 256, 0, s>>>((const T *)x, (const T *)W.gate_up, hid, Ie, k, offsets, perm,
+                                                   active, mbuf);
+        moe_expert_kernel<T, 1><<<g1, 256, 0, s>>>(mbuf, (const T *)W.down, Ie, hid, k, offsets, perm, active, ybuf);
+    }
     moe_combine_kernel<T><<<dim3((hid + 255) / 256, T_), 256, 0, s>>>(ybuf, (const T *)w, inv, hid, k, rows, (T *)out);
     return hipGetLastError();
 }
 
-hipError_t launch_moe(int dt, const void *x, int T, int hid, const void *Wr, int E, int k, int norm, int Ie,
-                      const void *Wgu, const void *Wd, int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
-    if (dt == DT_BF16) return moe_t<bf16>(x, T, hid, Wr, E, k, norm, Ie, Wgu, Wd, idx, w, out, ws, s);
-    return moe_t<float>(x, T, hid, Wr, E, k, norm, Ie, Wgu, Wd, idx, w, out, ws, s);
+hipError_t launch_moe(int dt, const void *x, int T, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,
+                      int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
+    if (dt == DT_BF16) return moe_t<bf16>(x, T, hid, W, E, k, norm, Ie, idx, w, out, ws, s);
+    if (W.q8) return hipErrorInvalidValue;  // 8-bit weights come with the bf16 model dtype only
+    return moe_t<float>(x, T, hid, W, E, k, norm, Ie, idx, w, out, ws, s);
 }
 
 }  // namespace q3

@@ -31,17 +31,6 @@ static __device__ __forceinline__ float epi_q8(int epi, float a, float b, const 
     return a;
 }
 
-// 16 codes of one 128-bit word against 16 activations: returns sum x*q, adds sum x to *xs.
-static __device__ __forceinline__ float dot16_q8(u32x4 c, const float *xf) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) a += xf[4 * i + b] * (float)((w[i] >> (8 * b)) & 0xffu);
-    return a;
-}
-
 // Every code, scale and bias load of the lane's chunks (c = lane + 64 u, u < QU) is issued
 // before any arithmetic, so a wave keeps its whole row in flight; K <= 64 * 16 * QU, QU = 2, 4
 // or 8 picked from K (registers for unused chunks would lower the occupancy).

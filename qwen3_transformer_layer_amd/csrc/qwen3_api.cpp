@@ -14,6 +14,7 @@
 //              dense: m = swiglu(y2 Wgu^T)                 linear, SwiGLU epilogue
 //                     pend = rho(m Wdown^T)                linear
 //              MoE:   pend = moe(y2)                       router/top-k/sort/experts/combine
+//   (in an MoE configuration a layer with a router is sparse, one without runs the dense MLP)
 //   after the last layer: out = RMSNorm(rho(h + pend))     add_rmsnorm
 #include <stdarg.h>
 #include <stdio.h>
@@ -146,7 +147,8 @@ int check_config(const qwen3_config *c, std::string *why) {
             return bad(QWEN3_ERR_UNSUPPORTED, "MoE needs 1 <= top_k <= min(16, n_experts) and n_experts <= 256");
         if (c->moe_intermediate < 64 || c->moe_intermediate % 64)
             return bad(QWEN3_ERR_UNSUPPORTED, "moe_intermediate must be a positive multiple of 64");
-        if (c->quant_bits) return bad(QWEN3_ERR_UNSUPPORTED, "quantised MoE experts are not supported");
+        if (c->intermediate != 0 && (c->intermediate < 64 || c->intermediate % 64))
+            return bad(QWEN3_ERR_UNSUPPORTED, "intermediate must be 0 or a positive multiple of 64");
     } else {
         if (c->intermediate < 64 || c->intermediate % 64)
             return bad(QWEN3_ERR_UNSUPPORTED, "intermediate must be a positive multiple of 64");
@@ -162,6 +164,17 @@ int check_config(const qwen3_config *c, std::string *why) {
 }
 
 bool is_q8(const qwen3_handle *h) { return h->cfg.quant_bits == 8; }
+
+// Layer kind: sparse MoE block iff the configuration has experts and the layer a router.
+bool moe_layer(const qwen3_config &c, const qwen3_layer_weights &L) { return c.n_experts > 0 && L.router; }
+
+hipError_t moe(qwen3_handle *h, const qwen3_layer_weights &L, const void *x, int T, int32_t *idx, void *w, void *out) {
+    const qwen3_config &c = h->cfg;
+    const MoeWeights W{L.router, L.router_s, L.router_b, L.exp_gate_up, L.exp_gate_up_s, L.exp_gate_up_b,
+                       L.exp_down, L.exp_down_s, L.exp_down_b, is_q8(h)};
+    return launch_moe(c.dtype, x, T, c.hidden, W, c.n_experts, c.top_k, c.norm_topk_prob, c.moe_intermediate, idx,
+                      w, out, h->moe_ws, h->stream);
+}
 
 hipError_t linear(qwen3_handle *h, const void *x, int M, int K, const void *W, const void *Ws, const void *Wb, int N,
                   int epi, const void *res, void *out) {
@@ -246,11 +259,9 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
         HIPCHECK(h, linear(h, h->a, 1, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : hnext, hnext));
         HIPCHECK(h, mark(h, K_O, false));
         hcur = hnext;
-        if (c.n_experts > 0) {
+        if (moe_layer(c, L)) {
             HIPCHECK(h, launch_add_rmsnorm(dt, hcur, nullptr, L.post_norm, nullptr, h->y, 1, hid, c.rms_eps, s));
-            HIPCHECK(h, launch_moe(dt, h->y, 1, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
-                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
-                                   h->moe_ws, s));
+            HIPCHECK(h, moe(h, L, h->y, 1, h->moe_idx, h->moe_w, h->pend));
         } else {
             HIPCHECK(h, mark(h, K_GU, true));
             HIPCHECK(h, linear_norm(h, hcur, nullptr, L.post_norm, nullptr, hid, L.gate_up, L.gate_up_s, L.gate_up_b,
@@ -291,10 +302,8 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         HIPCHECK(h, linear(h, h->a, T, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
         HIPCHECK(h, mark(h, K_O, false));
         HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, T, hid, c.rms_eps, s));
-        if (c.n_experts > 0) {
-            HIPCHECK(h, launch_moe(dt, h->y, T, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
-                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
-                                   h->moe_ws, s));
+        if (moe_layer(c, L)) {
+            HIPCHECK(h, moe(h, L, h->y, T, h->moe_idx, h->moe_w, h->pend));
         } else {
             HIPCHECK(h, mark(h, K_GU, true));
             HIPCHECK(h, linear(h, h->y, T, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
@@ -336,10 +345,8 @@ int run_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
                                                   h->sin_t, kc, vc, pos, c.capacity, h->a, h->attn_ws, s));
         HIPCHECK(h, linear(h, h->a, B, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
         HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, B, hid, c.rms_eps, s));
-        if (c.n_experts > 0) {
-            HIPCHECK(h, launch_moe(dt, h->y, B, hid, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
-                                   c.moe_intermediate, L.exp_gate_up, L.exp_down, h->moe_idx, h->moe_w, h->pend,
-                                   h->moe_ws, s));
+        if (moe_layer(c, L)) {
+            HIPCHECK(h, moe(h, L, h->y, B, h->moe_idx, h->moe_w, h->pend));
         } else {
             HIPCHECK(h, linear(h, h->y, B, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
                                nullptr, h->m));
@@ -427,10 +434,14 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
         const qwen3_layer_weights &Lw = w->layers[l];
         if (!Lw.in_norm || !Lw.post_norm || !Lw.q_norm || !Lw.k_norm || !Lw.qkv || !Lw.o) return QWEN3_ERR_NULL_WEIGHT;
         if (q8 && (!Lw.qkv_s || !Lw.qkv_b || !Lw.o_s || !Lw.o_b)) return QWEN3_ERR_NULL_WEIGHT;
-        if (moe) {
-            if (!Lw.router || !Lw.exp_gate_up || !Lw.exp_down) return QWEN3_ERR_NULL_WEIGHT;
-        } else {
+        if (moe && Lw.router) {
+            if (!Lw.exp_gate_up || !Lw.exp_down) return QWEN3_ERR_NULL_WEIGHT;
+            if (q8 && (!Lw.router_s || !Lw.router_b || !Lw.exp_gate_up_s || !Lw.exp_gate_up_b || !Lw.exp_down_s ||
+                       !Lw.exp_down_b))
+                return QWEN3_ERR_NULL_WEIGHT;
+        } else {  // dense MLP (every layer of a dense configuration; router-less layers of an MoE one)
             if (!Lw.gate_up || !Lw.down) return QWEN3_ERR_NULL_WEIGHT;
+            if (cfg->intermediate < 64) return QWEN3_ERR_UNSUPPORTED;
             if (q8 && (!Lw.gate_up_s || !Lw.gate_up_b || !Lw.down_s || !Lw.down_b)) return QWEN3_ERR_NULL_WEIGHT;
         }
     }
@@ -560,10 +571,10 @@ int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out,
     if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
     if (T < 1 || T > c.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, c.max_tokens);
     const qwen3_layer_weights &L = h->layers[layer];
+    if (!moe_layer(c, L)) return fail(h, QWEN3_ERR_ARG, "layer %d is a dense layer", layer);
     int32_t *idx = topk_idx ? topk_idx : h->moe_idx;
     void *w = topk_w ? topk_w : h->moe_w;
-    HIPCHECK(h, launch_moe(c.dtype, x, T, c.hidden, L.router, c.n_experts, c.top_k, c.norm_topk_prob,
-                           c.moe_intermediate, L.exp_gate_up, L.exp_down, idx, w, out, h->moe_ws, h->stream));
+    HIPCHECK(h, moe(h, L, x, T, idx, w, out));
     return QWEN3_OK;
 }
 

@@ -75,8 +75,8 @@ int qwen3_op_moe(int dtype, const void *x, int T, int hid, const void *router, i
     if (T < 1 || hid < 64 || hid % 64 || E < 1 || E > 256 || k < 1 || k > 16 || k > E || Ie < 64 || Ie % 64)
         return QWEN3_ERR_ARG;
     if (ws_bytes < moe_workspace(T, hid, E, k, Ie, dtype)) return QWEN3_ERR_WORKSPACE;
-    return hip_rc(launch_moe(dtype, x, T, hid, router, E, k, norm, Ie, exp_gate_up, exp_down, idx, w, out, ws,
-                             (hipStream_t)stream));
+    const MoeWeights W{router, nullptr, nullptr, exp_gate_up, nullptr, nullptr, exp_down, nullptr, nullptr, false};
+    return hip_rc(launch_moe(dtype, x, T, hid, W, E, k, norm, Ie, idx, w, out, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"
