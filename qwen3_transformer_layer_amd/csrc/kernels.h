@@ -92,6 +92,10 @@ struct MoeWeights {
 size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt);
 hipError_t launch_moe(int dt, const void *x, int T, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,
                       int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
+// One token with the RMSNorm in front: y = rho(nw * rho(h * r)) (the post-attention norm of a
+// decode step), then the MoE block of y; out, idx, w and ws as for launch_moe with T = 1.
+hipError_t launch_moe_norm1(int dt, const void *h, const void *nw, float eps, int hid, const MoeWeights &W, int E,
+                            int k, int norm, int Ie, int32_t *idx, void *w, void *out, void *ws, hipStream_t s);
 
 // ---- output head + greedy token (kernels_head.hip): logits fp32 [T][V] and/or argmax int32 [T];
 // keys: 64 T 64-bit words of scratch

@@ -16,14 +16,18 @@
 //     expert in one block (LDS counts, a wave scan, then each chunk of 256 rows
 //     ranked against the rows before it), giving per-expert row ranges, the
 //     sorted-to-row permutation, its inverse and the list of experts that received
-//     rows.  For T == 1, moe_route1_kernel does steps 2 and 3 in one wave: the k
-//     selected experts are distinct, so the sorted layout is their ascending order;
+//     rows;
 //  4. moe_expert_kernel: grid (wave group, active expert); each wave streams
 //     weight rows of its expert (the gate/up pair of one output in the first
 //     pass, four output rows in the second) once per group of 8 routed rows, so
 //     every hit expert's weights are read from HBM once for up to 8 tokens;
 //  5. moe_combine_kernel: out[t] = rho(sum_s rho(y[t,s] * w[t,s])), slot order,
 //     one thread per output element.
+// One token (T == 1, the decode step) takes three launches instead: the router projection
+// (with the post-attention RMSNorm in its prologue when the caller passes the norm weight),
+// moe_gu1_kernel (every block repeats the softmax/top-k of its token from the logits and
+// streams the gate|up rows of its slot's expert) and moe_down1_kernel (down rows of every
+// slot for four outputs per block, then the weighted slot sum in slot order).
 // 8-bit weights (bf16 model; the quantised gate Linear and QuantizedSwitchLinear experts of
 // qwen3-moe.ts): the router goes through the 8-bit projection kernels and
 // moe_expert_q8_kernel replaces step 4 with the same work mapping, a lane taking 16 codes
@@ -99,14 +103,18 @@ __device__ __forceinline__ void select_topk(const float (&v)[EPL], int E, int k,
 // Softmax over the token's E logits in fp32, probabilities rounded to the model dtype
 // (v[i] for expert lane + 64 i; -inf past E).
 template <typename T, int EPL>
-__device__ __forceinline__ void softmax_probs(const T *l, int E, int lane, float (&v)[EPL]) {
-    float m = -INFINITY;
+__device__ __forceinline__ void load_logits(const T *l, int E, int lane, float (&v)[EPL]) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         v[i] = e < E ? to_f(l[e]) : -INFINITY;
-        m = fmaxf(m, v[i]);
     }
+}
+template <typename T, int EPL>
+__device__ __forceinline__ void softmax_inplace(int E, int lane, float (&v)[EPL]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
     m = wave_max(m);
     float z = 0.f;
 #pragma unroll
@@ -121,6 +129,11 @@ __device__ __forceinline__ void softmax_probs(const T *l, int E, int lane, float
         const int e = lane + 64 * i;
         v[i] = e < E ? rho<T>(v[i] / z) : -INFINITY;
     }
+}
+template <typename T, int EPL>
+__device__ __forceinline__ void softmax_probs(const T *l, int E, int lane, float (&v)[EPL]) {
+    load_logits<T, EPL>(l, E, lane, v);
+    softmax_inplace<T, EPL>(E, lane, v);
 }
 
 template <typename T>
@@ -146,40 +159,6 @@ __global__ void __launch_bounds__(64) moe_topk_kernel(const T *__restrict__ logi
     int isel[16];
     select_topk<EPL>(v, E, k, lane, psel, isel);
     if (lane == 0) write_routing<T>(t, k, norm, psel, isel, idx, wout);
-}
-
-// T == 1: routing plus the sorted layout the expert kernels read.  The k selected experts are
-// distinct, so the row of slot s goes to position rank(s) = #{s' : e_s' < e_s}; the expert
-// of rank r owns rows [r, r + 1).  offsets is written only at the selected experts and their
-// successors (offsets[e + 1] = rank + 1 is also the start of expert e + 1 when that one is
-// selected); the expert kernels read no other entry.
-template <typename T>
-__global__ void __launch_bounds__(64) moe_route1_kernel(const T *__restrict__ logits, int E, int k, int norm,
-                                                        int32_t *__restrict__ idx, T *__restrict__ wout,
-                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-                                                        int32_t *__restrict__ inv, int32_t *__restrict__ active) {
-    constexpr int EPL = 4;
-    const int lane = threadIdx.x;
-    float v[EPL];
-    softmax_probs<T, EPL>(logits, E, lane, v);
-    float psel[16];
-    int isel[16];
-    select_topk<EPL>(v, E, k, lane, psel, isel);
-    if (lane == 0) {
-        write_routing<T>(0, k, norm, psel, isel, idx, wout);
-        active[0] = k;
-    }
-    if (lane < k) {
-        int e = 0, rank = 0;
-        for (int s = 0; s < k; ++s)
-            if (s == lane) e = isel[s];
-        for (int s = 0; s < k; ++s) rank += isel[s] < e;
-        perm[rank] = lane;
-        inv[lane] = rank;
-        active[1 + rank] = e;
-        offsets[e] = rank;
-        offsets[e + 1] = rank + 1;
-    }
 }
 
 // ------------------------------------------------------------ stable counting sort by expert
@@ -403,6 +382,182 @@ __global__ void __launch_bounds__(256) moe_expert_q8_kernel(const bf16 *__restri
     }
 }
 
+// ------------------------------------------------------------ one token (T == 1)
+// acc[q] += W_q . x over K inputs: NR weight rows in storage type T, U 16-byte chunks per lane
+// in flight per row before any arithmetic; x in LDS or global memory.
+template <typename T, int NR, int U>
+__device__ __forceinline__ void rows_dot(const T *const (&w)[NR], const T *x, int K, int lane, float (&acc)[NR]) {
+    constexpr int VN = Vec<T>::N;
+    const int nc = K / VN;
+    for (int c0 = 0; c0 < nc; c0 += 64 * U) {
+        u32x4 wv[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + lane + 64 * u;
+#pragma unroll
+            for (int q = 0; q < NR; ++q) wv[u][q] = c < nc ? ld_stream(w[q] + (size_t)c * VN) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nc) {
+                float xf[VN];
+                Vec<T>::expand(ld16(x + (size_t)c * VN), xf);
+#pragma unroll
+                for (int q = 0; q < NR; ++q) {
+                    float wf[VN];
+                    Vec<T>::expand(wv[u][q], wf);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) acc[q] += wf[i] * xf[i];
+                }
+            }
+        }
+    }
+}
+
+// The 8-bit form: rows of u8 codes with bf16 scale and bias per 64 codes; chunk c is codes
+// 16c..16c+15 in group c / 4; x bf16.
+template <int NR, int U>
+__device__ __forceinline__ void rows_dot_q8(const uint8_t *const (&w)[NR], const bf16 *const (&sc)[NR],
+                                            const bf16 *const (&bi)[NR], const bf16 *x, int K, int lane,
+                                            float (&acc)[NR]) {
+    const int nc = K / 16;
+    for (int c0 = 0; c0 < nc; c0 += 64 * U) {
+        u32x4 wv[U][NR];
+        float sv[U][NR], bv[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + lane + 64 * u;
+#pragma unroll
+            for (int q = 0; q < NR; ++q) {
+                const bool ok = c < nc;
+                wv[u][q] = ok ? ld_stream(w[q] + (size_t)c * 16) : u32x4{0, 0, 0, 0};
+                sv[u][q] = ok ? to_f(sc[q][c >> 2]) : 0.f;
+                bv[u][q] = ok ? to_f(bi[q][c >> 2]) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nc) {
+                float xf[16];
+                Vec<bf16>::expand(ld16(x + (size_t)c * 16), xf);
+                Vec<bf16>::expand(ld16(x + (size_t)c * 16 + 8), xf + 8);
+                float xs = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xs += xf[i];
+#pragma unroll
+                for (int q = 0; q < NR; ++q) acc[q] += sv[u][q] * dot16_q8(wv[u][q], xf) + bv[u][q] * xs;
+            }
+        }
+    }
+}
+
+// grid (ceil(Ie / 4), k), 256 threads, hid * sizeof(T) bytes of dynamic LDS.  x: the hidden
+// row, normalised here with nw (RMSNorm, eps) or, with nw == NULL, already normalised.
+// Every block ranks the E logits with the code of moe_topk_kernel, so all blocks agree;
+// block (0, 0) writes idx / wsel.  m [k][Ie] in slot order.
+template <typename T, bool Q8>
+__global__ void __launch_bounds__(256) moe_gu1_kernel(const T *__restrict__ x, const T *__restrict__ nw, float eps,
+                                                      const T *__restrict__ logits, int E, int k, int norm,
+                                                      const void *__restrict__ Wgu, const bf16 *__restrict__ Ws,
+                                                      const bf16 *__restrict__ Wb, int hid, int Ie,
+                                                      int32_t *__restrict__ idx, T *__restrict__ wsel,
+                                                      T *__restrict__ m) {
+    constexpr int VN = Vec<T>::N;
+    constexpr int EPL = 4;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    T *ys = (T *)smem_raw;
+    __shared__ float red[8];
+    __shared__ int sel;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, s = blockIdx.y;
+    float v[EPL];
+    if (wave == 0) load_logits<T, EPL>(logits, E, lane, v);  // in flight during the norm
+    if (nw) {
+        norm_prologue<T>(x, nullptr, nw, eps, nullptr, hid, ys, red);
+    } else {
+        for (int c = threadIdx.x; c < hid / VN; c += blockDim.x) *(u32x4 *)&ys[c * VN] = ld16(x + (size_t)c * VN);
+        __syncthreads();
+    }
+    if (wave == 0) {
+        softmax_inplace<T, EPL>(E, lane, v);
+        float psel[16];
+        int isel[16];
+        select_topk<EPL>(v, E, k, lane, psel, isel);
+        if (lane == 0) {
+            int e = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (q == s) e = isel[q];
+            sel = e;
+            if (blockIdx.x == 0 && s == 0) write_routing<T>(0, k, norm, psel, isel, idx, wsel);
+        }
+    }
+    __syncthreads();
+    const int e = sel, n = blockIdx.x * 4 + wave;
+    if (n >= Ie) return;
+    const size_t g = (size_t)e * 2 * Ie + n, u = g + Ie;  // gate and up rows
+    float acc[2] = {0.f, 0.f};
+    if constexpr (Q8) {
+        const int ng = hid / 64;
+        const uint8_t *W8 = (const uint8_t *)Wgu;
+        const uint8_t *const w[2] = {W8 + g * hid, W8 + u * hid};
+        const bf16 *const sc[2] = {Ws + g * ng, Ws + u * ng}, *const bi[2] = {Wb + g * ng, Wb + u * ng};
+        rows_dot_q8<2, 2>(w, sc, bi, (const bf16 *)ys, hid, lane, acc);
+    } else {
+        const T *WT = (const T *)Wgu;
+        const T *const w[2] = {WT + g * hid, WT + u * hid};
+        rows_dot<T, 2, 4>(w, ys, hid, lane, acc);
+    }
+    const float s0 = wave_sum(acc[0]), s1 = wave_sum(acc[1]);
+    if (lane == 0) m[(size_t)s * Ie + n] = from_f<T>(rho<T>(silu_f32(rho<T>(s0))) * rho<T>(s1));
+}
+
+// grid hid / 4, 512 threads: wave w takes slots w, w + 8 (k <= 16) and computes outputs
+// 4x..4x+3 of its slot's expert from m[s]; part[s][q] = rho(rho(y) * w_s); the block sums the
+// slots in slot order, as moe_combine_kernel does.
+template <typename T, bool Q8>
+__global__ void __launch_bounds__(512) moe_down1_kernel(const T *__restrict__ m, const void *__restrict__ Wd,
+                                                        const bf16 *__restrict__ Ws, const bf16 *__restrict__ Wb,
+                                                        int Ie, int hid, int E, int k,
+                                                        const int32_t *__restrict__ idx, const T *__restrict__ wsel,
+                                                        T *__restrict__ out) {
+    constexpr int NO = 4;
+    __shared__ float part[16][NO];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n0 = blockIdx.x * NO;
+    for (int s = wave; s < k; s += 8) {
+        const int e = idx[s];
+        float acc[NO] = {0.f, 0.f, 0.f, 0.f};
+        if ((unsigned)e < (unsigned)E) {  // always: the routing names valid experts
+            const size_t r0 = (size_t)e * hid + n0;
+            if constexpr (Q8) {
+                const int ng = Ie / 64;
+                const uint8_t *W8 = (const uint8_t *)Wd;
+                const uint8_t *const w[NO] = {W8 + r0 * Ie, W8 + (r0 + 1) * Ie, W8 + (r0 + 2) * Ie, W8 + (r0 + 3) * Ie};
+                const bf16 *const sc[NO] = {Ws + r0 * ng, Ws + (r0 + 1) * ng, Ws + (r0 + 2) * ng, Ws + (r0 + 3) * ng};
+                const bf16 *const bi[NO] = {Wb + r0 * ng, Wb + (r0 + 1) * ng, Wb + (r0 + 2) * ng, Wb + (r0 + 3) * ng};
+                rows_dot_q8<NO, 1>(w, sc, bi, (const bf16 *)m + (size_t)s * Ie, Ie, lane, acc);
+            } else {
+                const T *WT = (const T *)Wd;
+                const T *const w[NO] = {WT + r0 * Ie, WT + (r0 + 1) * Ie, WT + (r0 + 2) * Ie, WT + (r0 + 3) * Ie};
+                rows_dot<T, NO, 2>(w, m + (size_t)s * Ie, Ie, lane, acc);
+            }
+        }
+        const float ws = to_f(wsel[s]);
+#pragma unroll
+        for (int q = 0; q < NO; ++q) {
+            const float y = wave_sum(acc[q]);
+            if (lane == 0) part[s][q] = rho<T>(rho<T>(y) * ws);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < NO) {
+        float a = 0.f;
+        for (int s = 0; s < k; ++s) a += part[s][threadIdx.x];
+        out[n0 + threadIdx.x] = from_f<T>(a);
+    }
+}
+
 // ------------------------------------------------------------ weighted slot sum
 // grid (hid / 256, T): one thread per output element; the token's k sorted positions and
 // weights are loaded first, so the k row reads are in flight together.
@@ -429,6 +584,47 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ 
 }
 
 // ------------------------------------------------------------ dispatch
+// One token: router projection (norm prologue when nw), moe_gu1_kernel, moe_down1_kernel.
+template <typename T>
+static hipError_t moe1_t(const void *x, const void *nw, float eps, int hid, const MoeWeights &W, int E, int k,
+                         int norm, int Ie, int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
+    const int dt = DtOf<T>::value;
+    const MoeWs L = moe_layout(1, hid, E, k, Ie, dt);
+    char *base = (char *)ws;
+    T *logits = (T *)(base + L.logits), *mbuf = (T *)(base + L.m);
+    if (W.q8 && !std::is_same<T, bf16>::value) return hipErrorInvalidValue;
+    hipError_t e;
+    if (W.q8)
+        e = nw ? launch_linear_q8_norm(x, nullptr, nw, eps, nullptr, hid, (const uint8_t *)W.router, W.router_s,
+                                       W.router_b, 64, E, EPI_STORE, logits, s)
+               : launch_linear_q8(x, 1, hid, (const uint8_t *)W.router, W.router_s, W.router_b, 64, E, EPI_STORE,
+                                  nullptr, logits, s);
+    else
+        e = nw ? launch_linear_norm(dt, x, nullptr, nw, eps, nullptr, hid, W.router, E, EPI_STORE, logits, s)
+               : launch_linear(dt, x, 1, hid, W.router, E, EPI_STORE, nullptr, logits, s);
+    if (e != hipSuccess) return e;
+    const dim3 g1((Ie + 3) / 4, k);
+    const size_t lds = (size_t)hid * sizeof(T);
+    const bf16 *gs = (const bf16 *)W.gate_up_s, *gb = (const bf16 *)W.gate_up_b;
+    const bf16 *ds = (const bf16 *)W.down_s, *db = (const bf16 *)W.down_b;
+    if (W.q8) {
+        if constexpr (std::is_same<T, bf16>::value) {
+            moe_gu1_kernel<T, true><<<g1, 256, lds, s>>>((const T *)x, (const T *)nw, eps, logits, E, k, norm,
+                                                         W.gate_up, gs, gb, hid, Ie, idx, (T *)w, mbuf);
+            moe_down1_kernel<T, true><<<hid / 4, 512, 0, s>>>(mbuf, W.down, ds, db, Ie, hid, E, k, idx, (const T *)w,
+                                                              (T *)out);
+        } else {
+            return hipErrorInvalidValue;  // 8-bit weights come with the bf16 model dtype only
+        }
+    } else {
+        moe_gu1_kernel<T, false><<<g1, 256, lds, s>>>((const T *)x, (const T *)nw, eps, logits, E, k, norm,
+                                                      W.gate_up, gs, gb, hid, Ie, idx, (T *)w, mbuf);
+        moe_down1_kernel<T, false><<<hid / 4, 512, 0, s>>>(mbuf, W.down, ds, db, Ie, hid, E, k, idx, (const T *)w,
+                                                           (T *)out);
+    }
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,
                         int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
@@ -440,16 +636,13 @@ static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int
     int32_t *inv = (int32_t *)(base + L.inv), *active = (int32_t *)(base + L.active);
     T *mbuf = (T *)(base + L.m), *ybuf = (T *)(base + L.y);
     const int rows = T_ * k;
+    if (T_ == 1) return moe1_t<T>(x, nullptr, 0.f, hid, W, E, k, norm, Ie, idx, w, out, ws, s);
     hipError_t e = W.q8 ? launch_linear_q8(x, T_, hid, (const uint8_t *)W.router, W.router_s, W.router_b, 64, E,
                                            EPI_STORE, nullptr, logits, s)
                         : launch_linear(dt, x, T_, hid, W.router, E, EPI_STORE, nullptr, logits, s);
     if (e != hipSuccess) return e;
-    if (T_ == 1) {
-        moe_route1_kernel<T><<<1, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w, offsets, perm, inv, active);
-    } else {
-        moe_topk_kernel<T><<<T_, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w);
-        moe_sort_kernel<<<1, 256, 0, s>>>(idx, rows, E, offsets, perm, inv, active);
-    }
+    moe_topk_kernel<T><<<T_, 64, 0, s>>>(logits, E, k, norm, idx, (T *)w);
+    moe_sort_kernel<<<1, 256, 0, s>>>(idx, rows, E, offsets, perm, inv, active);
     const int na_max = rows < E ? rows : E;
     const dim3 g0((Ie + 3) / 4, na_max), g1((hid + 15) / 16, na_max);
     if constexpr (std::is_same<T, bf16>::value) {
@@ -469,6 +662,13 @@ static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int
     }
     moe_combine_kernel<T><<<dim3((hid + 255) / 256, T_), 256, 0, s>>>(ybuf, (const T *)w, inv, hid, k, rows, (T *)out);
     return hipGetLastError();
+}
+
+hipError_t launch_moe_norm1(int dt, const void *h, const void *nw, float eps, int hid, const MoeWeights &W, int E,
+                            int k, int norm, int Ie, int32_t *idx, void *w, void *out, void *ws, hipStream_t s) {
+    if (dt == DT_BF16) return moe1_t<bf16>(h, nw, eps, hid, W, E, k, norm, Ie, idx, w, out, ws, s);
+    if (W.q8) return hipErrorInvalidValue;
+    return moe1_t<float>(h, nw, eps, hid, W, E, k, norm, Ie, idx, w, out, ws, s);
 }
 
 hipError_t launch_moe(int dt, const void *x, int T, int hid, const MoeWeights &W, int E, int k, int norm, int Ie,

@@ -168,12 +168,15 @@ bool is_q8(const qwen3_handle *h) { return h->cfg.quant_bits == 8; }
 // Layer kind: sparse MoE block iff the configuration has experts and the layer a router.
 bool moe_layer(const qwen3_config &c, const qwen3_layer_weights &L) { return c.n_experts > 0 && L.router; }
 
+MoeWeights moe_weights(const qwen3_handle *h, const qwen3_layer_weights &L) {
+    return MoeWeights{L.router, L.router_s, L.router_b, L.exp_gate_up, L.exp_gate_up_s, L.exp_gate_up_b,
+                      L.exp_down, L.exp_down_s, L.exp_down_b, is_q8(h)};
+}
+
 hipError_t moe(qwen3_handle *h, const qwen3_layer_weights &L, const void *x, int T, int32_t *idx, void *w, void *out) {
     const qwen3_config &c = h->cfg;
-    const MoeWeights W{L.router, L.router_s, L.router_b, L.exp_gate_up, L.exp_gate_up_s, L.exp_gate_up_b,
-                       L.exp_down, L.exp_down_s, L.exp_down_b, is_q8(h)};
-    return launch_moe(c.dtype, x, T, c.hidden, W, c.n_experts, c.top_k, c.norm_topk_prob, c.moe_intermediate, idx,
-                      w, out, h->moe_ws, h->stream);
+    return launch_moe(c.dtype, x, T, c.hidden, moe_weights(h, L), c.n_experts, c.top_k, c.norm_topk_prob,
+                      c.moe_intermediate, idx, w, out, h->moe_ws, h->stream);
 }
 
 hipError_t linear(qwen3_handle *h, const void *x, int M, int K, const void *W, const void *Ws, const void *Wb, int N,
@@ -259,9 +262,10 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
         HIPCHECK(h, linear(h, h->a, 1, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : hnext, hnext));
         HIPCHECK(h, mark(h, K_O, false));
         hcur = hnext;
-        if (moe_layer(c, L)) {
-            HIPCHECK(h, launch_add_rmsnorm(dt, hcur, nullptr, L.post_norm, nullptr, h->y, 1, hid, c.rms_eps, s));
-            HIPCHECK(h, moe(h, L, h->y, 1, h->moe_idx, h->moe_w, h->pend));
+        if (moe_layer(c, L)) {  // post-attention norm in the router's and experts' prologues
+            HIPCHECK(h, launch_moe_norm1(dt, hcur, L.post_norm, c.rms_eps, hid, moe_weights(h, L), c.n_experts,
+                                         c.top_k, c.norm_topk_prob, c.moe_intermediate, h->moe_idx, h->moe_w,
+                                         h->pend, h->moe_ws, s));
         } else {
             HIPCHECK(h, mark(h, K_GU, true));
             HIPCHECK(h, linear_norm(h, hcur, nullptr, L.post_norm, nullptr, hid, L.gate_up, L.gate_up_s, L.gate_up_b,
