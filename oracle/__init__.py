@@ -41,7 +41,8 @@ class OrcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim",
                                             "intermediate", "capacity")] + \
                [("rms_eps", ctypes.c_float), ("mode", ctypes.c_int)] + \
-               [(n, ctypes.c_int) for n in ("n_experts", "top_k", "moe_intermediate", "norm_topk_prob")]
+               [(n, ctypes.c_int) for n in ("n_experts", "top_k", "moe_intermediate", "norm_topk_prob", "qk_norm",
+                                            "attention_bias", "window")]
 
 
 _P = ctypes.c_void_p
@@ -49,7 +50,7 @@ _P = ctypes.c_void_p
 
 class OrcLayer(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("in_norm", "post_norm", "q_norm", "k_norm", "qkv", "o", "gate_up",
-                                  "down", "router", "exp_gate_up", "exp_down")]
+                                  "down", "router", "exp_gate_up", "exp_down", "qkv_bias")]
 
 
 def lib():
@@ -67,7 +68,7 @@ def lib():
         L.orc_head.argtypes = [p, i, i, p, i, i, p, p]
         L.orc_rope_table.argtypes = [i, i, ctypes.c_double, i, p, p]
         L.orc_rope.argtypes = [p, i, p, p, i, p]
-        L.orc_attention.argtypes = [p, p, p, i, i, i, i, i, i, i, p, p]
+        L.orc_attention.argtypes = [p, p, p, i, i, i, i, i, i, i, i, p, p]
         L.orc_swiglu.argtypes = [p, i, i, i, p]
         L.orc_router.argtypes = [p, i, i, p, i, i, i, i, p, p, p]
         L.orc_moe_block.argtypes = [p, i, i, p, i, i, i, i, p, p, i, i, p, p, p]
@@ -167,15 +168,16 @@ def rope(x, cos_row, sin_row, mode="bf16") -> np.ndarray:
     return out.reshape(x.shape)
 
 
-def attention(q, K, V, p0, mode="bf16", want_probs=False):
-    """q [T][H][D]; K, V [KV][cap][D]; returns a [T][H*D] (and probs [T][H][p0+T])."""
+def attention(q, K, V, p0, mode="bf16", want_probs=False, window=0):
+    """q [T][H][D]; K, V [KV][cap][D]; returns a [T][H*D] (and probs [T][H][p0+T]).
+    window > 0: each query sees only the `window` most recent positions up to its own."""
     q, K, V = _f32(q), _f32(K), _f32(V)
     T, H, D = q.shape
     KV, cap, D2 = K.shape
     assert D2 == D and V.shape == K.shape and p0 + T <= cap
     out = np.empty((T, H * D), np.float32)
     probs = np.empty((T, H, p0 + T), np.float32) if want_probs else None
-    lib().orc_attention(_ptr(q), _ptr(K), _ptr(V), T, H, KV, D, cap, int(p0), _mode(mode), _ptr(out),
+    lib().orc_attention(_ptr(q), _ptr(K), _ptr(V), T, H, KV, D, cap, int(p0), int(window), _mode(mode), _ptr(out),
                         _ptr(probs))
     return (out, probs) if want_probs else out
 
@@ -255,7 +257,8 @@ class Stack:
         self.length = 0
         self._c = OrcConfig(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                             cfg.intermediate, cfg.capacity, cfg.rms_eps, self.mode, cfg.n_experts, cfg.top_k,
-                            cfg.moe_intermediate, cfg.norm_topk_prob)
+                            cfg.moe_intermediate, cfg.norm_topk_prob, int(bool(cfg.qk_norm)),
+                            int(bool(cfg.attention_bias)), cfg.sliding_window)
         arr = (OrcLayer * cfg.n_layers)()
         for i, Ld in enumerate(self.layers):
             for name, _ in OrcLayer._fields_:

@@ -142,7 +142,7 @@ extern "C" void orc_rope(const float *x, int D, const float *c, const float *s, 
 /* ---------------------------------------------------------------- attention */
 
 extern "C" void orc_attention(const float *q, const float *K, const float *V, int T, int H, int KV,
-                              int D, int cap, int p0, int mode, float *out, float *probs) {
+                              int D, int cap, int p0, int window, int mode, float *out, float *probs) {
     const int group = H / KV;
     const float scale = (float)(1.0 / sqrt((double)D));
     const int nk = p0 + T;
@@ -150,30 +150,31 @@ extern "C" void orc_attention(const float *q, const float *K, const float *V, in
     for (int t = 0; t < T; ++t) {
         for (int h = 0; h < H; ++h) {
             const int p = p0 + t;          /* absolute position of the query */
+            const int lo = window > 0 ? std::max(0, p - window + 1) : 0; /* first visible key */
             const int g = h / group;       /* kv head read by q head h */
             const float *qv = q + ((size_t)t * H + h) * D;
             const float *Kg = K + (size_t)g * cap * D;
             const float *Vg = V + (size_t)g * cap * D;
-            std::vector<float> s(p + 1), e(p + 1);
+            std::vector<float> s(p + 1), e(p + 1, 0.0f);
             float m = -INFINITY;
-            for (int j = 0; j <= p; ++j) {
+            for (int j = lo; j <= p; ++j) {
                 s[j] = dot(qv, Kg + (size_t)j * D, D) * scale;
                 m = std::max(m, s[j]);
             }
             double l = 0.0;
-            for (int j = 0; j <= p; ++j) {
+            for (int j = lo; j <= p; ++j) {
                 e[j] = expf(s[j] - m);
                 l += (double)e[j];
             }
             const float lf = (float)l;
             for (int d = 0; d < D; ++d) {
                 double acc = 0.0;
-                for (int j = 0; j <= p; ++j) acc += (double)e[j] * (double)Vg[(size_t)j * D + d];
+                for (int j = lo; j <= p; ++j) acc += (double)e[j] * (double)Vg[(size_t)j * D + d];
                 out[(size_t)t * H * D + (size_t)h * D + d] = rho((float)acc / lf, mode);
             }
             if (probs) {
                 float *pr = probs + ((size_t)t * H + h) * nk;
-                for (int j = 0; j < nk; ++j) pr[j] = j <= p ? e[j] / lf : 0.0f;
+                for (int j = 0; j < nk; ++j) pr[j] = (j >= lo && j <= p) ? e[j] / lf : 0.0f;
             }
         }
     }
@@ -341,6 +342,8 @@ extern "C" int orc_forward(const orc_config *cfg, const orc_layer *layers, const
         if (moe ? (!L.exp_gate_up || !L.exp_down || cfg->top_k < 1 || cfg->top_k > cfg->n_experts)
                 : (!L.gate_up || !L.down || I < 1))
             return ORC_ERR_ARG;
+        if ((cfg->qk_norm && (!L.q_norm || !L.k_norm)) || (cfg->attention_bias && !L.qkv_bias))
+            return ORC_ERR_ARG;
     }
 
     std::vector<float> h(x, x + (size_t)T * hid), pend((size_t)T * hid), y((size_t)T * hid);
@@ -360,6 +363,10 @@ extern "C" int orc_forward(const orc_config *cfg, const orc_layer *layers, const
         for (int t = 0; t < T; ++t)
             orc_rmsnorm(&h[(size_t)t * hid], L.in_norm, hid, eps, mode, &y[(size_t)t * hid]);
         orc_linear(y.data(), T, hid, L.qkv, nqkv, mode, qkv.data());
+        if (cfg->attention_bias) /* [P2]: the bias is a separate add after the projection */
+            for (int t = 0; t < T; ++t)
+                for (int i = 0; i < nqkv; ++i)
+                    qkv[(size_t)t * nqkv + i] = rho(qkv[(size_t)t * nqkv + i] + L.qkv_bias[i], mode);
 
         for (int t = 0; t < T; ++t) {
             const int p = p0 + t;
@@ -367,18 +374,20 @@ extern "C" int orc_forward(const orc_config *cfg, const orc_layer *layers, const
             const float *c = cos_tab + (size_t)p * D, *s = sin_tab + (size_t)p * D;
             for (int hh = 0; hh < H; ++hh) {
                 float *qh = &q[((size_t)t * H + hh) * D];
-                orc_rmsnorm(row + (size_t)hh * D, L.q_norm, D, eps, mode, qh);
+                if (cfg->qk_norm) orc_rmsnorm(row + (size_t)hh * D, L.q_norm, D, eps, mode, qh);
+                else memcpy(qh, row + (size_t)hh * D, sizeof(float) * D);
                 orc_rope(qh, D, c, s, mode, qh);
             }
             for (int g = 0; g < KV; ++g) {
                 std::vector<float> kg(D);
-                orc_rmsnorm(row + (size_t)(H + g) * D, L.k_norm, D, eps, mode, kg.data());
+                if (cfg->qk_norm) orc_rmsnorm(row + (size_t)(H + g) * D, L.k_norm, D, eps, mode, kg.data());
+                else memcpy(kg.data(), row + (size_t)(H + g) * D, sizeof(float) * D);
                 orc_rope(kg.data(), D, c, s, mode, kg.data());
                 memcpy(Kl + ((size_t)g * cap + p) * D, kg.data(), sizeof(float) * D);
                 memcpy(Vl + ((size_t)g * cap + p) * D, row + (size_t)(H + KV + g) * D, sizeof(float) * D);
             }
         }
-        orc_attention(q.data(), Kl, Vl, T, H, KV, D, cap, p0, mode, a.data(), NULL);
+        orc_attention(q.data(), Kl, Vl, T, H, KV, D, cap, p0, cfg->window, mode, a.data(), NULL);
 
         orc_linear(a.data(), T, H * D, L.o, hid, mode, o.data());
         for (size_t i = 0; i < h.size(); ++i) h[i] = rho(h[i] + o[i], mode);

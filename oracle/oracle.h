@@ -89,16 +89,19 @@ void orc_rope(const float *x, int D, const float *cos_row, const float *sin_row,
 
 /* Causal GQA attention ([P1] forward(): scaled_dot_product_attention with
  * mask "causal" when T > 1; docstring "attention over keys 0..pos (fp32
- * softmax, one rounding)"; [P2] repeat_kv group = H / KV).
+ * softmax, one rounding)"; [P2] repeat_kv group = H / KV; [P2]
+ * Qwen3DecoderSpec mask: Causal or SlidingWindow(w)).
  *   q:   [T][H][D] (post-norm, post-RoPE)
  *   K,V: [KV][cap][D] cache of one layer (positions 0..p0+T-1 valid)
- *   query t sits at absolute position p = p0 + t and sees keys 0..p;
+ *   query t sits at absolute position p = p0 + t and sees keys lo..p, where
+ *   lo = 0 (window <= 0: causal) or max(0, p - window + 1) (a sliding window
+ *   of the window most recent positions, the query's own included);
  *   q head h reads kv head h / (H/KV);
  *   s_j = fp32(q.K_j) * fp32(1/sqrt(D)); e_j = expf(s_j - max s);
  *   out[t][h*D + d] = rho(sum_j e_j V_j[d] / sum_j e_j).
- * probs (optional, may be NULL): [T][H][p0+T] receives e_j / sum e (0 past p). */
+ * probs (optional, may be NULL): [T][H][p0+T] receives e_j / sum e (0 outside lo..p). */
 void orc_attention(const float *q, const float *K, const float *V, int T, int H, int KV, int D,
-                   int cap, int p0, int mode, float *out, float *probs);
+                   int cap, int p0, int window, int mode, float *out, float *probs);
 
 /* SwiGLU on fused gate|up rows ([P1] forward(): silu in fp32 on the model
  * dtype gate, rounded once, then times up, rounded once):
@@ -139,6 +142,11 @@ typedef struct {
     float rms_eps;
     int mode;                 /* ORC_BF16 or ORC_FP32 */
     int n_experts, top_k, moe_intermediate, norm_topk_prob; /* n_experts == 0: dense MLP */
+    /* [P2] Qwen3DecoderSpec switches: qk_norm (1: per-head q/k RMSNorm before RoPE, Qwen3;
+     * 0: RoPE on the projections, Qwen2), attention_bias (1: q/k/v bias added to the
+     * projection, each add rounded: [P2] mm then add), window (0: causal; w > 0: the
+     * SlidingWindow(w) mask of orc_attention). */
+    int qk_norm, attention_bias, window;
 } orc_config;
 /* Layer kind ([P3] Qwen3MoeDecoderLayer: a layer runs the sparse MoE block unless its index is
  * in mlp_only_layers or (index + 1) is not a multiple of decoder_sparse_step, and the dense
@@ -155,6 +163,7 @@ typedef struct {
     const float *router;   /* [E][hid] (MoE layers; NULL: dense layer of an MoE stack) */
     const float *exp_gate_up; /* [E][2Ie][hid] */
     const float *exp_down;    /* [E][hid][Ie] */
+    const float *qkv_bias;    /* [(H+2KV)D] (attention_bias) */
 } orc_layer;
 
 /* One forward call of the stack ([P1] Backbone.forward): x [T][hid] at

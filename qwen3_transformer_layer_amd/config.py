@@ -32,6 +32,9 @@ class Qwen3Config:
     quant_bits: int = 0            # 0: bf16/fp32 weights; 8: u8 codes + bf16 scale/bias per group
     quant_group: int = 64
     seed: int = 0
+    qk_norm: bool = True           # page 2 Qwen3DecoderSpec switches: per-head q/k RMSNorm (Qwen3;
+    attention_bias: bool = False   # Qwen2 skips it), q/k/v projection bias (Qwen2) and the
+    sliding_window: int = 0        # attention mask: 0 causal, w > 0 SlidingWindow(w)
     decoder_sparse_step: int = 1   # MoE layer selection ("@mlx-bun/inference" qwen3-moe.ts,
     mlp_only_layers: tuple = ()    # Qwen3MoeDecoderLayer): see is_moe_layer
 

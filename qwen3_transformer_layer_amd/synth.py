@@ -6,7 +6,8 @@ so both sides see byte-identical inputs.
 
 Every tensor gets its own generator, seeded with FNV-1a-64 of
 "{config seed}/{tensor name}" (low 63 bits), and is drawn as float32 normals:
-linear weights 0.02*z, norm weights 1 + 0.1*z, K/V pre-fill and hidden states z,
+linear weights 0.02*z, norm weights 1 + 0.1*z, q/k/v biases 0.5*z, K/V pre-fill and
+hidden states z,
 then cast (round-to-nearest-even) to the model dtype.  8-bit quantised
 projections are drawn directly in their stored form: codes around 127.5 with
 spread 42.5, per-group scales near 3.8e-4 and biases near -127.5*scale, which is
@@ -85,9 +86,12 @@ def layer_weights(cfg: Qwen3Config, layer: int, device="cpu") -> dict:
     w = {
         "in_norm": norm_weight(cfg, p + "in_norm", hid, device),
         "post_norm": norm_weight(cfg, p + "post_norm", hid, device),
-        "q_norm": norm_weight(cfg, p + "q_norm", D, device),
-        "k_norm": norm_weight(cfg, p + "k_norm", D, device),
     }
+    if cfg.qk_norm:
+        w["q_norm"] = norm_weight(cfg, p + "q_norm", D, device)
+        w["k_norm"] = norm_weight(cfg, p + "k_norm", D, device)
+    if cfg.attention_bias:  # N(0, 0.5): the size of a projection output at hidden ~ 1000
+        w["qkv_bias"] = (0.5 * randn(cfg, p + "qkv_bias", (cfg.qkv_rows,), device)).to(model_dtype(cfg))
     moe_layer = cfg.is_moe_layer(layer)
     names = ("qkv", "o") if moe_layer else PROJ_SHAPES
     for n in names:

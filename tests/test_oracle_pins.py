@@ -654,3 +654,145 @@ def test_moe_stack_rejects_a_layer_without_its_weights(orc):
     st = orc.Stack(cfg, layers, w["final_norm"].float().numpy(), "fp32")
     st.forward(x)
     assert st.length == 2
+
+
+# ------------------------------------------------------------------ Qwen2 switches and sliding windows
+
+@pytest.mark.parametrize("window,p0,T", [(1, 0, 9), (3, 0, 12), (5, 7, 6), (4, 20, 1), (64, 3, 10)])
+def test_attention_window_brute_force_vs_sdpa_fp64(orc, window, p0, T):
+    """SlidingWindow(w): query p sees keys max(0, p-w+1)..p.  torch SDPA in float64 with an
+    explicit mask built from that definition, GQA by repeat."""
+    rng = np.random.default_rng(40 + window)
+    H, KV, D, cap = 4, 2, 64, 40
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    K = rng.standard_normal((KV, cap, D)).astype(np.float32)
+    V = rng.standard_normal((KV, cap, D)).astype(np.float32)
+    got, probs = orc.attention(q, K, V, p0, "fp32", want_probs=True, window=window)
+    n = p0 + T
+    mask = torch.zeros(T, n, dtype=torch.bool)
+    for t in range(T):
+        p = p0 + t
+        mask[t, max(0, p - window + 1):p + 1] = True
+    qt = torch.from_numpy(q).double().transpose(0, 1)                       # [H][T][D]
+    kt = torch.from_numpy(K[:, :n]).double().repeat_interleave(H // KV, 0)  # [H][n][D]
+    vt = torch.from_numpy(V[:, :n]).double().repeat_interleave(H // KV, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    ref = ref.transpose(0, 1).reshape(T, H * D).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=2e-5)
+    assert np.all(probs[:, :, :][~np.broadcast_to(mask.numpy()[:, None, :], probs.shape)] == 0)
+
+
+def test_attention_window_reductions(orc):
+    """A window covering every earlier position is causal attention bit for bit; a window of
+    one returns the query's own value row exactly."""
+    rng = np.random.default_rng(45)
+    H, KV, D, cap, p0, T = 4, 1, 64, 32, 5, 9
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    K = rng.standard_normal((KV, cap, D)).astype(np.float32)
+    V = rng.standard_normal((KV, cap, D)).astype(np.float32)
+    for mode in ("fp32", "bf16"):
+        causal = orc.attention(q, K, V, p0, mode)
+        assert np.array_equal(orc.attention(q, K, V, p0, mode, window=p0 + T), causal)
+        assert np.array_equal(orc.attention(q, K, V, p0, mode, window=1000), causal)
+    one = orc.attention(q, K, V, p0, "fp32", window=1).reshape(T, H, D)
+    for t in range(T):
+        assert np.array_equal(one[t], np.broadcast_to(V[0, p0 + t], (H, D)))
+
+
+def _hf_qwen2_family(cfg, w, dtype=torch.float64):
+    """transformers' Qwen2 (q/k/v bias, no q/k norm) or Qwen3 (q/k norm, no bias) with the
+    synthetic weights; sliding_window > 0 makes every layer a sliding-window layer."""
+    from transformers import Qwen2Config, Qwen2Model, Qwen3Config, Qwen3Model
+    common = dict(vocab_size=16, hidden_size=cfg.hidden, intermediate_size=cfg.intermediate,
+                  num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
+                  num_key_value_heads=cfg.n_kv_heads, rms_norm_eps=cfg.rms_eps,
+                  rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta},
+                  max_position_embeddings=cfg.capacity, use_sliding_window=cfg.sliding_window > 0,
+                  sliding_window=cfg.sliding_window or None, max_window_layers=0)
+    if cfg.qk_norm:
+        hc = Qwen3Config(head_dim=cfg.head_dim, attention_bias=False, **common)
+        hc._attn_implementation = "eager"
+        m = Qwen3Model(hc).to(dtype).eval()
+    else:
+        assert cfg.hidden == cfg.n_heads * cfg.head_dim  # Qwen2 derives head_dim
+        hc = Qwen2Config(**common)
+        hc._attn_implementation = "eager"
+        m = Qwen2Model(hc).to(dtype).eval()
+    assert all(t == ("sliding_attention" if cfg.sliding_window else "full_attention") for t in hc.layer_types)
+    HD, KVD, I = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.intermediate
+    with torch.no_grad():
+        for l, L in enumerate(w["layers"]):
+            ml = m.layers[l]
+            t = {k: v.to(dtype) for k, v in L.items()}
+            a = ml.self_attn
+            a.q_proj.weight.copy_(t["qkv"][:HD])
+            a.k_proj.weight.copy_(t["qkv"][HD:HD + KVD])
+            a.v_proj.weight.copy_(t["qkv"][HD + KVD:])
+            if cfg.attention_bias:
+                a.q_proj.bias.copy_(t["qkv_bias"][:HD])
+                a.k_proj.bias.copy_(t["qkv_bias"][HD:HD + KVD])
+                a.v_proj.bias.copy_(t["qkv_bias"][HD + KVD:])
+            a.o_proj.weight.copy_(t["o"])
+            if cfg.qk_norm:
+                a.q_norm.weight.copy_(t["q_norm"])
+                a.k_norm.weight.copy_(t["k_norm"])
+            ml.mlp.gate_proj.weight.copy_(t["gate_up"][:I])
+            ml.mlp.up_proj.weight.copy_(t["gate_up"][I:])
+            ml.mlp.down_proj.weight.copy_(t["down"])
+            ml.input_layernorm.weight.copy_(t["in_norm"])
+            ml.post_attention_layernorm.weight.copy_(t["post_norm"])
+        m.norm.weight.copy_(w["final_norm"].to(dtype))
+    return m
+
+
+@pytest.mark.parametrize("qk_norm,bias,window", [(False, True, 0), (False, True, 5), (True, False, 6)])
+def test_qwen2_family_stack_fp32_matches_transformers_fp64(orc, qk_norm, bias, window):
+    """Page 2's switches against independent float64 models: Qwen2 (bias, no q/k norm), Qwen2
+    with every layer sliding-window, Qwen3 with a sliding window.  A 12-token prefill then 6
+    decode steps, so the window cuts keys in both phases."""
+    from qwen3_transformer_layer_amd import synth
+    cfg = _tiny_cfg().replace(qk_norm=qk_norm, attention_bias=bias, sliding_window=window)
+    w = synth.model_weights(cfg)
+    assert ("q_norm" in w["layers"][0]) == qk_norm and ("qkv_bias" in w["layers"][0]) == bias
+    x = synth.hidden_states(cfg, 18)
+    st = _oracle_stack(orc, cfg, w, "fp32")
+    got = np.concatenate([st.forward(x[:12].numpy())] + [st.forward(x[12 + i:13 + i].numpy()) for i in range(6)])
+    m = _hf_qwen2_family(cfg, w)
+    ref = _hf_run(m, [x[:12].double()] + [x[12 + i:13 + i].double() for i in range(6)], cfg)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(got - ref)) / rms < 2e-5
+    if window:  # the window changes the result (so the comparison above sees it)
+        causal = _oracle_stack(orc, cfg.replace(sliding_window=0), w, "fp32")
+        full = np.concatenate([causal.forward(x[:12].numpy())] +
+                              [causal.forward(x[12 + i:13 + i].numpy()) for i in range(6)])
+        assert np.max(np.abs(full - got)) / rms > 1e-2
+
+
+def test_qwen2_bf16_close_to_transformers_fp64(orc):
+    """bf16 mode with the bias as its own rounded add (page 2: mm, then add) stays within bf16
+    noise of the float64 Qwen2 model, whose Linear adds the bias inside the projection."""
+    from qwen3_transformer_layer_amd import synth
+    cfg = _tiny_cfg().replace(dtype="bf16", n_layers=1, qk_norm=False, attention_bias=True, sliding_window=4)
+    w = synth.model_weights(cfg)
+    x = synth.hidden_states(cfg, 12)
+    st = _oracle_stack(orc, cfg, w, "bf16")
+    got = np.concatenate([st.forward(x[:8].float().numpy())] + [st.forward(x[8 + i:9 + i].float().numpy())
+                                                                 for i in range(4)])
+    m = _hf_qwen2_family(cfg, w)
+    ref = _hf_run(m, [x[:8].double()] + [x[8 + i:9 + i].double() for i in range(4)], cfg)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert rel.max() < 3e-2
+
+
+def test_stack_rejects_missing_switch_weights(orc):
+    from qwen3_transformer_layer_amd import synth
+    cfg = _tiny_cfg().replace(n_layers=1, attention_bias=True)
+    w = synth.model_weights(cfg)
+    layers = [{k: v.float().numpy() for k, v in L.items()} for L in w["layers"]]
+    x = synth.hidden_states(cfg, 2).numpy()
+    bad = [{k: v for k, v in layers[0].items() if k != "qkv_bias"}]
+    with pytest.raises(ValueError):
+        orc.Stack(cfg, bad, w["final_norm"].float().numpy(), "fp32").forward(x)
+    bad = [{k: v for k, v in layers[0].items() if k != "k_norm"}]
+    with pytest.raises(ValueError):
+        orc.Stack(cfg, bad, w["final_norm"].float().numpy(), "fp32").forward(x)
