@@ -91,10 +91,14 @@ typedef struct {
     int n_experts, top_k, moe_intermediate, norm_topk_prob; /* n_experts == 0: dense MLP */
     int quant_bits, quant_group; /* 0 (plain weights) or 8 with quant_group 64 */
     int max_tokens;            /* largest T per call; sizes the workspace */
+    int sliding_window;        /* 0: causal (keys 0..p); w > 0: SlidingWindow(w), keys max(0, p-w+1)..p
+                                  ("rlx_flow/blocks/qwen3_decoder.rs", Qwen3DecoderSpec mask) */
 } qwen3_config;
 
 typedef struct {
-    const void *in_norm, *post_norm, *q_norm, *k_norm; /* [hidden], [hidden], [D], [D] */
+    const void *in_norm, *post_norm, *q_norm, *k_norm; /* [hidden], [hidden], [D], [D]; q_norm and
+                                                          k_norm both NULL: no per-head q/k RMSNorm
+                                                          (Qwen3DecoderSpec qk_norm off, Qwen2) */
     const void *qkv, *o, *gate_up, *down;               /* plain weights, or u8 codes if quantised */
     const void *qkv_s, *qkv_b, *o_s, *o_b;              /* bf16 per-group scale and bias (quantised) */
     const void *gate_up_s, *gate_up_b, *down_s, *down_b;
@@ -102,6 +106,8 @@ typedef struct {
     const void *router_s, *router_b;                    /* bf16 per-group scale and bias of the */
     const void *exp_gate_up_s, *exp_gate_up_b;          /* quantised MoE weights */
     const void *exp_down_s, *exp_down_b;
+    const void *qkv_bias;     /* [(H+2KV)*D] model dtype or NULL (Qwen2 attention_bias: q|k|v each
+                                 become rho(x + b) after the projection) */
 } qwen3_layer_weights;
 
 typedef struct {

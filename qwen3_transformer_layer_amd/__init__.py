@@ -37,7 +37,7 @@ def c_config(cfg: Qwen3Config, max_tokens: int) -> _lib.Config:
     return _lib.Config(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate,
                        cfg.vocab, cfg.capacity, cfg.rms_eps, cfg.rope_theta, DTYPES[cfg.dtype], cfg.n_experts,
                        cfg.top_k, cfg.moe_intermediate, cfg.norm_topk_prob, cfg.quant_bits, cfg.quant_group,
-                       max_tokens)
+                       max_tokens, cfg.sliding_window)
 
 
 def qwen3_workspace_bytes(cfg: Qwen3Config, max_tokens: int) -> int:

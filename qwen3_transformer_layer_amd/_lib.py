@@ -22,12 +22,12 @@ class Config(ctypes.Structure):
                                   "vocab", "capacity")] + \
                [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("dtype", _I)] + \
                [(n, _I) for n in ("n_experts", "top_k", "moe_intermediate", "norm_topk_prob", "quant_bits",
-                                  "quant_group", "max_tokens")]
+                                  "quant_group", "max_tokens", "sliding_window")]
 
 
 LAYER_FIELDS = ("in_norm", "post_norm", "q_norm", "k_norm", "qkv", "o", "gate_up", "down", "qkv_s", "qkv_b", "o_s",
                 "o_b", "gate_up_s", "gate_up_b", "down_s", "down_b", "router", "exp_gate_up", "exp_down",
-                "router_s", "router_b", "exp_gate_up_s", "exp_gate_up_b", "exp_down_s", "exp_down_b")
+                "router_s", "router_b", "exp_gate_up_s", "exp_gate_up_b", "exp_down_s", "exp_down_b", "qkv_bias")
 
 
 class LayerWeights(ctypes.Structure):

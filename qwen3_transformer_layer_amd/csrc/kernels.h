@@ -24,11 +24,13 @@ hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const v
 // RoPE table [cap][D] (cos, sin) in storage dt.
 hipError_t launch_rope_table(int dt, int cap, int D, double theta, void *cos_t, void *sin_t, hipStream_t s);
 
-// Per token t and head: per-head RMSNorm (q_norm / k_norm weights), RoPE at p0 + t,
-// q to q_out [T][H][D]; k and v written to the cache at position p0 + t.
+// Per token t and head: bias add (bias [(H+2KV)D] or NULL), per-head RMSNorm (q_norm / k_norm
+// weights; both NULL: no norm), RoPE at p0 + t, q to q_out [T][H][D]; k and v (plus bias)
+// written to the cache at position p0 + t.
 hipError_t launch_qknorm_rope_kv(int dt, const void *qkv, int T, int H, int KV, int D, const void *q_norm,
-                                 const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
-                                 int cap, void *q_out, void *k_cache, void *v_cache, hipStream_t s);
+                                 const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                 const void *sin_t, int p0, int cap, void *q_out, void *k_cache, void *v_cache,
+                                 hipStream_t s);
 
 // out = epilogue(x [M][K] . W^T), W [rows][K] row-major.
 //  EPI_STORE:  out[m][n] = rho(acc), n < N (W has N rows)
@@ -55,27 +57,30 @@ hipError_t launch_linear_q8(const void *x, int M, int K, const uint8_t *codes, c
 
 // Causal GQA attention of T queries at positions p0..p0+T-1 against cache entries
 // 0..p0+T-1: q [T][H][D] -> out [T][H*D].  ws: fp32 scratch of attention_workspace() bytes.
+// window: 0 causal (query at p sees keys 0..p) or w > 0, a sliding window (keys max(0, p-w+1)..p).
 hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,
-                            int D, int cap, int p0, void *out, float *ws, size_t ws_bytes, hipStream_t s);
+                            int D, int cap, int p0, int window, void *out, float *ws, size_t ws_bytes, hipStream_t s);
 size_t attention_workspace(int T, int H, int KV, int D, int cap);
-// Decode step (T == 1) at position p0 fused with the per-head q/k RMSNorm, RoPE and the
-// cache write: qkv [(H+2KV)D] of the token -> out [H*D]; writes K/V at p0.  The scratch of
+// Decode step (T == 1) at position p0 fused with the bias add (bias or NULL), the per-head
+// q/k RMSNorm (q_norm and k_norm, or both NULL), RoPE and the cache write: qkv [(H+2KV)D] of
+// the token -> out [H*D]; writes K/V at p0; window as for launch_attention.  The scratch of
 // attention_workspace(T, ...) holds min(T, DECODE_MAXB) seats' partials.
 hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV, int D, const void *q_norm,
-                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
-                                         int cap, void *k_cache, void *v_cache, void *out, float *ws, hipStream_t s);
+                                         const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                         const void *sin_t, int p0, int cap, int window, void *k_cache,
+                                         void *v_cache, void *out, float *ws, hipStream_t s);
 // The same for B <= DECODE_MAXB seats at once (one token each, the same weights): seat b's
 // q|k|v row b of qkv [B][(H+2KV)D], its layer cache kc[b] / vc[b] ([KV][cap][D]) and position
 // p[b]; out row b of [B][H*D].
 constexpr int DECODE_MAXB = 16;
 struct DecodeBatch {
     void *kc[DECODE_MAXB], *vc[DECODE_MAXB];
-    int p[DECODE_MAXB], chunk[DECODE_MAXB], nsplit[DECODE_MAXB];
+    int p[DECODE_MAXB], lo[DECODE_MAXB], chunk[DECODE_MAXB], nsplit[DECODE_MAXB];
 };
 hipError_t launch_attention_decode_batch(int dt, const void *qkv, int B, int H, int KV, int D, const void *q_norm,
-                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t,
-                                         void *const *k_cache, void *const *v_cache, const int *p, int cap, void *out,
-                                         float *ws, hipStream_t s);
+                                         const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                         const void *sin_t, void *const *k_cache, void *const *v_cache, const int *p,
+                                         int cap, int window, void *out, float *ws, hipStream_t s);
 
 // ---- MoE block: router logits rho(x . Wr^T), rho(softmax) over all E experts, top-k
 // (ties to the lower index, slot order descending probability), renormalised weights

@@ -26,6 +26,7 @@
 //    parts so the probability weights keep ~16 bits instead of bf16's 8.
 //  - attn_rowwise_kernel (T > 1, fp32 strict mode): one wave per (query, head),
 //    online softmax over key blocks of 64.
+#include <climits>
 #include <math.h>
 
 #include "attn_core.h"
@@ -33,6 +34,10 @@
 #include "kernels.h"
 
 namespace q3 {
+
+// First key a query at position p sees: 0 (causal) or the start of a sliding window of w
+// positions ("rlx_flow/blocks/qwen3_decoder.rs", Qwen3DecoderSpec mask SlidingWindow(w)).
+static inline int window_lo(int p, int window) { return window > 0 && p - window + 1 > 0 ? p - window + 1 : 0; }
 
 static inline int decode_chunk(int nkeys, int KV) {  // keys per split of a T == 1 step
     int c = (nkeys * KV + 511) / 512;
@@ -73,15 +78,16 @@ __device__ __forceinline__ void decode_core(const float *qs, const T *__restrict
 // q [H][D] already normalised and rotated; the cache already holds position nkeys - 1.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ q, const T *__restrict__ Kc,
-                                                          const T *__restrict__ Vc, int cap, int nkeys, int chunk,
-                                                          float scale, float *__restrict__ part, int nsplit) {
+                                                          const T *__restrict__ Vc, int cap, int lo, int nkeys,
+                                                          int chunk, float scale, float *__restrict__ part,
+                                                          int nsplit) {
     extern __shared__ float smem[];
     float *sc = smem;                  // [G][chunk]
     float *red = smem + G * chunk;     // [4][G][D]
     __shared__ float qs[G * D];
     __shared__ float mrow[G], lrow[G];
     const int s = blockIdx.x, g = blockIdx.y;
-    const int j0 = s * chunk, j1 = min(nkeys, j0 + chunk);
+    const int j0 = lo + s * chunk, j1 = min(nkeys, j0 + chunk);
     const T *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
     u32x4 kp[DEC_PF], vp[DEC_PF];
     decode_prefetch<T, D>(Kg, Vg, j0, j1, kp, vp);
@@ -93,13 +99,16 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T *__restrict__ 
 
 // Fused decode step at position p = nkeys - 1: per-head RMSNorm of the group's q heads and
 // (in the split holding p) of k, RoPE at p, and the cache write of k and v at p, then the
-// split's attention.  qkv: [(H+2KV)D] for the one token.
+// split's attention over keys lo + s chunk ..  qkv: [(H+2KV)D] for the one token.  With a
+// bias [(H+2KV)D] each q/k/v element is first rho(x + b); with q_norm == k_norm == NULL the
+// per-head norm is skipped (page 2's qk_norm / attention_bias switches).
 template <typename T, int D, int G>
 __device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm,
-                                                   const T *__restrict__ k_norm, float eps, const T *__restrict__ cos_t,
-                                                   const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc,
-                                                   int cap, int nkeys, int chunk, float scale, float *__restrict__ part,
-                                                   int nsplit, int s, int g) {
+                                                   const T *__restrict__ k_norm, const T *__restrict__ bias, float eps,
+                                                   const T *__restrict__ cos_t, const T *__restrict__ sin_t,
+                                                   T *__restrict__ Kc, T *__restrict__ Vc, int cap, int lo, int nkeys,
+                                                   int chunk, float scale, float *__restrict__ part, int nsplit, int s,
+                                                   int g) {
     extern __shared__ float smem[];
     float *sc = smem;
     float *red = smem + G * chunk;
@@ -107,7 +116,7 @@ __device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, in
     __shared__ float kvs[2 * D];
     __shared__ float mrow[G], lrow[G];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j0 = s * chunk, j1 = min(nkeys, j0 + chunk);
+    const int j0 = lo + s * chunk, j1 = min(nkeys, j0 + chunk);
     const int p = nkeys - 1;
     const bool has_p = j1 == nkeys;
     T *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
@@ -117,18 +126,23 @@ __device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, in
     const int nheads = G + (has_p ? 1 : 0);
     for (int hh = wave; hh < nheads; hh += 4) {
         const bool is_q = hh < G;
-        const T *row = qkv + (size_t)(is_q ? g * G + hh : H + g) * D;
+        const size_t ro = (size_t)(is_q ? g * G + hh : H + g) * D;
+        const T *row = qkv + ro;
         const T *wn = is_q ? q_norm : k_norm;
         const bool on = lane < half;
         float x1 = 0.f, x2 = 0.f;
         if (on) {
             x1 = to_f(row[lane]);
             x2 = to_f(row[lane + half]);
+            if (bias) {
+                x1 = rho<T>(x1 + to_f(bias[ro + lane]));
+                x2 = rho<T>(x2 + to_f(bias[ro + lane + half]));
+            }
         }
         const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + eps);
         if (on) {
-            const float n1 = rho<T>(to_f(wn[lane]) * rho<T>(x1 * r));
-            const float n2 = rho<T>(to_f(wn[lane + half]) * rho<T>(x2 * r));
+            const float n1 = wn ? rho<T>(to_f(wn[lane]) * rho<T>(x1 * r)) : x1;
+            const float n2 = wn ? rho<T>(to_f(wn[lane + half]) * rho<T>(x2 * r)) : x2;
             const float c1 = to_f(cos_t[(size_t)p * D + lane]), s1 = to_f(sin_t[(size_t)p * D + lane]);
             const float c2 = to_f(cos_t[(size_t)p * D + lane + half]), s2 = to_f(sin_t[(size_t)p * D + lane + half]);
             const float o1 = rho<T>(n1 * c1 - n2 * s1), o2 = rho<T>(n2 * c2 + n1 * s2);
@@ -143,7 +157,11 @@ __device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, in
                 kd[lane + half] = from_f<T>(o2);
                 const T *vrow = qkv + (size_t)(H + KV + g) * D;
                 T *vd = Vg + (size_t)p * D;
-                const T v1 = vrow[lane], v2 = vrow[lane + half];
+                T v1 = vrow[lane], v2 = vrow[lane + half];
+                if (bias) {
+                    v1 = from_f<T>(to_f(v1) + to_f(bias[(size_t)(H + KV + g) * D + lane]));
+                    v2 = from_f<T>(to_f(v2) + to_f(bias[(size_t)(H + KV + g) * D + lane + half]));
+                }
                 vd[lane] = v1;
                 vd[lane + half] = v2;
                 kvs[D + lane] = to_f(v1);
@@ -158,11 +176,12 @@ __device__ __forceinline__ void decode_fused_block(const T *__restrict__ qkv, in
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) attn_decode_fused_kernel(
-    const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm, float eps,
-    const T *__restrict__ cos_t, const T *__restrict__ sin_t, T *__restrict__ Kc, T *__restrict__ Vc, int cap,
-    int nkeys, int chunk, float scale, float *__restrict__ part, int nsplit) {
-    decode_fused_block<T, D, G>(qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, Kc, Vc, cap, nkeys, chunk, scale, part,
-                                nsplit, blockIdx.x, blockIdx.y);
+    const T *__restrict__ qkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm,
+    const T *__restrict__ bias, float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t,
+    T *__restrict__ Kc, T *__restrict__ Vc, int cap, int lo, int nkeys, int chunk, float scale,
+    float *__restrict__ part, int nsplit) {
+    decode_fused_block<T, D, G>(qkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, Kc, Vc, cap, lo, nkeys, chunk,
+                                scale, part, nsplit, blockIdx.x, blockIdx.y);
 }
 
 // Several seats at once (blockIdx.z = seat b): seat b's q|k|v row, cache, position and split
@@ -170,13 +189,13 @@ __global__ void __launch_bounds__(256) attn_decode_fused_kernel(
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) attn_decode_fused_batch_kernel(
     const T *__restrict__ qkv, int nqkv, int H, int KV, const T *__restrict__ q_norm, const T *__restrict__ k_norm,
-    float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t, DecodeBatch bt, int cap, float scale,
-    float *__restrict__ part, size_t part_stride) {
+    const T *__restrict__ bias, float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t, DecodeBatch bt,
+    int cap, float scale, float *__restrict__ part, size_t part_stride) {
     const int b = blockIdx.z;
     if ((int)blockIdx.x >= bt.nsplit[b]) return;  // uniform over the block
-    decode_fused_block<T, D, G>(qkv + (size_t)b * nqkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, (T *)bt.kc[b],
-                                (T *)bt.vc[b], cap, bt.p[b] + 1, bt.chunk[b], scale, part + (size_t)b * part_stride,
-                                bt.nsplit[b], blockIdx.x, blockIdx.y);
+    decode_fused_block<T, D, G>(qkv + (size_t)b * nqkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t,
+                                (T *)bt.kc[b], (T *)bt.vc[b], cap, bt.lo[b], bt.p[b] + 1, bt.chunk[b], scale,
+                                part + (size_t)b * part_stride, bt.nsplit[b], blockIdx.x, blockIdx.y);
 }
 
 // Merge the splits of one head: out = rho(sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M)).
@@ -240,7 +259,7 @@ __global__ void __launch_bounds__(256) attn_combine_batch_kernel(const float *__
 template <typename T>
 __global__ void __launch_bounds__(64) attn_rowwise_kernel(const T *__restrict__ q, const T *__restrict__ Kc,
                                                           const T *__restrict__ Vc, int H, int KV, int D, int cap,
-                                                          int p0, float scale, T *__restrict__ out) {
+                                                          int p0, int window, float scale, T *__restrict__ out) {
     __shared__ float qs[128];
     __shared__ float es[64];
     const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
@@ -250,10 +269,11 @@ __global__ void __launch_bounds__(64) attn_rowwise_kernel(const T *__restrict__ 
     for (int d = lane; d < D; d += 64) qs[d] = to_f(q[((size_t)t * H + h) * D + d]);
     __syncthreads();
     float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int jb = 0; jb <= p; jb += 64) {
+    const int lo = window > 0 && p - window + 1 > 0 ? p - window + 1 : 0;  // the first chunk holds key lo
+    for (int jb = lo & ~63; jb <= p; jb += 64) {
         const int j = jb + lane;
         float sj = -INFINITY;
-        if (j <= p) {
+        if (j >= lo && j <= p) {
             float dotv = 0.f;
             for (int d = 0; d < D; ++d) dotv += qs[d] * to_f(Kg[(size_t)j * D + d]);
             sj = dotv * scale;
@@ -300,7 +320,7 @@ __device__ __forceinline__ s16x4 lds_tr_b64(const uint16_t *p) {
 template <int D, int G>
 __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ Kc, const bf16 *__restrict__ Vc, int T, int H, int KV,
-    int cap, int p0, float scale_log2, bf16 *__restrict__ out) {
+    int cap, int p0, int window, float scale_log2, bf16 *__restrict__ out) {
     constexpr int QB = G >= 4 ? 16 : 64 / G;   // queries per block
     constexpr int QG = QB / 16;                // 16-query groups per head
     constexpr int NW = G * QG;                 // waves
@@ -362,13 +382,17 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
     };
 
     const int nkt = kmax / 64 + 1;
-    gload(0);
+    // sliding window: keys below the block's first window start are never visible
+    const int kt0 = window > 0 && p0 + t0 - window + 1 > 0 ? (p0 + t0 - window + 1) / 64 : 0;
+    const int wlo = window > 0 ? p0 + wq0 - window + 1 : 0;          // the wave's lowest window start
+    const int qlo = window > 0 ? qpos - window + 1 : INT_MIN;         // this lane's query
+    gload(kt0 * 64);
     sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int k0 = kt * 64, buf = kt & 1;
+    for (int kt = kt0; kt < nkt; ++kt) {
+        const int k0 = kt * 64, buf = (kt - kt0) & 1;
         if (kt + 1 < nkt) gload(k0 + 64);
-        if (k0 <= wlast) {
+        if (k0 <= wlast && k0 + 63 >= wlo) {
             const uint16_t *Kt = Ks[buf], *Vt = Vs[buf];
             f32x4 sacc[4];
 #pragma unroll
@@ -380,21 +404,24 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
                     sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
                 }
             }
-            const bool need_mask = k0 + 63 > p0 + wq0;
+            const bool need_mask = k0 + 63 > p0 + wq0 || (window > 0 && k0 < wlast - window + 1);
             float tmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     float sv = sacc[kb][a] * scale_log2;
-                    if (need_mask && k0 + kb * 16 + quad * 4 + a > qpos) sv = -INFINITY;
+                    const int key = k0 + kb * 16 + quad * 4 + a;
+                    if (need_mask && (key > qpos || key < qlo)) sv = -INFINITY;
                     sacc[kb][a] = sv;
                     tmax = fmaxf(tmax, sv);
                 }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            // a query whose window has not started yet has no visible key: its p stay 0
             const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
             float psum = 0.f;
             bf16x8 phi[2], plo[2];
 #pragma unroll
@@ -403,7 +430,7 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
-                        const float pv = __builtin_amdgcn_exp2f(sacc[2 * kc + hf][a] - m_new);
+                        const float pv = __builtin_amdgcn_exp2f(sacc[2 * kc + hf][a] - m_sub);
                         psum += pv;
                         const __bf16 hb = (__bf16)pv;
                         phi[kc][hf * 4 + a] = hb;
@@ -475,7 +502,7 @@ struct FaGeo {
 template <int G>
 __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
                                                                   const bf16 *__restrict__ Vc, int T, int H, int KV,
-                                                                  int cap, int p0, float scale_log2,
+                                                                  int cap, int p0, int window, float scale_log2,
                                                                   bf16 *__restrict__ out) {
     using F = FaGeo<G>;
     constexpr int D = F::D, RB = F::RB, KT = F::KT;
@@ -492,6 +519,10 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
     const int tq = min(t0 + qi, T - 1), qpos = p0 + tq;
     const int kmax = p0 + min(t0 + 31, T - 1);  // the block's queries see keys 0..kmax
     const int nkt = kmax / KT + 1;
+    // sliding window: the block's queries see keys kmin..kmax, query qpos keys qlo..qpos
+    const int kmin = window > 0 && p0 + t0 - window + 1 > 0 ? p0 + t0 - window + 1 : 0;
+    const int kt0 = kmin / KT;
+    const int qlo = window > 0 ? qpos - window + 1 : INT_MIN;
     const bf16 *Kg = Kc + (size_t)g * cap * D, *Vg = Vc + (size_t)g * cap * D;
     const unsigned lds0 = (unsigned)(uintptr_t)fa_smem;
 
@@ -524,13 +555,13 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
     float m_run = -INFINITY, l_run = 0.f;
     const int gi = lane >> 4, sl = lane & 15;  // transpose-read group and source lane
 
-    issue(0);
-    for (int kt = 0; kt < nkt; ++kt) {
+    issue(kt0);
+    for (int kt = kt0; kt < nkt; ++kt) {
         wait_vm<0>();
         __syncthreads();  // stage kt landed for every wave; every wave finished kt - 1
         if (kt + 1 < nkt) issue(kt + 1);
         const int kb0 = kt * KT + 32 * par;  // this wave's 32 keys
-        if (kb0 > kmax) continue;            // all masked for every query of the block
+        if (kb0 > kmax || kb0 + 31 < kmin) continue;  // all masked for every query of the block
         const unsigned char *Ks = fa_smem + (kt % F::ST) * F::STAGE, *Vs = Ks + F::TILE;
         f32x16 sc;
 #pragma unroll
@@ -544,12 +575,13 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
             }
         }
         // accumulator v of S^T: key kb0 + 8 (v / 4) + 4 hh + v % 4, query qi
-        const bool need_mask = kb0 + 31 > p0 + t0;
+        const bool need_mask = kb0 + 31 > p0 + t0 || (window > 0 && kb0 < kmax - window + 1);
         float tmax = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             float sv = sc[v] * scale_log2;
-            if (need_mask && kb0 + 8 * (v >> 2) + 4 * hh + (v & 3) > qpos) sv = -INFINITY;
+            const int key = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (need_mask && (key > qpos || key < qlo)) sv = -INFINITY;
             sc[v] = sv;
             tmax = fmaxf(tmax, sv);
         }
@@ -643,7 +675,7 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
 
 template <int G>
 static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T, int H, int KV, int cap, int p0,
-                             float sl2, bf16 *out, hipStream_t s) {
+                             int window, float sl2, bf16 *out, hipStream_t s) {
     const size_t lds = FaGeo<G>::LDS;
     static bool attr = false;
     if (!attr) {
@@ -653,41 +685,47 @@ static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T,
         attr = true;
     }
     const int ntiles = (T + 31) / 32;
-    attn_prefill_fa_kernel<G><<<ntiles * KV, 128 * G, lds, s>>>(q, k, v, T, H, KV, cap, p0, sl2, out);
+    attn_prefill_fa_kernel<G><<<ntiles * KV, 128 * G, lds, s>>>(q, k, v, T, H, KV, cap, p0, window, sl2, out);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------ dispatch
 template <typename T, int D, int G>
 static void decode_launch(bool fused, dim3 grid, size_t lds, hipStream_t s, const void *q, const void *qkv, int H,
-                          int KV, const void *qn, const void *kn, float eps, const void *cs, const void *sn, void *kc,
-                          void *vc, int cap, int nkeys, int chunk, float scale, float *ws, int nsplit) {
+                          int KV, const void *qn, const void *kn, const void *bias, float eps, const void *cs,
+                          const void *sn, void *kc, void *vc, int cap, int lo, int nkeys, int chunk, float scale,
+                          float *ws, int nsplit) {
     if (fused)
         attn_decode_fused_kernel<T, D, G><<<grid, 256, lds, s>>>((const T *)qkv, H, KV, (const T *)qn, (const T *)kn,
-                                                                  eps, (const T *)cs, (const T *)sn, (T *)kc, (T *)vc,
-                                                                  cap, nkeys, chunk, scale, ws, nsplit);
+                                                                  (const T *)bias, eps, (const T *)cs, (const T *)sn,
+                                                                  (T *)kc, (T *)vc, cap, lo, nkeys, chunk, scale, ws,
+                                                                  nsplit);
     else
-        attn_decode_kernel<T, D, G><<<grid, 256, lds, s>>>((const T *)q, (const T *)kc, (const T *)vc, cap, nkeys,
+        attn_decode_kernel<T, D, G><<<grid, 256, lds, s>>>((const T *)q, (const T *)kc, (const T *)vc, cap, lo, nkeys,
                                                             chunk, scale, ws, nsplit);
 }
 
 template <typename T, int D>
 static hipError_t decode_t(bool fused, const void *q, const void *qkv, int H, int KV, const void *qn, const void *kn,
-                           float eps, const void *cs, const void *sn, void *kc, void *vc, int cap, int nkeys,
-                           void *out, float *ws, hipStream_t s) {
+                           const void *bias, float eps, const void *cs, const void *sn, void *kc, void *vc, int cap,
+                           int nkeys, int window, void *out, float *ws, hipStream_t s) {
     const int G = H / KV;
-    const int chunk = decode_chunk(nkeys, KV);
-    const int nsplit = (nkeys + chunk - 1) / chunk;
+    const int lo = window_lo(nkeys - 1, window), nvis = nkeys - lo;  // keys lo..nkeys-1
+    const int chunk = decode_chunk(nvis, KV);
+    const int nsplit = (nvis + chunk - 1) / chunk;
     const float scale = (float)(1.0 / sqrt((double)D));
     const size_t lds = ((size_t)G * chunk + 4 * (size_t)G * D) * sizeof(float);
     const dim3 grid(nsplit, KV);
+#define DECODE_CASE(GG)                                                                                          \
+    case GG:                                                                                                     \
+        decode_launch<T, D, GG>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, bias, eps, cs, sn, kc, vc, cap, lo,  \
+                                nkeys, chunk, scale, ws, nsplit);                                                \
+        break;
     switch (G) {
-    case 1: decode_launch<T, D, 1>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 2: decode_launch<T, D, 2>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 4: decode_launch<T, D, 4>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
-    case 8: decode_launch<T, D, 8>(fused, grid, lds, s, q, qkv, H, KV, qn, kn, eps, cs, sn, kc, vc, cap, nkeys, chunk, scale, ws, nsplit); break;
+        DECODE_CASE(1) DECODE_CASE(2) DECODE_CASE(4) DECODE_CASE(8)
     default: return hipErrorInvalidValue;
     }
+#undef DECODE_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_combine_kernel<T, D><<<H, 256, 0, s>>>(ws, nsplit, (T *)out);
@@ -695,33 +733,35 @@ static hipError_t decode_t(bool fused, const void *q, const void *qkv, int H, in
 }
 
 hipError_t launch_attention_decode_fused(int dt, const void *qkv, int H, int KV, int D, const void *q_norm,
-                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
-                                         int cap, void *k_cache, void *v_cache, void *out, float *ws,
-                                         hipStream_t s) {
+                                         const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                         const void *sin_t, int p0, int cap, int window, void *k_cache,
+                                         void *v_cache, void *out, float *ws, hipStream_t s) {
+    if ((q_norm == nullptr) != (k_norm == nullptr)) return hipErrorInvalidValue;
     const int nkeys = p0 + 1;
     if (dt == DT_BF16)
-        return D == 128 ? decode_t<bf16, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
-                                              v_cache, cap, nkeys, out, ws, s)
-                        : decode_t<bf16, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
-                                             v_cache, cap, nkeys, out, ws, s);
-    return D == 128 ? decode_t<float, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
-                                           v_cache, cap, nkeys, out, ws, s)
-                    : decode_t<float, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache,
-                                          v_cache, cap, nkeys, out, ws, s);
+        return D == 128 ? decode_t<bf16, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t,
+                                              k_cache, v_cache, cap, nkeys, window, out, ws, s)
+                        : decode_t<bf16, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t,
+                                             k_cache, v_cache, cap, nkeys, window, out, ws, s);
+    return D == 128 ? decode_t<float, 128>(true, nullptr, qkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                           v_cache, cap, nkeys, window, out, ws, s)
+                    : decode_t<float, 64>(true, nullptr, qkv, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                          v_cache, cap, nkeys, window, out, ws, s);
 }
 
 template <typename T, int D, int G>
 static void batch_launch(dim3 grid, size_t lds, hipStream_t s, const T *qkv, int nqkv, int H, int KV, const T *qn,
-                         const T *kn, float eps, const T *cs, const T *sn, const DecodeBatch &bt, int cap, float scale,
-                         float *ws, size_t stride) {
-    attn_decode_fused_batch_kernel<T, D, G><<<grid, 256, lds, s>>>(qkv, nqkv, H, KV, qn, kn, eps, cs, sn, bt, cap, scale,
-                                                                   ws, stride);
+                         const T *kn, const T *bias, float eps, const T *cs, const T *sn, const DecodeBatch &bt,
+                         int cap, float scale, float *ws, size_t stride) {
+    attn_decode_fused_batch_kernel<T, D, G><<<grid, 256, lds, s>>>(qkv, nqkv, H, KV, qn, kn, bias, eps, cs, sn, bt, cap,
+                                                                   scale, ws, stride);
 }
 
 template <typename T, int D>
-static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const void *qn, const void *kn, float eps,
-                                 const void *cs, const void *sn, void *const *kc, void *const *vc, const int *p,
-                                 int cap, void *out, float *ws, hipStream_t s) {
+static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const void *qn, const void *kn,
+                                 const void *bias, float eps, const void *cs, const void *sn, void *const *kc,
+                                 void *const *vc, const int *p, int cap, int window, void *out, float *ws,
+                                 hipStream_t s) {
     const int G = H / KV;
     DecodeBatch bt{};
     int maxsplit = 0, maxchunk = 0;
@@ -729,8 +769,10 @@ static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const vo
         bt.kc[b] = kc[b];
         bt.vc[b] = vc[b];
         bt.p[b] = p[b];
-        bt.chunk[b] = decode_chunk(p[b] + 1, KV);
-        bt.nsplit[b] = (p[b] + bt.chunk[b]) / bt.chunk[b];
+        bt.lo[b] = window_lo(p[b], window);
+        const int nvis = p[b] + 1 - bt.lo[b];
+        bt.chunk[b] = decode_chunk(nvis, KV);
+        bt.nsplit[b] = (nvis + bt.chunk[b] - 1) / bt.chunk[b];
         maxsplit = bt.nsplit[b] > maxsplit ? bt.nsplit[b] : maxsplit;
         maxchunk = bt.chunk[b] > maxchunk ? bt.chunk[b] : maxchunk;
     }
@@ -740,11 +782,12 @@ static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const vo
     const int nqkv = (H + 2 * KV) * D;
     const dim3 grid(maxsplit, KV, B);
     const T *q = (const T *)qkv, *qnn = (const T *)qn, *knn = (const T *)kn, *c = (const T *)cs, *sv = (const T *)sn;
+    const T *bb = (const T *)bias;
     switch (G) {
-    case 1: batch_launch<T, D, 1>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
-    case 2: batch_launch<T, D, 2>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
-    case 4: batch_launch<T, D, 4>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
-    case 8: batch_launch<T, D, 8>(grid, lds, s, q, nqkv, H, KV, qnn, knn, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 1: batch_launch<T, D, 1>(grid, lds, s, q, nqkv, H, KV, qnn, knn, bb, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 2: batch_launch<T, D, 2>(grid, lds, s, q, nqkv, H, KV, qnn, knn, bb, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 4: batch_launch<T, D, 4>(grid, lds, s, q, nqkv, H, KV, qnn, knn, bb, eps, c, sv, bt, cap, scale, ws, stride); break;
+    case 8: batch_launch<T, D, 8>(grid, lds, s, q, nqkv, H, KV, qnn, knn, bb, eps, c, sv, bt, cap, scale, ws, stride); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -754,37 +797,38 @@ static hipError_t decode_batch_t(const void *qkv, int B, int H, int KV, const vo
 }
 
 hipError_t launch_attention_decode_batch(int dt, const void *qkv, int B, int H, int KV, int D, const void *q_norm,
-                                         const void *k_norm, float eps, const void *cos_t, const void *sin_t,
-                                         void *const *k_cache, void *const *v_cache, const int *p, int cap, void *out,
-                                         float *ws, hipStream_t s) {
+                                         const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                         const void *sin_t, void *const *k_cache, void *const *v_cache, const int *p,
+                                         int cap, int window, void *out, float *ws, hipStream_t s) {
     if (B < 1 || B > DECODE_MAXB) return hipErrorInvalidValue;
+    if ((q_norm == nullptr) != (k_norm == nullptr)) return hipErrorInvalidValue;
     if (dt == DT_BF16)
-        return D == 128 ? decode_batch_t<bf16, 128>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
-                                                    p, cap, out, ws, s)
-                        : decode_batch_t<bf16, 64>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
-                                                   p, cap, out, ws, s);
-    return D == 128 ? decode_batch_t<float, 128>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
-                                                 p, cap, out, ws, s)
-                    : decode_batch_t<float, 64>(qkv, B, H, KV, q_norm, k_norm, eps, cos_t, sin_t, k_cache, v_cache,
-                                                p, cap, out, ws, s);
+        return D == 128 ? decode_batch_t<bf16, 128>(qkv, B, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                                    v_cache, p, cap, window, out, ws, s)
+                        : decode_batch_t<bf16, 64>(qkv, B, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                                   v_cache, p, cap, window, out, ws, s);
+    return D == 128 ? decode_batch_t<float, 128>(qkv, B, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                                 v_cache, p, cap, window, out, ws, s)
+                    : decode_batch_t<float, 64>(qkv, B, H, KV, q_norm, k_norm, bias, eps, cos_t, sin_t, k_cache,
+                                                v_cache, p, cap, window, out, ws, s);
 }
 
 hipError_t launch_attention(int dt, const void *q, const void *k_cache, const void *v_cache, int T, int H, int KV,
-                            int D, int cap, int p0, void *out, float *ws, size_t ws_bytes, hipStream_t s) {
+                            int D, int cap, int p0, int window, void *out, float *ws, size_t ws_bytes, hipStream_t s) {
     (void)ws_bytes;
     const float scale = (float)(1.0 / sqrt((double)D));
     if (T == 1) {
         const int nkeys = p0 + 1;
         void *kc = (void *)k_cache, *vc = (void *)v_cache;
         if (dt == DT_BF16)
-            return D == 128 ? decode_t<bf16, 128>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc,
-                                                  vc, cap, nkeys, out, ws, s)
-                            : decode_t<bf16, 64>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc,
-                                                 vc, cap, nkeys, out, ws, s);
-        return D == 128 ? decode_t<float, 128>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc, vc,
-                                               cap, nkeys, out, ws, s)
-                        : decode_t<float, 64>(false, q, nullptr, H, KV, nullptr, nullptr, 0.f, nullptr, nullptr, kc, vc,
-                                              cap, nkeys, out, ws, s);
+            return D == 128 ? decode_t<bf16, 128>(false, q, nullptr, H, KV, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                                  nullptr, kc, vc, cap, nkeys, window, out, ws, s)
+                            : decode_t<bf16, 64>(false, q, nullptr, H, KV, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                                 nullptr, kc, vc, cap, nkeys, window, out, ws, s);
+        return D == 128 ? decode_t<float, 128>(false, q, nullptr, H, KV, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                               nullptr, kc, vc, cap, nkeys, window, out, ws, s)
+                        : decode_t<float, 64>(false, q, nullptr, H, KV, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                              nullptr, kc, vc, cap, nkeys, window, out, ws, s);
     }
     if (dt == DT_BF16) {
         const float sl2 = scale * 1.4426950408889634f;
@@ -792,17 +836,17 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
         bf16 *oo = (bf16 *)out;
         const int G = H / KV;
         if (D == 128) {
-            if (G == 1) return prefill_fa<1>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
-            if (G == 2) return prefill_fa<2>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
-            if (G == 4) return prefill_fa<4>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
-            if (G == 8) return prefill_fa<8>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo, s);
+            if (G == 1) return prefill_fa<1>(qq, kk, vv, T, H, KV, cap, p0, window, sl2, oo, s);
+            if (G == 2) return prefill_fa<2>(qq, kk, vv, T, H, KV, cap, p0, window, sl2, oo, s);
+            if (G == 4) return prefill_fa<4>(qq, kk, vv, T, H, KV, cap, p0, window, sl2, oo, s);
+            if (G == 8) return prefill_fa<8>(qq, kk, vv, T, H, KV, cap, p0, window, sl2, oo, s);
             return hipErrorInvalidValue;
         }
         const int QB = G >= 4 ? 16 : 64 / G, NT = 64 * (G >= 8 ? 8 : 4);
         const dim3 grid((T + QB - 1) / QB, KV);
 #define PREFILL_CASE(DD, GG)                                                                                   \
     if (D == DD && G == GG) {                                                                                  \
-        attn_prefill_mfma_kernel<DD, GG><<<grid, NT, 0, s>>>(qq, kk, vv, T, H, KV, cap, p0, sl2, oo);          \
+        attn_prefill_mfma_kernel<DD, GG><<<grid, NT, 0, s>>>(qq, kk, vv, T, H, KV, cap, p0, window, sl2, oo);  \
         return hipGetLastError();                                                                              \
     }
         PREFILL_CASE(128, 1) PREFILL_CASE(128, 2) PREFILL_CASE(128, 4) PREFILL_CASE(128, 8)
@@ -811,7 +855,7 @@ hipError_t launch_attention(int dt, const void *q, const void *k_cache, const vo
         return hipErrorInvalidValue;
     }
     attn_rowwise_kernel<float><<<dim3(T, H), 64, 0, s>>>((const float *)q, (const float *)k_cache,
-                                                          (const float *)v_cache, H, KV, D, cap, p0, scale,
+                                                          (const float *)v_cache, H, KV, D, cap, p0, window, scale,
                                                           (float *)out);
     return hipGetLastError();
 }

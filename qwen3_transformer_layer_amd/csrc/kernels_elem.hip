@@ -181,6 +181,10 @@ hipError_t launch_rope_table(int dt, int cap, int D, double theta, void *cos_t, 
 }
 
 // ------------------------------------------------------------ q/k RMSNorm + RoPE + KV write
+// Page 2's switches ("rlx_flow/blocks/qwen3_decoder.rs", Qwen3DecoderSpec): with a bias
+// [(H+2KV)D] every q, k and v element first becomes rho(x + b) (the add after the
+// projection, rounded); with q_norm == k_norm == NULL (Qwen2) RoPE takes the projection
+// (plus bias) as it is.
 // One block per token, its waves looping over the heads.  Lane i owns the rotate-half
 // pair (i, i + D/2), so the norm's sum of squares is one wave reduction and the rotation needs no
 // exchange.  Heads 0..H-1 are query heads (written to q_out), H..H+KV-1 key
@@ -188,8 +192,8 @@ hipError_t launch_rope_table(int dt, int cap, int D, double theta, void *cos_t, 
 template <typename T>
 __global__ void __launch_bounds__(256) qknorm_rope_kv_kernel(
     const T *__restrict__ qkv, int H, int KV, int D, const T *__restrict__ q_norm, const T *__restrict__ k_norm,
-    float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t, int p0, int cap, T *__restrict__ q_out,
-    T *__restrict__ kc, T *__restrict__ vc) {
+    const T *__restrict__ bias, float eps, const T *__restrict__ cos_t, const T *__restrict__ sin_t, int p0, int cap,
+    T *__restrict__ q_out, T *__restrict__ kc, T *__restrict__ vc) {
     const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = D / 2, nqkv = (H + 2 * KV) * D;
     const int p = p0 + t;
@@ -207,13 +211,17 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_kernel(
         if (on) {
             x1 = to_f(row[lane]);
             x2 = to_f(row[lane + half]);
+            if (bias) {
+                x1 = rho<T>(x1 + to_f(bias[(size_t)hh * D + lane]));
+                x2 = rho<T>(x2 + to_f(bias[(size_t)hh * D + lane + half]));
+            }
         }
         const float ss = wave_sum(x1 * x1 + x2 * x2);
         const float r = 1.0f / sqrtf(ss / (float)D + eps);
         if (!on) continue;
         const T *wn = hh < H ? q_norm : k_norm;
-        const float n1 = rho<T>(to_f(wn[lane]) * rho<T>(x1 * r));
-        const float n2 = rho<T>(to_f(wn[lane + half]) * rho<T>(x2 * r));
+        const float n1 = wn ? rho<T>(to_f(wn[lane]) * rho<T>(x1 * r)) : x1;
+        const float n2 = wn ? rho<T>(to_f(wn[lane + half]) * rho<T>(x2 * r)) : x2;
         const T o1 = from_f<T>(n1 * c1 - n2 * s1);
         const T o2 = from_f<T>(n2 * c2 + n1 * s2);
         if (hh < H) {
@@ -227,8 +235,14 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_kernel(
             kd[lane + half] = o2;
             const T *vrow = qkv + (size_t)t * nqkv + (size_t)(H + KV + g) * D;
             T *vd = vc + ((size_t)g * cap + p) * D;
-            vd[lane] = vrow[lane];
-            vd[lane + half] = vrow[lane + half];
+            if (bias) {
+                const T *vb = bias + (size_t)(H + KV + g) * D;
+                vd[lane] = from_f<T>(to_f(vrow[lane]) + to_f(vb[lane]));
+                vd[lane + half] = from_f<T>(to_f(vrow[lane + half]) + to_f(vb[lane + half]));
+            } else {
+                vd[lane] = vrow[lane];
+                vd[lane + half] = vrow[lane + half];
+            }
         }
     }
 }
@@ -240,8 +254,8 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_kernel(
 template <int D>
 __global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
     const bf16 *__restrict__ qkv, int H, int KV, const bf16 *__restrict__ q_norm, const bf16 *__restrict__ k_norm,
-    float eps, const bf16 *__restrict__ cos_t, const bf16 *__restrict__ sin_t, int p0, int cap,
-    bf16 *__restrict__ q_out, bf16 *__restrict__ kc, bf16 *__restrict__ vc) {
+    const bf16 *__restrict__ bias, float eps, const bf16 *__restrict__ cos_t, const bf16 *__restrict__ sin_t, int p0,
+    int cap, bf16 *__restrict__ q_out, bf16 *__restrict__ kc, bf16 *__restrict__ vc) {
     constexpr int LPH = D / 8, HPW = 64 / LPH, half = D / 2;  // lanes per head, heads per wave
     const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane % LPH, sub = lane / LPH, e1 = 4 * li, e2 = e1 + half;
@@ -255,10 +269,13 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
     ld4(sin_t + (size_t)p * D + e1, s1);
     ld4(cos_t + (size_t)p * D + e2, c2);
     ld4(sin_t + (size_t)p * D + e2, s2);
-    ld4(q_norm + e1, wq1);
-    ld4(q_norm + e2, wq2);
-    ld4(k_norm + e1, wk1);
-    ld4(k_norm + e2, wk2);
+    const bool nrm = q_norm != nullptr;
+    if (nrm) {
+        ld4(q_norm + e1, wq1);
+        ld4(q_norm + e2, wq2);
+        ld4(k_norm + e1, wk1);
+        ld4(k_norm + e2, wk2);
+    }
     const int nh = H + KV;
     for (int hb = wave * HPW; hb < nh; hb += HPW * (blockDim.x >> 6)) {
         const int hh = hb + sub;
@@ -267,6 +284,16 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
         if (on) {
             ld4(qkv + (size_t)t * nqkv + (size_t)hh * D + e1, x1);
             ld4(qkv + (size_t)t * nqkv + (size_t)hh * D + e2, x2);
+            if (bias) {
+                float b1[4], b2[4];
+                ld4(bias + (size_t)hh * D + e1, b1);
+                ld4(bias + (size_t)hh * D + e2, b2);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x1[e] = rho<bf16>(x1[e] + b1[e]);
+                    x2[e] = rho<bf16>(x2[e] + b2[e]);
+                }
+            }
         }
         float ss = 0.f;
 #pragma unroll
@@ -279,8 +306,8 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
         float o1[4], o2[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float n1 = rho<bf16>((isq ? wq1[e] : wk1[e]) * rho<bf16>(x1[e] * r));
-            const float n2 = rho<bf16>((isq ? wq2[e] : wk2[e]) * rho<bf16>(x2[e] * r));
+            const float n1 = nrm ? rho<bf16>((isq ? wq1[e] : wk1[e]) * rho<bf16>(x1[e] * r)) : x1[e];
+            const float n2 = nrm ? rho<bf16>((isq ? wq2[e] : wk2[e]) * rho<bf16>(x2[e] * r)) : x2[e];
             o1[e] = n1 * c1[e] - n2 * s1[e];
             o2[e] = n2 * c2[e] + n1 * s2[e];
         }
@@ -297,37 +324,49 @@ __global__ void __launch_bounds__(256) qknorm_rope_kv_vec_kernel(
             *(uint2 *)(kd + e2) = w2;
             const bf16 *vrow = qkv + (size_t)t * nqkv + (size_t)(H + KV + g) * D;
             bf16 *vd = vc + ((size_t)g * cap + p) * D;
-            *(uint2 *)(vd + e1) = *(const uint2 *)(vrow + e1);
-            *(uint2 *)(vd + e2) = *(const uint2 *)(vrow + e2);
+            if (bias) {
+                float v1[4], v2[4], b1[4], b2[4];
+                ld4(vrow + e1, v1);
+                ld4(vrow + e2, v2);
+                ld4(bias + (size_t)(H + KV + g) * D + e1, b1);
+                ld4(bias + (size_t)(H + KV + g) * D + e2, b2);
+                *(uint2 *)(vd + e1) = uint2{pack_bf2(v1[0] + b1[0], v1[1] + b1[1]), pack_bf2(v1[2] + b1[2], v1[3] + b1[3])};
+                *(uint2 *)(vd + e2) = uint2{pack_bf2(v2[0] + b2[0], v2[1] + b2[1]), pack_bf2(v2[2] + b2[2], v2[3] + b2[3])};
+            } else {
+                *(uint2 *)(vd + e1) = *(const uint2 *)(vrow + e1);
+                *(uint2 *)(vd + e2) = *(const uint2 *)(vrow + e2);
+            }
         }
     }
 }
 
 hipError_t launch_qknorm_rope_kv(int dt, const void *qkv, int T, int H, int KV, int D, const void *q_norm,
-                                 const void *k_norm, float eps, const void *cos_t, const void *sin_t, int p0,
-                                 int cap, void *q_out, void *k_cache, void *v_cache, hipStream_t s) {
+                                 const void *k_norm, const void *bias, float eps, const void *cos_t,
+                                 const void *sin_t, int p0, int cap, void *q_out, void *k_cache, void *v_cache,
+                                 hipStream_t s) {
+    if ((q_norm == nullptr) != (k_norm == nullptr)) return hipErrorInvalidValue;
     const dim3 grid(T);
     if (dt == DT_BF16 && (D == 128 || D == 64)) {
         const bf16 *a = (const bf16 *)qkv, *qn = (const bf16 *)q_norm, *kn = (const bf16 *)k_norm;
-        const bf16 *ct = (const bf16 *)cos_t, *st = (const bf16 *)sin_t;
+        const bf16 *b = (const bf16 *)bias, *ct = (const bf16 *)cos_t, *st = (const bf16 *)sin_t;
         if (D == 128)
-            qknorm_rope_kv_vec_kernel<128><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, eps, ct, st, p0, cap, (bf16 *)q_out,
-                                                                 (bf16 *)k_cache, (bf16 *)v_cache);
+            qknorm_rope_kv_vec_kernel<128><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, b, eps, ct, st, p0, cap,
+                                                                 (bf16 *)q_out, (bf16 *)k_cache, (bf16 *)v_cache);
         else
-            qknorm_rope_kv_vec_kernel<64><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, eps, ct, st, p0, cap, (bf16 *)q_out,
-                                                                (bf16 *)k_cache, (bf16 *)v_cache);
+            qknorm_rope_kv_vec_kernel<64><<<grid, 256, 0, s>>>(a, H, KV, qn, kn, b, eps, ct, st, p0, cap,
+                                                                (bf16 *)q_out, (bf16 *)k_cache, (bf16 *)v_cache);
         return hipGetLastError();
     }
     if (dt == DT_BF16)
         qknorm_rope_kv_kernel<bf16><<<grid, 256, 0, s>>>((const bf16 *)qkv, H, KV, D, (const bf16 *)q_norm,
-                                                        (const bf16 *)k_norm, eps, (const bf16 *)cos_t,
-                                                        (const bf16 *)sin_t, p0, cap, (bf16 *)q_out,
-                                                        (bf16 *)k_cache, (bf16 *)v_cache);
+                                                        (const bf16 *)k_norm, (const bf16 *)bias, eps,
+                                                        (const bf16 *)cos_t, (const bf16 *)sin_t, p0, cap,
+                                                        (bf16 *)q_out, (bf16 *)k_cache, (bf16 *)v_cache);
     else
         qknorm_rope_kv_kernel<float><<<grid, 256, 0, s>>>((const float *)qkv, H, KV, D, (const float *)q_norm,
-                                                         (const float *)k_norm, eps, (const float *)cos_t,
-                                                         (const float *)sin_t, p0, cap, (float *)q_out,
-                                                         (float *)k_cache, (float *)v_cache);
+                                                         (const float *)k_norm, (const float *)bias, eps,
+                                                         (const float *)cos_t, (const float *)sin_t, p0, cap,
+                                                         (float *)q_out, (float *)k_cache, (float *)v_cache);
     return hipGetLastError();
 }
 

@@ -142,6 +142,7 @@ int check_config(const qwen3_config *c, std::string *why) {
     if (c->hidden % 128) return bad(QWEN3_ERR_UNSUPPORTED, "hidden must be a multiple of 128");
     if (!(c->rms_eps >= 0.0f)) return bad(QWEN3_ERR_ARG, "rms_eps must be >= 0");
     if (!(c->rope_theta > 1.0)) return bad(QWEN3_ERR_ARG, "rope_theta must be > 1");
+    if (c->sliding_window < 0) return bad(QWEN3_ERR_ARG, "sliding_window must be 0 (causal) or positive");
     if (c->n_experts > 0) {
         if (c->n_experts > 256 || c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
             return bad(QWEN3_ERR_UNSUPPORTED, "MoE needs 1 <= top_k <= min(16, n_experts) and n_experts <= 256");
@@ -254,9 +255,9 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
                                     h->qkv));
         HIPCHECK(h, mark(h, K_QKV, false));
         HIPCHECK(h, mark(h, K_ATTN, true));
-        HIPCHECK(h, launch_attention_decode_fused(dt, h->qkv, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t,
-                                                  h->sin_t, p0, c.capacity, h->kc + l * layer_kv,
-                                                  h->vc + l * layer_kv, h->a, h->attn_ws, s));
+        HIPCHECK(h, launch_attention_decode_fused(dt, h->qkv, H, KV, D, L.q_norm, L.k_norm, L.qkv_bias, c.rms_eps,
+                                                  h->cos_t, h->sin_t, p0, c.capacity, c.sliding_window,
+                                                  h->kc + l * layer_kv, h->vc + l * layer_kv, h->a, h->attn_ws, s));
         HIPCHECK(h, mark(h, K_ATTN, false));
         HIPCHECK(h, mark(h, K_O, true));
         HIPCHECK(h, linear(h, h->a, 1, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : hnext, hnext));
@@ -296,11 +297,12 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         HIPCHECK(h, mark(h, K_QKV, true));
         HIPCHECK(h, linear(h, h->y, T, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
         HIPCHECK(h, mark(h, K_QKV, false));
-        HIPCHECK(h, launch_qknorm_rope_kv(dt, h->qkv, T, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t, h->sin_t,
-                                          p0, c.capacity, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv, s));
+        HIPCHECK(h, launch_qknorm_rope_kv(dt, h->qkv, T, H, KV, D, L.q_norm, L.k_norm, L.qkv_bias, c.rms_eps, h->cos_t,
+                                          h->sin_t, p0, c.capacity, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv,
+                                          s));
         HIPCHECK(h, mark(h, K_ATTN, true));
         HIPCHECK(h, launch_attention(dt, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv, T, H, KV, D, c.capacity, p0,
-                                     h->a, h->attn_ws, 0, s));
+                                     c.sliding_window, h->a, h->attn_ws, 0, s));
         HIPCHECK(h, mark(h, K_ATTN, false));
         HIPCHECK(h, mark(h, K_O, true));
         HIPCHECK(h, linear(h, h->a, T, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
@@ -345,8 +347,9 @@ int run_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
             kc[b] = seats[b]->kc + l * layer_kv;
             vc[b] = seats[b]->vc + l * layer_kv;
         }
-        HIPCHECK(h, launch_attention_decode_batch(dt, h->qkv, B, H, KV, D, L.q_norm, L.k_norm, c.rms_eps, h->cos_t,
-                                                  h->sin_t, kc, vc, pos, c.capacity, h->a, h->attn_ws, s));
+        HIPCHECK(h, launch_attention_decode_batch(dt, h->qkv, B, H, KV, D, L.q_norm, L.k_norm, L.qkv_bias, c.rms_eps,
+                                                  h->cos_t, h->sin_t, kc, vc, pos, c.capacity, c.sliding_window, h->a,
+                                                  h->attn_ws, s));
         HIPCHECK(h, linear(h, h->a, B, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
         HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, B, hid, c.rms_eps, s));
         if (moe_layer(c, L)) {
@@ -368,7 +371,7 @@ bool same_model(const qwen3_handle *a, const qwen3_handle *b) {
         x.head_dim != y.head_dim || x.intermediate != y.intermediate || x.capacity != y.capacity ||
         x.rms_eps != y.rms_eps || x.rope_theta != y.rope_theta || x.dtype != y.dtype || x.n_experts != y.n_experts ||
         x.top_k != y.top_k || x.moe_intermediate != y.moe_intermediate || x.norm_topk_prob != y.norm_topk_prob ||
-        x.quant_bits != y.quant_bits || x.quant_group != y.quant_group)
+        x.quant_bits != y.quant_bits || x.quant_group != y.quant_group || x.sliding_window != y.sliding_window)
         return false;
     if (a->final_norm != b->final_norm) return false;
     for (int l = 0; l < x.n_layers; ++l)
@@ -436,7 +439,8 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
     const bool q8 = cfg->quant_bits == 8, moe = cfg->n_experts > 0;
     for (int l = 0; l < cfg->n_layers; ++l) {
         const qwen3_layer_weights &Lw = w->layers[l];
-        if (!Lw.in_norm || !Lw.post_norm || !Lw.q_norm || !Lw.k_norm || !Lw.qkv || !Lw.o) return QWEN3_ERR_NULL_WEIGHT;
+        if (!Lw.in_norm || !Lw.post_norm || !Lw.qkv || !Lw.o) return QWEN3_ERR_NULL_WEIGHT;
+        if ((Lw.q_norm == nullptr) != (Lw.k_norm == nullptr)) return QWEN3_ERR_NULL_WEIGHT;  // both or neither
         if (q8 && (!Lw.qkv_s || !Lw.qkv_b || !Lw.o_s || !Lw.o_b)) return QWEN3_ERR_NULL_WEIGHT;
         if (moe && Lw.router) {
             if (!Lw.exp_gate_up || !Lw.exp_down) return QWEN3_ERR_NULL_WEIGHT;
@@ -489,7 +493,9 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
                                   (void *)h->sin_t, h->stream);
         }
     }
-    if (e == hipSuccess && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
+    bool qwen3_layers = cfg->sliding_window == 0;  // the persistent kernel: causal, q/k norm, no bias
+    for (int l = 0; l < cfg->n_layers; ++l) qwen3_layers = qwen3_layers && w->layers[l].q_norm && !w->layers[l].qkv_bias;
+    if (e == hipSuccess && qwen3_layers && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
                                                cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->intermediate,
                                                cfg->capacity) &&
         decode_mk_max_blocks(cfg->hidden, cfg->intermediate, cfg->n_heads, cfg->n_kv_heads) >= decode_mk_blocks()) {

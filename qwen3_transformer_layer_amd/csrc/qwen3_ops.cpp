@@ -43,7 +43,7 @@ int qwen3_op_qknorm_rope_kv(int dtype, const void *qkv, int T, int H, int KV, in
     if (!dt_ok(dtype)) return QWEN3_ERR_DTYPE;
     if (!qkv || !q_norm || !k_norm || !cos_t || !sin_t || !q_out || !k_cache || !v_cache) return QWEN3_ERR_ARG;
     if (T < 1 || H < 1 || KV < 1 || H % KV || (D != 64 && D != 128) || p0 < 0 || p0 + T > cap) return QWEN3_ERR_ARG;
-    return hip_rc(launch_qknorm_rope_kv(dtype, qkv, T, H, KV, D, q_norm, k_norm, eps, cos_t, sin_t, p0, cap, q_out,
+    return hip_rc(launch_qknorm_rope_kv(dtype, qkv, T, H, KV, D, q_norm, k_norm, nullptr, eps, cos_t, sin_t, p0, cap, q_out,
                                         k_cache, v_cache, (hipStream_t)stream));
 }
 
@@ -59,7 +59,7 @@ int qwen3_op_attention(int dtype, const void *q, const void *k_cache, const void
     const int G = H / KV;
     if ((D != 64 && D != 128) || (G != 1 && G != 2 && G != 4 && G != 8)) return QWEN3_ERR_UNSUPPORTED;
     if (T == 1 && (!ws || ws_bytes < attention_workspace(T, H, KV, D, cap))) return QWEN3_ERR_WORKSPACE;
-    return hip_rc(launch_attention(dtype, q, k_cache, v_cache, T, H, KV, D, cap, p0, out, (float *)ws, ws_bytes,
+    return hip_rc(launch_attention(dtype, q, k_cache, v_cache, T, H, KV, D, cap, p0, 0, out, (float *)ws, ws_bytes,
                                    (hipStream_t)stream));
 }
 
