@@ -64,6 +64,14 @@ Q8_DECODE_STEP_BYTES = 28 * (Q8_WEIGHTS + Q8_WEIGHTS // 64 * 4 + 8 * 4096 * 128 
 # bf16 prefill.
 Q8_PREFILL_T = 512
 Q8_PREFILL_FLOPS = 28 * (2 * Q8_PREFILL_T * Q8_WEIGHTS + 4 * 128 * 16 * Q8_PREFILL_T * (Q8_PREFILL_T + 1) // 2)
+# Qwen2-style switches on the 1.7B shape (no per-head q/k norm, q|k|v bias, sliding window of
+# 1024): decode at position 4095 reads the weights, the bias and only the window's K/V.
+QW2_WINDOW = 1024
+QW2_DECODE_STEP_BYTES = 28 * (50_331_648 * 2 + 8 * QW2_WINDOW * 128 * 2 * 2 + 2 * 2048 * 2 + 4096 * 2 + 8 * 128 * 2 * 2)
+# prefill T = 2048 from an empty cache: projections plus the visible (query, key) pairs
+QW2_PREFILL_T = 2048
+QW2_PAIRS = sum(min(t + 1, QW2_WINDOW) for t in range(QW2_PREFILL_T))
+QW2_PREFILL_FLOPS = 28 * (2 * QW2_PREFILL_T * 50_331_648 + 4 * 128 * 16 * QW2_PAIRS)
 
 
 def log(*a):
@@ -334,6 +342,57 @@ def q8_bench(steps: int, warmup: int, iters: int):
     return res
 
 
+def qwen2_bench(steps: int, warmup: int, iters: int):
+    """Page 2's switches on the 1.7B shape: no per-head q/k norm, q|k|v bias, a sliding window
+    of 1024 positions; a T = 1 step at position 4095 and a 2048-token prefill."""
+    import torch
+
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_PREFILL
+
+    cfg = QWEN3_1P7B_PREFILL.replace(name="qwen2-style-1.7b", qk_norm=False, attention_bias=True,
+                                     sliding_window=QW2_WINDOW)
+    dev = "cuda"
+    log("qwen2: building 28-layer weights (bias, no q/k norm, window 1024) and a 4096-position cache")
+    w = synth.model_weights(cfg, dev)
+    K, V = synth.kv_cache(cfg, 4095, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    seat = q3.Seat(cfg, w, max_tokens=QW2_PREFILL_T, k_cache=K, v_cache=V, stream=stream)
+    x1 = synth.hidden_states(cfg, 1, dev)
+    xp = synth.hidden_states(cfg, QW2_PREFILL_T, dev, name="xp")
+    o1 = torch.empty_like(x1)
+    op = torch.empty_like(xp)
+    torch.cuda.synchronize()
+
+    def dec():
+        seat.length = 4095
+        q3.qwen3_forward_hidden(seat.handle, x1, o1)
+
+    def pre():
+        seat.length = 0
+        q3.qwen3_forward_hidden(seat.handle, xp, op)
+
+    t_dec = _graph_seconds(dec, stream, steps, warmup)
+    t_pre = _graph_seconds(pre, stream, iters, 2)
+    q3.qwen3_check_device_errors(seat.handle)
+    res = {"workload": "Qwen3-1.7B shape with page 2's Qwen2 switches: no per-head q/k norm, q|k|v bias, "
+                       f"SlidingWindow({QW2_WINDOW})",
+           "decode_path": "persistent kernel" if q3.qwen3_get_decode_path(seat.handle) == 2 else "one kernel per step",
+           "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
+           "decode_step_bytes": QW2_DECODE_STEP_BYTES, "decode_gbps": round(QW2_DECODE_STEP_BYTES / t_dec / 1e9, 1),
+           "decode_hbm_frac": round(QW2_DECODE_STEP_BYTES / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
+           "prefill_T": QW2_PREFILL_T, "prefill_ms": round(t_pre * 1e3, 3),
+           "prefill_tflops": round(QW2_PREFILL_FLOPS / t_pre / 1e12, 1),
+           "prefill_mfma_frac": round(QW2_PREFILL_FLOPS / t_pre / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    log(f"qwen2: decode {t_dec * 1e3:.3f} ms/step ({res['decode_gbps']} GB/s), prefill T=2048 {t_pre * 1e3:.3f} ms "
+        f"({res['prefill_tflops']} TFLOP/s)")
+    del seat, w, K, V
+    torch.cuda.empty_cache()
+    return res
+
+
 def batch_bench(Bs=(8, 16), steps: int = 30, warmup: int = 3):
     """B seats of the 1.7B-shaped bf16 stack, each at position 4095 over its own ctx-4096 cache,
     one token each per step (qwen3_forward_batch).  Bytes per step: the weights once, plus each
@@ -478,7 +537,8 @@ def main():
         return
     if args.variants_only:
         print(json.dumps({"moe": moe_bench(30, 3), "moe_q8": moe_bench(30, 3, q8=True), "q8": q8_bench(30, 3, 5),
-                          "head": head_bench(50, 5), "batch": batch_bench()}), flush=True)
+                          "qwen2": qwen2_bench(30, 3, 5), "head": head_bench(50, 5), "batch": batch_bench()}),
+              flush=True)
         return
     if args.copy_calib:
         copy_calibration()
@@ -487,6 +547,7 @@ def main():
     moe = None if args.no_variants else moe_bench(30, 3)
     moe_q8 = None if args.no_variants else moe_bench(30, 3, q8=True)
     q8 = None if args.no_variants else q8_bench(30, 3, 5)
+    qwen2 = None if args.no_variants else qwen2_bench(30, 3, 5)
     head = None if args.no_variants else head_bench(50, 5)
     batch = None if args.no_variants else batch_bench()
     cpu = None if args.no_cpu else cpu_baseline()
@@ -530,6 +591,7 @@ def main():
         "moe": moe,
         "moe_q8": moe_q8,
         "q8": q8,
+        "qwen2_window": qwen2,
         "head": head,
         "batch_decode": batch,
         "cpu_baseline": cpu,
