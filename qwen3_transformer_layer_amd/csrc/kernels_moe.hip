@@ -382,6 +382,78 @@ __global__ void __launch_bounds__(256) moe_expert_q8_kernel(const bf16 *__restri
     }
 }
 
+// MFMA form of moe_expert_kernel for bf16 when K % 256 == 0 (v_mfma_f32_16x16x32_bf16, as in
+// kernels_linear.hip's gemv_mfma_kernel): block (16 outputs, active expert) with 8 waves, each
+// a K/8 slice; A = up to 16 routed rows of the expert (lane i: row i % 16, k 8 (i / 16) ..),
+// B = 16 weight rows (the gate and the up rows in PASS 0), so each weight chunk is loaded once
+// per group of 16 rows and meets all of them in one MFMA.  The 8 partial tiles are summed in
+// LDS in wave order; wave 0 applies the epilogue of the scalar kernel.
+template <int PASS>
+__global__ void __launch_bounds__(512) moe_expert_mfma_kernel(const bf16 *__restrict__ xin, const bf16 *__restrict__ W,
+                                                              int K, int N, int k, const int32_t *__restrict__ offsets,
+                                                              const int32_t *__restrict__ perm,
+                                                              const int32_t *__restrict__ active,
+                                                              bf16 *__restrict__ out) {
+    constexpr int NWV = 8, U = 8;
+    constexpr int NT = PASS == 0 ? 2 : 1;  // gate and up tiles
+    __shared__ f32x4 part[NWV - 1][NT][64];
+    const int slot = blockIdx.y;
+    if (slot >= active[0]) return;  // uniform over the block
+    const int e = active[1 + slot];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16, r = lane & 15, h = lane >> 4;
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    const size_t wrows = PASS == 0 ? 2 * (size_t)N : (size_t)N;
+    const bf16 *wr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wr[t] = W + ((size_t)e * wrows + (size_t)t * N + min(n0 + r, N - 1)) * K + 8 * h;
+    const int ks = K / NWV, k0 = wave * ks;  // this wave's K slice, a multiple of 32
+    for (int rb = r0; rb < r1; rb += 16) {
+        const int i = rb + min(r, r1 - 1 - rb);  // rows past the expert's last repeat it (not stored)
+        const bf16 *xr = (PASS == 0 ? xin + (size_t)(perm[i] / k) * K : xin + (size_t)i * K) + 8 * h;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = k0; kb < k0 + ks; kb += 32 * U) {
+            u32x4 wv[NT][U], xv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kk = kb + 32 * u;
+                const bool ok = kk < k0 + ks;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) wv[t][u] = ok ? ld_stream(wr[t] + kk) : u32x4{0, 0, 0, 0};
+                xv[u] = ok ? ld16(xr + kk) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, xv[u]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wv[t][u]), acc[t], 0, 0, 0);
+            }
+        }
+        if (wave > 0)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) part[wave - 1][t][lane] = acc[t];
+        __syncthreads();
+        if (wave == 0 && n0 + r < N) {
+#pragma unroll
+            for (int w = 0; w < NWV - 1; ++w)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] += part[w][t][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = rb + 4 * h + j;  // C element j of lane: row 4 (lane / 16) + j, output lane % 16
+                if (row >= r1) continue;
+                const float v = PASS == 0 ? rho<bf16>(silu_f32(rho<bf16>(acc[0][j]))) * rho<bf16>(acc[NT - 1][j])
+                                          : acc[0][j];
+                out[(size_t)row * N + n0 + r] = from_f<bf16>(v);
+            }
+        }
+        __syncthreads();  // part[] is rewritten by the next group
+    }
+}
+
 // ------------------------------------------------------------ one token (T == 1)
 // acc[q] += W_q . x over K inputs: NR weight rows in storage type T, U 16-byte chunks per lane
 // in flight per row before any arithmetic; x in LDS or global memory.
@@ -656,9 +728,22 @@ static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int
         }
     }
     if (!W.q8) {
-        moe_expert_kernel<T, 0><<<g0, 256, 0, s>>>((const T *)x, (const T *)W.gate_up, hid, Ie, k, offsets, perm,
-                                                   active, mbuf);
-        moe_expert_kernel<T, 1><<<g1, 256, 0, s>>>(mbuf, (const T *)W.down, Ie, hid, k, offsets, perm, active, ybuf);
+        bool mfma = false;
+        if constexpr (std::is_same<T, bf16>::value) {
+            if (hid % 256 == 0 && Ie % 256 == 0) {
+                mfma = true;
+                moe_expert_mfma_kernel<0><<<dim3((Ie + 15) / 16, na_max), 512, 0, s>>>(
+                    (const bf16 *)x, (const bf16 *)W.gate_up, hid, Ie, k, offsets, perm, active, mbuf);
+                moe_expert_mfma_kernel<1><<<dim3((hid + 15) / 16, na_max), 512, 0, s>>>(
+                    mbuf, (const bf16 *)W.down, Ie, hid, k, offsets, perm, active, ybuf);
+            }
+        }
+        if (!mfma) {
+            moe_expert_kernel<T, 0><<<g0, 256, 0, s>>>((const T *)x, (const T *)W.gate_up, hid, Ie, k, offsets, perm,
+                                                       active, mbuf);
+            moe_expert_kernel<T, 1><<<g1, 256, 0, s>>>(mbuf, (const T *)W.down, Ie, hid, k, offsets, perm, active,
+                                                       ybuf);
+        }
     }
     moe_combine_kernel<T><<<dim3((hid + 255) / 256, T_), 256, 0, s>>>(ybuf, (const T *)w, inv, hid, k, rows, (T *)out);
     return hipGetLastError();
