@@ -66,21 +66,6 @@ template <int EPI, int BN> __device__ __forceinline__ int w_row(int nb, int r, i
     return min(nb * BN + r, N - 1);
 }
 
-// Eight codes (two words, little-endian bytes) as exact bf16 values: the integer through fp32,
-// whose low 16 bits are zero for 0..255, then the high halves packed.
-__device__ __forceinline__ bf16x8 codes8(uint32_t w0, uint32_t w1) {
-    u32x4 r;
-    const uint32_t w[2] = {w0, w1};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float f0 = (float)(w[h] & 0xffu), f1 = (float)((w[h] >> 8) & 0xffu);
-        const float f2 = (float)((w[h] >> 16) & 0xffu), f3 = (float)(w[h] >> 24);
-        r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-        r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-    }
-    return __builtin_bit_cast(bf16x8, r);
-}
-
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // 4-byte direct-to-LDS copy: lane l's word lands at lds + 4 l.

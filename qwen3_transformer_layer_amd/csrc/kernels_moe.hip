@@ -454,6 +454,97 @@ __global__ void __launch_bounds__(512) moe_expert_mfma_kernel(const bf16 *__rest
     }
 }
 
+// The 8-bit form (K % 256 == 0; 4 waves, each a K/4 slice of whole groups of 64).  A group is
+// two MFMA steps; lane (r, h) takes codes 16 h .. 16 h + 15 of the group (one 16-byte load),
+// the first 8 in the first step and the rest in the second, and the activations of the same
+// k: the steps cover k = 16 h + 0..7 and 16 h + 8..15, all 64 between them.  Codes are exact
+// in bf16.  Per group P = x . q (gate and up tiles) and S = sum of x (an MFMA against ones, in
+// the same register layout) fold as acc += s P + b S with the scale and bias of the lane's
+// weight row, all fp32.
+template <int PASS>
+__global__ void __launch_bounds__(256) moe_expert_q8_mfma_kernel(const bf16 *__restrict__ xin,
+                                                                 const uint8_t *__restrict__ codes,
+                                                                 const bf16 *__restrict__ scale,
+                                                                 const bf16 *__restrict__ bias, int K, int N, int k,
+                                                                 const int32_t *__restrict__ offsets,
+                                                                 const int32_t *__restrict__ perm,
+                                                                 const int32_t *__restrict__ active,
+                                                                 bf16 *__restrict__ out) {
+    constexpr int NWV = 4, U = 4;  // groups in flight per lane
+    constexpr int NT = PASS == 0 ? 2 : 1;
+    __shared__ f32x4 part[NWV - 1][NT][64];
+    const int slot = blockIdx.y;
+    if (slot >= active[0]) return;  // uniform over the block
+    const int e = active[1 + slot];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16, r = lane & 15, h = lane >> 4;
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    const size_t wrows = PASS == 0 ? 2 * (size_t)N : (size_t)N;
+    const int ng = K / 64;
+    size_t wrow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wrow[t] = (size_t)e * wrows + (size_t)t * N + min(n0 + r, N - 1);
+    const int gs = ng / NWV, g0 = wave * gs;  // this wave's groups
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = r0; rb < r1; rb += 16) {
+        const int i = rb + min(r, r1 - 1 - rb);
+        const bf16 *xr = (PASS == 0 ? xin + (size_t)(perm[i] / k) * K : xin + (size_t)i * K) + 16 * h;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = zero;
+        for (int gb = g0; gb < g0 + gs; gb += U) {
+            u32x4 cv[NT][U], xa[U], xb[U];
+            float sv[NT][U], bv[NT][U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = gb + u;
+                const bool ok = g < g0 + gs;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    cv[t][u] = ok ? ld_stream(codes + wrow[t] * K + (size_t)g * 64 + 16 * h) : u32x4{0, 0, 0, 0};
+                    sv[t][u] = ok ? to_f(scale[wrow[t] * ng + g]) : 0.f;
+                    bv[t][u] = ok ? to_f(bias[wrow[t] * ng + g]) : 0.f;
+                }
+                xa[u] = ok ? ld16(xr + (size_t)g * 64) : u32x4{0, 0, 0, 0};
+                xb[u] = ok ? ld16(xr + (size_t)g * 64 + 8) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, xa[u]), a1 = __builtin_bit_cast(bf16x8, xb[u]);
+                f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, S, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, codes8(cv[t][u][0], cv[t][u][1]), zero, 0, 0, 0);
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, codes8(cv[t][u][2], cv[t][u][3]), P, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[t][j] += sv[t][u] * P[j] + bv[t][u] * S[j];
+                }
+            }
+        }
+        if (wave > 0)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) part[wave - 1][t][lane] = acc[t];
+        __syncthreads();
+        if (wave == 0 && n0 + r < N) {
+#pragma unroll
+            for (int w = 0; w < NWV - 1; ++w)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] += part[w][t][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = rb + 4 * h + j;
+                if (row >= r1) continue;
+                const float v = PASS == 0 ? rho<bf16>(silu_f32(rho<bf16>(acc[0][j]))) * rho<bf16>(acc[NT - 1][j])
+                                          : acc[0][j];
+                out[(size_t)row * N + n0 + r] = from_f<bf16>(v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------ one token (T == 1)
 // acc[q] += W_q . x over K inputs: NR weight rows in storage type T, U 16-byte chunks per lane
 // in flight per row before any arithmetic; x in LDS or global memory.
@@ -718,7 +809,14 @@ static hipError_t moe_t(const void *x, int T_, int hid, const MoeWeights &W, int
     const int na_max = rows < E ? rows : E;
     const dim3 g0((Ie + 3) / 4, na_max), g1((hid + 15) / 16, na_max);
     if constexpr (std::is_same<T, bf16>::value) {
-        if (W.q8) {
+        if (W.q8 && hid % 256 == 0 && Ie % 256 == 0) {
+            moe_expert_q8_mfma_kernel<0><<<dim3((Ie + 15) / 16, na_max), 256, 0, s>>>(
+                (const bf16 *)x, (const uint8_t *)W.gate_up, (const bf16 *)W.gate_up_s, (const bf16 *)W.gate_up_b, hid,
+                Ie, k, offsets, perm, active, mbuf);
+            moe_expert_q8_mfma_kernel<1><<<dim3((hid + 15) / 16, na_max), 256, 0, s>>>(
+                mbuf, (const uint8_t *)W.down, (const bf16 *)W.down_s, (const bf16 *)W.down_b, Ie, hid, k, offsets,
+                perm, active, ybuf);
+        } else if (W.q8) {
             moe_expert_q8_kernel<0><<<g0, 256, 0, s>>>((const bf16 *)x, (const uint8_t *)W.gate_up,
                                                        (const bf16 *)W.gate_up_s, (const bf16 *)W.gate_up_b, hid, Ie,
                                                        k, offsets, perm, active, mbuf);
