@@ -15,8 +15,9 @@
 //    the row (chunk ^ ((row >> 1) & 7) for 128-B rows, chunk ^ ((row >> 2) & 3) for 64-B rows),
 //    so 16 lanes reading 16 consecutive rows at one chunk hit distinct banks.  A copy's lane
 //    -> address map writes that layout directly.
-//  - Tile shapes, the largest that still gives >= 192 tiles: 256 x 128 with 8 waves (gate|up
-//    and q|k|v at T = 2048), 128 x 128 with 8 waves (o_proj and down at T = 2048), else
+//  - Tile shapes, the largest that still gives >= 192 tiles: 128 x 256 with 8 waves for gate|up
+//    (T >= 512; 131 -> 121 us at T = 2048 against 256 x 128), 256 x 128 with 8 waves (q|k|v
+//    at T = 2048), 128 x 128 with 8 waves (o_proj and down at T = 2048), else
 //    128 x 64 (64 x 128 for SWIGLU, whose waves hold gate/up pairs) with 4 waves.  Measured
 //    against one 128 x 256 / 4-wave tiling at T = 2048: gate|up 148 -> 125 us, q|k|v 48 -> 40,
 //    o_proj 40 -> 31; at T = 512 o_proj 54 -> 20 and down 101 -> 38.  8-bit weights: 128 x
@@ -157,7 +158,38 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
         if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
         const unsigned char *As = smem + (kt % C::ST) * C::STAGE;
         const unsigned char *Bs = As + C::A_BYTES;
-        if (!C::Q8) {
+        if constexpr (!C::Q8 && C::NI == 2 && C::NT == 2) {
+            // 64 x 64 per wave: all fragments of the K step are named up front and the schedule is
+            // pinned to the reads of k-slice 0, then one MFMA per read of the later slices, so the
+            // reads of slice kk+1 overlap the MFMAs of slice kk (left to itself the compiler reuses
+            // one fragment set and waits on every read; gate|up at T = 2048 ~130 -> ~118 us)
+            constexpr int NKK = C::BK / 16, RPK = C::NI + C::NT, MPK = C::NI * C::NT;
+            bf16x8 af[NKK][C::NI], bfr[NKK][C::NT];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i)
+                    af[kk][i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), c));
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) bfr[kk][j] = *(const bf16x8 *)(Bs + offB<false>(brow[j] + (lane & 31), c));
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+            static_assert(MPK == RPK, "one read per MFMA");
+            __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);  // DS reads of slice 0
+#pragma unroll
+            for (int r = 0; r < (NKK - 1) * RPK; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MPK, 0);  // MFMAs of the last slice
+        } else if (!C::Q8) {
 #pragma unroll
             for (int kk = 0; kk < C::BK / 16; ++kk) {
                 const int c = 2 * kk + (lane >> 5);
@@ -249,6 +281,7 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
 
 namespace {
 typedef g2::Cfg<256, 128, 3, 4, 2, false> Wide;    // 8 waves, 64 x 64 per wave, 144 KB LDS
+typedef g2::Cfg<128, 256, 3, 2, 4, false> WideN;   // 8 waves, 64 x 64 per wave, 144 KB LDS (gate|up)
 typedef g2::Cfg<128, 128, 4, 4, 2, false> Mid;     // 8 waves, 32 x 64 per wave, 128 KB LDS
 typedef g2::Cfg<128, 64, 4, 2, 2, false> SmallN;   // 4 waves, 64 x 32 per wave, 96 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 2, false> SmallM;   // 4 waves, 32 x 64 per wave, 96 KB LDS
@@ -293,6 +326,8 @@ hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, in
                            hipStream_t s) {
     const bf16 *a = (const bf16 *)x, *r = (const bf16 *)res;
     bf16 *o = (bf16 *)out;
+    if (epi == EPI_SWIGLU && tiles<WideN>(M, N, epi) >= 192)
+        return launch_c<EPI_SWIGLU, WideN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
     if (tiles<Wide>(M, N, epi) >= 192) return launch_e<Wide>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
     if (tiles<Mid>(M, N, epi) >= 192) return launch_e<Mid>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
     if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, SmallM>(a, M, K, W, nullptr, nullptr, N, r, o, s);

@@ -5,14 +5,16 @@
 // Launch sequence of one forward call of T tokens ("maya2_mlx/backbone.py",
 // Backbone.forward, with its deferred MLP residual `pend`):
 //   layer 0:   y = RMSNorm(x)                              add_rmsnorm
-//   layer l>0: h = rho(h + pend); y = RMSNorm(h)           add_rmsnorm (fused add)
+//   layer l>0: h = rho(h + pend); y = RMSNorm(h)           add_rmsnorm (fused add; for T > 1 after a
+//                                                          dense MLP the add already ran in down)
 //              qkv = rho(y Wqkv^T)                         linear (GEMV / MFMA GEMM)
 //              q, K[p], V[p] = norm + RoPE + cache write    qknorm_rope_kv
 //              a = attention(q, K[0..p], V[0..p])           split-K decode | flash prefill
 //              h = rho(h + rho(a Wo^T))                    linear, residual epilogue
 //              y2 = RMSNorm(h)                             add_rmsnorm
 //              dense: m = swiglu(y2 Wgu^T)                 linear, SwiGLU epilogue
-//                     pend = rho(m Wdown^T)                linear
+//                     pend = rho(m Wdown^T)                linear (T > 1: h = rho(h + pend) in its
+//                                                          residual epilogue, same roundings)
 //              MoE:   pend = moe(y2)                       router/top-k/sort/experts/combine
 //   (in an MoE configuration a layer with a router is sparse, one without runs the dense MLP)
 //   after the last layer: out = RMSNorm(rho(h + pend))     add_rmsnorm
@@ -289,11 +291,13 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
     const int nqkv = (H + 2 * KV) * D, p0 = h->length;
     const size_t es = esize(c), layer_kv = (size_t)KV * c.capacity * D * es;
     hipStream_t s = h->stream;
+    bool pend_live = false;  // the last MLP left its output in pend (MoE); dense layers add it in place
     for (int l = 0; l < c.n_layers; ++l) {
         const qwen3_layer_weights &L = h->layers[l];
         // deferred residual + input norm; layer 0 normalises x directly
         if (l == 0) HIPCHECK(h, launch_add_rmsnorm(dt, x, nullptr, L.in_norm, nullptr, h->y, T, hid, c.rms_eps, s));
-        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, L.in_norm, h->h, h->y, T, hid, c.rms_eps, s));
+        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, L.in_norm,
+                                            pend_live ? h->h : nullptr, h->y, T, hid, c.rms_eps, s));
         HIPCHECK(h, mark(h, K_QKV, true));
         HIPCHECK(h, linear(h, h->y, T, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
         HIPCHECK(h, mark(h, K_QKV, false));
@@ -308,20 +312,22 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         HIPCHECK(h, linear(h, h->a, T, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
         HIPCHECK(h, mark(h, K_O, false));
         HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, T, hid, c.rms_eps, s));
-        if (moe_layer(c, L)) {
+        pend_live = moe_layer(c, L);
+        if (pend_live) {
             HIPCHECK(h, moe(h, L, h->y, T, h->moe_idx, h->moe_w, h->pend));
         } else {
             HIPCHECK(h, mark(h, K_GU, true));
             HIPCHECK(h, linear(h, h->y, T, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
                                nullptr, h->m));
             HIPCHECK(h, mark(h, K_GU, false));
+            // the deferred add h = rho(h + rho(m Wdown^T)) happens in the down projection's epilogue
             HIPCHECK(h, mark(h, K_DOWN, true));
-            HIPCHECK(h, linear(h, h->m, T, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_STORE, nullptr,
-                               h->pend));
+            HIPCHECK(h, linear(h, h->m, T, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_RESID, h->h, h->h));
             HIPCHECK(h, mark(h, K_DOWN, false));
         }
     }
-    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, h->final_norm, nullptr, out, T, hid, c.rms_eps, s));
+    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, h->final_norm, nullptr, out, T, hid,
+                                   c.rms_eps, s));
     return QWEN3_OK;
 }
 
@@ -338,10 +344,12 @@ int run_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
     int pos[DECODE_MAXB];
     void *kc[DECODE_MAXB], *vc[DECODE_MAXB];
     for (int b = 0; b < B; ++b) pos[b] = seats[b]->length;
+    bool pend_live = false;  // as in run_layers: only an MoE layer leaves its output in pend
     for (int l = 0; l < c.n_layers; ++l) {
         const qwen3_layer_weights &L = h->layers[l];
         if (l == 0) HIPCHECK(h, launch_add_rmsnorm(dt, x, nullptr, L.in_norm, nullptr, h->y, B, hid, c.rms_eps, s));
-        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, L.in_norm, h->h, h->y, B, hid, c.rms_eps, s));
+        else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, L.in_norm,
+                                            pend_live ? h->h : nullptr, h->y, B, hid, c.rms_eps, s));
         HIPCHECK(h, linear(h, h->y, B, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
         for (int b = 0; b < B; ++b) {
             kc[b] = seats[b]->kc + l * layer_kv;
@@ -352,16 +360,17 @@ int run_batch(qwen3_handle *const *seats, int B, const void *x, void *out) {
                                                   h->attn_ws, s));
         HIPCHECK(h, linear(h, h->a, B, H * D, L.o, L.o_s, L.o_b, hid, EPI_RESID, l == 0 ? x : h->h, h->h));
         HIPCHECK(h, launch_add_rmsnorm(dt, h->h, nullptr, L.post_norm, nullptr, h->y, B, hid, c.rms_eps, s));
-        if (moe_layer(c, L)) {
+        pend_live = moe_layer(c, L);
+        if (pend_live) {
             HIPCHECK(h, moe(h, L, h->y, B, h->moe_idx, h->moe_w, h->pend));
         } else {
             HIPCHECK(h, linear(h, h->y, B, hid, L.gate_up, L.gate_up_s, L.gate_up_b, c.intermediate, EPI_SWIGLU,
                                nullptr, h->m));
-            HIPCHECK(h, linear(h, h->m, B, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_STORE, nullptr,
-                               h->pend));
+            HIPCHECK(h, linear(h, h->m, B, c.intermediate, L.down, L.down_s, L.down_b, hid, EPI_RESID, h->h, h->h));
         }
     }
-    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, h->pend, h->final_norm, nullptr, out, B, hid, c.rms_eps, s));
+    HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, h->final_norm, nullptr, out, B, hid,
+                                   c.rms_eps, s));
     return QWEN3_OK;
 }
 
