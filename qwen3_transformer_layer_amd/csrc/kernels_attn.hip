@@ -478,42 +478,45 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
 }
 
 // ------------------------------------------------------------ bf16 causal flash prefill, head_dim 128
-// Block: 32 queries x the G heads of one kv head; two waves per head, wave parity w splits
-// every 64-key tile into halves (keys 32 w .. 32 w + 31), so a CU holds 2 waves per SIMD and
-// one wave's softmax arithmetic overlaps another's MFMAs.  Each wave keeps its own running
-// maximum, sum and O; at the end the parity-1 wave hands them over through LDS and the
-// parity-0 wave merges (log-sum-exp scaling) and stores.  The running maximum is raised only
+// Block: 32 queries x the G heads of one kv head; NP waves per head (NP = 4 for G <= 2, else
+// 2), wave part w takes keys 32 w .. 32 w + 31 of every (32 NP)-key tile, so a block holds
+// 2 waves per SIMD on its own and one wave's softmax arithmetic overlaps another's MFMAs.
+// (With two key halves and two blocks per CU, a CU whose light block finished ran its heavy
+// block at one wave per SIMD, latency-bound: 4 parts, 60 -> 52 us at T = 2048.)  Each wave
+// keeps its own running maximum, sum and O; at the end parts 1..NP-1 hand them over through
+// LDS and part 0 merges (log-sum-exp scaling) and stores.  The running maximum is raised only
 // when a tile's maximum exceeds it by more than 8 (base 2), so probabilities stay <= 2^8 in
-// fp32 and the O rescale is rare; the normalised result is the same softmax.
-// LDS: per stage a K tile and a V tile of 64 rows x 256 B.  K rows: 16-byte chunk c at slot
-// c ^ (row & 15) (16 lanes reading 16 rows at one chunk hit distinct banks); V rows: chunk c
-// at slot c ^ (4 (row & 3)) (a transpose read covers 4 rows x 32 B per 16 lanes: distinct
-// banks for 32 lanes).
+// fp32 and the O rescale is rare; the normalised result is the same softmax.  Query tiles
+// are dispatched heaviest (most keys) first, so the blocks that start last are the short
+// ones.
+// LDS: per stage a K tile and a V tile of 32 NP rows x 256 B.  K rows: 16-byte chunk c at
+// slot c ^ (row & 15) (16 lanes reading 16 rows at one chunk hit distinct banks); V rows:
+// chunk c at slot c ^ (4 (row & 3)) (a transpose read covers 4 rows x 32 B per 16 lanes:
+// distinct banks for 32 lanes).
 template <int G>
 struct FaGeo {
-    static constexpr int D = 128, RB = 256, KT = 64, ST = 2, NW = 2 * G;
+    static constexpr int NP = G <= 2 ? 4 : 2;  // key parts (waves) per head
+    static constexpr int D = 128, RB = 256, KT = 32 * NP, ST = 2, NW = NP * G;
     static constexpr int TILE = KT * RB, STAGE = 2 * TILE;
     static constexpr int COPIES = STAGE / 1024, PW = COPIES / NW, HALF = PW / 2;
     static constexpr int MERGE = D * 32 * 4 + 2 * 32 * 4;  // O, then m and l of 32 queries (fp32)
-    static constexpr int LDS = (ST * STAGE > G * MERGE) ? ST * STAGE : G * MERGE;
+    static constexpr int LDS = (ST * STAGE > G * (NP - 1) * MERGE) ? ST * STAGE : G * (NP - 1) * MERGE;
     static_assert(COPIES % (2 * NW) == 0, "K and V copies split evenly over the waves");
 };
 
 template <int G>
-__global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
+__global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
                                                                   const bf16 *__restrict__ Vc, int T, int H, int KV,
                                                                   int cap, int p0, int window, float scale_log2,
                                                                   bf16 *__restrict__ out) {
     using F = FaGeo<G>;
     constexpr int D = F::D, RB = F::RB, KT = F::KT;
     extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
-    const int ntiles = (T + 31) / 32, heavy = (ntiles + 1) / 2;
-    // query tile order: the heavy half from the last tile down, then the light half from the
-    // first tile up, so the two blocks a CU holds at once carry about equal causal work
+    const int ntiles = (T + 31) / 32;
     const int bi = (int)(blockIdx.x / KV), g = blockIdx.x % KV;
-    const int qt = bi < heavy ? ntiles - 1 - bi : bi - heavy;
+    const int qt = ntiles - 1 - bi;  // heaviest query tiles first
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hw = wave >> 1, par = wave & 1;
+    const int hw = wave / F::NP, par = wave % F::NP;
     const int h = g * G + hw, t0 = qt * 32;
     const int qi = lane & 31, hh = lane >> 5;
     const int tq = min(t0 + qi, T - 1), qpos = p0 + tq;
@@ -635,10 +638,12 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
             }
         }
     }
-    // merge the two key halves of each head: parity 1 hands over (m, l, O) through LDS
+    // merge the key parts of each head: parts 1..NP-1 hand over (m, l, O) through LDS
     __syncthreads();  // every wave is done with the K/V tiles
-    float *mb = (float *)(fa_smem + hw * F::MERGE);  // O as [dt][v][lane], then m[32], l[32]
-    if (par == 1) {
+    // part w's buffer: O as [dt][v][lane], then m[32], l[32]
+    auto mbuf = [&](int w) { return (float *)(fa_smem + (hw * (F::NP - 1) + w - 1) * F::MERGE); };
+    if (par > 0) {
+        float *mb = mbuf(par);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -650,10 +655,17 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
     }
     __syncthreads();
     if (par == 0 && t0 + qi < T) {
-        const float m1 = mb[D * 32 + qi], l1 = mb[D * 32 + 32 + qi];
-        const float m = fmaxf(m_run, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-        const float inv = 1.0f / (l_run * a0 + l1 * a1);
+        float m = m_run;
+#pragma unroll
+        for (int w = 1; w < F::NP; ++w) m = fmaxf(m, mbuf(w)[D * 32 + qi]);
+        float a[F::NP], lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < F::NP; ++w) {
+            const float mw = w ? mbuf(w)[D * 32 + qi] : m_run, lw = w ? mbuf(w)[D * 32 + 32 + qi] : l_run;
+            a[w] = __builtin_amdgcn_exp2f(mw - m);
+            lsum += lw * a[w];
+        }
+        const float inv = 1.0f / lsum;
         bf16 *dst = out + (size_t)tq * H * D + (size_t)h * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -663,7 +675,10 @@ __global__ void __launch_bounds__(128 * G) attn_prefill_fa_kernel(const bf16 *__
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * v4 + e;
-                    r[e] = (o[dt][v] * a0 + mb[(dt * 16 + v) * 64 + lane] * a1) * inv;
+                    float t = o[dt][v] * a[0];
+#pragma unroll
+                    for (int w = 1; w < F::NP; ++w) t += mbuf(w)[(dt * 16 + v) * 64 + lane] * a[w];
+                    r[e] = t * inv;
                 }
                 uint2 w;
                 w.x = pack_bf2(r[0], r[1]);
@@ -685,7 +700,8 @@ static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T,
         attr = true;
     }
     const int ntiles = (T + 31) / 32;
-    attn_prefill_fa_kernel<G><<<ntiles * KV, 128 * G, lds, s>>>(q, k, v, T, H, KV, cap, p0, window, sl2, out);
+    attn_prefill_fa_kernel<G><<<ntiles * KV, 64 * FaGeo<G>::NW, lds, s>>>(q, k, v, T, H, KV, cap, p0, window, sl2,
+                                                                          out);
     return hipGetLastError();
 }
 
