@@ -519,6 +519,8 @@ def main():
                     help="time only the MoE and 8-bit workloads (for profiling)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the one-kernel-per-step decode path (for profiling)")
+    ap.add_argument("--only", choices=["moe", "moe_q8", "q8", "qwen2", "head", "batch"],
+                    help="time only this variant workload (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a 1 GiB device copy first (hardware-counter scale for profiling)")
     args = ap.parse_args()
@@ -534,6 +536,12 @@ def main():
     if args.prefill_only:
         pre = prefill_bench(args.prefill_iters)
         print(json.dumps({"prefill_ms": pre["ms"], "prefill_tflops": pre["tflops"]}), flush=True)
+        return
+    if args.only:
+        legs = {"moe": lambda: moe_bench(30, 3), "moe_q8": lambda: moe_bench(30, 3, q8=True),
+                "q8": lambda: q8_bench(30, 3, 5), "qwen2": lambda: qwen2_bench(30, 3, 5),
+                "head": lambda: head_bench(50, 5), "batch": batch_bench}
+        print(json.dumps({args.only: legs[args.only]()}), flush=True)
         return
     if args.variants_only:
         print(json.dumps({"moe": moe_bench(30, 3), "moe_q8": moe_bench(30, 3, q8=True), "q8": q8_bench(30, 3, 5),

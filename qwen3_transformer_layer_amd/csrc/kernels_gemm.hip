@@ -20,8 +20,13 @@
 //    at T = 2048), 128 x 128 with 8 waves (o_proj and down at T = 2048), else
 //    128 x 64 (64 x 128 for SWIGLU, whose waves hold gate/up pairs) with 4 waves.  Measured
 //    against one 128 x 256 / 4-wave tiling at T = 2048: gate|up 148 -> 125 us, q|k|v 48 -> 40,
-//    o_proj 40 -> 31; at T = 512 o_proj 54 -> 20 and down 101 -> 38.  8-bit weights: 128 x
-//    128 with 4 waves, else 64 x 128 (the copy kinds must split evenly over the waves).
+//    o_proj 40 -> 31; at T = 512 o_proj 54 -> 20 and down 101 -> 38.  8-bit weights: the
+//    per-group fold (2 FMAs per accumulator element) costs about as many cycles as the group's
+//    MFMAs, so 8 waves per CU let one wave's fold overlap another's MFMAs: 128 x 256 with 8
+//    waves when it gives >= 192 tiles, then 128 x 128 (SwiGLU) or 64 x 128 with 8 waves, else
+//    64 x 64 with 4 waves (3 blocks per CU).  Against the 4-wave 128 x 128 / 64 x 128 tilings
+//    at T = 512: gate|up 96 -> 67 us, down 77 -> 60, o_proj 32 -> 24, q|k|v 32 -> 28.  A
+//    stage's copies are padded with dummies to a multiple of the wave count.
 //  - 8-bit weights (one K step = one group): the codes (64 B per row) are copied to LDS like
 //    the bf16 operand; the scale and bias words of the group arrive by 4-byte direct copies
 //    (the aligned word holding groups 2i and 2i+1).  K is interleaved per lane so one 16-byte
@@ -45,9 +50,15 @@ template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_> struct Cfg {
     static constexpr int A_BYTES = BM * RBA, B_BYTES = BN * RBB, SB_BYTES = Q8 ? BN * 8 : 0;
     static constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;
     static constexpr int ACOP = A_BYTES / 1024, NBIG = (A_BYTES + B_BYTES) / 1024, NSMALL = SB_BYTES / 256;
-    static constexpr int OPS = NBIG + NSMALL, PW = OPS / NW, APW = ACOP / NW, BPW = NBIG / NW;
+    // copies per stage, padded to a multiple of the wave count with 4-byte dummy copies into a
+    // junk LDS word (every wave then issues the same number of copies per stage, which its
+    // vector-memory waits count on)
+    static constexpr int OPS = (NBIG + NSMALL + NW - 1) / NW * NW, PAD = OPS - NBIG - NSMALL;
+    static constexpr int PW = OPS / NW, APW = ACOP / NW, BPW = NBIG / NW;
+    static constexpr int JUNK = PAD ? 256 : 0, LDS = ST * STAGE + JUNK;
     static constexpr int WTM = BM / WM, WTN = BN / WN, NI = WTM / 32, NT = WTN / 32;
-    static_assert(OPS % NW == 0 && ACOP % NW == 0 && NBIG % NW == 0, "copy kinds split evenly over the waves");
+    static_assert(ACOP % NW == 0 && NBIG % NW == 0, "row copies split evenly over the waves");
+    static_assert(PAD == 0 || Q8, "only the scale/bias copies are padded");
     static_assert(NI >= 1 && NT >= 1, "wave tile at least 32 x 32");
 };
 
@@ -116,12 +127,16 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
                     dma16(src, __builtin_amdgcn_readfirstlane(st + d * 1024));
                 }
             } else {
-                const int sm = d - C::NBIG;  // 256-B word copies: scale, then bias
-                const int part = sm % (C::BN / 64), which = sm / (C::BN / 64);
-                const int wr = w_row<EPI, C::BN>(nb, part * 64 + lane, N);
-                const bf16 *arr = which ? bias : scale;
-                dma4(arr + (size_t)wr * ng + (kt & ~1),
-                     __builtin_amdgcn_readfirstlane(st + C::A_BYTES + C::B_BYTES + sm * 256));
+                const int sm = d - C::NBIG;  // 256-B word copies: scale, then bias, then padding
+                if (C::PAD && sm >= C::NSMALL) {
+                    dma4(scale, __builtin_amdgcn_readfirstlane(lds0 + C::ST * C::STAGE));
+                } else {
+                    const int part = sm % (C::BN / 64), which = sm / (C::BN / 64);
+                    const int wr = w_row<EPI, C::BN>(nb, part * 64 + lane, N);
+                    const bf16 *arr = which ? bias : scale;
+                    dma4(arr + (size_t)wr * ng + (kt & ~1),
+                         __builtin_amdgcn_readfirstlane(st + C::A_BYTES + C::B_BYTES + sm * 256));
+                }
             }
         }
     };
@@ -287,6 +302,9 @@ typedef g2::Cfg<128, 64, 4, 2, 2, false> SmallN;   // 4 waves, 64 x 32 per wave,
 typedef g2::Cfg<64, 128, 4, 2, 2, false> SmallM;   // 4 waves, 32 x 64 per wave, 96 KB LDS
 typedef g2::Cfg<128, 128, 4, 2, 2, true> Quant;    // 4 waves, 100 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 2, true> QuantS;    // 4 waves, 68 KB LDS
+typedef g2::Cfg<128, 256, 3, 2, 4, true> QuantW;   // 8 waves, 64 x 64 per wave, 102 KB LDS
+typedef g2::Cfg<64, 128, 4, 2, 4, true> QuantS8;   // 8 waves, 32 x 32 per wave, 68 KB LDS
+typedef g2::Cfg<64, 64, 4, 2, 2, true> QuantT;     // 4 waves, 32 x 32 per wave, 50 KB LDS (3 blocks per CU)
 
 // Output tiles of a BM x BN weight-row tiling (a SWIGLU tile covers BN/2 outputs).
 template <class C> long tiles(int M, int N, int epi) {
@@ -299,7 +317,7 @@ hipError_t launch_c(const bf16 *x, int M, int K, const void *W, const bf16 *sc, 
                     bf16 *out, hipStream_t s) {
     const int cols = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;
     const dim3 grid((N + cols - 1) / cols, (M + C::BM - 1) / C::BM);
-    const size_t lds = (size_t)C::ST * C::STAGE;
+    const size_t lds = (size_t)C::LDS;
     static bool attr = false;  // more than the default 64 KB of dynamic LDS
     if (!attr) {
         const hipError_t e = hipFuncSetAttribute((const void *)gemm_mfma_kernel<EPI, C>,
@@ -315,6 +333,13 @@ template <class C>
 hipError_t launch_e(int epi, const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N,
                     const bf16 *r, bf16 *o, hipStream_t s) {
     if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, C>(x, M, K, W, sc, bi, N, r, o, s);
+    if (epi == EPI_RESID) return launch_c<EPI_RESID, C>(x, M, K, W, sc, bi, N, r, o, s);
+    return launch_c<EPI_STORE, C>(x, M, K, W, sc, bi, N, r, o, s);
+}
+// the store and residual epilogues only (tilings whose waves hold single 32-column tiles)
+template <class C>
+hipError_t launch_sr(int epi, const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N,
+                     const bf16 *r, bf16 *o, hipStream_t s) {
     if (epi == EPI_RESID) return launch_c<EPI_RESID, C>(x, M, K, W, sc, bi, N, r, o, s);
     return launch_c<EPI_STORE, C>(x, M, K, W, sc, bi, N, r, o, s);
 }
@@ -342,8 +367,15 @@ bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias) {
 hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                               int N, int epi, const void *res, void *out, hipStream_t s) {
     const bf16 *a = (const bf16 *)x, *sc = (const bf16 *)scale, *bi = (const bf16 *)bias, *r = (const bf16 *)res;
-    if (tiles<Quant>(M, N, epi) >= 192) return launch_e<Quant>(epi, a, M, K, codes, sc, bi, N, r, (bf16 *)out, s);
-    return launch_e<QuantS>(epi, a, M, K, codes, sc, bi, N, r, (bf16 *)out, s);
+    bf16 *o = (bf16 *)out;
+    if (epi == EPI_SWIGLU) {
+        if (tiles<QuantW>(M, N, epi) >= 192) return launch_c<EPI_SWIGLU, QuantW>(a, M, K, codes, sc, bi, N, r, o, s);
+        if (tiles<Quant>(M, N, epi) >= 192) return launch_c<EPI_SWIGLU, Quant>(a, M, K, codes, sc, bi, N, r, o, s);
+        return launch_c<EPI_SWIGLU, QuantS>(a, M, K, codes, sc, bi, N, r, o, s);
+    }
+    if (tiles<QuantW>(M, N, epi) >= 192) return launch_sr<QuantW>(epi, a, M, K, codes, sc, bi, N, r, o, s);
+    if (tiles<QuantS8>(M, N, epi) >= 192) return launch_sr<QuantS8>(epi, a, M, K, codes, sc, bi, N, r, o, s);
+    return launch_sr<QuantT>(epi, a, M, K, codes, sc, bi, N, r, o, s);
 }
 
 }  // namespace q3
