@@ -153,17 +153,25 @@ hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const v
 // inv_j = fp32(theta^(-2j/D)) (rounded to the storage type: the bf16 model holds
 // the inverse frequencies as a bf16 buffer); angle = fp32(p * inv_j);
 // value = rho(fp32(cos(angle))) from double-precision cos/sin of the fp32 angle.
+// The fp32 value is what gets rounded to the table type: without the empty asm the compiler
+// fuses "double -> fp32 -> bf16" into one rounding straight from double, which differs from
+// the two roundings on a few entries.
+__device__ __forceinline__ float pin_f32(float f) {
+    __asm__ volatile("" : "+v"(f));
+    return f;
+}
+
 template <typename T>
 __global__ void rope_table_kernel(int cap, int D, double theta, T *__restrict__ cos_t, T *__restrict__ sin_t) {
     const int half = D / 2;
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)cap * half) return;
     const int p = (int)(idx / half), j = (int)(idx % half);
-    float inv = (float)(1.0 / pow(theta, (2.0 * j) / (double)D));
+    float inv = pin_f32((float)(1.0 / pow(theta, (2.0 * j) / (double)D)));
     inv = rho<T>(inv);
     const float ang = (float)p * inv;
-    const T c = from_f<T>((float)cos((double)ang));
-    const T sn = from_f<T>((float)sin((double)ang));
+    const T c = from_f<T>(pin_f32((float)cos((double)ang)));
+    const T sn = from_f<T>(pin_f32((float)sin((double)ang)));
     cos_t[(size_t)p * D + j] = c;
     cos_t[(size_t)p * D + j + half] = c;
     sin_t[(size_t)p * D + j] = sn;
