@@ -10,7 +10,17 @@
 
 namespace q3 {
 
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+// What the fused q|k|v epilogue (EPI_QKV) needs besides the GEMM operands: per-head q/k RMSNorm
+// weights (both null: no q/k norm), q|k|v bias (or null), the RoPE table, the first position
+// p0 of the call, and the destinations: q [T][H][D], the layer's K and V caches [KV][cap][D].
+struct QkvEpi {
+    const void *q_norm = nullptr, *k_norm = nullptr, *bias = nullptr, *cos_t = nullptr, *sin_t = nullptr;
+    float eps = 0.f;
+    int H = 0, KV = 0, p0 = 0, cap = 0;
+    void *q_out = nullptr, *kc = nullptr, *vc = nullptr;
+};
 
 // out[t] = E[ids[t]] (ids outside [0, vocab) read row 0 and set *err).
 hipError_t launch_embed(int dt, const int32_t *ids, int T, const void *E, int vocab, int hid, void *out,
@@ -112,6 +122,10 @@ hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int 
 bool gemm_dma_ok(int M, int K, int N);
 hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, int epi, const void *res, void *out,
                            hipStream_t s);
+// q|k|v projection of T > 1 tokens with the per-head q/k RMSNorm, RoPE and K/V cache write in
+// the epilogue (bf16, head_dim 128): true when the tiling it needs fills the chip at this M.
+bool gemm_qkv_fused_ok(int M, int K, int H, int KV, int D);
+hipError_t launch_gemm_qkv_fused(const void *x, int M, int K, const void *W, const QkvEpi &qe, hipStream_t s);
 bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias);
 hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                               int N, int epi, const void *res, void *out, hipStream_t s);

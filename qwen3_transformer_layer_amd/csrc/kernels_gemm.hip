@@ -89,12 +89,128 @@ __device__ __forceinline__ void dma4(const void *g, unsigned lds) {
 
 }  // namespace g2
 
+// The q|k|v epilogue of "maya2_mlx/backbone.py" (forward: the fused projection, per-head
+// q/k RMSNorm with its two roundings, RoPE in fp32 on the table values with one rounding, the
+// cache write), for a tile of BN = 128 = head_dim columns, i.e. one head: tile nb is q head nb
+// (nb < H), k head nb - H, or v head nb - H - KV.  Each row's 128 columns sit in the two
+// waves wn = 0, 1 of the same wm (64 each), so the row's sum of squares and each RoPE pair
+// (c, c + 64) are completed through LDS with the partner wave.  With a bias (page 2's Qwen2
+// switch) every value is rho(rho(x W^T) + b) first.
+template <class C>
+__device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const QkvEpi &qe, unsigned char *smem, int M,
+                                             int m0, int nb, int wm, int wn, int wave, int lane) {
+    static_assert(C::BN == 128 && C::WN == 2 && C::NT == 2 && !C::Q8, "one head of 128 columns over two waves");
+    constexpr int RW = C::WTM;                  // rows per wave
+    constexpr int YP = 65;                      // padded row of the exchange buffer (fp32 words)
+    constexpr int Y_BYTES = C::NW * RW * YP * 4, RED = RW * 33;
+    static_assert(Y_BYTES + 2 * C::NW * RW * 4 <= C::ST * C::STAGE, "exchange buffers fit in the stages");
+    static_assert(C::NW * RED * 4 <= Y_BYTES, "row partials fit under the exchange buffer");
+    const int H = qe.H, KV = qe.KV;
+    const bool isq = nb < H, isv = nb >= H + KV;
+    const bf16 *bias = (const bf16 *)qe.bias;
+    auto row_of = [&](int i, int v) { return i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); };  // in the wave
+    auto col_of = [&](int j) { return wn * 64 + j * 32 + (lane & 31); };                          // in the head
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) {
+            const float b = bias ? to_f(bias[(size_t)nb * 128 + col_of(j)]) : 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float a = rho<bf16>(acc[i][j][v]);
+                if (bias) a = rho<bf16>(a + b);
+                acc[i][j][v] = a;
+            }
+        }
+    __syncthreads();  // every wave is done with the last K step's LDS stage
+    if (isv) {
+        bf16 *vc = (bf16 *)qe.vc + (size_t)(nb - H - KV) * qe.cap * 128;
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * RW + row_of(i, v);
+                if (row >= M) continue;
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j)
+                    vc[(size_t)(qe.p0 + row) * 128 + col_of(j)] = from_f<bf16>(acc[i][j][v]);
+            }
+        return;
+    }
+    float *ybuf = (float *)smem;                   // [NW][RW][YP]; first the row partials [NW][RW][33]
+    float *ssb = (float *)(smem + Y_BYTES);        // [NW][RW] half-row sums of squares
+    float *rb = ssb + C::NW * RW;                  // [NW][RW] 1 / rms of the wave's rows
+    const bf16 *nw = (const bf16 *)(isq ? qe.q_norm : qe.k_norm);
+    if (nw) {
+        float *red = ybuf + wave * RED;
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[row_of(i, v) * 33 + (lane & 31)] = acc[i][0][v] * acc[i][0][v] + acc[i][1][v] * acc[i][1][v];
+        // a wave's LDS accesses complete in order: lane r now sums row r of its own partials
+        if (lane < RW) {
+            float ss = 0.f;
+#pragma unroll
+            for (int t = 0; t < 32; ++t) ss += red[lane * 33 + t];
+            ssb[wave * RW + lane] = ss;
+        }
+        __syncthreads();
+        if (lane < RW) {
+            const int partner = wm * C::WN + (wn ^ 1);
+            const float ss = ssb[wave * RW + lane] + ssb[partner * RW + lane];
+            rb[wave * RW + lane] = 1.0f / sqrtf(ss / 128.0f + qe.eps);
+        }
+        float w[C::NT];
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) w[j] = to_f(nw[col_of(j)]);
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float r = rb[wave * RW + row_of(i, v)];
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) acc[i][j][v] = rho<bf16>(w[j] * rho<bf16>(acc[i][j][v] * r));
+            }
+        __syncthreads();  // the row partials under the exchange buffer are consumed
+    }
+    // RoPE pairs (c, c + 64): the partner wave holds the other half of each pair
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) ybuf[(wave * RW + row_of(i, v)) * YP + j * 32 + (lane & 31)] = acc[i][j][v];
+    __syncthreads();
+    const int partner = wm * C::WN + (wn ^ 1);
+    const bf16 *cs = (const bf16 *)qe.cos_t, *sn = (const bf16 *)qe.sin_t;
+    bf16 *dst = isq ? (bf16 *)qe.q_out : (bf16 *)qe.kc + (size_t)(nb - H) * qe.cap * 128;
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int rl = row_of(i, v), row = m0 + wm * RW + rl;
+            if (row >= M) continue;
+            const int p = qe.p0 + row;
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) {
+                const int c = col_of(j);
+                const float y = acc[i][j][v], yp = ybuf[(partner * RW + rl) * YP + j * 32 + (lane & 31)];
+                const float cv = to_f(cs[(size_t)p * 128 + c]), sv = to_f(sn[(size_t)p * 128 + c]);
+                const float o = wn == 0 ? y * cv - yp * sv : y * cv + yp * sv;
+                const size_t at = isq ? ((size_t)row * H + nb) * 128 + c : (size_t)p * 128 + c;
+                dst[at] = from_f<bf16>(o);
+            }
+        }
+}
+
 // W: bf16 weight rows, or (Q8) the u8 codes with their scale and bias arrays [rows][K/64].
 template <int EPI, class C>
 __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restrict__ A, int M, int K,
                                                           const void *__restrict__ W, const bf16 *__restrict__ scale,
                                                           const bf16 *__restrict__ bias, int N,
-                                                          const bf16 *__restrict__ res, bf16 *__restrict__ out) {
+                                                          const bf16 *__restrict__ res, bf16 *__restrict__ out,
+                                                          QkvEpi qe) {
     using namespace g2;
     static_assert(EPI != EPI_SWIGLU || C::NT % 2 == 0, "a SWIGLU wave holds gate and up tiles in pairs");
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -263,6 +379,10 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
         }
     }
 
+    if constexpr (EPI == EPI_QKV) {
+        qkv_epilogue<C>(acc, qe, smem, M, m0, nb, wm, wn, wave, lane);
+        return;
+    }
     // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
@@ -314,7 +434,7 @@ template <class C> long tiles(int M, int N, int epi) {
 
 template <int EPI, class C>
 hipError_t launch_c(const bf16 *x, int M, int K, const void *W, const bf16 *sc, const bf16 *bi, int N, const bf16 *res,
-                    bf16 *out, hipStream_t s) {
+                    bf16 *out, hipStream_t s, const QkvEpi &qe = QkvEpi()) {
     const int cols = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;
     const dim3 grid((N + cols - 1) / cols, (M + C::BM - 1) / C::BM);
     const size_t lds = (size_t)C::LDS;
@@ -325,7 +445,7 @@ hipError_t launch_c(const bf16 *x, int M, int K, const void *W, const bf16 *sc, 
         if (e != hipSuccess) return e;
         attr = true;
     }
-    gemm_mfma_kernel<EPI, C><<<grid, C::NTH, lds, s>>>(x, M, K, W, sc, bi, N, res, out);
+    gemm_mfma_kernel<EPI, C><<<grid, C::NTH, lds, s>>>(x, M, K, W, sc, bi, N, res, out, qe);
     return hipGetLastError();
 }
 
@@ -358,6 +478,15 @@ hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, in
     if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, SmallM>(a, M, K, W, nullptr, nullptr, N, r, o, s);
     if (epi == EPI_RESID) return launch_c<EPI_RESID, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
     return launch_c<EPI_STORE, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+}
+
+bool gemm_qkv_fused_ok(int M, int K, int H, int KV, int D) {
+    return D == 128 && gemm_dma_ok(M, K, (H + 2 * KV) * D) && tiles<Wide>(M, (H + 2 * KV) * D, EPI_STORE) >= 192;
+}
+
+hipError_t launch_gemm_qkv_fused(const void *x, int M, int K, const void *W, const QkvEpi &qe, hipStream_t s) {
+    const int N = (qe.H + 2 * qe.KV) * 128;
+    return launch_c<EPI_QKV, Wide>((const bf16 *)x, M, K, W, nullptr, nullptr, N, nullptr, nullptr, s, qe);
 }
 
 bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias) {

@@ -8,7 +8,8 @@
 //   layer l>0: h = rho(h + pend); y = RMSNorm(h)           add_rmsnorm (fused add; for T > 1 after a
 //                                                          dense MLP the add already ran in down)
 //              qkv = rho(y Wqkv^T)                         linear (GEMV / MFMA GEMM)
-//              q, K[p], V[p] = norm + RoPE + cache write    qknorm_rope_kv
+//              q, K[p], V[p] = norm + RoPE + cache write    qknorm_rope_kv (bf16, T large enough for
+//                                                          256 x 128 tiles: the projection's epilogue)
 //              a = attention(q, K[0..p], V[0..p])           split-K decode | flash prefill
 //              h = rho(h + rho(a Wo^T))                    linear, residual epilogue
 //              y2 = RMSNorm(h)                             add_rmsnorm
@@ -299,11 +300,31 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, L.in_norm,
                                             pend_live ? h->h : nullptr, h->y, T, hid, c.rms_eps, s));
         HIPCHECK(h, mark(h, K_QKV, true));
-        HIPCHECK(h, linear(h, h->y, T, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
-        HIPCHECK(h, mark(h, K_QKV, false));
-        HIPCHECK(h, launch_qknorm_rope_kv(dt, h->qkv, T, H, KV, D, L.q_norm, L.k_norm, L.qkv_bias, c.rms_eps, h->cos_t,
-                                          h->sin_t, p0, c.capacity, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv,
-                                          s));
+        if (dt == QWEN3_BF16 && !is_q8(h) && gemm_qkv_fused_ok(T, hid, H, KV, D)) {
+            // q/k norm, RoPE and the cache write in the projection's epilogue
+            QkvEpi qe;
+            qe.q_norm = L.q_norm;
+            qe.k_norm = L.k_norm;
+            qe.bias = L.qkv_bias;
+            qe.cos_t = h->cos_t;
+            qe.sin_t = h->sin_t;
+            qe.eps = c.rms_eps;
+            qe.H = H;
+            qe.KV = KV;
+            qe.p0 = p0;
+            qe.cap = c.capacity;
+            qe.q_out = h->q;
+            qe.kc = h->kc + l * layer_kv;
+            qe.vc = h->vc + l * layer_kv;
+            HIPCHECK(h, launch_gemm_qkv_fused(h->y, T, hid, L.qkv, qe, s));
+            HIPCHECK(h, mark(h, K_QKV, false));
+        } else {
+            HIPCHECK(h, linear(h, h->y, T, hid, L.qkv, L.qkv_s, L.qkv_b, nqkv, EPI_STORE, nullptr, h->qkv));
+            HIPCHECK(h, mark(h, K_QKV, false));
+            HIPCHECK(h, launch_qknorm_rope_kv(dt, h->qkv, T, H, KV, D, L.q_norm, L.k_norm, L.qkv_bias, c.rms_eps,
+                                              h->cos_t, h->sin_t, p0, c.capacity, h->q, h->kc + l * layer_kv,
+                                              h->vc + l * layer_kv, s));
+        }
         HIPCHECK(h, mark(h, K_ATTN, true));
         HIPCHECK(h, launch_attention(dt, h->q, h->kc + l * layer_kv, h->vc + l * layer_kv, T, H, KV, D, c.capacity, p0,
                                      c.sliding_window, h->a, h->attn_ws, 0, s));

@@ -84,6 +84,23 @@ def test_1p7b_prefill_window(orc, window):
     assert ek <= BF16_TOL
 
 
+@pytest.mark.parametrize("qk_norm,bias", [(True, False), (False, True), (True, True)])
+def test_1p7b_prefill_fused_qkv_epilogue(orc, qk_norm, bias):
+    """Two 1600-token prefill calls on the 1.7B attention shape, the second at p0 = 1600: both
+    take the q|k|v GEMM whose epilogue does the q/k norm, RoPE and K/V cache write (256 x 128
+    tiles, the last row tile ragged), with and without the q/k norm and bias; the MLP is
+    narrowed to keep the oracle quick."""
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_PREFILL
+    cfg = QWEN3_1P7B_PREFILL.replace(n_layers=1, qk_norm=qk_norm, attention_bias=bias, intermediate=512,
+                                     capacity=3200)
+    seat, st, got, ref = _run(orc, cfg, [1600, 1600])
+    e = gate(got, ref, "bf16")
+    ek = max_row_rel_l2(np32(seat.k)[0, :, :3200], st.k[0, :, :3200])
+    ev = max_row_rel_l2(np32(seat.v)[0, :, :3200], st.v[0, :, :3200])
+    say(f"1.7B fused q|k|v prefill qk_norm={qk_norm} bias={bias}: out {e:.2e}, K {ek:.2e}, V {ev:.2e}")
+    assert ek <= BF16_TOL and ev <= BF16_TOL and seat.length == 3200
+
+
 @pytest.mark.parametrize("qk_norm,bias,window", [(True, False, 1000), (False, True, 0), (False, True, 300)])
 def test_1p7b_decode_switches(orc, qk_norm, bias, window):
     """Decode at position 4095 (ctx 4096) on the kernel-per-step path (the persistent kernel
