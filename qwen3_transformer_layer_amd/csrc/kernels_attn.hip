@@ -640,14 +640,16 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
     }
     // merge the key parts of each head: parts 1..NP-1 hand over (m, l, O) through LDS
     __syncthreads();  // every wave is done with the K/V tiles
-    // part w's buffer: O as [dt][v][lane], then m[32], l[32]
+    // part w's buffer: O as [dt][v / 4][lane][v % 4] (16-byte accesses), then m[32], l[32]
     auto mbuf = [&](int w) { return (float *)(fa_smem + (hw * (F::NP - 1) + w - 1) * F::MERGE); };
     if (par > 0) {
         float *mb = mbuf(par);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mb[(dt * 16 + v) * 64 + lane] = o[dt][v];
+            for (int v4 = 0; v4 < 4; ++v4)
+                *(f32x4 *)&mb[((dt * 4 + v4) * 64 + lane) * 4] =
+                    f32x4{o[dt][4 * v4], o[dt][4 * v4 + 1], o[dt][4 * v4 + 2], o[dt][4 * v4 + 3]};
         if (lane < 32) {
             mb[D * 32 + lane] = m_run;
             mb[D * 32 + 32 + lane] = l_run;
@@ -671,13 +673,15 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
+                f32x4 part[F::NP - 1];
+#pragma unroll
+                for (int w = 1; w < F::NP; ++w) part[w - 1] = *(const f32x4 *)&mbuf(w)[((dt * 4 + v4) * 64 + lane) * 4];
                 float r[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * v4 + e;
-                    float t = o[dt][v] * a[0];
+                    float t = o[dt][4 * v4 + e] * a[0];
 #pragma unroll
-                    for (int w = 1; w < F::NP; ++w) t += mbuf(w)[(dt * 16 + v) * 64 + lane] * a[w];
+                    for (int w = 1; w < F::NP; ++w) t += part[w - 1][e] * a[w];
                     r[e] = t * inv;
                 }
                 uint2 w;

@@ -101,7 +101,7 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
                                              int m0, int nb, int wm, int wn, int wave, int lane) {
     static_assert(C::BN == 128 && C::WN == 2 && C::NT == 2 && !C::Q8, "one head of 128 columns over two waves");
     constexpr int RW = C::WTM;                  // rows per wave
-    constexpr int YP = 65;                      // padded row of the exchange buffer (fp32 words)
+    constexpr int YP = 68;                      // exchange-buffer row (fp32 words; 16-byte aligned)
     constexpr int Y_BYTES = C::NW * RW * YP * 4, RED = RW * 33;
     static_assert(Y_BYTES + 2 * C::NW * RW * 4 <= C::ST * C::STAGE, "exchange buffers fit in the stages");
     static_assert(C::NW * RED * 4 <= Y_BYTES, "row partials fit under the exchange buffer");
@@ -123,24 +123,10 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
             }
         }
     __syncthreads();  // every wave is done with the last K step's LDS stage
-    if (isv) {
-        bf16 *vc = (bf16 *)qe.vc + (size_t)(nb - H - KV) * qe.cap * 128;
-#pragma unroll
-        for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * RW + row_of(i, v);
-                if (row >= M) continue;
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j)
-                    vc[(size_t)(qe.p0 + row) * 128 + col_of(j)] = from_f<bf16>(acc[i][j][v]);
-            }
-        return;
-    }
     float *ybuf = (float *)smem;                   // [NW][RW][YP]; first the row partials [NW][RW][33]
     float *ssb = (float *)(smem + Y_BYTES);        // [NW][RW] half-row sums of squares
     float *rb = ssb + C::NW * RW;                  // [NW][RW] 1 / rms of the wave's rows
-    const bf16 *nw = (const bf16 *)(isq ? qe.q_norm : qe.k_norm);
+    const bf16 *nw = isv ? nullptr : (const bf16 *)(isq ? qe.q_norm : qe.k_norm);
     if (nw) {
         float *red = ybuf + wave * RED;
 #pragma unroll
@@ -174,7 +160,9 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
             }
         __syncthreads();  // the row partials under the exchange buffer are consumed
     }
-    // RoPE pairs (c, c + 64): the partner wave holds the other half of each pair
+    // The wave's values go to LDS in the accumulator layout and come back as 8 consecutive
+    // columns of one row per lane, so the RoPE table reads and the stores are 16 bytes wide; the
+    // partner wave's region holds the other half (c +- 64) of each RoPE pair.
 #pragma unroll
     for (int i = 0; i < C::NI; ++i)
 #pragma unroll
@@ -182,26 +170,36 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
 #pragma unroll
             for (int j = 0; j < C::NT; ++j) ybuf[(wave * RW + row_of(i, v)) * YP + j * 32 + (lane & 31)] = acc[i][j][v];
     __syncthreads();
-    const int partner = wm * C::WN + (wn ^ 1);
+    const int partner = wm * C::WN + (wn ^ 1), c8 = (lane & 7) * 8;
     const bf16 *cs = (const bf16 *)qe.cos_t, *sn = (const bf16 *)qe.sin_t;
-    bf16 *dst = isq ? (bf16 *)qe.q_out : (bf16 *)qe.kc + (size_t)(nb - H) * qe.cap * 128;
+    bf16 *dst = isq ? (bf16 *)qe.q_out
+                    : (bf16 *)(isv ? qe.vc : qe.kc) + (size_t)(nb - H - (isv ? KV : 0)) * qe.cap * 128;
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i)
+    for (int t = 0; t < RW / 8; ++t) {
+        const int rl = (lane >> 3) + 8 * t, row = m0 + wm * RW + rl;
+        if (row >= M) continue;
+        const int p = qe.p0 + row, c = wn * 64 + c8;
+        const f32x4 *yo = (const f32x4 *)&ybuf[(wave * RW + rl) * YP + c8];
+        float y[8], o[8];
+        *(f32x4 *)&y[0] = yo[0];
+        *(f32x4 *)&y[4] = yo[1];
+        if (isv) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rl = row_of(i, v), row = m0 + wm * RW + rl;
-            if (row >= M) continue;
-            const int p = qe.p0 + row;
+            for (int e = 0; e < 8; ++e) o[e] = y[e];
+        } else {
+            const f32x4 *yq = (const f32x4 *)&ybuf[(partner * RW + rl) * YP + c8];
+            float yp[8], cv[8], sv[8];
+            *(f32x4 *)&yp[0] = yq[0];
+            *(f32x4 *)&yp[4] = yq[1];
+            const u32x4 cw = ld16(cs + (size_t)p * 128 + c), sw = ld16(sn + (size_t)p * 128 + c);
+            Vec<bf16>::expand(cw, cv);
+            Vec<bf16>::expand(sw, sv);
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) {
-                const int c = col_of(j);
-                const float y = acc[i][j][v], yp = ybuf[(partner * RW + rl) * YP + j * 32 + (lane & 31)];
-                const float cv = to_f(cs[(size_t)p * 128 + c]), sv = to_f(sn[(size_t)p * 128 + c]);
-                const float o = wn == 0 ? y * cv - yp * sv : y * cv + yp * sv;
-                const size_t at = isq ? ((size_t)row * H + nb) * 128 + c : (size_t)p * 128 + c;
-                dst[at] = from_f<bf16>(o);
-            }
+            for (int e = 0; e < 8; ++e) o[e] = wn == 0 ? y[e] * cv[e] - yp[e] * sv[e] : y[e] * cv[e] + yp[e] * sv[e];
         }
+        const size_t at = isq ? ((size_t)row * H + nb) * 128 + c : (size_t)p * 128 + c;
+        *(u32x4 *)(dst + at) = u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
+    }
 }
 
 // W: bf16 weight rows, or (Q8) the u8 codes with their scale and bias arrays [rows][K/64].
