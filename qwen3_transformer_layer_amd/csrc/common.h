@@ -47,6 +47,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// a + w . x over one 16-byte piece of each (8 bf16 or 4 fp32 elements).  bf16 pairs go through
+// v_dot2c_f32_bf16 (the products are exact in fp32, the sum is accumulated in fp32); the words
+// are copied out of the vectors first (a bit cast applied to a vector element directly was
+// compiled as a read of element 0).
+template <typename T> __device__ __forceinline__ float dot16(u32x4 w, u32x4 x, float a);
+template <> __device__ __forceinline__ float dot16<bf16>(u32x4 w, u32x4 x, float a) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q], xq = x[q];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wq), __builtin_bit_cast(bf16x2, xq), a, false);
+    }
+    return a;
+}
+template <> __device__ __forceinline__ float dot16<float>(u32x4 w, u32x4 x, float a) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a += __uint_as_float(w[q]) * __uint_as_float(x[q]);
+    return a;
+}
+
 // 16-byte global loads: streamed (non-temporal) for weights read once, plain otherwise.
 __device__ __forceinline__ u32x4 ld_stream(const void *p) {
     return __builtin_nontemporal_load((const u32x4 *)p);

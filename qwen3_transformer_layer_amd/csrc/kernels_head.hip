@@ -73,17 +73,9 @@ __global__ void __launch_bounds__(256) head_kernel(const T *__restrict__ x, int 
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + 64 * u;
                 if (c < nc) {
-                    float wf[VN];
-                    Vec<T>::expand(wv[u], wf);
 #pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        if (m < M) {
-                            float xf[VN];
-                            Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)c * VN), xf);
-#pragma unroll
-                            for (int e = 0; e < VN; ++e) a[m] += wf[e] * xf[e];
-                        }
-                    }
+                    for (int m = 0; m < MR; ++m)
+                        if (m < M) a[m] = dot16<T>(wv[u], ld16(x + (size_t)m * K + (size_t)c * VN), a[m]);
                 }
             }
         }

@@ -58,37 +58,25 @@ __global__ void __launch_bounds__(256) gemv_kernel(const T *__restrict__ x, int 
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float wf0[VN], wf1[VN];
-            Vec<T>::expand(wv0[u], wf0);
-            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 if (m < M) {
-                    float xf[VN];
-                    Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)(c + 64 * u) * VN), xf);
-#pragma unroll
-                    for (int e = 0; e < VN; ++e) {
-                        a0[m] += wf0[e] * xf[e];
-                        if (EPI == EPI_SWIGLU) a1[m] += wf1[e] * xf[e];
-                    }
+                    const u32x4 xv = ld16(x + (size_t)m * K + (size_t)(c + 64 * u) * VN);
+                    a0[m] = dot16<T>(wv0[u], xv, a0[m]);
+                    if (EPI == EPI_SWIGLU) a1[m] = dot16<T>(wv1[u], xv, a1[m]);
                 }
             }
         }
     }
     for (; c < nc; c += 64) {
-        float wf0[VN], wf1[VN];
-        Vec<T>::expand(ld_stream(w0 + (size_t)c * VN), wf0);
-        if (EPI == EPI_SWIGLU) Vec<T>::expand(ld_stream(w1 + (size_t)c * VN), wf1);
+        const u32x4 wt0 = ld_stream(w0 + (size_t)c * VN);
+        const u32x4 wt1 = EPI == EPI_SWIGLU ? ld_stream(w1 + (size_t)c * VN) : wt0;
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m < M) {
-                float xf[VN];
-                Vec<T>::expand(ld16(x + (size_t)m * K + (size_t)c * VN), xf);
-#pragma unroll
-                for (int e = 0; e < VN; ++e) {
-                    a0[m] += wf0[e] * xf[e];
-                    if (EPI == EPI_SWIGLU) a1[m] += wf1[e] * xf[e];
-                }
+                const u32x4 xv = ld16(x + (size_t)m * K + (size_t)c * VN);
+                a0[m] = dot16<T>(wt0, xv, a0[m]);
+                if (EPI == EPI_SWIGLU) a1[m] = dot16<T>(wt1, xv, a1[m]);
             }
         }
     }
@@ -140,15 +128,9 @@ __global__ void __launch_bounds__(256) gemv_norm_kernel(const T *__restrict__ h_
     for (int u = 0; u < U; ++u) {
         const int c = lane + 64 * u;
         if (c < nc) {
-            float wf0[VN], wf1[VN], xf[VN];
-            Vec<T>::expand(wv0[u], wf0);
-            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
-            Vec<T>::expand(*(const u32x4 *)&ys[c * VN], xf);
-#pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                a0 += wf0[e] * xf[e];
-                if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
-            }
+            const u32x4 xv = *(const u32x4 *)&ys[c * VN];
+            a0 = dot16<T>(wv0[u], xv, a0);
+            if (EPI == EPI_SWIGLU) a1 = dot16<T>(wv1[u], xv, a1);
         }
     }
     int c = lane + 64 * U;
@@ -160,27 +142,15 @@ __global__ void __launch_bounds__(256) gemv_norm_kernel(const T *__restrict__ h_
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float wf0[VN], wf1[VN], xf[VN];
-            Vec<T>::expand(wv0[u], wf0);
-            if (EPI == EPI_SWIGLU) Vec<T>::expand(wv1[u], wf1);
-            Vec<T>::expand(*(const u32x4 *)&ys[(c + 64 * u) * VN], xf);
-#pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                a0 += wf0[e] * xf[e];
-                if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
-            }
+            const u32x4 xv = *(const u32x4 *)&ys[(c + 64 * u) * VN];
+            a0 = dot16<T>(wv0[u], xv, a0);
+            if (EPI == EPI_SWIGLU) a1 = dot16<T>(wv1[u], xv, a1);
         }
     }
     for (; c < nc; c += 64) {
-        float wf0[VN], wf1[VN], xf[VN];
-        Vec<T>::expand(ld_stream(w0 + (size_t)c * VN), wf0);
-        if (EPI == EPI_SWIGLU) Vec<T>::expand(ld_stream(w1 + (size_t)c * VN), wf1);
-        Vec<T>::expand(*(const u32x4 *)&ys[c * VN], xf);
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-            a0 += wf0[e] * xf[e];
-            if (EPI == EPI_SWIGLU) a1 += wf1[e] * xf[e];
-        }
+        const u32x4 xv = *(const u32x4 *)&ys[c * VN];
+        a0 = dot16<T>(ld_stream(w0 + (size_t)c * VN), xv, a0);
+        if (EPI == EPI_SWIGLU) a1 = dot16<T>(ld_stream(w1 + (size_t)c * VN), xv, a1);
     }
     const float s0 = wave_sum(a0);
     const float s1 = EPI == EPI_SWIGLU ? wave_sum(a1) : 0.f;

@@ -269,18 +269,15 @@ __global__ void __launch_bounds__(256) moe_expert_kernel(const T *__restrict__ x
 #pragma unroll
             for (int m = 0; m < MR; ++m) a[q][m] = 0.f;
         for (int c = lane; c < nc; c += 64) {
-            float wf[NR][VN];
+            u32x4 wv[NR];
 #pragma unroll
-            for (int q = 0; q < NR; ++q) Vec<T>::expand(ld_stream(wr[q] + (size_t)c * VN), wf[q]);
+            for (int q = 0; q < NR; ++q) wv[q] = ld_stream(wr[q] + (size_t)c * VN);
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 if (m < nr) {
-                    float xf[VN];
-                    Vec<T>::expand(ld16(xr[m] + (size_t)c * VN), xf);
+                    const u32x4 xv = ld16(xr[m] + (size_t)c * VN);
 #pragma unroll
-                    for (int q = 0; q < NR; ++q)
-#pragma unroll
-                        for (int x = 0; x < VN; ++x) a[q][m] += wf[q][x] * xf[x];
+                    for (int q = 0; q < NR; ++q) a[q][m] = dot16<T>(wv[q], xv, a[q][m]);
                 }
             }
         }
@@ -564,15 +561,9 @@ __device__ __forceinline__ void rows_dot(const T *const (&w)[NR], const T *x, in
         for (int u = 0; u < U; ++u) {
             const int c = c0 + lane + 64 * u;
             if (c < nc) {
-                float xf[VN];
-                Vec<T>::expand(ld16(x + (size_t)c * VN), xf);
+                const u32x4 xv = ld16(x + (size_t)c * VN);
 #pragma unroll
-                for (int q = 0; q < NR; ++q) {
-                    float wf[VN];
-                    Vec<T>::expand(wv[u][q], wf);
-#pragma unroll
-                    for (int i = 0; i < VN; ++i) acc[q] += wf[i] * xf[i];
-                }
+                for (int q = 0; q < NR; ++q) acc[q] = dot16<T>(wv[u][q], xv, acc[q]);
             }
         }
     }
