@@ -501,11 +501,18 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         if (nK > 0) {
             // scores; K chunk i holds keys j0 + KPC*i ..; the lane's piece k is key 4k + kslot,
             // dims sub*8 .. sub*8+7
-            float qf[G][8];
+            // q and the new key are bf16 values (rounded after RoPE), so packing them is exact and
+            // each 8-dim piece of a score is four v_dot2c_f32_bf16
+            u32x4 qp[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[h][e] = qs[h * D + sub * 8 + e];
+            for (int h = 0; h < G; ++h) {
+                const float *qh = qs + h * D + sub * 8;
+                qp[h] = u32x4{pack_bf2(qh[0], qh[1]), pack_bf2(qh[2], qh[3]), pack_bf2(qh[4], qh[5]),
+                              pack_bf2(qh[6], qh[7])};
+            }
+            const float *kn = kvs + sub * 8;
+            const u32x4 knew = {pack_bf2(kn[0], kn[1]), pack_bf2(kn[2], kn[3]), pack_bf2(kn[4], kn[5]),
+                                pack_bf2(kn[6], kn[7])};
             for (int i = wave; i < nK; i += NC) {
                 const unsigned g = gb + S.oK() + i;
                 const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
@@ -515,17 +522,10 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int j = j0 + i * KPC + 4 * k + kslot;
-                    float kf[8];
-                    Vec<bf16>::expand(kr[k], kf);
-                    if (j == jspec) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) kf[e] = kvs[sub * 8 + e];
-                    }
+                    const u32x4 kw = j == jspec ? knew : kr[k];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        float s = 0.f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) s += qf[h][e] * kf[e];
+                        float s = dot16<bf16>(qp[h], kw, 0.f);
                         s = row16_sum(s);  // the key's 16 lanes form one DPP row
                         if (sub == 0 && j < j1) sc[h * CHUNK_MAX + (j - j0)] = s * A.scale;
                     }
