@@ -97,6 +97,12 @@ __global__ void __launch_bounds__(256) add_rmsnorm_reg_kernel(const T *__restric
     const int nc = n / VN;
     float v[MAXC][VN];
     float ss = 0.f;
+    u32x4 wraw[MAXC];  // the norm weights are loaded with h, not after the reduction
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < nc) wraw[i] = ld16(w + (size_t)c * VN);
+    }
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int c = threadIdx.x + 256 * i;
@@ -119,7 +125,7 @@ __global__ void __launch_bounds__(256) add_rmsnorm_reg_kernel(const T *__restric
         const int c = threadIdx.x + 256 * i;
         if (c < nc) {
             float wv[VN], o[VN];
-            Vec<T>::expand(ld16(w + (size_t)c * VN), wv);
+            Vec<T>::expand(wraw[i], wv);
 #pragma unroll
             for (int e = 0; e < VN; ++e) o[e] = wv[e] * rho<T>(v[i][e] * r);
             store_vec<T>(y + row * n + (size_t)c * VN, o);

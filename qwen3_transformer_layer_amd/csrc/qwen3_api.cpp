@@ -300,7 +300,9 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, L.in_norm,
                                             pend_live ? h->h : nullptr, h->y, T, hid, c.rms_eps, s));
         HIPCHECK(h, mark(h, K_QKV, true));
-        if (dt == QWEN3_BF16 && !is_q8(h) && gemm_qkv_fused_ok(T, hid, H, KV, D)) {
+        const bool al16 = ((uintptr_t)h->cos_t | (uintptr_t)h->sin_t | (uintptr_t)h->q | (uintptr_t)h->kc |
+                           (uintptr_t)h->vc) % 16 == 0;  // the fused epilogue reads and writes 16 bytes at a time
+        if (dt == QWEN3_BF16 && !is_q8(h) && al16 && gemm_qkv_fused_ok(T, hid, H, KV, D)) {
             // q/k norm, RoPE and the cache write in the projection's epilogue
             QkvEpi qe;
             qe.q_norm = L.q_norm;
