@@ -71,13 +71,13 @@ constexpr long LSPIN = 1L << 22;     // LDS wait rounds before a waiter gives up
 static_assert(NS >= NL * DL, "the ring holds every stream wave's chunks in flight");
 static_assert(4 * (DL - 1) <= 63, "vector-memory counter range");
 
-struct DevLayer {
-    const bf16 *in_norm, *post_norm, *q_norm, *k_norm, *qkv, *o, *gu, *down;
+struct DevLayer {  // q_norm / k_norm both null: no per-head q/k norm; qkv_bias null: no bias
+    const bf16 *in_norm, *post_norm, *q_norm, *k_norm, *qkv, *o, *gu, *down, *qkv_bias;
 };
 
 struct Args {
     const DevLayer *layers;
-    int n_layers, H, KV, cap, p, nsplit, chunk;
+    int n_layers, H, KV, cap, p, nsplit, chunk, window;  // window 0: causal
     float eps, scale;
     const bf16 *x, *final_norm, *cos_t, *sin_t;
     bf16 *out, *kc, *vc;
@@ -360,7 +360,8 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     const int p = A.p, nkeys = p + 1;
     const int bpg = NB / KV;               // attention blocks per kv head (= splits)
     const int ag = b / bpg, as = b % bpg;  // this block's (kv head, split)
-    const int j0 = as * A.chunk, j1 = min(nkeys, j0 + A.chunk);
+    const int lo = A.window > 0 ? max(0, nkeys - A.window) : 0;  // first visible key (sliding window)
+    const int j0 = lo + as * A.chunk, j1 = min(nkeys, j0 + A.chunk);
     const int nK = j0 < j1 ? (j1 - j0 + KPC - 1) / KPC : 0;
     const bool has_p = j0 < nkeys && j1 == nkeys;
     const Seq<QPB, GPB, DCH> S(nK);
@@ -404,10 +405,12 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             w_in[k] = to_f(opaque(L.in_norm)[tid + NCT * k]);
             w_post[k] = to_f(opaque(L.post_norm)[tid + NCT * k]);
         }
-        w_qn[0] = to_f(opaque(L.q_norm)[lane]);
-        w_qn[1] = to_f(opaque(L.q_norm)[lane + half]);
-        w_kn[0] = to_f(opaque(L.k_norm)[lane]);
-        w_kn[1] = to_f(opaque(L.k_norm)[lane + half]);
+        if (L.q_norm) {
+            w_qn[0] = to_f(opaque(L.q_norm)[lane]);
+            w_qn[1] = to_f(opaque(L.q_norm)[lane + half]);
+            w_kn[0] = to_f(opaque(L.k_norm)[lane]);
+            w_kn[1] = to_f(opaque(L.k_norm)[lane + half]);
+        }
     };
     load_small(0);
 
@@ -446,8 +449,11 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         for (int i = wave; i < QPB; i += NC) {
             const unsigned g = gb + i;
             const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
-            const float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
+            float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
             chunk_put(done, g, lane);
+            // a q|k|v bias is its own rounded add after the projection: rho(rho(x W^T) + b)
+            const bf16 *qb = lay[l].qkv_bias;
+            if (qb) acc = rho<bf16>(acc) + to_f(opaque(qb)[(size_t)b * QPB + i]);
             if (lane == 0) xstore(opaque(A.x_qkv) + (size_t)b * QPB + i, tagw(tag, acc));
         }
 
@@ -477,10 +483,13 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             const bool is_q = hh < G;
             const uint16_t *row = qraw + hh * D;
             const float x1 = bfv(row[lane]), x2 = bfv(row[lane + half]);
-            const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + A.eps);
-            const float wn1 = is_q ? w_qn[0] : w_kn[0], wn2 = is_q ? w_qn[1] : w_kn[1];
-            const float n1 = rho<bf16>(wn1 * rho<bf16>(x1 * r));
-            const float n2 = rho<bf16>(wn2 * rho<bf16>(x2 * r));
+            float n1 = x1, n2 = x2;  // without the per-head norm RoPE takes the projection as it is
+            if (lay[l].q_norm) {
+                const float r = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + A.eps);
+                const float wn1 = is_q ? w_qn[0] : w_kn[0], wn2 = is_q ? w_qn[1] : w_kn[1];
+                n1 = rho<bf16>(wn1 * rho<bf16>(x1 * r));
+                n2 = rho<bf16>(wn2 * rho<bf16>(x2 * r));
+            }
             const float o1 = rho<bf16>(n1 * c1 - n2 * s1), o2 = rho<bf16>(n2 * c2 + n1 * s2);
             if (is_q) {
                 qs[hh * D + lane] = o1;
@@ -822,14 +831,16 @@ hipError_t decode_mk_init(void *ws, int n_layers, int H, int KV, int hid, int I,
     return hipStreamSynchronize(s);  // layer_ptrs is a caller's host array
 }
 
-hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, int cap, int p, float eps,
-                            const void *x, void *out, const void *final_norm, const void *cos_t, const void *sin_t,
-                            void *kc, void *vc, int *err, hipStream_t s) {
+hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, int cap, int p, int window,
+                            float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
+                            const void *sin_t, void *kc, void *vc, int *err, hipStream_t s) {
     const MkLayout L = mk_layout(n_layers, H, KV, hid, I);
     char *b = (char *)ws;
     const int nsplit = mk::NB / KV;
     const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
-    if (!fn || p < 0 || p >= cap || n_layers < 1 || n_layers > mk::MAXL || mk_chunk(p + 1, nsplit) > mk::CHUNK_MAX)
+    const int nvis = window > 0 ? min(p + 1, window) : p + 1;  // keys the new token sees
+    if (!fn || p < 0 || p >= cap || window < 0 || n_layers < 1 || n_layers > mk::MAXL ||
+        mk_chunk(nvis, nsplit) > mk::CHUNK_MAX)
         return hipErrorInvalidValue;
     mk::Args A;
     A.layers = (const mk::DevLayer *)(b + L.layers);
@@ -839,7 +850,8 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
     A.cap = cap;
     A.p = p;
     A.nsplit = nsplit;
-    A.chunk = mk_chunk(p + 1, nsplit);
+    A.chunk = mk_chunk(nvis, nsplit);
+    A.window = window;
     A.eps = eps;
     A.scale = (float)(1.0 / sqrt((double)mk::D));
     A.x = (const bf16 *)x;

@@ -235,8 +235,8 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
     if (h->mk_ready && h->decode_path != 1) {
         HIPCHECK(h, mark(h, K_STEP, true));
         HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate,
-                                     c.capacity, h->length, c.rms_eps, x, out, h->final_norm, h->cos_t, h->sin_t, h->kc,
-                                     h->vc, h->dev_err, h->stream));
+                                     c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
+                                     h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
         HIPCHECK(h, mark(h, K_STEP, false));
         return QWEN3_OK;
     }
@@ -525,17 +525,16 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
                                   (void *)h->sin_t, h->stream);
         }
     }
-    bool qwen3_layers = cfg->sliding_window == 0;  // the persistent kernel: causal, q/k norm, no bias
-    for (int l = 0; l < cfg->n_layers; ++l) qwen3_layers = qwen3_layers && w->layers[l].q_norm && !w->layers[l].qkv_bias;
-    if (e == hipSuccess && qwen3_layers && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
+    if (e == hipSuccess && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
                                                cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->intermediate,
                                                cfg->capacity) &&
         decode_mk_max_blocks(cfg->hidden, cfg->intermediate, cfg->n_heads, cfg->n_kv_heads) >= decode_mk_blocks()) {
         std::vector<const void *> ptrs;
         for (int l = 0; l < cfg->n_layers; ++l) {
             const qwen3_layer_weights &Lw = w->layers[l];
-            const void *row[8] = {Lw.in_norm, Lw.post_norm, Lw.q_norm, Lw.k_norm, Lw.qkv, Lw.o, Lw.gate_up, Lw.down};
-            ptrs.insert(ptrs.end(), row, row + 8);
+            const void *row[9] = {Lw.in_norm,  Lw.post_norm, Lw.q_norm, Lw.k_norm,  Lw.qkv,
+                                  Lw.o,        Lw.gate_up,   Lw.down,   Lw.qkv_bias};
+            ptrs.insert(ptrs.end(), row, row + 9);
         }
         h->mk_ws = b + L.mk;
         e = decode_mk_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, cfg->hidden, cfg->intermediate,

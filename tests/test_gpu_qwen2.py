@@ -101,23 +101,28 @@ def test_1p7b_prefill_fused_qkv_epilogue(orc, qk_norm, bias):
     assert ek <= BF16_TOL and ev <= BF16_TOL and seat.length == 3200
 
 
+@pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("qk_norm,bias,window", [(True, False, 1000), (False, True, 0), (False, True, 300)])
-def test_1p7b_decode_switches(orc, qk_norm, bias, window):
-    """Decode at position 4095 (ctx 4096) on the kernel-per-step path (the persistent kernel
-    runs only the causal, normed, bias-free layer), then a 64-token chunk at p0 = 4096."""
+def test_1p7b_decode_switches(orc, qk_norm, bias, window, path):
+    """Decode at position 4095 (ctx 4096) on the kernel-per-step path (1) and on the persistent
+    kernel (2: bias as its own rounded add, no q/k norm, attention splits over the window's
+    keys), then a 64-token chunk at p0 = 4096."""
     import qwen3_transformer_layer_amd as q3
     from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE
     cfg = QWEN3_1P7B_DECODE.replace(n_layers=1, qk_norm=qk_norm, attention_bias=bias, sliding_window=window,
                                     capacity=4160)
-    seat, st, got, ref = _run(orc, cfg, [1, 64], filled=4095)
-    assert q3.qwen3_get_decode_path(seat.handle) == 1
+    seat, st, got, ref = _run(orc, cfg, [1, 64], filled=4095, path=path)
+    assert q3.qwen3_get_decode_path(seat.handle) == path
+    q3.qwen3_check_device_errors(seat.handle)
     e1 = gate(got[:1], ref[:1], "bf16")
     e2 = gate(got[1:], ref[1:], "bf16")
     say(f"1.7B decode qk_norm={qk_norm} bias={bias} window={window}: decode {e1:.2e}, chunk {e2:.2e}")
 
 
-def test_window_wider_than_capacity_is_causal_bitwise():
-    """sliding_window >= capacity changes nothing: identical outputs and caches."""
+@pytest.mark.parametrize("path", [1, 2])
+def test_window_wider_than_capacity_is_causal_bitwise(path):
+    """sliding_window >= capacity changes nothing: identical outputs and caches, on either decode
+    path."""
     import qwen3_transformer_layer_amd as q3
     from qwen3_transformer_layer_amd import synth
     from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE
@@ -126,7 +131,8 @@ def test_window_wider_than_capacity_is_causal_bitwise():
     w = synth.model_weights(base, DEV)
     a = q3.Seat(base, w, max_tokens=100)
     b = q3.Seat(wide, w, max_tokens=100)
-    q3.qwen3_set_decode_path(a.handle, 1)
+    q3.qwen3_set_decode_path(a.handle, path)
+    q3.qwen3_set_decode_path(b.handle, path)
     x = synth.hidden_states(base, 103, DEV)
     ga = torch.cat([a.forward_hidden(x[:100])] + [a.forward_hidden(x[100 + i:101 + i]) for i in range(3)])
     gb = torch.cat([b.forward_hidden(x[:100])] + [b.forward_hidden(x[100 + i:101 + i]) for i in range(3)])
