@@ -34,6 +34,8 @@
 //    through fp32).  Per group the MFMAs form P = x . q, and one more MFMA against a ones
 //    operand forms S = sum of x over the group in the same register layout; the group then
 //    folds as acc += s * P + b * S (the same sum regrouped, all fp32).
+//  - EPI_QKV (bf16, 256 x 128 tiles: one head of 128 columns per tile): the q|k|v projection
+//    with the per-head q/k RMSNorm, RoPE and the K/V cache write in the epilogue (qkv_epilogue).
 //  - Rows past M and weight rows past N are clamped to the last valid row on load and
 //    skipped on store.  K must be a multiple of 64 (of 128 for 8-bit weights).
 #include "common.h"
