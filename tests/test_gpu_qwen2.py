@@ -119,6 +119,20 @@ def test_1p7b_decode_switches(orc, qk_norm, bias, window, path):
     say(f"1.7B decode qk_norm={qk_norm} bias={bias} window={window}: decode {e1:.2e}, chunk {e2:.2e}")
 
 
+@pytest.mark.parametrize("window,filled", [(1, 0), (1, 4095), (7, 3), (7, 40), (300, 299), (300, 300), (5000, 4095)])
+def test_persistent_decode_window_edges(orc, window, filled):
+    """The persistent kernel's window bounds at one decode step: a window of one key, windows
+    just wider and just narrower than p + 1, one wider than the context, and position 0."""
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE
+    cfg = QWEN3_1P7B_DECODE.replace(n_layers=1, sliding_window=window, capacity=4096)
+    seat, st, got, ref = _run(orc, cfg, [1], filled=filled, path=2)
+    assert q3.qwen3_get_decode_path(seat.handle) == 2
+    q3.qwen3_check_device_errors(seat.handle)
+    e = gate(got, ref, "bf16")
+    say(f"persistent decode window={window} at position {filled}: {e:.2e}")
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_window_wider_than_capacity_is_causal_bitwise(path):
     """sliding_window >= capacity changes nothing: identical outputs and caches, on either decode
