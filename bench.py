@@ -525,7 +525,7 @@ def main():
                     help="run a 1 GiB device copy first (hardware-counter scale for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import torch
