@@ -157,6 +157,43 @@ __device__ __forceinline__ void poll_bf16(const uint32_t *src, int n, unsigned t
     }
 }
 
+// The SwiGLU output travels as one 64-bit word per (block, wave): tag << 48 | three bf16
+// values, those of the wave's gate|up pairs w, w + NC, w + 2 NC (2048 words instead of 6144,
+// four polls per thread instead of twelve).  Word u = block * NC + wave; its values go to
+// dst[block * GPB + wave + NC * j].
+template <int NPT, int GPB>
+__device__ __forceinline__ void poll_m3(const uint64_t *src, int nw, unsigned tag, uint16_t *dst, int *err,
+                                        unsigned *abt, int tid) {
+    uint64_t v[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int t = tid + NCT * k;
+        v[k] = t < nw ? xload64(src + t) : ((uint64_t)tag << 48);
+    }
+    long s = 0;
+    while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) ok &= (unsigned)(v[k] >> 48) == tag;
+        if (ok) break;
+        if (spin_out(++s, err, abt)) break;
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int t = tid + NCT * k;
+            if ((unsigned)(v[k] >> 48) != tag) v[k] = xload64(src + t);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int t = tid + NCT * k;
+        if (t < nw) {
+            const int bb = t / NC, w = t % NC;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) dst[bb * GPB + w + NC * j] = (uint16_t)(v[k] >> (16 * j));
+        }
+    }
+}
+
 // ---------------------------------------------------------------- LDS handshakes
 __device__ __forceinline__ unsigned lds_acquire(const unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -338,7 +375,7 @@ __device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const De
 template <int QPB, int GPB, int DCH, int G>
 __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     constexpr int IM = GPB * NB;
-    constexpr int HPT = HID / NCT, IPT = IM / NCT;  // words per compute thread of a hidden / intermediate vector
+    constexpr int HPT = HID / NCT;  // words per compute thread of a hidden vector
     constexpr int OPB = HID / NB;
     constexpr int RSH = rep_stride(HID), RSM = rep_stride(IM);
     static_assert(IM * 2 == DCH * CHB && HID % NCT == 0 && IM % NCT == 0 && OPB == NC, "shape");
@@ -705,6 +742,8 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         if (l + 1 < A.n_layers) load_small(l + 1);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         const X4 xg = load_x(ys, lane);
+        static_assert(GPB == 3 * NC, "three SwiGLU outputs per wave, packed into one exchange word");
+        uint64_t mword = (uint64_t)tag << 48;
         for (int i = wave; i < GPB; i += NC) {
             const unsigned g = gb + S.oG() + 2 * i;
             const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
@@ -713,14 +752,16 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             const unsigned char *cu = chunk_get(ring, ready, g + 1, &abt, opaque(A.err));
             const float us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
             chunk_put(done, g + 1, lane);
-            if (lane < NREP)
-                xstore(opaque(A.x_m) + lane * RSM + b * GPB + i,
-                       tagw(tag, rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us)));
+            const float mv = rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us);
+            mword |= (uint64_t)f2bf_bits(mv) << (16 * ((i - wave) / NC));
         }
+        if (lane < NREP) xstore64((uint64_t *)opaque(A.x_m) + lane * (RSM / 2) + b * NC + wave, mword);
 
         // ---------------- step 6: pend = rho(m . Wdown^T) for this wave's row
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // ys (y2) fully consumed before it receives m
-        poll_bf16<IPT>(opaque(A.x_m) + (b % NREP) * RSM, IM, tag, ys, opaque(A.err), &abt, tid);
+        static_assert(RSM % 2 == 0 && NB * NC % NCT == 0, "packed SwiGLU words: replica spacing, words per thread");
+        poll_m3<NB * NC / NCT, GPB>((const uint64_t *)opaque(A.x_m) + (b % NREP) * (RSM / 2), NB * NC, tag, ys,
+                                    opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         {
             float a = 0.f;
