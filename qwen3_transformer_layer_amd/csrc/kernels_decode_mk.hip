@@ -62,7 +62,9 @@ constexpr int MAXL = 63;             // layers (tags are call * 64 + layer)
 // Every block reads the whole of each exchanged vector.  Read from one copy, 256 blocks
 // would poll the same few KB, which sit in a few memory channels; producers therefore write
 // NREP copies, spaced so they fall in different channels, and block b reads copy b % NREP.
-constexpr int NREP = 8;
+// Each copy costs the producers a store per value: on the 1.7B shape 4 copies beat 1, 2, 8
+// and 16 (ms per step 1.004, 0.982, 0.977, 0.992, 1.048 for 1, 2, 4, 8, 16 on one box).
+constexpr int NREP = 4;
 __host__ __device__ constexpr int rep_stride(int words) {  // words between copies
     return ((words * 4 + 4095) / 4096 * 4096 + 1280) / 4;
 }
