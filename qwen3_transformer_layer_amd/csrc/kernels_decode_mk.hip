@@ -48,7 +48,8 @@ namespace mk {
 constexpr int NB = 256;              // blocks, one per CU
 constexpr int NC = 8;                // compute waves per block
 // 3 stream waves with 3 chunks in flight each beat 2 x 4 (the earlier choice), 3 x 4, 4 x 3 and
-// 4 x 4 on the 1.7B shape (ms per step 0.911 against 0.960, 0.939, 0.965, 0.965 on one box)
+// 4 x 4 on the 1.7B shape (ms per step 0.911 against 0.960, 0.939, 0.965, 0.965 on one box), and
+// 3 x 2, 4 x 2 (0.916 against 0.929, 0.947 on another)
 constexpr int NL = 3;                // stream waves per block
 constexpr int NCT = 64 * NC;         // compute threads
 constexpr int NTH = 64 * (NC + NL);  // threads per block
