@@ -132,17 +132,26 @@ def decode_bench(steps: int, warmup: int, compare: bool = True):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             step()
-        for _ in range(warmup):
-            graph.replay()
+        with torch.cuda.stream(stream):  # replays launch on the current stream
+            for _ in range(warmup):
+                graph.replay()
         torch.cuda.synchronize()
+        # timed region: K replays of the captured step on `stream`, bracketed by device
+        # synchronisation (wall clock) and by HIP events recorded on the same stream
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for _ in range(steps):
-            graph.replay()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            ev1.record(stream)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
+        ev_us = ev0.elapsed_time(ev1) * 1e3 / steps
+        q3.qwen3_check_device_errors(seat.handle)
         del graph
-        # eager pass with the timer on the dominant kernel: the whole-step kernel on the
-        # persistent path, the gate|up projection otherwise
+        # eager pass with the library's own per-launch timer on the dominant kernel: the
+        # whole-step kernel on the persistent path, the gate|up projection otherwise
         kind = 5 if used == 2 else 2
         L.qwen3_kernel_timer(seat.handle.ptr, kind, 1)
         t0 = time.perf_counter()
@@ -156,11 +165,11 @@ def decode_bench(steps: int, warmup: int, compare: bool = True):
         L.qwen3_kernel_timer(seat.handle.ptr, kind, 0)
         q3.qwen3_check_device_errors(seat.handle)
         k_us = tot.value * 1e3 / max(cnt.value, 1)
-        log(f"decode path {used}: graph {dt * 1e6:.1f} us/step, eager {dt_eager * 1e6:.1f} us/step, "
-            f"timed kernel {k_us:.2f} us/launch over {cnt.value} launches")
+        log(f"decode path {used}: graph {dt * 1e6:.1f} us/step (events on the stream {ev_us:.1f} us per replay), "
+            f"eager {dt_eager * 1e6:.1f} us/step, timed kernel {k_us:.2f} us/launch over {cnt.value} launches")
         return {"path": used, "ms_per_step": dt * 1e3, "eager_ms_per_step": dt_eager * 1e3,
-                "tokens_per_s": 1.0 / dt, "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "kernel_us": k_us,
-                "launches": cnt.value}
+                "tokens_per_s": 1.0 / dt, "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "replay_event_us": ev_us,
+                "eager_kernel_us": k_us, "launches": cnt.value}
 
     res = run(0)
     res["kernels_path"] = run(1) if res["path"] == 2 and compare else None
@@ -473,36 +482,72 @@ def head_bench(steps: int, warmup: int):
     return res
 
 
-def cpu_baseline(sample_layers: int = 4):
-    """The oracle on the host: a decode step of the same shape over `sample_layers` layers
-    (same per-layer work as the 28-layer step), scaled to a 28-layer step."""
+def cpu_baseline():
+    """The oracle (plain C++, OpenMP over output rows and heads) on the host cores, on the same
+    workloads as the GPU legs, as planned for the reported CPU baseline:
+    - the full 28-layer ctx-4096 T=1 decode step at position 4095 (median of 3 with every
+      core, plus one run on a single thread): this is `value`, in decode tokens/s;
+    - one layer of the 2048-token causal prefill (measured once with every core); the
+      28-layer figure is that time x 28 and is labelled extrapolated.
+    Inputs are host copies of the same seeded tensors the GPU legs use."""
     import numpy as np
-    import torch
 
     import oracle
     from qwen3_transformer_layer_amd import synth
-    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE, QWEN3_1P7B_PREFILL
 
     cores = len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
-    cfg = QWEN3_1P7B_DECODE.replace(n_layers=sample_layers)
+    cfg = QWEN3_1P7B_DECODE
+    log(f"cpu baseline: oracle on {cores} host cores, 28-layer decode step")
     w = synth.model_weights(cfg, "cuda")
     K, V = synth.kv_cache(cfg, 4095, "cuda")
     layers = [{k: v.float().cpu().numpy() for k, v in L.items()} for L in w["layers"]]
     st = oracle.Stack(cfg, layers, w["final_norm"].float().cpu().numpy(), "bf16", kcache=K.float().cpu().numpy(),
                       vcache=V.float().cpu().numpy())
+    del w, K, V
     x = synth.hidden_states(cfg, 1, "cuda").float().cpu().numpy()
-    times = []
-    for _ in range(3):
+
+    def step():
         st.length = 4095
         t0 = time.perf_counter()
         st.forward(x)
-        times.append(time.perf_counter() - t0)
-    t_layer = float(np.median(times)) / sample_layers
-    t_step = t_layer * 28
-    return {"value": 1.0 / t_step, "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
-            "sample": f"{sample_layers} of 28 layers of the ctx-4096 T=1 decode step, median of 3, "
-                      f"scaled x{28 / sample_layers:g} to a full step ({t_step * 1e3:.1f} ms/step)"}
+        return time.perf_counter() - t0
+
+    t_all = float(np.median([step() for _ in range(3)]))
+    oracle.set_threads(1)
+    t_one = step()
+    oracle.set_threads(cores)
+    del st, layers
+    log(f"cpu baseline: decode step {t_all * 1e3:.1f} ms ({cores} threads), {t_one * 1e3:.1f} ms (1 thread); "
+        "one prefill layer at T=2048")
+    pcfg = QWEN3_1P7B_PREFILL.replace(n_layers=1, capacity=PREFILL_T)
+    wp = synth.model_weights(pcfg, "cuda")
+    lp = [{k: v.float().cpu().numpy() for k, v in L.items()} for L in wp["layers"]]
+    sp = oracle.Stack(pcfg, lp, wp["final_norm"].float().cpu().numpy(), "bf16")
+    xp = synth.hidden_states(QWEN3_1P7B_PREFILL, PREFILL_T, "cuda").float().cpu().numpy()
+    del wp
+    t0 = time.perf_counter()
+    sp.forward(xp)
+    t_pre = time.perf_counter() - t0
+    layer_flops = PREFILL_FLOPS / 28
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    log(f"cpu baseline: prefill layer {t_pre:.2f} s")
+    return {"value": round(1.0 / t_all, 3), "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"full 28-layer ctx-4096 T=1 decode step at position 4095, median of 3 "
+                      f"({t_all * 1e3:.1f} ms/step); plus one layer of the 2048-token prefill",
+            "cpu_model": cpu_model,
+            "decode_ms_per_step": round(t_all * 1e3, 2),
+            "decode_ms_per_step_1_thread": round(t_one * 1e3, 2),
+            "decode_tokens_per_s_1_thread": round(1.0 / t_one, 3),
+            "prefill_layer_s_measured": round(t_pre, 3),
+            "prefill_layer_gflops": round(layer_flops / t_pre / 1e9, 2),
+            "prefill_28_layers_s_extrapolated": round(t_pre * 28, 2)}
 
 
 def main():
@@ -566,7 +611,11 @@ def main():
     else:
         rl_kernel = "gate|up projection GEMV with SwiGLU epilogue (T=1)"
         rl_bytes = GU_LAUNCH_BYTES
-    achieved = rl_bytes / (dec["kernel_us"] * 1e-6) / 1e9
+    # the dominant kernel's average launch time: on the persistent path one graph replay is one
+    # launch, so the events around the timed replays give it directly; otherwise the library's
+    # per-launch event timer from the eager pass
+    launch_us = dec["replay_event_us"] if dec["path"] == 2 else dec["eager_kernel_us"]
+    achieved = rl_bytes / (launch_us * 1e-6) / 1e9
     kp = dec["kernels_path"]
     line = {
         "metric": "decode tokens/s + HBM GB/s (T=1, ctx 4096); prefill TFLOP/s at T=2048",
@@ -594,8 +643,11 @@ def main():
         "prefill_ms": None if pre is None else round(pre["ms"], 3),
         "roofline": {"kernel": rl_kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": rl_bytes, "avg_launch_us": round(dec["kernel_us"], 3),
-                     "launches": dec["launches"]},
+                     "bytes_per_launch": rl_bytes, "avg_launch_us": round(launch_us, 3),
+                     "timer": ("HIP events on the library's stream around the timed graph replays (one launch "
+                               "per replay)") if dec["path"] == 2 else
+                              "the library's per-launch HIP events on its stream, eager pass",
+                     "eager_launch_us": round(dec["eager_kernel_us"], 3), "launches": args.steps},
         "moe": moe,
         "moe_q8": moe_q8,
         "q8": q8,

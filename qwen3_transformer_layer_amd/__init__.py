@@ -8,7 +8,10 @@ kernels; there is no Python or CPU fallback, and a missing library raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
+import sys
+import weakref
 
 import torch
 
@@ -45,6 +48,26 @@ def qwen3_workspace_bytes(cfg: Qwen3Config, max_tokens: int) -> int:
     return _lib.load().qwen3_workspace_bytes(ctypes.byref(c))
 
 
+_live = weakref.WeakSet()  # handles not yet destroyed
+
+
+def _destroy_all() -> None:
+    """Destroy every live handle while the HIP runtime is still up (registered with atexit,
+    so it runs before interpreter teardown and before the runtime's own exit handlers):
+    the handle's timer events are released by hipEventDestroy, which must not run after
+    the runtime has begun to shut down."""
+    hs = list(_live)
+    if not hs:
+        return
+    if torch.cuda.is_initialized():
+        torch.cuda.synchronize()
+    for h in hs:
+        h.close()
+
+
+atexit.register(_destroy_all)
+
+
 class _Handle:
     """Owns the C handle plus references to every borrowed buffer, so none is freed early."""
 
@@ -52,11 +75,19 @@ class _Handle:
         self.ptr = ptr
         self.cfg = cfg
         self.keep = keep
+        _live.add(self)
 
-    def __del__(self):
+    def close(self) -> None:
         if getattr(self, "ptr", None) and _lib._lib is not None:
             _lib._lib.qwen3_destroy(self.ptr)
-            self.ptr = None
+        self.ptr = None
+        _live.discard(self)
+
+    def __del__(self):
+        # during interpreter teardown the atexit hook has already destroyed every handle;
+        # make no library call then
+        if not sys.is_finalizing():
+            self.close()
 
 
 def qwen3_init(cfg: Qwen3Config, weights: dict, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -159,9 +190,8 @@ def qwen3_get_decode_path(h: _Handle) -> int:
 
 
 def qwen3_destroy(h: _Handle) -> None:
-    if h.ptr:
-        _lib.load().qwen3_destroy(h.ptr)
-        h.ptr = None
+    _lib.load()
+    h.close()
 
 
 def qwen3_rope_table(capacity: int, head_dim: int, theta: float, dtype: str, device="cuda", stream=None):
