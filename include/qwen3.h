@@ -35,6 +35,14 @@
  *    qwen3_last_error() then describes the failure.  A QWEN3_ERR_HIP from a
  *    launch can leave work partly enqueued.
  *  - A handle is one seat and is not thread-safe.
+ *  - Alignment: the kernels move weight, cache, table and activation rows in
+ *    16-byte vector accesses, so every device pointer qwen3_init takes (each
+ *    weight, scale, bias and norm vector, the embedding and RoPE tables, both
+ *    caches) and the hidden-state inputs and outputs of the forward calls must
+ *    be 16-byte aligned; token ids, routing outputs, logits and argmax need
+ *    their element alignment.  A misaligned pointer gives QWEN3_ERR_ARG before
+ *    anything is enqueued (torch allocations are aligned; a view at an odd
+ *    element offset may not be).
  *
  * Layouts (row-major, model dtype = bf16 or fp32 unless stated):
  *  - projection weights are [out][in]: q|k|v fused as [(H+2KV)*D][hidden]
@@ -209,7 +217,15 @@ int qwen3_set_stream(qwen3_handle *h, void *stream);
  * <= 8192, on a device that holds 256 co-resident blocks of 512 threads), else one kernel per
  * step of the layer; 1: always one kernel per step; 2: require the persistent kernel
  * (QWEN3_ERR_UNSUPPORTED when unavailable).  Both compute the same values up to fp32
- * summation order.  qwen3_get_decode_path returns the path T == 1 calls take (1 or 2). */
+ * summation order.  qwen3_get_decode_path returns the path T == 1 calls take (1 or 2).
+ * The persistent kernel's blocks wait on each other's results, so all 256 must run at once:
+ * an eager call launches it cooperatively (the runtime guarantees co-residency or fails the
+ * launch), but a launch recorded into a HIP graph is a plain launch, and co-residency then
+ * rests on the occupancy check qwen3_init made and on no other work holding CUs while the
+ * graph runs (the GPU used by this process alone, no kernels on other streams overlapping
+ * the step).  If blocks cannot all run, every wait gives up after about a second: the call
+ * still returns QWEN3_OK (it only enqueues), the step's outputs are invalid, and only
+ * qwen3_check_device_errors reports it (QWEN3_ERR_HIP). */
 int qwen3_set_decode_path(qwen3_handle *h, int path);
 int qwen3_get_decode_path(const qwen3_handle *h);
 

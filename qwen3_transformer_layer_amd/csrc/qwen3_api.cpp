@@ -169,6 +169,34 @@ int check_config(const qwen3_config *c, std::string *why) {
 
 bool is_q8(const qwen3_handle *h) { return h->cfg.quant_bits == 8; }
 
+// Device buffers are read and written in 16-byte vector accesses (weight rows, cache rows,
+// table rows, activation rows); NULL counts as aligned.
+bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool al_elem(const void *p, size_t es) { return ((uintptr_t)p & (es - 1)) == 0; }
+
+// The first misaligned device pointer of the weights and caches, or nullptr.
+const char *misaligned(const qwen3_config *cfg, const qwen3_weights *w, const void *kc, const void *vc) {
+    if (!al16(kc)) return "k_cache";
+    if (!al16(vc)) return "v_cache";
+    if (!al16(w->embed)) return "embed";
+    if (!al16(w->final_norm)) return "final_norm";
+    if (!al16(w->rope_cos) || !al16(w->rope_sin)) return "rope table";
+    static const char *names[] = {"in_norm",  "post_norm",     "q_norm",        "k_norm",     "qkv",
+                                  "o",        "gate_up",       "down",          "qkv_s",      "qkv_b",
+                                  "o_s",      "o_b",           "gate_up_s",     "gate_up_b",  "down_s",
+                                  "down_b",   "router",        "exp_gate_up",   "exp_down",   "router_s",
+                                  "router_b", "exp_gate_up_s", "exp_gate_up_b", "exp_down_s", "exp_down_b",
+                                  "qkv_bias"};
+    static_assert(sizeof(qwen3_layer_weights) == sizeof(names) / sizeof(names[0]) * sizeof(void *),
+                  "every layer field is a pointer named above");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const void *const *f = (const void *const *)&w->layers[l];
+        for (size_t i = 0; i < sizeof(names) / sizeof(names[0]); ++i)
+            if (!al16(f[i])) return names[i];
+    }
+    return nullptr;
+}
+
 // Layer kind: sparse MoE block iff the configuration has experts and the layer a router.
 bool moe_layer(const qwen3_config &c, const qwen3_layer_weights &L) { return c.n_experts > 0 && L.router; }
 
@@ -300,9 +328,9 @@ int run_layers(qwen3_handle *h, const void *x, int T, void *out) {
         else HIPCHECK(h, launch_add_rmsnorm(dt, h->h, pend_live ? h->pend : nullptr, L.in_norm,
                                             pend_live ? h->h : nullptr, h->y, T, hid, c.rms_eps, s));
         HIPCHECK(h, mark(h, K_QKV, true));
-        const bool al16 = ((uintptr_t)h->cos_t | (uintptr_t)h->sin_t | (uintptr_t)h->q | (uintptr_t)h->kc |
-                           (uintptr_t)h->vc) % 16 == 0;  // the fused epilogue reads and writes 16 bytes at a time
-        if (dt == QWEN3_BF16 && !is_q8(h) && al16 && gemm_qkv_fused_ok(T, hid, H, KV, D)) {
+        // the fused epilogue reads and writes 16 bytes at a time: the table, q and the caches
+        // are 16-byte aligned (checked by qwen3_init; workspace pieces are 256-byte aligned)
+        if (dt == QWEN3_BF16 && !is_q8(h) && gemm_qkv_fused_ok(T, hid, H, KV, D)) {
             // q/k norm, RoPE and the cache write in the projection's epilogue
             QkvEpi qe;
             qe.q_norm = L.q_norm;
@@ -420,6 +448,7 @@ int qwen3_forward_batch(qwen3_handle *const *seats, int B, const void *x, void *
     qwen3_handle *h = seats[0];
     h->err.clear();
     if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (!al16(x) || !al16(out)) return fail(h, QWEN3_ERR_ARG, "input and output must be 16-byte aligned");
     if (B < 1 || B > DECODE_MAXB) return fail(h, QWEN3_ERR_ARG, "B=%d outside 1..%d", B, DECODE_MAXB);
     if (B > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "B=%d exceeds the first seat's max_tokens=%d", B, h->cfg.max_tokens);
     for (int b = 0; b < B; ++b) {
@@ -468,6 +497,7 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
     if (!workspace || ws_bytes < L.total || ((uintptr_t)workspace & 255)) return QWEN3_ERR_WORKSPACE;
     if (!w->final_norm) return QWEN3_ERR_NULL_WEIGHT;
     if ((w->rope_cos == nullptr) != (w->rope_sin == nullptr)) return QWEN3_ERR_ARG;
+    if (misaligned(cfg, w, k_cache, v_cache)) return QWEN3_ERR_ARG;
     const bool q8 = cfg->quant_bits == 8, moe = cfg->n_experts > 0;
     for (int l = 0; l < cfg->n_layers; ++l) {
         const qwen3_layer_weights &Lw = w->layers[l];
@@ -564,6 +594,7 @@ int qwen3_forward_hidden(qwen3_handle *h, const void *x, int T, void *out) {
     if (!h) return QWEN3_ERR_ARG;
     h->err.clear();
     if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (!al16(x) || !al16(out)) return fail(h, QWEN3_ERR_ARG, "input and output must be 16-byte aligned");
     if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
     if (h->length + T > h->cfg.capacity)
         return fail(h, QWEN3_ERR_CAPACITY, "context %d exceeds capacity %d", h->length + T, h->cfg.capacity);
@@ -577,6 +608,8 @@ int qwen3_head(qwen3_handle *h, const void *hs, int T, const void *head, int V, 
     h->err.clear();
     if (!hs) return fail(h, QWEN3_ERR_ARG, "null hidden states");
     if (!logits && !argmax) return fail(h, QWEN3_ERR_ARG, "neither logits nor argmax requested");
+    if (!al16(hs) || !al16(head) || !al_elem(logits, 4) || !al_elem(argmax, 4))
+        return fail(h, QWEN3_ERR_ARG, "hidden states and head must be 16-byte aligned, logits and argmax 4-byte");
     if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
     if (!head) {
         if (!h->embed || h->cfg.vocab < 1) return fail(h, QWEN3_ERR_NULL_WEIGHT, "no head and no embedding table");
@@ -592,6 +625,7 @@ int qwen3_forward(qwen3_handle *h, const int32_t *tokens, int T, void *out) {
     if (!h) return QWEN3_ERR_ARG;
     h->err.clear();
     if (!tokens || !out) return fail(h, QWEN3_ERR_ARG, "null tokens or output");
+    if (!al_elem(tokens, 4) || !al16(out)) return fail(h, QWEN3_ERR_ARG, "token ids must be 4-byte, the output 16-byte aligned");
     if (!h->embed || h->cfg.vocab < 1) return fail(h, QWEN3_ERR_NULL_WEIGHT, "no embedding table");
     if (T < 1 || T > h->cfg.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, h->cfg.max_tokens);
     if (h->length + T > h->cfg.capacity)
@@ -610,6 +644,8 @@ int qwen3_moe_block(qwen3_handle *h, int layer, const void *x, int T, void *out,
     if (c.n_experts <= 0) return fail(h, QWEN3_ERR_ARG, "not an MoE configuration");
     if (layer < 0 || layer >= c.n_layers) return fail(h, QWEN3_ERR_ARG, "layer %d out of range", layer);
     if (!x || !out) return fail(h, QWEN3_ERR_ARG, "null input or output");
+    if (!al16(x) || !al16(out) || !al_elem(topk_idx, 4) || !al_elem(topk_w, esize(c)))
+        return fail(h, QWEN3_ERR_ARG, "input and output must be 16-byte aligned, the routing outputs element-aligned");
     if (T < 1 || T > c.max_tokens) return fail(h, QWEN3_ERR_ARG, "T=%d outside 1..max_tokens=%d", T, c.max_tokens);
     const qwen3_layer_weights &L = h->layers[layer];
     if (!moe_layer(c, L)) return fail(h, QWEN3_ERR_ARG, "layer %d is a dense layer", layer);

@@ -97,3 +97,32 @@ def test_ops_reject_bad_arguments_before_launch(lib):
         _lib.ERR_ARG                                                                                # p0 + T > cap
     assert lib.qwen3_rope_table(64, 96, 1e6, 0, fake, fake, None) == _lib.ERR_ARG
     assert lib.qwen3_status_string(-3) == b"context exceeds capacity"
+
+
+def test_init_rejects_misaligned_pointers_before_any_gpu_work(lib):
+    """Every weight, cache and table pointer must be 16-byte aligned (the kernels read rows
+    with 16-byte vector loads); a misaligned one is rejected on the host, before any HIP
+    call, so this runs without a GPU and the fake addresses are never dereferenced."""
+    from qwen3_transformer_layer_amd import _lib
+    c = _cfg(n_layers=2)
+    need = lib.qwen3_workspace_bytes(ctypes.byref(c))
+    base = 1 << 32
+    fields = [n for n, _ in _lib.LayerWeights._fields_]
+    plain = {"in_norm", "post_norm", "q_norm", "k_norm", "qkv", "o", "gate_up", "down"}
+    for bad in ("in_norm", "q_norm", "qkv", "down", "kc", "vc", "embed", "final_norm", "rope"):
+        layers = (_lib.LayerWeights * 2)()
+        for l in range(2):
+            for i, name in enumerate(fields):
+                if name in plain:
+                    setattr(layers[l], name, base + (1 + l * 64 + i) * 4096 + (2 if bad == name and l == 1 else 0))
+        emb = base + 900 * 4096 + (8 if bad == "embed" else 0)
+        fn = base + 901 * 4096 + (2 if bad == "final_norm" else 0)
+        rc_ = (base + 902 * 4096 + (4 if bad == "rope" else 0), base + 903 * 4096)
+        w = _lib.Weights(emb, fn, rc_[0], rc_[1], layers)
+        kc = ctypes.c_void_p(base + 904 * 4096 + (2 if bad == "kc" else 0))
+        vc = ctypes.c_void_p(base + 905 * 4096 + (6 if bad == "vc" else 0))
+        ws = ctypes.c_void_p(base + 4096 * 4096)
+        h = ctypes.c_void_p()
+        assert lib.qwen3_init(ctypes.byref(c), ctypes.byref(w), kc, vc, ws, need, None, ctypes.byref(h)) == \
+            _lib.ERR_ARG, bad
+        assert not h.value
