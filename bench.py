@@ -93,7 +93,7 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     torch.cuda.empty_cache()
 
 
-def decode_bench(steps: int, warmup: int, compare: bool = True):
+def decode_bench(steps: int, warmup: int, compare: bool = True, eager: bool = True):
     """Time `steps` replays of one captured decode step (HIP graph on a side stream), then
     `steps` eager steps with HIP events around the dominant kernel's launches on the
     library's stream.  Done for the default T = 1 path (the persistent decode kernel) and,
@@ -150,6 +150,11 @@ def decode_bench(steps: int, warmup: int, compare: bool = True):
         ev_us = ev0.elapsed_time(ev1) * 1e3 / steps
         q3.qwen3_check_device_errors(seat.handle)
         del graph
+        if not eager and used == 2:  # the roofline time comes from the replay events
+            log(f"decode path {used}: graph {dt * 1e6:.1f} us/step (events on the stream {ev_us:.1f} us per replay)")
+            return {"path": used, "ms_per_step": dt * 1e3, "eager_ms_per_step": None, "tokens_per_s": 1.0 / dt,
+                    "hbm_gbps": DECODE_STEP_BYTES / dt / 1e9, "replay_event_us": ev_us, "eager_kernel_us": None,
+                    "launches": 0}
         # eager pass with the library's own per-launch timer on the dominant kernel: the
         # whole-step kernel on the persistent path, the gate|up projection otherwise
         kind = 5 if used == 2 else 2
@@ -566,6 +571,8 @@ def main():
                     help="skip timing the one-kernel-per-step decode path (for profiling)")
     ap.add_argument("--only", choices=["moe", "moe_q8", "q8", "qwen2", "head", "batch"],
                     help="time only this variant workload (for profiling)")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip the eager decode pass timed by the library's per-launch events (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a 1 GiB device copy first (hardware-counter scale for profiling)")
     args = ap.parse_args()
@@ -595,7 +602,7 @@ def main():
         return
     if args.copy_calib:
         copy_calibration()
-    dec = decode_bench(args.steps, args.warmup, compare=not args.no_compare)
+    dec = decode_bench(args.steps, args.warmup, compare=not args.no_compare, eager=not args.no_eager)
     pre = None if args.no_prefill else prefill_bench(args.prefill_iters)
     moe = None if args.no_variants else moe_bench(30, 3)
     moe_q8 = None if args.no_variants else moe_bench(30, 3, q8=True)
@@ -625,7 +632,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 4),
-        "eager_ms_per_step": round(dec["eager_ms_per_step"], 4),
+        "eager_ms_per_step": None if dec["eager_ms_per_step"] is None else round(dec["eager_ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -647,7 +654,8 @@ def main():
                      "timer": ("HIP events on the library's stream around the timed graph replays (one launch "
                                "per replay)") if dec["path"] == 2 else
                               "the library's per-launch HIP events on its stream, eager pass",
-                     "eager_launch_us": round(dec["eager_kernel_us"], 3), "launches": args.steps},
+                     "eager_launch_us": None if dec["eager_kernel_us"] is None else round(dec["eager_kernel_us"], 3),
+                     "launches": args.steps},
         "moe": moe,
         "moe_q8": moe_q8,
         "q8": q8,
