@@ -202,6 +202,21 @@ int qwen3_forward_batch(qwen3_handle *const *seats, int B, const void *x, void *
  * QWEN3_ERR_NULL_WEIGHT (no head and no embedding table). */
 int qwen3_head(qwen3_handle *h, const void *hs, int T, const void *head, int V, float *logits, int32_t *argmax);
 
+/* qwen3_head without a handle or workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same logits and greedy token as qwen3_head, for hs [T][hidden] and head [V][hidden] in
+ * `dtype`, enqueued on `stream` (which must belong to the current device; NULL = the null
+ * stream).  The per-row greedy-token keys live in a static array the library keeps on each
+ * device for the rest of the process (QWEN3_HEAD_STATIC_MAX_T * 64 64-bit words, 128 KB);
+ * nothing is allocated, and the call clears the keys itself.  Calls that overlap on one
+ * device (other streams, other threads) share that array and race: serialise them.
+ * Errors: QWEN3_ERR_DTYPE; QWEN3_ERR_ARG for a null or misaligned pointer, neither output
+ * requested, T outside 1..QWEN3_HEAD_STATIC_MAX_T, V < 1, or hidden not a positive multiple
+ * of 64; QWEN3_ERR_HIP when the array's address cannot be found or a launch fails. */
+#define QWEN3_HEAD_STATIC_MAX_T 256
+int qwen3_head_static(int dtype, const void *hs, int T, int hidden, const void *head, int V, float *logits,
+                      int32_t *argmax, void *stream);
+
 /* Set the seat length (0 <= length <= capacity): a pre-filled cache, or a
  * rewind.  Entries at positions >= length are never read and are overwritten
  * by the next forward. */

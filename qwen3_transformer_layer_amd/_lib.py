@@ -67,6 +67,7 @@ def load():
         "qwen3_moe_block": (_I, [H, _I, _P, _I, _P, _P, _P]),
         "qwen3_head": (_I, [H, _P, _I, _P, _I, _P, _P]),
         "qwen3_forward_batch": (_I, [_P, _I, _P, _P]),
+        "qwen3_head_static": (_I, [_I, _P, _I, _I, _P, _I, _P, _P, _P]),
         "qwen3_set_length": (_I, [H, _I]),
         "qwen3_get_length": (_I, [H]),
         "qwen3_set_stream": (_I, [H, _P]),

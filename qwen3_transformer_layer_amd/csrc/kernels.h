@@ -116,6 +116,11 @@ hipError_t launch_moe_norm1(int dt, const void *h, const void *nw, float eps, in
 // keys: 64 T 64-bit words of scratch
 hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int V, float *logits, int32_t *argmax,
                        unsigned long long *keys, hipStream_t s);
+// The same with the keys in the library's per-device static array (no workspace, nothing
+// allocated): T <= HEAD_STATIC_MAX_T rows; the stream must belong to the current device.
+constexpr int HEAD_STATIC_MAX_T = 256;
+hipError_t launch_head_static(int dt, const void *hs, int T, int K, const void *W, int V, float *logits,
+                              int32_t *argmax, hipStream_t s);
 
 // ---- MFMA projections for M > 16 (kernels_gemm.hip): LDS-DMA pipeline, K % 64 == 0 (bf16
 // weights) or K % 128 == 0 and 4-byte aligned scale/bias (8-bit weights)

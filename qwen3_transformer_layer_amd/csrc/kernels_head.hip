@@ -12,6 +12,8 @@
 // row in a register; the block's four are reduced in LDS and one 64-bit atomicMax per (block,
 // row) goes to one of HS slots of the row (block % HS), so no address takes more than about 32
 // atomics; head_final_kernel reduces the slots and turns the key into an index.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -127,6 +129,47 @@ hipError_t launch_head(int dt, const void *hs, int T, int K, const void *W, int 
     }
     if (argmax) head_final_kernel<<<T, 64, 0, s>>>(keys, T, argmax);
     return hipGetLastError();
+}
+
+// ---- the same head for callers that cannot allocate: the greedy-token keys live in one
+// file-scope device array instead of a workspace.  Each device holds its own copy of the array
+// until the process ends; its device address is looked up once per device (the array's name in
+// host code is a host-side stand-in, never a device address) and kept.  Every call on a device
+// shares that device's array: head_init_kernel clears the keys each call, and calls that
+// overlap on one device race on them.
+static __device__ __align__(256) unsigned long long scratch[HEAD_STATIC_MAX_T * HS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+unsigned long long *scratch_ptr[MAX_DEVICES];  // per device; null until looked up
+}  // namespace
+
+hipError_t head_static_scratch(unsigned long long **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = (unsigned long long *)p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_head_static(int dt, const void *hs, int T, int K, const void *W, int V, float *logits,
+                              int32_t *argmax, hipStream_t s) {
+    if (T < 1 || T > HEAD_STATIC_MAX_T) return hipErrorInvalidValue;
+    unsigned long long *keys = nullptr;
+    if (argmax) {
+        const hipError_t e = head_static_scratch(&keys);
+        if (e != hipSuccess) return e;
+    }
+    return launch_head(dt, hs, T, K, W, V, logits, argmax, keys, s);
 }
 
 }  // namespace q3

@@ -621,6 +621,18 @@ int qwen3_head(qwen3_handle *h, const void *hs, int T, const void *head, int V, 
     return QWEN3_OK;
 }
 
+int qwen3_head_static(int dtype, const void *hs, int T, int hidden, const void *head, int V, float *logits,
+                      int32_t *argmax, void *stream) {
+    if (dtype != QWEN3_BF16 && dtype != QWEN3_FP32) return QWEN3_ERR_DTYPE;
+    if (!hs || !head || (!logits && !argmax)) return QWEN3_ERR_ARG;
+    if (T < 1 || T > QWEN3_HEAD_STATIC_MAX_T || V < 1 || hidden < 64 || hidden % 64) return QWEN3_ERR_ARG;
+    if (!al16(hs) || !al16(head) || !al_elem(logits, 4) || !al_elem(argmax, 4)) return QWEN3_ERR_ARG;
+    static_assert(QWEN3_HEAD_STATIC_MAX_T == HEAD_STATIC_MAX_T, "header and library agree on the limit");
+    return launch_head_static(dtype, hs, T, hidden, head, V, logits, argmax, (hipStream_t)stream) == hipSuccess
+               ? QWEN3_OK
+               : QWEN3_ERR_HIP;
+}
+
 int qwen3_forward(qwen3_handle *h, const int32_t *tokens, int T, void *out) {
     if (!h) return QWEN3_ERR_ARG;
     h->err.clear();
