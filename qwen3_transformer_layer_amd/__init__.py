@@ -83,10 +83,10 @@ class _Handle:
         self.ptr = None
         _live.discard(self)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # during interpreter teardown the atexit hook has already destroyed every handle;
-        # make no library call then
-        if not sys.is_finalizing():
+        # make no library call then (module globals may already be gone: the check is bound here)
+        if not _finalizing():
             self.close()
 
 
