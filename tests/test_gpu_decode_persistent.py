@@ -117,8 +117,8 @@ def test_persistent_full_stack(orc):
         f"new K/V layer 0 {kv0:.2e}, all layers {kv:.2e}")
     # Through 28 layers both paths drift from the oracle (and from each other: the two differ
     # in fp32 summation order) by bf16 rounding chains, so the deep-stack figures are reported
-    # with a loose sanity bound; the gated parity is the one-layer test above.
-    assert e < 0.1 and e_paths < 0.1 and kv0 <= BF16_TOL
+    # with a regression bound (the drift measures ~2.8%); the gated parity is the one-layer test above.
+    assert e < 0.05 and e_paths < 0.05 and kv0 <= BF16_TOL
 
 
 def test_persistent_consecutive_steps(orc):

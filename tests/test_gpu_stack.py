@@ -127,7 +127,8 @@ def test_qwen3_1p7b_decode_full_stack(orc):
     got, ref, kv_e, _ = _decode_case(orc, QWEN3_1P7B_DECODE, None, 4095)
     e = max_row_rel_l2(got, ref)
     say(f"1.7B decode, 28 layers, ctx 4096: out rel L2 {e:.2e} (reported), new K/V entries {kv_e:.2e}")
-    assert e < 0.1
+    # regression bound: the 28-layer bf16 drift measures ~2.8% on both decode paths
+    assert e < 0.05
 
 
 def test_qwen3_1p7b_prefill_one_layer(orc):
