@@ -338,12 +338,21 @@ def q8_bench(steps: int, warmup: int, iters: int):
         seat.length = 0
         q3.qwen3_forward_hidden(seat.handle, xp, op)
 
+    path = q3.qwen3_get_decode_path(seat.handle)
     t_dec = _graph_seconds(dec, stream, steps, warmup)
+    q3.qwen3_check_device_errors(seat.handle)
+    t_dec_kernels = None
+    if path == 2:  # the one-kernel-per-step path beside it
+        q3.qwen3_set_decode_path(seat.handle, 1)
+        t_dec_kernels = _graph_seconds(dec, stream, steps, warmup)
+        q3.qwen3_set_decode_path(seat.handle, 0)
     t_pre = _graph_seconds(pre, stream, iters, 2)
     q3.qwen3_check_device_errors(seat.handle)
     res = {"workload": "Qwen3-1.7B shape, 8-bit affine group-quantised projections (u8 codes, bf16 scale and "
                        "bias per 64 along K)",
+           "decode_path": {1: "one kernel per step", 2: "persistent"}.get(path, path),
            "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
+           "decode_ms_per_step_one_kernel_per_step": None if t_dec_kernels is None else round(t_dec_kernels * 1e3, 4),
            "decode_step_bytes": Q8_DECODE_STEP_BYTES, "decode_gbps": round(Q8_DECODE_STEP_BYTES / t_dec / 1e9, 1),
            "decode_hbm_frac": round(Q8_DECODE_STEP_BYTES / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
            "prefill_T": Q8_PREFILL_T, "prefill_ms": round(t_pre * 1e3, 3),

@@ -183,8 +183,9 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 
 // Returns p unchanged through an empty asm the compiler cannot see into: addresses derived
 // from it are then computed where they are used instead of being hoisted out of the layer
-// loop and kept live (in registers, or spilled) across every step.  The pointer is
-// wave-uniform (readfirstlane places it in scalar registers) and points to global memory:
+// loop and kept live (in registers, or spilled) across every step.  The pointer must be
+// wave-uniform (readfirstlane places lane 0's value in scalar registers; a per-lane choice
+// between two arrays would silently become lane 0's choice) and point to global memory:
 // going through a global-address-space pointer keeps the accesses global, not flat (flat
 // accesses also count against the LDS wait counter).
 template <typename T> __device__ __forceinline__ T *opaque(T *p) {

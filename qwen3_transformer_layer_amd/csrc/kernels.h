@@ -135,18 +135,21 @@ bool gemm_q8_dma_ok(int M, int K, int N, const void *scale, const void *bias);
 hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes, const void *scale, const void *bias,
                               int N, int epi, const void *res, void *out, hipStream_t s);
 
-// ---- persistent decode step (kernels_decode_mk.hip): dense bf16 stacks of supported shape
+// ---- persistent decode step (kernels_decode_mk.hip): dense bf16 stacks of supported shape,
+// bf16 or 8-bit (groups of 64) weights
 bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I, int cap);
 size_t decode_mk_workspace(int n_layers, int H, int KV, int hid, int I);
 // Copies the per-layer weight pointers (host array of 9 pointers per layer: in_norm, post_norm,
-// q_norm, k_norm, qkv, o, gate_up, down, qkv_bias; q/k norm and bias may be null) into ws and
-// clears the exchange buffers; synchronises s.
+// q_norm, k_norm, qkv, o, gate_up, down, qkv_bias; q/k norm and bias may be null; with 8-bit
+// weights the projections are the code arrays and layer_q8_ptrs holds 8 pointers per layer:
+// qkv, o, gate_up, down scale then bias; else null) into ws and clears the exchange buffers;
+// synchronises s.
 hipError_t decode_mk_init(void *ws, int n_layers, int H, int KV, int hid, int I, const void *layer_ptrs,
-                          hipStream_t s);
-hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, int cap, int p, int window,
+                          const void *layer_q8_ptrs, hipStream_t s);
+hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, bool q8, int cap, int p, int window,
                             float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
                             const void *sin_t, void *kc, void *vc, int *err, hipStream_t s);
-int decode_mk_max_blocks(int hid, int I, int H, int KV);
+int decode_mk_max_blocks(int hid, int I, int H, int KV, bool q8);
 int decode_mk_blocks();
 
 }  // namespace q3

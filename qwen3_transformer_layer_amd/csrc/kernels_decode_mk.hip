@@ -28,6 +28,12 @@
 // overwrites the slot.  Compute waves synchronise among themselves with an LDS counter
 // barrier (the stream waves take part in no barrier after the prologue).
 //
+// 8-bit weights (u8 codes, bf16 scale s and bias b per group of 64 along K; w = s q + b in
+// fp32, never rounded): a ring chunk holds the codes of two weight rows of 2048 (two q|k|v or
+// o_proj rows, or the gate and the up row of one SwiGLU output) or one third of a down row,
+// and a 256-byte side slot holds their groups' scales and biases.  A lane's dot is the
+// regrouped sum s (x . q) + b (sum x) over each 16-code piece it holds.
+//
 // Exchange protocol between blocks (no grid barrier, no cache-maintenance fences): every
 // value handed to other blocks is written as one 32-bit word (tag << 16 | bf16 bits) or one
 // 64-bit word (tag << 32 | fp32 bits) with an agent-scope relaxed atomic store, which
@@ -57,6 +63,8 @@ constexpr int D = 128;               // head dimension
 constexpr int HID = 2048;            // hidden size: one chunk is one weight row of HID bf16
 constexpr int CHB = HID * 2;         // chunk bytes
 constexpr int NS = 30;               // ring slots (120 KB)
+constexpr int NSQ = 28;              // ring slots with 8-bit weights (112 KB + 7 KB of scale/bias slots)
+constexpr int SBB = 256;             // scale/bias bytes per chunk (8-bit weights)
 constexpr int DL = 3;                // chunks in flight per stream wave while the ring has room
 constexpr int KPC = CHB / (D * 2);   // keys per K or V chunk (16)
 constexpr int CHUNK_MAX = 256;       // keys per attention split
@@ -73,15 +81,22 @@ __host__ __device__ constexpr int rep_stride(int words) {  // words between copi
 }
 constexpr long SPIN = 1L << 21;      // global poll rounds before a waiter gives up (order of a second)
 constexpr long LSPIN = 1L << 22;     // LDS wait rounds before a waiter gives up (order of a second)
-static_assert(NS >= NL * DL, "the ring holds every stream wave's chunks in flight");
-static_assert(4 * (DL - 1) <= 63, "vector-memory counter range");
+static_assert(NSQ >= NL * DL, "the ring holds every stream wave's chunks in flight");
+static_assert(5 * (DL - 1) <= 63, "vector-memory counter range");
+template <bool Q8> __host__ __device__ constexpr int ring_slots() { return Q8 ? NSQ : NS; }
 
 struct DevLayer {  // q_norm / k_norm both null: no per-head q/k norm; qkv_bias null: no bias
     const bf16 *in_norm, *post_norm, *q_norm, *k_norm, *qkv, *o, *gu, *down, *qkv_bias;
 };
 
+struct DevLayerQ {  // 8-bit weights: the per-group scale and bias arrays [rows][K / 64]
+    const bf16 *qkv_s, *qkv_b, *o_s, *o_b, *gu_s, *gu_b, *down_s, *down_b;
+};
+static_assert(sizeof(DevLayerQ) == 64, "four (scale, bias) pairs of 16 bytes, read as pairs");
+
 struct Args {
     const DevLayer *layers;
+    const DevLayerQ *layersq;  // 8-bit weights only
     int n_layers, H, KV, cap, p, nsplit, chunk, window;  // window 0: causal
     float eps, scale;
     const bf16 *x, *final_norm, *cos_t, *sin_t;
@@ -230,17 +245,18 @@ __device__ __forceinline__ void cbar(unsigned *ctr, unsigned &ep, unsigned *abt,
 }
 
 // Wait until ring chunk g has landed; returns its slot.
+template <int NSL = NS>
 __device__ __forceinline__ const unsigned char *chunk_get(const unsigned char *ring, const unsigned *ready,
                                                           unsigned g, unsigned *abt, int *err) {
-    const unsigned s = g % NS, gen = g / NS;
+    const unsigned s = g % NSL, gen = g / NSL;
     lds_wait_ge(ready + s, gen + 1u, abt, err);
     return ring + (size_t)s * CHB;
 }
 // The wave's reads of chunk g are complete: its slot may be refilled.
-__device__ __forceinline__ void chunk_put(unsigned *done, unsigned g, int lane) {
+template <int NSL = NS> __device__ __forceinline__ void chunk_put(unsigned *done, unsigned g, int lane) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (lane == 0)
-        __hip_atomic_fetch_add(done + g % NS, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(done + g % NSL, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 __device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
@@ -275,6 +291,64 @@ __device__ __forceinline__ float dot_chunk(const unsigned char *c, const X4 &x, 
     return a;
 }
 
+// 8-bit weights: a lane's activations for a row of 2048 codes, elements 16 lane .. + 15
+// (first 1 KB of the row's codes) and 1024 + 16 lane .. + 15 (second 1 KB), as bf16 pairs,
+// and the fp32 sums of each 16 (the bias term of the group fold).
+struct X8 {
+    u32x4 v[4];
+    float s0, s1;
+};
+__device__ __forceinline__ X8 load_x8(const uint16_t *x, int lane) {
+    X8 r;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        r.v[2 * k] = *(const u32x4 *)(x + 1024 * k + 16 * lane);
+        r.v[2 * k + 1] = *(const u32x4 *)(x + 1024 * k + 16 * lane + 8);
+    }
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = r.v[2 * k + h][q];
+                s[k] += bf_lo(w) + bf_hi(w);
+            }
+    r.s0 = s[0];
+    r.s1 = s[1];
+    return r;
+}
+// 16 codes (one 16-byte piece) against 16 activations (two bf16x8): the codes are exact bf16
+// values, so each pair is one v_dot2c_f32_bf16 (exact products, fp32 sum).
+__device__ __forceinline__ float dot16_codes(u32x4 c, u32x4 xa, u32x4 xb, float a) {
+    const bf16x8 c0 = codes8(c[0], c[1]), c1 = codes8(c[2], c[3]);
+    const u32x4 w0 = __builtin_bit_cast(u32x4, c0), w1 = __builtin_bit_cast(u32x4, c1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w0[q], xq = xa[q];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wq), __builtin_bit_cast(bf16x2, xq), a, false);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w1[q], xq = xb[q];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wq), __builtin_bit_cast(bf16x2, xq), a, false);
+    }
+    return a;
+}
+// A lane's part of one row of 2048 codes: pieces p0 (codes 16 lane ..) and p1 (1024 + 16 lane ..)
+// of the chunk, with the row's 32 scales at sb[0..31] and biases at sb[32..63]:
+// s_g0 (x . q)_0 + b_g0 (sum x)_0 + s_g1 (x . q)_1 + b_g1 (sum x)_1, groups g0 = lane / 4 and
+// g1 = 16 + lane / 4.  Not summed over the wave.
+__device__ __forceinline__ float dot_q8_row(const unsigned char *c, int p0, int p1, const uint16_t *sb, const X8 &x,
+                                            int lane) {
+    const u32x4 c0 = *(const u32x4 *)(c + p0 * 1024 + lane * 16), c1 = *(const u32x4 *)(c + p1 * 1024 + lane * 16);
+    const int g0 = lane >> 2, g1 = 16 + (lane >> 2);
+    const float s0 = bfv(sb[g0]), b0 = bfv(sb[32 + g0]), s1 = bfv(sb[g1]), b1 = bfv(sb[32 + g1]);
+    const float P0 = dot16_codes(c0, x.v[0], x.v[1], 0.f), P1 = dot16_codes(c1, x.v[2], x.v[3], 0.f);
+    return (s0 * P0 + b0 * x.s0) + (s1 * P1 + b1 * x.s1);
+}
+
 // Sum over the compute waves; every compute thread gets the total.  Two alternating
 // partial buffers, so one barrier per call suffices.
 __device__ __forceinline__ float csum(float v, float (*red)[NC], unsigned &par, unsigned *bar, unsigned &ep,
@@ -293,53 +367,121 @@ __device__ __forceinline__ float csum(float v, float (*red)[NC], unsigned &par, 
 // ---------------------------------------------------------------- per-block chunk sequence
 // Per layer the block consumes, in this order: QPB q|k|v rows, nK K chunks and nK V chunks
 // of its attention split (KPC keys each), OPB o rows, GPB gate/up row pairs (gate, then
-// up), OPB down rows of DCH chunks each.
-template <int QPB, int GPB, int DCH> struct Seq {
+// up), OPB down rows of DCH chunks each.  With 8-bit weights a chunk holds two q|k|v or o rows,
+// or one gate/up pair (the gate row, then the up row), or one third of a down row.
+template <int QPB, int GPB, int DCH, bool Q8> struct Seq {
     static constexpr int OPB = HID / NB;  // o rows (= down rows) per block
+    static constexpr int QC = Q8 ? QPB / 2 : QPB, OC = Q8 ? OPB / 2 : OPB, GC = Q8 ? GPB : 2 * GPB, DC = OPB * DCH;
     int nK, cpl;
-    __device__ explicit Seq(int nK_) : nK(nK_), cpl(QPB + 2 * nK_ + OPB + 2 * GPB + OPB * DCH) {}
-    __device__ int oK() const { return QPB; }
-    __device__ int oV() const { return QPB + nK; }
-    __device__ int oO() const { return QPB + 2 * nK; }
-    __device__ int oG() const { return QPB + 2 * nK + OPB; }
-    __device__ int oD() const { return QPB + 2 * nK + OPB + 2 * GPB; }
+    __device__ explicit Seq(int nK_) : nK(nK_), cpl(QC + 2 * nK_ + OC + GC + DC) {}
+    __device__ int oK() const { return QC; }
+    __device__ int oV() const { return QC + nK; }
+    __device__ int oO() const { return QC + 2 * nK; }
+    __device__ int oG() const { return QC + 2 * nK + OC; }
+    __device__ int oD() const { return QC + 2 * nK + OC + GC; }
 };
 
-// Stream wave j (0 .. NL-1): chunks g = j, j + NL, ... of the whole step, in order.
-template <int QPB, int GPB, int DCH>
-__device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const DevLayer *lay, unsigned char *ring,
-                            unsigned *ready, const unsigned *done, unsigned *abt, int j, int ag, int j0, int j1) {
+// 4-byte direct-to-LDS copy: lane l's word lands at LDS byte address lds + 4 l.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const void *g, unsigned lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The scale and bias array pointers of field pair `pair` (0 q|k|v, 1 o, 2 gate|up, 3 down) of
+// a layer's 8-bit table entry, read with one scalar load that completes inside the asm.  A
+// vector load here would sit in the stream wave's vector-memory counter beside the ring copies,
+// and the compiler then waits for every copy in flight before it uses the pointers.
+__device__ __forceinline__ void load_scale_bias_ptrs(const DevLayerQ *e, int pair, const bf16 *&sc, const bf16 *&bi) {
+    const uint64_t a = (uint64_t)e + 16u * (unsigned)pair;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    u32x4 v;
+    __asm__ volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(((uint64_t)hi << 32) | lo) : "memory");
+    typedef __attribute__((address_space(1))) const bf16 GB;
+    sc = (const bf16 *)(GB *)(((uint64_t)v[1] << 32) | v[0]);
+    bi = (const bf16 *)(GB *)(((uint64_t)v[3] << 32) | v[2]);
+}
+
+// Stream wave j (0 .. NL-1): chunks g = j, j + NL, ... of the whole step, in order.  With 8-bit
+// weights every chunk is five copies (four 1 KB pieces of codes and one 256-byte scale/bias
+// copy into the chunk's side slot; a K/V chunk's fifth copy re-reads 256 bytes of its keys
+// into the unused side slot), so each chunk counts the same in the vector-memory counter.
+template <int QPB, int GPB, int DCH, bool Q8>
+__device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH, Q8> &S, const DevLayer *lay, unsigned char *ring,
+                            unsigned char *sbring, unsigned *ready, const unsigned *done, unsigned *abt, int j, int ag,
+                            int j0, int j1) {
     constexpr int IM = GPB * NB;
+    constexpr int NSL = ring_slots<Q8>(), VPC = Q8 ? 5 : 4;  // copies per chunk
     const int lane = tid_now() & 63, b = blockIdx.x;
     const unsigned total = (unsigned)A.n_layers * (unsigned)S.cpl;
     auto publish = [&](unsigned g) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) __hip_atomic_store(ready + g % NS, g / NS + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) __hip_atomic_store(ready + g % NSL, g / NSL + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
+    // The compiler places this code after the compute waves' code and merges their pending
+    // loads into its wait bookkeeping here; it cannot see the ring copies, which are asm, so
+    // registers it still believes in flight would get waits inside the issue sequence below.
+    // An explicit wait at entry (nothing of this wave is in flight yet) clears that state.
+    wait_vm<0>();
     // n: own chunks issued; pub: own chunks published (chunk k of this wave is g = j + NL k)
     unsigned n = 0, pub = 0;
     for (unsigned g = j; g < total; g += NL) {
         const int l = (int)(g / (unsigned)S.cpl), idx = (int)(g - (unsigned)l * (unsigned)S.cpl);
         const DevLayer &L = lay[l];
-        // the lane's source address for each of the chunk's four 1 KB pieces
+        // the lane's source address for each of the chunk's four 1 KB pieces (and, 8-bit, of
+        // its 4 bytes of the scale/bias copy)
         const unsigned char *src[4];
+        const void *sbsrc = nullptr;
         if (idx < S.oK() || idx >= S.oO()) {
-            const unsigned char *base;
-            if (idx < S.oK()) {
-                base = (const unsigned char *)opaque(L.qkv) + ((size_t)b * QPB + idx) * CHB;
-            } else if (idx < S.oG()) {
-                base = (const unsigned char *)opaque(L.o) + ((size_t)b * S.OPB + (idx - S.oO())) * CHB;
-            } else if (idx < S.oD()) {
-                const int i = idx - S.oG();
-                base = (const unsigned char *)opaque(L.gu) + ((size_t)((i & 1) ? IM : 0) + (size_t)b * GPB + (i >> 1)) * CHB;
+            if constexpr (Q8) {
+                // codes rows of 2048 bytes: pieces 0, 1 of row r0 and 2, 3 of row r1; the scale/bias
+                // copy: lanes 0-15 s[r0], 16-31 b[r0], 32-47 s[r1], 48-63 b[r1] (32 groups, 64 bytes each)
+                const unsigned char *W;
+                int r0, r1, ld = HID, ng = HID / 64, g0 = 0, pair;  // pair: the (scale, bias) field pair
+                if (idx < S.oK()) {
+                    W = (const unsigned char *)opaque(L.qkv), pair = 0;
+                    r0 = b * QPB + 2 * idx, r1 = r0 + 1;
+                } else if (idx < S.oG()) {
+                    W = (const unsigned char *)opaque(L.o), pair = 1;
+                    r0 = b * S.OPB + 2 * (idx - S.oO()), r1 = r0 + 1;
+                } else if (idx < S.oD()) {
+                    W = (const unsigned char *)opaque(L.gu), pair = 2;
+                    r0 = b * GPB + (idx - S.oG()), r1 = IM + r0;
+                } else {  // third t of down row r: codes t * 2048 .. + 2047, groups 32 t .. 32 t + 31
+                    const int i = idx - S.oD(), t = i % DCH;
+                    W = (const unsigned char *)opaque(L.down) + t * 2048, pair = 3;
+                    r0 = r1 = b * S.OPB + i / DCH, ld = IM, ng = IM / 64, g0 = 32 * t;
+                }
+                const bf16 *sc, *bi;
+                load_scale_bias_ptrs(A.layersq + l, pair, sc, bi);
+                const unsigned char *w0 = W + (size_t)r0 * ld, *w1 = W + (size_t)r1 * ld;
+                const bool second = idx >= S.oD();  // a down third: pieces 2, 3 repeat pieces 0, 1
+                src[0] = w0 + lane * 16;
+                src[1] = w0 + 1024 + lane * 16;
+                src[2] = second ? src[0] : w1 + lane * 16;
+                src[3] = second ? src[1] : w1 + 1024 + lane * 16;
+                const int q = lane >> 4, row = (q < 2) ? r0 : r1;
+                const bf16 *arr = (q & 1) ? bi : sc;  // a per-lane choice between two uniform arrays
+                sbsrc = (const void *)(arr + (size_t)row * ng + g0 + 2 * (lane & 15));
             } else {
-                const int i = idx - S.oD();
-                base = (const unsigned char *)opaque(L.down) + ((size_t)b * S.OPB + i / DCH) * ((size_t)IM * 2) +
-                       (size_t)(i % DCH) * CHB;
-            }
+                const unsigned char *base;
+                if (idx < S.oK()) {
+                    base = (const unsigned char *)opaque(L.qkv) + ((size_t)b * QPB + idx) * CHB;
+                } else if (idx < S.oG()) {
+                    base = (const unsigned char *)opaque(L.o) + ((size_t)b * S.OPB + (idx - S.oO())) * CHB;
+                } else if (idx < S.oD()) {
+                    const int i = idx - S.oG();
+                    base = (const unsigned char *)opaque(L.gu) + ((size_t)((i & 1) ? IM : 0) + (size_t)b * GPB + (i >> 1)) * CHB;
+                } else {
+                    const int i = idx - S.oD();
+                    base = (const unsigned char *)opaque(L.down) + ((size_t)b * S.OPB + i / DCH) * ((size_t)IM * 2) +
+                           (size_t)(i % DCH) * CHB;
+                }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) src[k] = base + k * 1024 + lane * 16;
+                for (int k = 0; k < 4; ++k) src[k] = base + k * 1024 + lane * 16;
+            }
         } else {
             const bool isV = idx >= S.oV();
             const int i = idx - (isV ? S.oV() : S.oK());
@@ -350,8 +492,9 @@ __device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const De
                 const int key = min(j0 + i * KPC + 4 * k + lane / 16, j1 - 1);
                 src[k] = (const unsigned char *)(cache + (size_t)key * D) + (lane % 16) * 16;
             }
+            sbsrc = src[0];
         }
-        const unsigned s = g % NS, gen = g / NS;
+        const unsigned s = g % NSL, gen = g / NSL;
         if (lds_acquire(done + s) < gen) {
             // The ring is full: the compute waves still read the slot's previous chunk.  Land
             // and publish everything in flight first (nothing else can be issued meanwhile),
@@ -364,9 +507,10 @@ __device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const De
         const unsigned dlds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
 #pragma unroll
         for (int k = 0; k < 4; ++k) dma16(src[k], dlds + k * 1024);
+        if constexpr (Q8) dma4(sbsrc, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(sbring + (size_t)s * SBB)));
         ++n;
         if (n - pub >= DL) {
-            wait_vm<4 * (DL - 1)>();  // all but this wave's last DL-1 chunks have landed
+            wait_vm<VPC * (DL - 1)>();  // all but this wave's last DL-1 chunks have landed
             for (; pub + (DL - 1) < n; ++pub) publish(j + NL * pub);
         }
     }
@@ -376,16 +520,18 @@ __device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH> &S, const De
 
 // ---------------------------------------------------------------- the kernel
 // QPB q|k|v rows and GPB gate/up pairs per block; DCH chunks per down row; G query heads
-// per kv head.
-template <int QPB, int GPB, int DCH, int G>
+// per kv head; Q8: 8-bit weights.
+template <int QPB, int GPB, int DCH, int G, bool Q8>
 __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     constexpr int IM = GPB * NB;
+    constexpr int NSL = ring_slots<Q8>();
     constexpr int HPT = HID / NCT;  // words per compute thread of a hidden vector
     constexpr int OPB = HID / NB;
     constexpr int RSH = rep_stride(HID), RSM = rep_stride(IM);
     static_assert(IM * 2 == DCH * CHB && HID % NCT == 0 && IM % NCT == 0 && OPB == NC, "shape");
-    __shared__ __attribute__((aligned(16))) unsigned char ring[NS * CHB];
-    __shared__ unsigned ready[NS], done[NS], bar, abt;
+    __shared__ __attribute__((aligned(16))) unsigned char ring[NSL * CHB];
+    __shared__ __attribute__((aligned(16))) unsigned char sbring[Q8 ? NSL * SBB : 16];  // 8-bit: scales and biases
+    __shared__ unsigned ready[NSL], done[NSL], bar, abt;
     __shared__ DevLayer lay[MAXL];
     __shared__ float hs[HID];                                 // residual stream h (fp32 of bf16 values)
     __shared__ __attribute__((aligned(16))) uint16_t ys[IM];  // current projection input (bf16 bits)
@@ -406,9 +552,9 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     const int j0 = lo + as * A.chunk, j1 = min(nkeys, j0 + A.chunk);
     const int nK = j0 < j1 ? (j1 - j0 + KPC - 1) / KPC : 0;
     const bool has_p = j0 < nkeys && j1 == nkeys;
-    const Seq<QPB, GPB, DCH> S(nK);
+    const Seq<QPB, GPB, DCH, Q8> S(nK);
 
-    for (int i = tid; i < NS; i += NTH) {
+    for (int i = tid; i < NSL; i += NTH) {
         ready[i] = 0;
         done[i] = 0;
     }
@@ -421,7 +567,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     __syncthreads();  // the only barrier of the whole block; the roles split here
 
     if (wave >= NC) {
-        stream_wave<QPB, GPB, DCH>(A, S, lay, ring, ready, done, &abt, wave - NC, ag, j0, j1);
+        stream_wave<QPB, GPB, DCH, Q8>(A, S, lay, ring, sbring, ready, done, &abt, wave - NC, ag, j0, j1);
         return;
     }
 
@@ -487,16 +633,35 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             }
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
-        const X4 xq = load_x(ys, lane);
-        for (int i = wave; i < QPB; i += NC) {
-            const unsigned g = gb + i;
-            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
-            float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
-            chunk_put(done, g, lane);
-            // a q|k|v bias is its own rounded add after the projection: rho(rho(x W^T) + b)
-            const bf16 *qb = lay[l].qkv_bias;
-            if (qb) acc = rho<bf16>(acc) + to_f(opaque(qb)[(size_t)b * QPB + i]);
-            if (lane == 0) xstore(opaque(A.x_qkv) + (size_t)b * QPB + i, tagw(tag, acc));
+        // a q|k|v bias is its own rounded add after the projection: rho(rho(x W^T) + b)
+        const bf16 *qb = lay[l].qkv_bias;
+        if constexpr (Q8) {
+            const X8 xq = load_x8(ys, lane);
+            for (int i = wave; i < S.QC; i += NC) {  // chunk i: rows 2 i and 2 i + 1 of the block's QPB
+                const unsigned g = gb + i;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSL) * SBB);
+                float a0 = wave_sum(dot_q8_row(c, 0, 1, sb, xq, lane));
+                float a1 = wave_sum(dot_q8_row(c, 2, 3, sb + 64, xq, lane));
+                chunk_put<NSL>(done, g, lane);
+                const int r0 = b * QPB + 2 * i;
+                if (qb) {
+                    a0 = rho<bf16>(a0) + to_f(opaque(qb)[r0]);
+                    a1 = rho<bf16>(a1) + to_f(opaque(qb)[r0 + 1]);
+                }
+                if (lane == 0) xstore(opaque(A.x_qkv) + r0, tagw(tag, a0));
+                if (lane == 1) xstore(opaque(A.x_qkv) + r0 + 1, tagw(tag, a1));
+            }
+        } else {
+            const X4 xq = load_x(ys, lane);
+            for (int i = wave; i < QPB; i += NC) {
+                const unsigned g = gb + i;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
+                chunk_put<NSL>(done, g, lane);
+                if (qb) acc = rho<bf16>(acc) + to_f(opaque(qb)[(size_t)b * QPB + i]);
+                if (lane == 0) xstore(opaque(A.x_qkv) + (size_t)b * QPB + i, tagw(tag, acc));
+            }
         }
 
         // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
@@ -566,7 +731,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
                                 pack_bf2(kn[6], kn[7])};
             for (int i = wave; i < nK; i += NC) {
                 const unsigned g = gb + S.oK() + i;
-                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
                 u32x4 kr[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) kr[k] = *(const u32x4 *)(c + k * 1024 + lane * 16);
@@ -581,7 +746,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
                         if (sub == 0 && j < j1) sc[h * CHUNK_MAX + (j - j0)] = s * A.scale;
                     }
                 }
-                chunk_put(done, g, lane);
+                chunk_put<NSL>(done, g, lane);
             }
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
@@ -612,7 +777,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
             for (int i = wave; i < nK; i += NC) {
                 const unsigned g = gb + S.oV() + i;
-                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
                 const int jb = j0 + i * KPC;
                 // all KPC rows are read (rows past the split's end hold a copy of its last key
                 // and get probability 0); reads first, then the arithmetic
@@ -638,7 +803,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
                         o[h][1] += pe[h][kk] * v1;
                     }
                 }
-                chunk_put(done, g, lane);
+                chunk_put<NSL>(done, g, lane);
             }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -716,11 +881,25 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row
         poll_bf16<HPT>(opaque(A.x_a) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
-        {
+        if constexpr (Q8) {
+            if (wave < S.OC) {  // chunk wave: rows 2 wave and 2 wave + 1 of the block's OPB
+                const unsigned g = gb + S.oO() + wave;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSL) * SBB);
+                const X8 xo = load_x8(ys, lane);
+                const float a0 = wave_sum(dot_q8_row(c, 0, 1, sb, xo, lane));
+                const float a1 = wave_sum(dot_q8_row(c, 2, 3, sb + 64, xo, lane));
+                chunk_put<NSL>(done, g, lane);
+                const int row = b * OPB + 2 * wave;
+                if (lane < NREP) xstore(opaque(A.x_h2) + lane * RSH + row, tagw(tag, hs[row] + rho<bf16>(a0)));
+                else if (lane >= 32 && lane < 32 + NREP)
+                    xstore(opaque(A.x_h2) + (lane - 32) * RSH + row + 1, tagw(tag, hs[row + 1] + rho<bf16>(a1)));
+            }
+        } else {
             const unsigned g = gb + S.oO() + wave;
-            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
+            const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
             const float acc = wave_sum(dot_chunk(c, load_x(ys, lane), lane, 0.f));
-            chunk_put(done, g, lane);
+            chunk_put<NSL>(done, g, lane);
             const int row = b * OPB + wave;
             if (lane < NREP) xstore(opaque(A.x_h2) + lane * RSH + row, tagw(tag, hs[row] + rho<bf16>(acc)));
         }
@@ -746,19 +925,33 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         }
         if (l + 1 < A.n_layers) load_small(l + 1);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
-        const X4 xg = load_x(ys, lane);
         static_assert(GPB == 3 * NC, "three SwiGLU outputs per wave, packed into one exchange word");
         uint64_t mword = (uint64_t)tag << 48;
-        for (int i = wave; i < GPB; i += NC) {
-            const unsigned g = gb + S.oG() + 2 * i;
-            const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
-            const float gs = wave_sum(dot_chunk(c, xg, lane, 0.f));
-            chunk_put(done, g, lane);
-            const unsigned char *cu = chunk_get(ring, ready, g + 1, &abt, opaque(A.err));
-            const float us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
-            chunk_put(done, g + 1, lane);
-            const float mv = rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us);
-            mword |= (uint64_t)f2bf_bits(mv) << (16 * ((i - wave) / NC));
+        if constexpr (Q8) {
+            const X8 xg = load_x8(ys, lane);
+            for (int i = wave; i < GPB; i += NC) {  // chunk i: the gate row and the up row of output i
+                const unsigned g = gb + S.oG() + i;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSL) * SBB);
+                const float gs = wave_sum(dot_q8_row(c, 0, 1, sb, xg, lane));
+                const float us = wave_sum(dot_q8_row(c, 2, 3, sb + 64, xg, lane));
+                chunk_put<NSL>(done, g, lane);
+                const float mv = rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us);
+                mword |= (uint64_t)f2bf_bits(mv) << (16 * ((i - wave) / NC));
+            }
+        } else {
+            const X4 xg = load_x(ys, lane);
+            for (int i = wave; i < GPB; i += NC) {
+                const unsigned g = gb + S.oG() + 2 * i;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                const float gs = wave_sum(dot_chunk(c, xg, lane, 0.f));
+                chunk_put<NSL>(done, g, lane);
+                const unsigned char *cu = chunk_get<NSL>(ring, ready, g + 1, &abt, opaque(A.err));
+                const float us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
+                chunk_put<NSL>(done, g + 1, lane);
+                const float mv = rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us);
+                mword |= (uint64_t)f2bf_bits(mv) << (16 * ((i - wave) / NC));
+            }
         }
         if (lane < NREP) xstore64((uint64_t *)opaque(A.x_m) + lane * (RSM / 2) + b * NC + wave, mword);
 
@@ -773,9 +966,14 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 #pragma unroll
             for (int q = 0; q < DCH; ++q) {
                 const unsigned g = gb + S.oD() + wave * DCH + q;
-                const unsigned char *c = chunk_get(ring, ready, g, &abt, opaque(A.err));
-                a = dot_chunk(c, load_x(ys + q * HID, lane), lane, a);
-                chunk_put(done, g, lane);
+                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                if constexpr (Q8) {  // third q of the row: codes q * 2048 .. + 2047
+                    const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSL) * SBB);
+                    a += dot_q8_row(c, 0, 1, sb, load_x8(ys + q * HID, lane), lane);
+                } else {
+                    a = dot_chunk(c, load_x(ys + q * HID, lane), lane, a);
+                }
+                chunk_put<NSL>(done, g, lane);
             }
             const float acc = wave_sum(a);
             if (lane < NREP) xstore(opaque(A.x_pend) + lane * RSH + b * OPB + wave, tagw(tag, acc));
@@ -807,26 +1005,18 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 }  // namespace mk
 
 // ------------------------------------------------------------ host side
-size_t decode_mk_workspace(int n_layers, int H, int KV, int hid, int I) {
-    const size_t nsplit = mk::NB / (KV > 0 ? KV : 1);
-    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    const size_t nqkv = (size_t)(H + 2 * KV) * mk::D;
-    const size_t rh = (size_t)mk::NREP * mk::rep_stride(hid) * 4, rm = (size_t)mk::NREP * mk::rep_stride(I) * 4;
-    return al(sizeof(mk::DevLayer) * n_layers) + al(nqkv * 4) + 3 * al(rh) + al(rm) +
-           al((size_t)H * nsplit * (mk::D + 2) * 8) + al(256);
-}
-
 namespace {
 struct MkLayout {
-    size_t layers, qkv, a, h2, m, pend, part, ctr;
+    size_t layers, layersq, qkv, a, h2, m, pend, part, ctr, total;
 };
 MkLayout mk_layout(int n_layers, int H, int KV, int hid, int I) {
-    const size_t nsplit = mk::NB / KV;
+    const size_t nsplit = mk::NB / (KV > 0 ? KV : 1);
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const size_t nqkv = (size_t)(H + 2 * KV) * mk::D;
     MkLayout L{};
     size_t o = 0;
     L.layers = o; o += al(sizeof(mk::DevLayer) * n_layers);
+    L.layersq = o; o += al(sizeof(mk::DevLayerQ) * n_layers);
     L.qkv = o; o += al(nqkv * 4);
     const size_t rh = (size_t)mk::NREP * mk::rep_stride(hid) * 4, rm = (size_t)mk::NREP * mk::rep_stride(I) * 4;
     L.a = o; o += al(rh);
@@ -834,16 +1024,17 @@ MkLayout mk_layout(int n_layers, int H, int KV, int hid, int I) {
     L.m = o; o += al(rm);
     L.pend = o; o += al(rh);
     L.part = o; o += al((size_t)H * nsplit * (mk::D + 2) * 8);
-    L.ctr = o;
+    L.ctr = o; o += al(256);
+    L.total = o;
     return L;
 }
 
-template <int QPB, int GPB, int DCH, int G> const void *mk_fn() {
-    return (const void *)mk::decode_mk_kernel<QPB, GPB, DCH, G>;
+template <int QPB, int GPB, int DCH, int G, bool Q8> const void *mk_fn() {
+    return (const void *)mk::decode_mk_kernel<QPB, GPB, DCH, G, Q8>;
 }
 
-const void *mk_select(int hid, int I, int G, int nqkv) {
-    if (hid == 2048 && I == 6144 && nqkv == 4096 && G == 2) return mk_fn<16, 24, 3, 2>();
+const void *mk_select(int hid, int I, int G, int nqkv, bool q8) {
+    if (hid == 2048 && I == 6144 && nqkv == 4096 && G == 2) return q8 ? mk_fn<16, 24, 3, 2, true>() : mk_fn<16, 24, 3, 2, false>();
     return nullptr;
 }
 
@@ -853,22 +1044,29 @@ int mk_chunk(int nkeys, int nsplit) {  // keys per split, a multiple of a K/V ch
 }
 }  // namespace
 
+size_t decode_mk_workspace(int n_layers, int H, int KV, int hid, int I) { return mk_layout(n_layers, H, KV, hid, I).total; }
+
 bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, int hid, int H, int KV, int D, int I,
                          int cap) {
-    if (dt != DT_BF16 || n_experts > 0 || quant_bits != 0 || D != mk::D) return false;
+    if (dt != DT_BF16 || n_experts > 0 || (quant_bits != 0 && quant_bits != 8) || D != mk::D) return false;
     if (n_layers < 1 || n_layers > mk::MAXL) return false;  // tags are call * 64 + layer
     if (hid != mk::HID || H * D != hid || H % KV || mk::NB % KV || mk::NB % H) return false;
     const int nsplit = mk::NB / KV;
     if (nsplit > mk::NSPLIT_MAX || mk_chunk(cap, nsplit) > mk::CHUNK_MAX) return false;
     if (nsplit * (2 + H * D / mk::NB) > mk::NC * (H / KV) * mk::D) return false;  // merge buffer fits in LDS
-    return mk_select(hid, I, H / KV, (H + 2 * KV) * D) != nullptr;
+    return mk_select(hid, I, H / KV, (H + 2 * KV) * D, quant_bits == 8) != nullptr;
 }
 
-hipError_t decode_mk_init(void *ws, int n_layers, int H, int KV, int hid, int I, const void *layer_ptrs, hipStream_t s) {
+hipError_t decode_mk_init(void *ws, int n_layers, int H, int KV, int hid, int I, const void *layer_ptrs,
+                          const void *layer_q8_ptrs, hipStream_t s) {
     const MkLayout L = mk_layout(n_layers, H, KV, hid, I);
     char *b = (char *)ws;
     hipError_t e = hipMemcpyAsync(b + L.layers, layer_ptrs, sizeof(mk::DevLayer) * n_layers, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return e;
+    if (layer_q8_ptrs) {
+        e = hipMemcpyAsync(b + L.layersq, layer_q8_ptrs, sizeof(mk::DevLayerQ) * n_layers, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+    }
     // exchange words start with tag 0xffff, never the tag of a first call's layer
     e = hipMemsetAsync(b + L.qkv, 0xff, L.ctr - L.qkv, s);
     if (e != hipSuccess) return e;
@@ -877,19 +1075,20 @@ hipError_t decode_mk_init(void *ws, int n_layers, int H, int KV, int hid, int I,
     return hipStreamSynchronize(s);  // layer_ptrs is a caller's host array
 }
 
-hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, int cap, int p, int window,
+hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int I, bool q8, int cap, int p, int window,
                             float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
                             const void *sin_t, void *kc, void *vc, int *err, hipStream_t s) {
     const MkLayout L = mk_layout(n_layers, H, KV, hid, I);
     char *b = (char *)ws;
     const int nsplit = mk::NB / KV;
-    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
+    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D, q8);
     const int nvis = window > 0 ? min(p + 1, window) : p + 1;  // keys the new token sees
     if (!fn || p < 0 || p >= cap || window < 0 || n_layers < 1 || n_layers > mk::MAXL ||
         mk_chunk(nvis, nsplit) > mk::CHUNK_MAX)
         return hipErrorInvalidValue;
     mk::Args A;
     A.layers = (const mk::DevLayer *)(b + L.layers);
+    A.layersq = (const mk::DevLayerQ *)(b + L.layersq);
     A.n_layers = n_layers;
     A.H = H;
     A.KV = KV;
@@ -925,8 +1124,8 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
     return hipLaunchKernel(fn, dim3(mk::NB), dim3(mk::NTH), args, 0, s);
 }
 
-int decode_mk_max_blocks(int hid, int I, int H, int KV) {
-    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D);
+int decode_mk_max_blocks(int hid, int I, int H, int KV, bool q8) {
+    const void *fn = mk_select(hid, I, H / KV, (H + 2 * KV) * mk::D, q8);
     if (!fn) return 0;
     int per_cu = 0, dev = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, mk::NTH, 0) != hipSuccess) return 0;

@@ -262,7 +262,7 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
     const qwen3_config &c = h->cfg;
     if (h->mk_ready && h->decode_path != 1) {
         HIPCHECK(h, mark(h, K_STEP, true));
-        HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate,
+        HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate, is_q8(h),
                                      c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
                                      h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
         HIPCHECK(h, mark(h, K_STEP, false));
@@ -558,17 +558,19 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
     if (e == hipSuccess && decode_mk_supported(cfg->n_layers, cfg->dtype, cfg->n_experts, cfg->quant_bits, cfg->hidden,
                                                cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->intermediate,
                                                cfg->capacity) &&
-        decode_mk_max_blocks(cfg->hidden, cfg->intermediate, cfg->n_heads, cfg->n_kv_heads) >= decode_mk_blocks()) {
-        std::vector<const void *> ptrs;
+        decode_mk_max_blocks(cfg->hidden, cfg->intermediate, cfg->n_heads, cfg->n_kv_heads, q8) >= decode_mk_blocks()) {
+        std::vector<const void *> ptrs, qptrs;
         for (int l = 0; l < cfg->n_layers; ++l) {
             const qwen3_layer_weights &Lw = w->layers[l];
             const void *row[9] = {Lw.in_norm,  Lw.post_norm, Lw.q_norm, Lw.k_norm,  Lw.qkv,
                                   Lw.o,        Lw.gate_up,   Lw.down,   Lw.qkv_bias};
             ptrs.insert(ptrs.end(), row, row + 9);
+            const void *qrow[8] = {Lw.qkv_s, Lw.qkv_b, Lw.o_s, Lw.o_b, Lw.gate_up_s, Lw.gate_up_b, Lw.down_s, Lw.down_b};
+            qptrs.insert(qptrs.end(), qrow, qrow + 8);
         }
         h->mk_ws = b + L.mk;
         e = decode_mk_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, cfg->hidden, cfg->intermediate,
-                           ptrs.data(), h->stream);
+                           ptrs.data(), q8 ? qptrs.data() : nullptr, h->stream);
         h->mk_ready = e == hipSuccess;
     }
     if (e != hipSuccess) {

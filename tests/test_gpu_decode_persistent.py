@@ -200,3 +200,76 @@ def test_decode_path_selection():
     with pytest.raises(q3.Qwen3Error):
         q3.qwen3_set_decode_path(seat.handle, 3)
     q3.qwen3_set_decode_path(seat.handle, 0)
+
+
+# ------------------------------------------------------------------ 8-bit weights
+
+@pytest.mark.parametrize("filled", [4095, 0, 31, 1000])
+def test_persistent_q8_one_layer_vs_oracle_and_kernels(orc, filled):
+    """The persistent step with 8-bit group-quantised projections (the 1.7B shape's q8
+    configuration): one layer against the oracle (weights dequantised exactly, never rounded)
+    and against the one-kernel-per-step path."""
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8
+    say(f"persistent decode, 8-bit weights, 1 layer, position {filled}")
+    cfg, w, mk, ref = _seats(QWEN3_1P7B_Q8, 1, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, 1, DEV)
+    a = mk.forward_hidden(x)
+    b = ref.forward_hidden(x)
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    o = st.forward(np32(x))
+    e, e_ref = max_row_rel_l2(np32(a), o), max_row_rel_l2(np32(b), o)
+    e_paths = max_row_rel_l2(np32(a), np32(b))
+    ek = max_row_rel_l2(np32(mk.k)[:, :, filled], st.k[:, :, filled])
+    ev = max_row_rel_l2(np32(mk.v)[:, :, filled], st.v[:, :, filled])
+    say(f"  vs oracle {e:.2e} (one-kernel-per-step path {e_ref:.2e}), vs that path {e_paths:.2e}, "
+        f"new K {ek:.2e}, new V {ev:.2e}")
+    gate(np32(a), o, "bf16")
+    assert max(ek, ev) <= BF16_TOL and e_paths <= BF16_TOL
+
+
+def test_persistent_q8_full_stack(orc):
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8
+    filled = 4095
+    say("persistent decode, 8-bit weights, 28 layers, ctx 4096")
+    cfg, w, mk, ref = _seats(QWEN3_1P7B_Q8, None, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, 1, DEV)
+    a = mk.forward_hidden(x)
+    b = ref.forward_hidden(x)
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    o = st.forward(np32(x))
+    e, e_ref, e_paths = max_row_rel_l2(np32(a), o), max_row_rel_l2(np32(b), o), max_row_rel_l2(np32(a), np32(b))
+    say(f"  vs oracle {e:.2e} (one-kernel-per-step path {e_ref:.2e}), vs that path {e_paths:.2e}")
+    assert e < 0.05 and e_paths < 0.05
+
+
+def test_persistent_q8_consecutive_steps_with_qwen2_switches(orc):
+    """8-bit weights with page 2's switches (no q/k norm, q|k|v bias, a sliding window of 40):
+    six steps in a row from position 50 over two layers, against the oracle and the kernel path."""
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_Q8
+    cfg0 = QWEN3_1P7B_Q8.replace(qk_norm=False, attention_bias=True, sliding_window=40)
+    filled, n = 50, 6
+    say(f"persistent decode, 8-bit weights + Qwen2 switches, 2 layers, {n} steps from position {filled}")
+    cfg, w, mk, ref = _seats(cfg0, 2, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, n, DEV)
+    outs = [mk.forward_hidden(x[i:i + 1]) for i in range(n)]
+    outs_ref = [ref.forward_hidden(x[i:i + 1]) for i in range(n)]
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    xs = np32(x)
+    worst = 0.0
+    for i in range(n):
+        worst = max(worst, max_row_rel_l2(np32(outs[i]), st.forward(xs[i:i + 1])))
+        assert max_row_rel_l2(np32(outs[i]), np32(outs_ref[i])) <= BF16_TOL
+    say(f"  worst step vs oracle {worst:.2e}")
+    assert worst <= 2 * BF16_TOL
