@@ -273,7 +273,14 @@ def moe_bench(steps: int, warmup: int, q8: bool = False):
         seat.length = 2047
         q3.qwen3_forward_hidden(seat.handle, x1, o1)
 
+    path = q3.qwen3_get_decode_path(seat.handle)
     t_dec = _graph_seconds(dec, stream, steps, warmup)
+    q3.qwen3_check_device_errors(seat.handle)
+    t_dec_kernels = None
+    if path == 2:  # the one-kernel-per-step path beside it
+        q3.qwen3_set_decode_path(seat.handle, 1)
+        t_dec_kernels = _graph_seconds(dec, stream, steps, warmup)
+        q3.qwen3_set_decode_path(seat.handle, 0)
 
     def call64():  # positions 0..63; cache entries at and past the length are never read
         seat.length = 0
@@ -295,7 +302,9 @@ def moe_bench(steps: int, warmup: int, q8: bool = False):
     b64 = cfg.n_layers * (qkv_o_router + 125.95 * expert_bytes)
     res = {"workload": f"Qwen3-MoE-shaped {'8-bit-weight (groups of 64) ' if q8 else ''}bf16 stack: 48 layers, "
                        "hidden 2048, 32 q / 4 kv heads, 128 experts, top-8 renormalised, expert intermediate 768",
+           "decode_path": {1: "one kernel per step", 2: "persistent"}.get(path, path),
            "decode_ms_per_step": round(t_dec * 1e3, 4), "decode_tokens_per_s": round(1 / t_dec, 2),
+           "decode_ms_per_step_one_kernel_per_step": None if t_dec_kernels is None else round(t_dec_kernels * 1e3, 4),
            "decode_step_bytes": step_bytes, "decode_gbps": round(step_bytes / t_dec / 1e9, 1),
            "decode_hbm_frac": round(step_bytes / t_dec / 1e9 / HBM_PEAK_GBPS, 4),
            "T64_ms": round(t64 * 1e3, 4), "T64_tokens_per_s": round(64 / t64, 1),

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqwen3.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["kernels_elem.hip", "kernels_linear.hip", "kernels_gemm.hip", "kernels_attn.hip", "kernels_moe.hip",
-           "kernels_q8.hip", "kernels_decode_mk.hip", "kernels_head.hip", "qwen3_api.cpp", "qwen3_ops.cpp"]
+           "kernels_q8.hip", "kernels_decode_mk.hip", "kernels_decode_moe.hip", "kernels_head.hip", "qwen3_api.cpp", "qwen3_ops.cpp"]
 ARCH = os.environ.get("QWEN3_OFFLOAD_ARCH", "gfx950")
 
 

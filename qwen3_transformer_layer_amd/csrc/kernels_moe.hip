@@ -39,6 +39,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "moe_route.h"
 
 namespace q3 {
 
@@ -66,68 +67,14 @@ MoeWs moe_layout(int T, int hid, int E, int k, int Ie, int dt) {
 size_t moe_workspace(int T, int hid, int E, int k, int Ie, int dt) { return moe_layout(T, hid, E, k, Ie, dt).total; }
 
 // ------------------------------------------------------------ softmax + top-k + renormalise
-// The k largest of the wave's values (lane l holds experts l + 64 i), ties to the lower
-// expert index: each round takes the maximum over the experts not taken yet (DPP) and the
-// lowest index holding it (ballots in index order).  A NaN ranks as -inf and experts e >= E
-// are never candidates, so every round picks a valid, new expert (k <= E).
-template <int EPL>
-__device__ __forceinline__ void select_topk(const float (&v)[EPL], int E, int k, int lane, float *psel, int *isel) {
-    float x[EPL];
-    unsigned taken = 0;  // bit i: expert lane + 64 i is selected or does not exist
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        x[i] = v[i] == v[i] ? v[i] : -INFINITY;
-        if (lane + 64 * i >= E) taken |= 1u << i;
-    }
-    for (int s = 0; s < k; ++s) {
-        float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (!((taken >> i) & 1u)) lm = fmaxf(lm, x[i]);
-        const float m = wave_max(lm);
-        int bi = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const unsigned long long msk = __ballot(!((taken >> i) & 1u) && x[i] == m);
-            if (msk) {
-                bi = 64 * i + (int)__builtin_ctzll(msk);
-                break;
-            }
-        }
-        psel[s] = m;
-        isel[s] = bi;
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    }
-}
-
-// Softmax over the token's E logits in fp32, probabilities rounded to the model dtype
-// (v[i] for expert lane + 64 i; -inf past E).
+// (select_topk and softmax_inplace: moe_route.h)
+// The token's E logits as fp32, v[i] for expert lane + 64 i (-inf past E), then their softmax.
 template <typename T, int EPL>
 __device__ __forceinline__ void load_logits(const T *l, int E, int lane, float (&v)[EPL]) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         v[i] = e < E ? to_f(l[e]) : -INFINITY;
-    }
-}
-template <typename T, int EPL>
-__device__ __forceinline__ void softmax_inplace(int E, int lane, float (&v)[EPL]) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
-    m = wave_max(m);
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? __expf(v[i] - m) : 0.f;
-        z += v[i];
-    }
-    z = wave_sum(z);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? rho<T>(v[i] / z) : -INFINITY;
     }
 }
 template <typename T, int EPL>

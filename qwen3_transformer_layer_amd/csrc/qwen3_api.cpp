@@ -50,9 +50,9 @@ struct qwen3_handle {
     unsigned long long *head_keys = nullptr;  // greedy-token keys, one per row
     int32_t *moe_idx = nullptr;
     void *moe_w = nullptr, *moe_ws = nullptr;
-    // persistent decode step (dense bf16 shapes it supports)
+    // persistent decode step (the dense bf16 / 8-bit shapes and the MoE shape it supports)
     void *mk_ws = nullptr;
-    bool mk_ready = false;
+    bool mk_ready = false, mk_moe = false;
     int decode_path = 0;  // 0 auto, 1 separate kernels, 2 persistent kernel
     // measurement: event pairs around launches of one kernel kind
     static constexpr int NKIND = 6;
@@ -77,6 +77,12 @@ struct Layout {
 };
 
 size_t esize(const qwen3_config &c) { return c.dtype == QWEN3_BF16 ? 2 : 4; }
+
+// A configuration the persistent MoE decode kernel is built for (its layers must all be MoE too)
+bool moe_mk_config(const qwen3_config &c) {
+    return c.n_experts > 0 && decode_moe_supported(c.n_layers, c.dtype, c.quant_bits, c.hidden, c.n_heads, c.n_kv_heads,
+                                                   c.head_dim, c.n_experts, c.top_k, c.moe_intermediate, c.capacity);
+}
 
 Layout layout(const qwen3_config &c) {
     Layout L{};
@@ -110,6 +116,8 @@ Layout layout(const qwen3_config &c) {
     if (decode_mk_supported(c.n_layers, c.dtype, c.n_experts, c.quant_bits, c.hidden, c.n_heads, c.n_kv_heads, c.head_dim,
                             c.intermediate, c.capacity))
         L.mk = take(decode_mk_workspace(c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate));
+    else if (moe_mk_config(c))
+        L.mk = take(decode_moe_workspace(c.n_layers, c.n_heads, c.n_kv_heads));
     L.total = o;
     return L;
 }
@@ -262,9 +270,14 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
     const qwen3_config &c = h->cfg;
     if (h->mk_ready && h->decode_path != 1) {
         HIPCHECK(h, mark(h, K_STEP, true));
-        HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate, is_q8(h),
-                                     c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
-                                     h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
+        if (h->mk_moe)
+            HIPCHECK(h, launch_decode_moe(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.n_experts, c.norm_topk_prob,
+                                          c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
+                                          h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
+        else
+            HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate,
+                                         is_q8(h), c.capacity, h->length, c.sliding_window, c.rms_eps, x, out,
+                                         h->final_norm, h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
         HIPCHECK(h, mark(h, K_STEP, false));
         return QWEN3_OK;
     }
@@ -572,6 +585,21 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
         e = decode_mk_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, cfg->hidden, cfg->intermediate,
                            ptrs.data(), q8 ? qptrs.data() : nullptr, h->stream);
         h->mk_ready = e == hipSuccess;
+    } else if (e == hipSuccess && moe_mk_config(*cfg) && decode_moe_max_blocks() >= decode_mk_blocks()) {
+        bool all_moe = true;  // the persistent MoE step has no dense-MLP layers
+        std::vector<const void *> ptrs;
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            const qwen3_layer_weights &Lw = w->layers[l];
+            all_moe = all_moe && Lw.router;
+            const void *row[10] = {Lw.in_norm, Lw.post_norm, Lw.q_norm,  Lw.k_norm,   Lw.qkv,
+                                   Lw.o,       Lw.router,    Lw.exp_gate_up, Lw.exp_down, Lw.qkv_bias};
+            ptrs.insert(ptrs.end(), row, row + 10);
+        }
+        if (all_moe) {
+            h->mk_ws = b + L.mk;
+            e = decode_moe_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, ptrs.data(), h->stream);
+            h->mk_ready = h->mk_moe = e == hipSuccess;
+        }
     }
     if (e != hipSuccess) {
         delete h;
