@@ -230,9 +230,10 @@ int qwen3_set_stream(qwen3_handle *h, void *stream);
  * kernel when the configuration and device support it, on a device that holds 256
  * co-resident blocks of 704 threads: dense bf16 stacks with bf16 or 8-bit group-quantised
  * projection weights (quant_group 64), head_dim 128, hidden 2048 = n_heads * head_dim,
- * intermediate 6144, 2 query heads per kv head, capacity <= 8192; or bf16 MoE stacks whose
- * every layer has a router, with hidden 2048, 32 q / 4 kv heads of 128, at most 128 experts,
- * top 8, moe_intermediate 768, capacity <= 8192 -- else one kernel per
+ * intermediate 6144, 2 query heads per kv head, capacity <= 8192; or MoE stacks (bf16 or
+ * 8-bit weights, router and experts included) whose every layer has a router, with hidden
+ * 2048, 32 q / 4 kv heads of 128, 8 to 128 experts, top 8, moe_intermediate 768, capacity
+ * <= 8192 -- else one kernel per
  * step of the layer; 1: always one kernel per step; 2: require the persistent kernel
  * (QWEN3_ERR_UNSUPPORTED when unavailable).  Both compute the same values up to fp32
  * summation order.  qwen3_get_decode_path returns the path T == 1 calls take (1 or 2).

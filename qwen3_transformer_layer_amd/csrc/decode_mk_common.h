@@ -294,6 +294,39 @@ __device__ __forceinline__ float csum(float v, float (*red)[NC], unsigned &par, 
     return t;
 }
 
+// Merge of the split-K attention partials of one output dim, from LDS: pm[s], pl[s] are split s's
+// max and sum, po[s * dpb + d] its output for dim d (an empty split has max -inf, sum 0).  Thread
+// t < LPD dpb takes dim t / LPD and splits t % LPD, + LPD, ...; the LPD lanes of a dim combine by
+// xor shuffles, giving a = (sum_s o_s e^(m_s - M)) / (sum_s l_s e^(m_s - M)), M = max_s m_s.
+// Returns true on the lane holding a dim's result (t % LPD == 0).  Splitting the serial loop over
+// the splits across lanes matters: each step of it is an LDS read's latency.
+template <int LPD>
+__device__ __forceinline__ bool merge_lds(const float *pm, const float *pl, const float *po, int ns, int dpb, int tid,
+                                          float *a) {
+    if (tid >= LPD * dpb) return false;
+    const int d = tid / LPD, pt = tid % LPD;
+    float M = -INFINITY;
+    for (int s = pt; s < ns; s += LPD) M = fmaxf(M, pm[s]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY)
+        for (int s = pt; s < ns; s += LPD) {
+            const float f = __expf(pm[s] - M);
+            L += pl[s] * f;
+            O += po[s * dpb + d] * f;
+        }
+#pragma unroll
+    for (int off = LPD / 2; off > 0; off >>= 1) {
+        const float M2 = __shfl_xor(M, off), L2 = __shfl_xor(L, off), O2 = __shfl_xor(O, off);
+        const float Mn = fmaxf(M, M2);
+        const float f1 = M == -INFINITY ? 0.f : __expf(M - Mn), f2 = M2 == -INFINITY ? 0.f : __expf(M2 - Mn);
+        L = L * f1 + L2 * f2;
+        O = O * f1 + O2 * f2;
+        M = Mn;
+    }
+    *a = O / L;
+    return pt == 0;
+}
+
 // 4-byte direct-to-LDS copy: lane l's word lands at LDS byte address lds + 4 l.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"

@@ -151,17 +151,20 @@ hipError_t launch_decode_mk(void *ws, int n_layers, int H, int KV, int hid, int 
                             const void *sin_t, void *kc, void *vc, int *err, hipStream_t s);
 int decode_mk_max_blocks(int hid, int I, int H, int KV, bool q8);
 int decode_mk_blocks();
-// ---- persistent decode step for Qwen3-MoE stacks (kernels_decode_moe.hip): bf16, hidden 2048,
-// 32 q / 4 kv heads of 128, E <= 128 experts, top 8, expert intermediate 768, every layer MoE.
-// layer_ptrs: n_layers rows of {in_norm, post_norm, q_norm, k_norm, qkv, o, router, exp_gate_up,
-// exp_down, qkv_bias}.
+// ---- persistent decode step for Qwen3-MoE stacks (kernels_decode_moe.hip): bf16 model with bf16
+// or 8-bit (groups of 64) weights, hidden 2048, 32 q / 4 kv heads of 128, E <= 128 experts, top 8,
+// expert intermediate 768, every layer MoE.  layer_ptrs: n_layers rows of {in_norm, post_norm,
+// q_norm, k_norm, qkv, o, router, exp_gate_up, exp_down, qkv_bias} (code arrays with 8-bit
+// weights); layer_q8_ptrs (8-bit, else null): n_layers rows of scale then bias of {qkv, o, router,
+// exp_gate_up, exp_down}.
 bool decode_moe_supported(int n_layers, int dt, int quant_bits, int hid, int H, int KV, int D, int E, int k, int Ie,
                           int cap);
 size_t decode_moe_workspace(int n_layers, int H, int KV);
-hipError_t decode_moe_init(void *ws, int n_layers, int H, int KV, const void *layer_ptrs, hipStream_t s);
-hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int norm_topk, int cap, int p, int window,
-                             float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
+hipError_t decode_moe_init(void *ws, int n_layers, int H, int KV, const void *layer_ptrs, const void *layer_q8_ptrs,
+                           hipStream_t s);
+hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int norm_topk, bool q8, int cap, int p,
+                             int window, float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
                              const void *sin_t, void *kc, void *vc, int *err, hipStream_t s);
-int decode_moe_max_blocks();
+int decode_moe_max_blocks(bool q8);
 
 }  // namespace q3

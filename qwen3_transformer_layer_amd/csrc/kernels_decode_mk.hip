@@ -250,8 +250,8 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     __shared__ float sc[G * CHUNK_MAX];
     __shared__ float red[NC * G * D];
     __shared__ float rsum[2][NC];
-    __shared__ float mrow[G], lrow[G];
     __shared__ float pm[NSPLIT_MAX], pl[NSPLIT_MAX];
+    __shared__ float mrow[G], lrow[G];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), b = blockIdx.x;
     const int H = A.H, KV = A.KV;
@@ -573,18 +573,11 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
                 }
             }
             cbar(&bar, ep, &abt, opaque(A.err), lane);
-            if (tid < dpb) {
-                float M = -INFINITY;
-                for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s]);
-                float Ls = 0.f, acc = 0.f;
-                for (int s = 0; s < ns; ++s) {
-                    const float f = __expf(pm[s] - M);
-                    Ls += pl[s] * f;
-                    acc += po[s * dpb + tid] * f;
-                }
-                const uint32_t w = tagw(tag, acc / Ls);
+            float av;
+            if (merge_lds<8>(pm, pl, po, ns, dpb, tid, &av)) {  // wave 0: 8 lanes per dim
+                const uint32_t w = tagw(tag, av);
 #pragma unroll
-                for (int r = 0; r < NREP; ++r) xstore(opaque(A.x_a) + r * RSH + mh * D + md0 + tid, w);
+                for (int r = 0; r < NREP; ++r) xstore(opaque(A.x_a) + r * RSH + mh * D + md0 + tid / 8, w);
             }
         }
 
@@ -764,6 +757,7 @@ bool decode_mk_supported(int n_layers, int dt, int n_experts, int quant_bits, in
     const int nsplit = mk::NB / KV;
     if (nsplit > mk::NSPLIT_MAX || mk_chunk(cap, nsplit) > mk::CHUNK_MAX) return false;
     if (nsplit * (2 + H * D / mk::NB) > mk::NC * (H / KV) * mk::D) return false;  // merge buffer fits in LDS
+    if (8 * (H * D / mk::NB) > 64) return false;  // the merge: one wave, 8 lanes per dim
     return mk_select(hid, I, H / KV, (H + 2 * KV) * D, quant_bits == 8) != nullptr;
 }
 

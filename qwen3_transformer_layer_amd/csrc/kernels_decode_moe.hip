@@ -32,6 +32,10 @@
 //    bytes from the expert of the slot they fall in.  A lane adds each 8-input piece to its
 //    slot's sum, the wave reduces the k sums, and the output is rho(sum_s rho(rho(y_s) w_s))
 //    with the sum in slot order.
+// 8-bit weights (router and experts included; u8 codes, bf16 scale and bias per 64 inputs) as in
+// the dense kernel: a ring chunk holds the codes of two q|k|v rows, one o_proj row (4096 codes),
+// one router row, the gate and the up row of one SwiGLU output, or one third of a virtual down
+// row, and a 256-byte side slot their groups' scales and biases; every chunk is five copies.
 #include "common.h"
 #include "decode_mk_common.h"
 #include "kernels.h"
@@ -55,15 +59,24 @@ constexpr int DCH = IM * 2 / CHB;  // chunks per virtual down row (3)
 constexpr int EMAX = 128;       // experts (two per lane in the routing wave)
 constexpr int CHM = 128;        // keys per attention split
 constexpr int NSM = 29;         // ring slots (116 KB)
+constexpr int NSMQ = 27;        // ring slots with 8-bit weights (108 KB + 6.75 KB of scale/bias slots)
+constexpr int SBM = 256;        // scale/bias bytes per chunk (8-bit weights)
 static_assert(NQKV % NB == 0 && IE % GPB == 0 && GPB == 3 * NC && IM * 2 == DCH * CHB && OPB == NC, "shape");
-static_assert(NSM >= NL * DL, "the ring holds every stream wave's chunks in flight");
+static_assert(NSMQ >= NL * DL, "the ring holds every stream wave's chunks in flight");
+template <bool Q8> __host__ __device__ constexpr int ring_slots() { return Q8 ? NSMQ : NSM; }
 
 struct DevLayer {  // q_norm / k_norm both null: no per-head q/k norm; qkv_bias null: no bias
     const bf16 *in_norm, *post_norm, *q_norm, *k_norm, *qkv, *o, *router, *exp_gu, *exp_down, *qkv_bias;
 };
 
+struct DevLayerQ {  // 8-bit weights: (scale, bias) array pairs [rows][K / 64] of q|k|v, o, router, experts
+    const bf16 *qkv_s, *qkv_b, *o_s, *o_b, *router_s, *router_b, *egu_s, *egu_b, *edown_s, *edown_b;
+};
+static_assert(sizeof(DevLayerQ) == 80, "five (scale, bias) pairs of 16 bytes, read as pairs");
+
 struct Args {
     const DevLayer *layers;
+    const DevLayerQ *layersq;  // 8-bit weights only
     int n_layers, H, KV, E, cap, p, nsplit, chunk, window, norm_topk;  // window 0: causal
     float eps, scale;
     const bf16 *x, *final_norm, *cos_t, *sin_t;
@@ -74,26 +87,49 @@ struct Args {
     int *err;
 };
 
-// Per layer the block consumes, in this order: QPB q|k|v rows, nK K chunks and nK V chunks of
-// its attention split, 2 OPB o_proj half rows, its router row (blocks b < E), GPB gate/up row
-// pairs (gate, then up), OPB virtual down rows of DCH chunks each.
-struct Seq {
+// Per layer the block consumes, in this order: its QPB q|k|v rows, nK K chunks and nK V chunks of
+// its attention split, its OPB o_proj rows, its router row (blocks b < E), its GPB gate/up row
+// pairs, OPB virtual down rows of DCH chunks each.  Chunks: bf16 -- one q|k|v row, half an o_proj
+// row, one router row, a gate or an up row, a third of a down row; 8-bit -- two q|k|v rows, one
+// o_proj row, one router row, a gate/up pair, a third of a down row.
+template <bool Q8> struct Seq {
+    static constexpr int QC = Q8 ? QPB / 2 : QPB, OC = Q8 ? OPB : 2 * OPB, GC = Q8 ? GPB : 2 * GPB, DC = OPB * DCH;
     int nK, rc, cpl;
-    __device__ Seq(int nK_, int rc_) : nK(nK_), rc(rc_), cpl(QPB + 2 * nK_ + 2 * OPB + rc_ + 2 * GPB + OPB * DCH) {}
-    __device__ int oK() const { return QPB; }
-    __device__ int oV() const { return QPB + nK; }
-    __device__ int oO() const { return QPB + 2 * nK; }
-    __device__ int oR() const { return QPB + 2 * nK + 2 * OPB; }
-    __device__ int oG() const { return QPB + 2 * nK + 2 * OPB + rc; }
-    __device__ int oD() const { return QPB + 2 * nK + 2 * OPB + rc + 2 * GPB; }
+    __device__ Seq(int nK_, int rc_) : nK(nK_), rc(rc_), cpl(QC + 2 * nK_ + OC + rc_ + GC + DC) {}
+    __device__ int oK() const { return QC; }
+    __device__ int oV() const { return QC + nK; }
+    __device__ int oO() const { return QC + 2 * nK; }
+    __device__ int oR() const { return QC + 2 * nK + OC; }
+    __device__ int oG() const { return QC + 2 * nK + OC + rc; }
+    __device__ int oD() const { return QC + 2 * nK + OC + rc + GC; }
 };
 
 // Release weights of a chunk: the stream wave refills slot s for chunk g once done[s] reaches
 // 8 (g / NSM), each earlier chunk of the slot having added 8 in all.
 constexpr unsigned REL = 8;
-__device__ __forceinline__ void chunk_put_w(unsigned *done, unsigned g, int lane, unsigned w) {
+template <int NSL> __device__ __forceinline__ void chunk_put_w(unsigned *done, unsigned g, int lane, unsigned w) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) __hip_atomic_fetch_add(done + g % NSM, w, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) __hip_atomic_fetch_add(done + g % NSL, w, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The (scale, bias) array pointers of field pair `pair` (0 q|k|v, 1 o, 2 router, 3 expert gate|up,
+// 4 expert down) of a layer's 8-bit entry, read with one scalar load completed inside the asm (a
+// vector load would sit in the stream wave's counter beside the ring copies).
+__device__ __forceinline__ void load_sb_pair(const DevLayerQ *e, int pair, const bf16 *&sc, const bf16 *&bi) {
+    const uint64_t a = (uint64_t)e + 16u * (unsigned)pair;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    u32x4 v;
+    __asm__ volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(((uint64_t)hi << 32) | lo) : "memory");
+    typedef __attribute__((address_space(1))) const bf16 GB;
+    sc = (const bf16 *)(GB *)(((uint64_t)v[1] << 32) | v[0]);
+    bi = (const bf16 *)(GB *)(((uint64_t)v[3] << 32) | v[2]);
+}
+
+// 8-bit: one 16-code piece against 16 activations, s (x . q) + b (sum x), for the down thirds.
+__device__ __forceinline__ float q8_piece(const unsigned char *c, int piece, float s, float b, u32x4 xa, u32x4 xb,
+                                          float xs, int lane) {
+    const u32x4 cw = *(const u32x4 *)(c + piece * 1024 + lane * 16);
+    return s * dot16_codes(cw, xa, xb, 0.f) + b * xs;
 }
 
 // A lane's four 8-input partial dots of a chunk (the X4 interleave: piece k covers inputs
@@ -116,11 +152,13 @@ __device__ __forceinline__ void dot_pieces(const unsigned char *c, const X4 &x, 
 
 // Stream wave j: chunks g = j, j + NL, ... of the whole step, in order.  Expert rows wait for
 // the layer's routing (rgen, route_e in LDS).
-__device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *ring, unsigned *ready,
-                            const unsigned *done, const unsigned *rgen, const int (*route_e)[KSEL], unsigned *abt,
-                            int j, int ag, int j0, int j1, int nK) {
+template <bool Q8>
+__device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *ring, unsigned char *sbring,
+                            unsigned *ready, const unsigned *done, const unsigned *rgen, const int (*route_e)[KSEL],
+                            unsigned *abt, int j, int ag, int j0, int j1, int nK) {
+    constexpr int NSM = ring_slots<Q8>(), VPC = Q8 ? 5 : 4;  // slots; copies per chunk
     const int lane = tid_now() & 63, b = blockIdx.x;
-    const Seq S(nK, b < A.E ? 1 : 0);
+    const Seq<Q8> S(nK, b < A.E ? 1 : 0);
     const unsigned total = (unsigned)A.n_layers * (unsigned)S.cpl;
     auto publish = [&](unsigned g) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -142,7 +180,69 @@ __device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *r
             routed = l + 1;
         }
         const unsigned char *src[4];
-        if (idx < S.oK()) {
+        const void *sbsrc = nullptr;  // 8-bit: the lane's 4 bytes of the chunk's scale/bias copy
+        if (Q8 && (idx < S.oK() || idx >= S.oO())) {
+            // codes: pieces 0, 1 from row r0 (at w0), pieces 2, 3 from row r1 (at w1); scale/bias copy:
+            // lanes 0-15 s[r0], 16-31 b[r0], 32-47 s[r1], 48-63 b[r1], two groups per lane from group
+            // g0 of r0 and g1 of r1 (ng groups per row)
+            const bf16 *sc, *bi;
+            const unsigned char *w0, *w1;
+            size_t r0, r1;
+            int ng = HID / 64, g0 = 0, g1 = 0;
+            if (idx < S.oK()) {
+                load_sb_pair(A.layersq + l, 0, sc, bi);
+                r0 = (size_t)b * QPB + 2 * idx, r1 = r0 + 1;
+                w0 = (const unsigned char *)opaque(L.qkv) + r0 * HID, w1 = w0 + HID;
+            } else if (idx < S.oR()) {  // o_proj row r (4096 codes): its halves as r0 and r1
+                load_sb_pair(A.layersq + l, 1, sc, bi);
+                r0 = r1 = (size_t)b * OPB + (idx - S.oO());
+                w0 = (const unsigned char *)opaque(L.o) + r0 * HD, w1 = w0 + HID;
+                ng = HD / 64, g1 = HID / 64;
+            } else if (idx < S.oG()) {  // router row b (pieces 2, 3 repeat 0, 1)
+                load_sb_pair(A.layersq + l, 2, sc, bi);
+                r0 = r1 = (size_t)b;
+                w0 = w1 = (const unsigned char *)opaque(L.router) + r0 * HID;
+            } else if (idx < S.oD()) {  // gate row and up row of output b * GPB + i
+                load_sb_pair(A.layersq + l, 3, sc, bi);
+                const int o = b * GPB + (idx - S.oG());
+                const int e = min(max(route_e[l & 1][o / IE], 0), A.E - 1);
+                r0 = (size_t)e * (2 * IE) + o % IE, r1 = r0 + IE;
+                w0 = (const unsigned char *)opaque(L.exp_gu) + r0 * HID, w1 = (const unsigned char *)opaque(L.exp_gu) + r1 * HID;
+            } else {
+                load_sb_pair(A.layersq + l, 4, sc, bi);
+                r0 = r1 = 0;
+                w0 = w1 = nullptr;
+            }
+            if (idx < S.oD()) {
+                src[0] = w0 + lane * 16;
+                src[1] = w0 + 1024 + lane * 16;
+                src[2] = w1 + lane * 16;
+                src[3] = w1 + 1024 + lane * 16;
+                if (idx >= S.oR() && idx < S.oG()) {  // router: one row
+                    src[2] = src[0];
+                    src[3] = src[1];
+                }
+                const int q = lane >> 4;
+                const bf16 *arr = (q & 1) ? bi : sc;  // a per-lane choice between two uniform arrays
+                sbsrc = (const void *)(arr + (q < 2 ? r0 * ng + g0 : r1 * ng + g1) + 2 * (lane & 15));
+            } else {  // third t of virtual down row n: codes 2048 t + 1024 k + 16 lane (k = 0, 1), gathered
+                const int i = idx - S.oD(), n_ = b * OPB + i / DCH, t = i % DCH;
+                const unsigned char *W = (const unsigned char *)opaque(L.exp_down);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int v = 2048 * t + 1024 * k + 16 * lane, s = v / IE, o = v - s * IE;
+                    const int e = min(max(route_e[l & 1][s], 0), A.E - 1);
+                    src[k] = W + ((size_t)e * HID + n_) * IE + o;
+                }
+                src[2] = src[0];
+                src[3] = src[1];
+                // the third's 32 groups: lanes 0-15 two scales each, 16-31 two biases; 32-63 repeat
+                const int gi = 2 * (lane & 15), vg = 2048 * t + 64 * gi, s = vg / IE;
+                const int e = min(max(route_e[l & 1][s], 0), A.E - 1);
+                const bf16 *arr = ((lane >> 4) & 1) ? bi : sc;
+                sbsrc = (const void *)(arr + ((size_t)e * HID + n_) * (IE / 64) + (vg - s * IE) / 64);
+            }
+        } else if (idx < S.oK()) {
             const unsigned char *base = (const unsigned char *)opaque(L.qkv) + ((size_t)b * QPB + idx) * CHB;
 #pragma unroll
             for (int k = 0; k < 4; ++k) src[k] = base + k * 1024 + lane * 16;
@@ -156,6 +256,7 @@ __device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *r
                 const int key = min(j0 + i * KPC + 4 * k + lane / 16, j1 - 1);
                 src[k] = (const unsigned char *)(cache + (size_t)key * D) + (lane % 16) * 16;
             }
+            sbsrc = src[0];  // 8-bit: a fifth copy into the unused side slot keeps five per chunk
         } else if (idx < S.oR()) {  // half h of o_proj row r
             const int i = idx - S.oO();
             const unsigned char *base =
@@ -192,9 +293,10 @@ __device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *r
         const unsigned dlds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(ring + (size_t)s * CHB));
 #pragma unroll
         for (int k = 0; k < 4; ++k) dma16(src[k], dlds + k * 1024);
+        if constexpr (Q8) dma4(sbsrc, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(sbring + (size_t)s * SBM)));
         ++n;
         if (n - pub >= DL) {
-            wait_vm<4 * (DL - 1)>();  // all but this wave's last DL-1 chunks have landed
+            wait_vm<VPC * (DL - 1)>();  // all but this wave's last DL-1 chunks have landed
             for (; pub + (DL - 1) < n; ++pub) publish(j + NL * pub);
         }
     }
@@ -202,11 +304,14 @@ __device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *r
     for (; pub < n; ++pub) publish(j + NL * pub);
 }
 
+template <bool Q8>
 __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
+    constexpr int NSM = ring_slots<Q8>();
     constexpr int HPT = HID / NCT;  // words per compute thread of a hidden vector
     constexpr int APT = HD / NCT;   // of the attention output
     constexpr int RSH = rep_stride(HID), RSA = rep_stride(HD), RSM = rep_stride(IM), RSR = rep_stride(EMAX);
     __shared__ __attribute__((aligned(16))) unsigned char ring[NSM * CHB];
+    __shared__ __attribute__((aligned(16))) unsigned char sbring[Q8 ? NSM * SBM : 16];  // 8-bit: scales and biases
     __shared__ unsigned ready[NSM], done[NSM], bar, abt, rgen;
     __shared__ DevLayer lay[MAXL];
     __shared__ float hs[HID];                                 // residual stream h (fp32 of bf16 values)
@@ -214,9 +319,9 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
     __shared__ __attribute__((aligned(16))) uint16_t qraw[G * D + 2 * D];
     __shared__ float qs[G * D], kvs[2 * D];
     __shared__ float sc[G * CHM];
-    __shared__ float po[NSPLIT_MAX / 4 * (HD / NB)];  // split merge: [ns][dims per block]
     __shared__ float rsum[2][NC];
-    __shared__ float pm[NSPLIT_MAX / 4], pl[NSPLIT_MAX / 4];
+    __shared__ float po[64 * (HD / NB)];  // split merge: [ns][dims per block]
+    __shared__ float pm[64], pl[64];
     __shared__ int route_e[2][KSEL];
     __shared__ float route_w[2][KSEL];
 
@@ -229,7 +334,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
     const int j0 = lo + as * A.chunk, j1 = min(nkeys, j0 + A.chunk);
     const int nK = j0 < j1 ? (j1 - j0 + KPC - 1) / KPC : 0;
     const bool has_p = j0 < nkeys && j1 == nkeys;
-    const Seq S(nK, b < A.E ? 1 : 0);
+    const Seq<Q8> S(nK, b < A.E ? 1 : 0);
 
     for (int i = tid; i < NSM; i += NTH) {
         ready[i] = 0;
@@ -246,7 +351,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
     __syncthreads();  // the only barrier of the whole block; the roles split here
 
     if (wave >= NC) {
-        stream_wave(A, lay, ring, ready, done, &rgen, route_e, &abt, wave - NC, ag, j0, j1, nK);
+        stream_wave<Q8>(A, lay, ring, sbring, ready, done, &rgen, route_e, &abt, wave - NC, ag, j0, j1, nK);
         return;
     }
 
@@ -311,7 +416,25 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
             }
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
-        {
+        if constexpr (Q8) {
+            const bf16 *qb = lay[l].qkv_bias;
+            const X8 xq = load_x8(ys, lane);
+            for (int i = wave; i < S.QC; i += NC) {  // chunk i: rows 2 i and 2 i + 1 of the block's QPB
+                const unsigned g = gb + i;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSM) * SBM);
+                float a0 = wave_sum(dot_q8_row(c, 0, 1, sb, xq, lane));
+                float a1 = wave_sum(dot_q8_row(c, 2, 3, sb + 64, xq, lane));
+                chunk_put_w<NSM>(done, g, lane, REL);
+                const int r0 = b * QPB + 2 * i;
+                if (qb) {
+                    a0 = rho<bf16>(a0) + to_f(opaque(qb)[r0]);
+                    a1 = rho<bf16>(a1) + to_f(opaque(qb)[r0 + 1]);
+                }
+                if (lane == 0) xstore(opaque(A.x_qkv) + r0, tagw(tag, a0));
+                if (lane == 1) xstore(opaque(A.x_qkv) + r0 + 1, tagw(tag, a1));
+            }
+        } else {
             // a q|k|v bias is its own rounded add after the projection: rho(rho(x W^T) + b)
             const bf16 *qb = lay[l].qkv_bias;
             const X4 xq = load_x(ys, lane);
@@ -319,7 +442,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
                 const unsigned g = gb + i;
                 const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
                 float acc = wave_sum(dot_chunk(c, xq, lane, 0.f));
-                chunk_put_w(done, g, lane, REL);
+                chunk_put_w<NSM>(done, g, lane, REL);
                 if (qb) acc = rho<bf16>(acc) + to_f(opaque(qb)[(size_t)b * QPB + i]);
                 if (lane == 0) xstore(opaque(A.x_qkv) + (size_t)b * QPB + i, tagw(tag, acc));
             }
@@ -413,7 +536,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
                     s = row16_sum(s);  // the key's 16 lanes form one DPP row
                     if (sub == 0 && j < j1) sc[h * CHM + (j - j0)] = s * A.scale;
                 }
-                chunk_put_w(done, g, lane, 1u);  // one of the chunk's G readers
+                chunk_put_w<NSM>(done, g, lane, 1u);  // one of the chunk's G readers
             }
             // softmax of head h over the split's keys (the wave's own scores)
             const int nj = j1 - j0;
@@ -450,7 +573,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
                     o0 += pe[kk] * v0;
                     o1 += pe[kk] * v1;
                 }
-                chunk_put_w(done, g, lane, 1u);  // one of the chunk's G readers
+                chunk_put_w<NSM>(done, g, lane, 1u);  // one of the chunk's G readers
             }
             uint64_t *pp = opaque(A.x_part) + ((size_t)(ag * G + h) * ns + as) * (D + 2);
             xstore64(pp + 2 + 2 * lane, ((uint64_t)tag << 32) | __float_as_uint(o0));
@@ -470,41 +593,47 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
 
         // ---------------- step 3: merge the splits of (head mh, dims md0 .. md0 + dpb)
         {
+            // the split maxima, sums and this block's dims of every split's output, each word polled
+            // by one thread, all of a thread's words in flight together
+            constexpr int NPM = (64 * (2 + dpb) + NCT - 1) / NCT;
             const int nwords = ns * (2 + dpb);
-            for (int t = tid; t < nwords; t += NCT) {
-                const uint64_t *src;
-                if (t < 2 * ns) src = opaque(A.x_part) + ((size_t)mh * ns + t / 2) * (D + 2) + (t % 2);
-                else {
-                    const int u = t - 2 * ns;
-                    src = opaque(A.x_part) + ((size_t)mh * ns + u / dpb) * (D + 2) + 2 + md0 + u % dpb;
-                }
-                uint64_t v = xload64(src);
-                long sp = 0;
-                while ((unsigned)(v >> 32) != tag) {
-                    if (spin_out(++sp, opaque(A.err), &abt)) break;
-                    v = xload64(src);
-                }
-                const float f = __uint_as_float((uint32_t)v);
+            uint64_t v[NPM];
+            const uint64_t *src[NPM];
+#pragma unroll
+            for (int k = 0; k < NPM; ++k) {
+                const int t = tid + NCT * k, u = t - 2 * ns;
+                src[k] = opaque(A.x_part) + (t >= nwords ? 0
+                                             : t < 2 * ns ? ((size_t)mh * ns + t / 2) * (D + 2) + (t % 2)
+                                                          : ((size_t)mh * ns + u / dpb) * (D + 2) + 2 + md0 + u % dpb);
+                v[k] = t < nwords ? xload64(src[k]) : ((uint64_t)tag << 32);
+            }
+            long sp = 0;
+            while (true) {
+                bool ok = true;
+#pragma unroll
+                for (int k = 0; k < NPM; ++k) ok &= (unsigned)(v[k] >> 32) == tag;
+                if (ok || spin_out(++sp, opaque(A.err), &abt)) break;
+#pragma unroll
+                for (int k = 0; k < NPM; ++k)
+                    if ((unsigned)(v[k] >> 32) != tag) v[k] = xload64(src[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < NPM; ++k) {
+                const int t = tid + NCT * k;
+                const float f = __uint_as_float((uint32_t)v[k]);
                 if (t < 2 * ns) {
                     if (t % 2 == 0) pm[t / 2] = f;
                     else pl[t / 2] = f;
-                } else {
+                } else if (t < nwords) {
                     po[t - 2 * ns] = f;
                 }
             }
             cbar(&bar, ep, &abt, opaque(A.err), lane);
-            if (tid < dpb) {
-                float M = -INFINITY;
-                for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s]);
-                float Ls = 0.f, acc = 0.f;
-                for (int s = 0; s < ns; ++s) {
-                    const float f = __expf(pm[s] - M);
-                    Ls += pl[s] * f;
-                    acc += po[s * dpb + tid] * f;
-                }
-                const uint32_t w = tagw(tag, acc / Ls);
+            float av;
+            if (merge_lds<8>(pm, pl, po, ns, dpb, tid, &av)) {  // waves 0-1: 8 lanes per dim
+                const uint32_t w = tagw(tag, av);
 #pragma unroll
-                for (int r = 0; r < NREP; ++r) xstore(opaque(A.x_a) + r * RSA + mh * D + md0 + tid, w);
+                for (int r = 0; r < NREP; ++r) xstore(opaque(A.x_a) + r * RSA + mh * D + md0 + tid / 8, w);
             }
         }
 
@@ -512,13 +641,22 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         poll_bf16<APT>(opaque(A.x_a) + (b % NREP) * RSA, HD, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         {
-            const unsigned g = gb + S.oO() + 2 * wave;
-            const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
-            float a = dot_chunk(c, load_x(ys, lane), lane, 0.f);
-            chunk_put_w(done, g, lane, REL);
-            const unsigned char *c2 = chunk_get<NSM>(ring, ready, g + 1, &abt, opaque(A.err));
-            a = dot_chunk(c2, load_x(ys + HID, lane), lane, a);
-            chunk_put_w(done, g + 1, lane, REL);
+            float a;
+            if constexpr (Q8) {  // one chunk: the row's two halves as the chunk's two 2048-code rows
+                const unsigned g = gb + S.oO() + wave;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSM) * SBM);
+                a = dot_q8_row(c, 0, 1, sb, load_x8(ys, lane), lane) + dot_q8_row(c, 2, 3, sb + 64, load_x8(ys + HID, lane), lane);
+                chunk_put_w<NSM>(done, g, lane, REL);
+            } else {
+                const unsigned g = gb + S.oO() + 2 * wave;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                a = dot_chunk(c, load_x(ys, lane), lane, 0.f);
+                chunk_put_w<NSM>(done, g, lane, REL);
+                const unsigned char *c2 = chunk_get<NSM>(ring, ready, g + 1, &abt, opaque(A.err));
+                a = dot_chunk(c2, load_x(ys + HID, lane), lane, a);
+                chunk_put_w<NSM>(done, g + 1, lane, REL);
+            }
             const float acc = wave_sum(a);
             const int row = b * OPB + wave;
             if (lane < NREP) xstore(opaque(A.x_h2) + lane * RSH + row, tagw(tag, hs[row] + rho<bf16>(acc)));
@@ -546,11 +684,16 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         if (l + 1 < A.n_layers) load_small(l + 1);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         const X4 xg = load_x(ys, lane);
+        const X8 xg8 = Q8 ? load_x8(ys, lane) : X8{};
         if (S.rc && wave == NC - 1) {  // router logit b = rho(y2 . Wr[b])
             const unsigned g = gb + S.oR();
             const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
-            const float acc = wave_sum(dot_chunk(c, xg, lane, 0.f));
-            chunk_put_w(done, g, lane, REL);
+            float acc;
+            if constexpr (Q8)
+                acc = wave_sum(dot_q8_row(c, 0, 1, (const uint16_t *)(sbring + (size_t)(g % NSM) * SBM), xg8, lane));
+            else
+                acc = wave_sum(dot_chunk(c, xg, lane, 0.f));
+            chunk_put_w<NSM>(done, g, lane, REL);
             if (lane < NREP) xstore(opaque(A.x_r) + lane * RSR + b, tagw(tag, rho<bf16>(acc)));
         }
         if (wave == 0) {  // the token's routing, the same in every block
@@ -588,13 +731,23 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         static_assert(GPB == 3 * NC, "three SwiGLU outputs per wave, packed into one exchange word");
         uint64_t mword = (uint64_t)tag << 48;
         for (int i = wave; i < GPB; i += NC) {
-            const unsigned g = gb + S.oG() + 2 * i;
-            const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
-            const float gs = wave_sum(dot_chunk(c, xg, lane, 0.f));
-            chunk_put_w(done, g, lane, REL);
-            const unsigned char *cu = chunk_get<NSM>(ring, ready, g + 1, &abt, opaque(A.err));
-            const float us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
-            chunk_put_w(done, g + 1, lane, REL);
+            float gs, us;
+            if constexpr (Q8) {  // chunk i: the gate row and the up row of output i
+                const unsigned g = gb + S.oG() + i;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSM) * SBM);
+                gs = wave_sum(dot_q8_row(c, 0, 1, sb, xg8, lane));
+                us = wave_sum(dot_q8_row(c, 2, 3, sb + 64, xg8, lane));
+                chunk_put_w<NSM>(done, g, lane, REL);
+            } else {
+                const unsigned g = gb + S.oG() + 2 * i;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                gs = wave_sum(dot_chunk(c, xg, lane, 0.f));
+                chunk_put_w<NSM>(done, g, lane, REL);
+                const unsigned char *cu = chunk_get<NSM>(ring, ready, g + 1, &abt, opaque(A.err));
+                us = wave_sum(dot_chunk(cu, xg, lane, 0.f));
+                chunk_put_w<NSM>(done, g + 1, lane, REL);
+            }
             const float mv = rho<bf16>(silu_f32(rho<bf16>(gs))) * rho<bf16>(us);
             mword |= (uint64_t)f2bf_bits(mv) << (16 * ((i - wave) / NC));
         }
@@ -614,16 +767,38 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
             for (int q = 0; q < DCH; ++q) {
                 const unsigned g = gb + S.oD() + wave * DCH + q;
                 const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
-                float pk[4];
-                dot_pieces(c, load_x(ys + q * HID, lane), lane, pk);
-                chunk_put_w(done, g, lane, REL);
+                if constexpr (Q8) {
+                    // third q: the lane's pieces are codes 2048 q + 1024 k + 16 lane .. + 15 (k = 0, 1), in
+                    // groups 16 k + lane / 4 of the third; slot s0 for lanes below lb, else s0 + 1
+                    const uint16_t *sb = (const uint16_t *)(sbring + (size_t)(g % NSM) * SBM);
+                    const X8 x8 = load_x8(ys + q * HID, lane);
+                    float pk[2];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    // inputs 2048 q + 512 k + 8 lane ..: slot s0 for lanes below lb, else s0 + 1
-                    const int base = 2048 * q + 512 * k, s0 = base / IE, lb = ((s0 + 1) * IE - base) / 8;
-                    const bool first = lane < lb;
-                    sacc[s0] += first ? pk[k] : 0.f;
-                    if (s0 + 1 < KSEL) sacc[s0 + 1] += first ? 0.f : pk[k];
+                    for (int k = 0; k < 2; ++k) {
+                        const int gq = 16 * k + (lane >> 2);
+                        pk[k] = q8_piece(c, k, bfv(sb[gq]), bfv(sb[32 + gq]), x8.v[2 * k], x8.v[2 * k + 1],
+                                         k ? x8.s1 : x8.s0, lane);
+                    }
+                    chunk_put_w<NSM>(done, g, lane, REL);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const int base = 2048 * q + 1024 * k, s0 = base / IE, lb = ((s0 + 1) * IE - base) / 16;
+                        const bool first = lane < lb;
+                        sacc[s0] += first ? pk[k] : 0.f;
+                        if (s0 + 1 < KSEL) sacc[s0 + 1] += first ? 0.f : pk[k];
+                    }
+                } else {
+                    float pk[4];
+                    dot_pieces(c, load_x(ys + q * HID, lane), lane, pk);
+                    chunk_put_w<NSM>(done, g, lane, REL);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        // inputs 2048 q + 512 k + 8 lane ..: slot s0 for lanes below lb, else s0 + 1
+                        const int base = 2048 * q + 512 * k, s0 = base / IE, lb = ((s0 + 1) * IE - base) / 8;
+                        const bool first = lane < lb;
+                        sacc[s0] += first ? pk[k] : 0.f;
+                        if (s0 + 1 < KSEL) sacc[s0 + 1] += first ? 0.f : pk[k];
+                    }
                 }
             }
             float acc = 0.f;
@@ -661,7 +836,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
 // ------------------------------------------------------------ host side
 namespace {
 struct MoeMkLayout {
-    size_t layers, qkv, a, h2, r, m, pend, part, ctr, total;
+    size_t layers, layersq, qkv, a, h2, r, m, pend, part, ctr, total;
 };
 MoeMkLayout moe_mk_layout(int n_layers, int H, int KV) {
     using namespace mkm;
@@ -670,6 +845,7 @@ MoeMkLayout moe_mk_layout(int n_layers, int H, int KV) {
     MoeMkLayout L{};
     size_t o = 0;
     L.layers = o; o += al(sizeof(DevLayer) * n_layers);
+    L.layersq = o; o += al(sizeof(DevLayerQ) * n_layers);
     L.qkv = o; o += al((size_t)NQKV * 4);
     L.a = o; o += al((size_t)NREP * rep_stride(HD) * 4);
     L.h2 = o; o += al((size_t)NREP * rep_stride(HID) * 4);
@@ -692,20 +868,25 @@ size_t decode_moe_workspace(int n_layers, int H, int KV) { return moe_mk_layout(
 bool decode_moe_supported(int n_layers, int dt, int quant_bits, int hid, int H, int KV, int D, int E, int k, int Ie,
                           int cap) {
     using namespace mkm;
-    if (dt != DT_BF16 || quant_bits != 0 || D != mk::D || hid != HID || H * D != HD || KV < 1 || H != G * KV) return false;
+    if (dt != DT_BF16 || (quant_bits != 0 && quant_bits != 8) || D != mk::D || hid != HID || H * D != HD || KV < 1 || H != G * KV) return false;
     if ((H + 2 * KV) * D != NQKV || mk::NB % KV || mk::NB % H) return false;
     if (n_layers < 1 || n_layers > mk::MAXL) return false;  // tags are call * 64 + layer
     if (E < KSEL || E > EMAX || E > mk::NB || k != KSEL || Ie != IE) return false;
     const int nsplit = mk::NB / KV;
-    if (nsplit > mk::NSPLIT_MAX / 4 || moe_mk_chunk(cap, nsplit) > CHM) return false;
+    if (nsplit > 64 || moe_mk_chunk(cap, nsplit) > CHM) return false;  // the split merge: two splits per lane
     return true;
 }
 
-hipError_t decode_moe_init(void *ws, int n_layers, int H, int KV, const void *layer_ptrs, hipStream_t s) {
+hipError_t decode_moe_init(void *ws, int n_layers, int H, int KV, const void *layer_ptrs, const void *layer_q8_ptrs,
+                           hipStream_t s) {
     const MoeMkLayout L = moe_mk_layout(n_layers, H, KV);
     char *b = (char *)ws;
     hipError_t e = hipMemcpyAsync(b + L.layers, layer_ptrs, sizeof(mkm::DevLayer) * n_layers, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return e;
+    if (layer_q8_ptrs) {
+        e = hipMemcpyAsync(b + L.layersq, layer_q8_ptrs, sizeof(mkm::DevLayerQ) * n_layers, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+    }
     // exchange words start with tag 0xffff, never the tag of a first call's layer
     e = hipMemsetAsync(b + L.qkv, 0xff, L.ctr - L.qkv, s);
     if (e != hipSuccess) return e;
@@ -714,7 +895,8 @@ hipError_t decode_moe_init(void *ws, int n_layers, int H, int KV, const void *la
     return hipStreamSynchronize(s);  // layer_ptrs is a caller's host array
 }
 
-hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int norm_topk, int cap, int p, int window,
+hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int norm_topk, bool q8, int cap, int p,
+                             int window,
                              float eps, const void *x, void *out, const void *final_norm, const void *cos_t,
                              const void *sin_t, void *kc, void *vc, int *err, hipStream_t s) {
     const MoeMkLayout L = moe_mk_layout(n_layers, H, KV);
@@ -725,6 +907,7 @@ hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int n
         return hipErrorInvalidValue;
     mkm::Args A;
     A.layers = (const mkm::DevLayer *)(b + L.layers);
+    A.layersq = (const mkm::DevLayerQ *)(b + L.layersq);
     A.n_layers = n_layers;
     A.H = H;
     A.KV = KV;
@@ -754,7 +937,7 @@ hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int n
     A.ctr = (unsigned *)(b + L.ctr);
     A.err = err;
     void *args[] = {&A};
-    const void *fn = (const void *)mkm::decode_moe_kernel;
+    const void *fn = q8 ? (const void *)mkm::decode_moe_kernel<true> : (const void *)mkm::decode_moe_kernel<false>;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(s, &cs);
     if (e != hipSuccess) return e;
@@ -764,11 +947,10 @@ hipError_t launch_decode_moe(void *ws, int n_layers, int H, int KV, int E, int n
     return hipLaunchKernel(fn, dim3(mk::NB), dim3(mk::NTH), args, 0, s);
 }
 
-int decode_moe_max_blocks() {
+int decode_moe_max_blocks(bool q8) {
     int per_cu = 0, dev = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)mkm::decode_moe_kernel, mk::NTH, 0) !=
-        hipSuccess)
-        return 0;
+    const void *fn = q8 ? (const void *)mkm::decode_moe_kernel<true> : (const void *)mkm::decode_moe_kernel<false>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, mk::NTH, 0) != hipSuccess) return 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;

@@ -272,7 +272,7 @@ int run_decode(qwen3_handle *h, const void *x, void *out) {
         HIPCHECK(h, mark(h, K_STEP, true));
         if (h->mk_moe)
             HIPCHECK(h, launch_decode_moe(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.n_experts, c.norm_topk_prob,
-                                          c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
+                                          is_q8(h), c.capacity, h->length, c.sliding_window, c.rms_eps, x, out, h->final_norm,
                                           h->cos_t, h->sin_t, h->kc, h->vc, h->dev_err, h->stream));
         else
             HIPCHECK(h, launch_decode_mk(h->mk_ws, c.n_layers, c.n_heads, c.n_kv_heads, c.hidden, c.intermediate,
@@ -585,19 +585,24 @@ int qwen3_init(const qwen3_config *cfg, const qwen3_weights *w, void *k_cache, v
         e = decode_mk_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, cfg->hidden, cfg->intermediate,
                            ptrs.data(), q8 ? qptrs.data() : nullptr, h->stream);
         h->mk_ready = e == hipSuccess;
-    } else if (e == hipSuccess && moe_mk_config(*cfg) && decode_moe_max_blocks() >= decode_mk_blocks()) {
+    } else if (e == hipSuccess && moe_mk_config(*cfg) && decode_moe_max_blocks(q8) >= decode_mk_blocks()) {
         bool all_moe = true;  // the persistent MoE step has no dense-MLP layers
-        std::vector<const void *> ptrs;
+        std::vector<const void *> ptrs, qptrs;
         for (int l = 0; l < cfg->n_layers; ++l) {
             const qwen3_layer_weights &Lw = w->layers[l];
             all_moe = all_moe && Lw.router;
             const void *row[10] = {Lw.in_norm, Lw.post_norm, Lw.q_norm,  Lw.k_norm,   Lw.qkv,
                                    Lw.o,       Lw.router,    Lw.exp_gate_up, Lw.exp_down, Lw.qkv_bias};
             ptrs.insert(ptrs.end(), row, row + 10);
+            const void *qrow[10] = {Lw.qkv_s,      Lw.qkv_b,         Lw.o_s,           Lw.o_b,
+                                    Lw.router_s,   Lw.router_b,      Lw.exp_gate_up_s, Lw.exp_gate_up_b,
+                                    Lw.exp_down_s, Lw.exp_down_b};
+            qptrs.insert(qptrs.end(), qrow, qrow + 10);
         }
         if (all_moe) {
             h->mk_ws = b + L.mk;
-            e = decode_moe_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, ptrs.data(), h->stream);
+            e = decode_moe_init(h->mk_ws, cfg->n_layers, cfg->n_heads, cfg->n_kv_heads, ptrs.data(),
+                                q8 ? qptrs.data() : nullptr, h->stream);
             h->mk_ready = h->mk_moe = e == hipSuccess;
         }
     }

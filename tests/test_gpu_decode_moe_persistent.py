@@ -6,14 +6,15 @@ intermediate 768 ("@mlx-bun/inference" qwen3-moe.ts, Qwen3MoeSparseMoeBlock; att
 "maya2_mlx/backbone.py" Backbone.forward).  Covers one layer at positions with 32 keys per
 attention split, fewer keys than splits and a single key; the full 48-layer stack; several
 consecutive steps; page 2's switches (no q/k norm, q|k|v bias, a sliding window); HIP-graph
-replays against the eager step; and the fallback for stacks with a dense-MLP layer.
+replays against the eager step; the fallback for stacks with a dense-MLP layer; and every
+weight 8-bit (router and experts included).
 
 Top-k: both GPU paths and the oracle round each router logit to bf16 after an fp32 (GPU) or
 float64 (oracle) dot, so a logit can land on the neighbouring bf16 value and the k-th pick
 can differ where two probabilities tie up to one bf16 step; the fixed seeds here give no such
 tie (a differing pick would show as a large output error).  Gates: bf16 per-row relative L2
-<= 2e-2 against the oracle per layer; the 48-layer stack is reported, with a bound above the
-drift both decode paths show there."""
+<= 2e-2 against the oracle per layer (and per step over 2-4 layers); the 48-layer stack is
+reported, with a bound that separates the drift both decode paths show there from a broken step."""
 import numpy as np
 import pytest
 import torch
@@ -119,10 +120,11 @@ def test_moe_persistent_full_stack(orc):
     ekv = max(max_row_rel_l2(np32(mk.k)[l, :, filled], st.k[l, :, filled]) for l in range(cfg.n_layers))
     say(f"  vs oracle {e:.2e} (one-kernel-per-step path {e_ref:.2e}), vs that path {e_paths:.2e}, "
         f"new K of every layer vs oracle {ekv:.2e}")
-    # 48 MoE layers: both paths drift from the oracle by ~8% (measured 7.7% persistent, 8.8% one
-    # kernel per step, 8.3% apart) while every single layer agrees bit for bit between the paths:
-    # rounding differences of the bf16 residual stream, amplified where they move a router pick
-    assert e < 0.15 and e_paths < 0.15
+    # 48 MoE layers: reported, with a bound that separates drift from a broken step (an unrelated
+    # output is ~1.4 away).  Each single layer agrees with the oracle within the gate, but a top-8
+    # pick is discontinuous: an fp32 summation-order change anywhere (measured: only the order of
+    # the split merge) moves the 48-layer distance between 0.08 and 0.16 for both paths.
+    assert e < 0.35 and e_paths < 0.35
 
 
 def test_moe_persistent_consecutive_steps(orc):
@@ -225,6 +227,78 @@ def test_moe_stack_with_a_dense_layer_takes_the_kernel_path():
     with pytest.raises(q3.Qwen3Error) as ei:
         q3.qwen3_set_decode_path(seat.handle, 2)
     assert ei.value.code == _lib.ERR_UNSUPPORTED
-    q8 = q3.Seat(QWEN3_MOE.replace(n_layers=1, quant_bits=8, quant_group=64),
-                 synth.model_weights(QWEN3_MOE.replace(n_layers=1, quant_bits=8, quant_group=64), DEV), max_tokens=1)
-    assert q3.qwen3_get_decode_path(q8.handle) == 1
+
+
+# ------------------------------------------------------------------ 8-bit weights
+
+def _q8(cfg):
+    return cfg.replace(quant_bits=8, quant_group=64)
+
+
+@pytest.mark.parametrize("filled", [2047, 0, 31, 1000])
+def test_moe_persistent_q8_one_layer_vs_oracle_and_kernels(orc, filled):
+    """Every weight 8-bit (router and experts included): one layer against the oracle (weights
+    dequantised exactly) and against the one-kernel-per-step path."""
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_MOE
+    say(f"persistent MoE decode, 8-bit weights, 1 layer, position {filled}")
+    cfg, w, mk, ref = _seats(_q8(QWEN3_MOE), 1, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, 1, DEV)
+    a = mk.forward_hidden(x)
+    b = ref.forward_hidden(x)
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    o = st.forward(np32(x))
+    e, e_ref = max_row_rel_l2(np32(a), o), max_row_rel_l2(np32(b), o)
+    e_paths = max_row_rel_l2(np32(a), np32(b))
+    ek = max_row_rel_l2(np32(mk.k)[:, :, filled], st.k[:, :, filled])
+    ev = max_row_rel_l2(np32(mk.v)[:, :, filled], st.v[:, :, filled])
+    say(f"  vs oracle {e:.2e} (one-kernel-per-step path {e_ref:.2e}), vs that path {e_paths:.2e}, "
+        f"new K {ek:.2e}, new V {ev:.2e}")
+    gate(np32(a), o, "bf16")
+    assert max(ek, ev) <= BF16_TOL and e_paths <= BF16_TOL
+
+
+def test_moe_persistent_q8_stack_steps(orc):
+    """8-bit weights, 4 layers, three steps in a row from position 1200, against the oracle and
+    the one-kernel-per-step path."""
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_MOE
+    filled, n = 1200, 3
+    say(f"persistent MoE decode, 8-bit weights, 4 layers, {n} steps from position {filled}")
+    cfg, w, mk, ref = _seats(_q8(QWEN3_MOE), 4, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, n, DEV)
+    outs = [mk.forward_hidden(x[i:i + 1]) for i in range(n)]
+    outs_ref = [ref.forward_hidden(x[i:i + 1]) for i in range(n)]
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    xs = np32(x)
+    worst = worst_paths = 0.0
+    for i in range(n):
+        worst = max(worst, max_row_rel_l2(np32(outs[i]), st.forward(xs[i:i + 1])))
+        worst_paths = max(worst_paths, max_row_rel_l2(np32(outs[i]), np32(outs_ref[i])))
+    say(f"  worst step vs oracle {worst:.2e}, vs one-kernel-per-step path {worst_paths:.2e}")
+    assert worst <= 2 * BF16_TOL and worst_paths <= 2 * BF16_TOL
+
+
+def test_moe_persistent_q8_full_stack(orc):
+    import qwen3_transformer_layer_amd as q3
+    from qwen3_transformer_layer_amd import synth
+    from qwen3_transformer_layer_amd.config import QWEN3_MOE
+    filled = 2047
+    say("persistent MoE decode, 8-bit weights, 48 layers, ctx 2048")
+    cfg, w, mk, ref = _seats(_q8(QWEN3_MOE), None, filled)
+    st = _oracle(orc, cfg, w, mk, filled)
+    x = synth.hidden_states(cfg, 1, DEV)
+    a = mk.forward_hidden(x)
+    b = ref.forward_hidden(x)
+    torch.cuda.synchronize()
+    q3.qwen3_check_device_errors(mk.handle)
+    o = st.forward(np32(x))
+    e, e_ref, e_paths = max_row_rel_l2(np32(a), o), max_row_rel_l2(np32(b), o), max_row_rel_l2(np32(a), np32(b))
+    say(f"  vs oracle {e:.2e} (one-kernel-per-step path {e_ref:.2e}), vs that path {e_paths:.2e}")
+    assert e < 0.35 and e_paths < 0.35  # reported; see the bf16 48-layer test
