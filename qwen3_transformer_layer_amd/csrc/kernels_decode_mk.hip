@@ -324,6 +324,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         // ---------------- step 1: h = rho(h + pend); y = RMSNorm(h); q|k|v rows
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave is done reading ys (the previous layer's down rows)
         if (l > 0) {
+            poll_pause<PAUSE_VEC>();
             poll_bf16<HPT>(opaque(A.x_pend) + (b % NREP) * RSH, HID, ptag, ys, opaque(A.err), &abt, tid);
 #pragma unroll
             for (int k = 0; k < HPT; ++k) {  // a thread's own elements only: no barrier needed
@@ -374,6 +375,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             }
         }
 
+        poll_pause<PAUSE_VEC>();
         // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
         if (nK > 0) {
             // the group's q heads, and for the block holding the new key its k and v heads, in
@@ -547,6 +549,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 
         // ---------------- step 3: merge the splits of (head mh, dims md0 .. md0 + dpb)
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // red has been read before it becomes the merge buffer
+        poll_pause<PAUSE_SPLIT>();
         {
             const int ns = A.nsplit;
             const int nwords = ns * (2 + dpb);
@@ -582,6 +585,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         }
 
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row
+        poll_pause<PAUSE_SPLIT>();
         poll_bf16<HPT>(opaque(A.x_a) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         if constexpr (Q8) {
@@ -609,6 +613,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 
         // ---------------- step 5: y2 = RMSNorm(h); gate|up row pairs + SwiGLU
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave has read ys and hs before they are replaced
+        poll_pause<PAUSE_VEC>();
         poll_bf16<HPT>(opaque(A.x_h2) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
         {
             float ss = 0.f;
@@ -660,6 +665,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 
         // ---------------- step 6: pend = rho(m . Wdown^T) for this wave's row
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // ys (y2) fully consumed before it receives m
+        poll_pause<PAUSE_VEC>();
         static_assert(RSM % 2 == 0 && NB * NC % NCT == 0, "packed SwiGLU words: replica spacing, words per thread");
         poll_m3<NB * NC / NCT, GPB>((const uint64_t *)opaque(A.x_m) + (b % NREP) * (RSM / 2), NB * NC, tag, ys,
                                     opaque(A.err), &abt, tid);

@@ -397,6 +397,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         // ---------------- step 1: h = rho(h + pend); y = RMSNorm(h); q|k|v rows
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave is done reading ys (the previous layer's m)
         if (l > 0) {
+            poll_pause<PAUSE_VEC>();
             poll_bf16<HPT>(opaque(A.x_pend) + (b % NREP) * RSH, HID, ptag, ys, opaque(A.err), &abt, tid);
 #pragma unroll
             for (int k = 0; k < HPT; ++k) {  // a thread's own elements only: no barrier needed
@@ -448,6 +449,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
             }
         }
 
+        poll_pause<PAUSE_VEC>();
         // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
         if (nK > 0) {
             // the group's q heads, and for the block holding the new key its k and v heads:
@@ -664,6 +666,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
 
         // ---------------- step 5: y2 = RMSNorm(h); router row; routing; gate|up row pairs + SwiGLU
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave has read ys and hs before they are replaced
+        poll_pause<PAUSE_VEC>();
         poll_bf16<HPT>(opaque(A.x_h2) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
         {
             float ss = 0.f;
@@ -697,6 +700,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
             if (lane < NREP) xstore(opaque(A.x_r) + lane * RSR + b, tagw(tag, rho<bf16>(acc)));
         }
         if (wave == 0) {  // the token's routing, the same in every block
+            poll_pause<PAUSE_VEC>();
             const uint32_t *src = opaque(A.x_r) + (b % NREP) * RSR;
             const int E = A.E;
             uint32_t v[2];
@@ -755,6 +759,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
 
         // ---------------- step 6: pend = rho(sum_s rho(rho(m_s . Wdown_e(s)[n]) w_s)) for this wave's row n
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // ys (y2) fully consumed; the routing weights are in LDS
+        poll_pause<PAUSE_VEC>();
         static_assert(RSM % 2 == 0 && NB * NC % NCT == 0, "packed SwiGLU words: replica spacing, words per thread");
         poll_m3<NB * NC / NCT, GPB>((const uint64_t *)opaque(A.x_m) + (b % NREP) * (RSM / 2), NB * NC, tag, ys,
                                     opaque(A.err), &abt, tid);
