@@ -594,6 +594,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         }
 
         // ---------------- step 3: merge the splits of (head mh, dims md0 .. md0 + dpb)
+        poll_pause<PAUSE_SPLIT>();
         {
             // the split maxima, sums and this block's dims of every split's output, each word polled
             // by one thread, all of a thread's words in flight together
@@ -640,6 +641,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         }
 
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row (two chunks)
+        poll_pause<PAUSE_SPLIT>();
         poll_bf16<APT>(opaque(A.x_a) + (b % NREP) * RSA, HD, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         {
