@@ -98,9 +98,42 @@ __device__ __forceinline__ void dma4(const void *g, unsigned lds) {
 // waves wn = 0, 1 of the same wm (64 each), so the row's sum of squares and each RoPE pair
 // (c, c + 64) are completed through LDS with the partner wave.  With a bias (page 2's Qwen2
 // switch) every value is rho(rho(x W^T) + b) first.
+// The RoPE table words, norm weights and bias this lane needs, loaded before the K loop so the
+// epilogue does not wait a memory round trip for them.
+template <class C> struct QkvPre {
+    static constexpr int RW = C::WTM;
+    u32x4 cw[RW / 8], sw[RW / 8];
+    float nw[C::NT], b[C::NT];
+};
 template <class C>
-__device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const QkvEpi &qe, unsigned char *smem, int M,
-                                             int m0, int nb, int wm, int wn, int wave, int lane) {
+__device__ __forceinline__ void qkv_prefetch(QkvPre<C> &pre, const QkvEpi &qe, int M, int m0, int nb, int wm, int wn,
+                                             int lane) {
+    constexpr int RW = C::WTM;
+    const int H = qe.H, KV = qe.KV;
+    const bool isq = nb < H, isv = nb >= H + KV;
+    const bf16 *bias = (const bf16 *)qe.bias;
+    const bf16 *nw = isv ? nullptr : (const bf16 *)(isq ? qe.q_norm : qe.k_norm);
+#pragma unroll
+    for (int j = 0; j < C::NT; ++j) {
+        const int col = wn * 64 + j * 32 + (lane & 31);
+        pre.b[j] = bias ? to_f(bias[(size_t)nb * 128 + col]) : 0.f;
+        pre.nw[j] = nw ? to_f(nw[col]) : 0.f;
+    }
+    if (isv) return;
+    const bf16 *cs = (const bf16 *)qe.cos_t, *sn = (const bf16 *)qe.sin_t;
+    const int c = wn * 64 + (lane & 7) * 8;
+#pragma unroll
+    for (int t = 0; t < RW / 8; ++t) {
+        const int row = min(m0 + wm * RW + (lane >> 3) + 8 * t, M - 1), p = qe.p0 + row;
+        pre.cw[t] = ld16(cs + (size_t)p * 128 + c);
+        pre.sw[t] = ld16(sn + (size_t)p * 128 + c);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const QkvPre<C> &pre, const QkvEpi &qe,
+                                             unsigned char *smem, int M, int m0, int nb, int wm, int wn, int wave,
+                                             int lane) {
     static_assert(C::BN == 128 && C::WN == 2 && C::NT == 2 && !C::Q8, "one head of 128 columns over two waves");
     constexpr int RW = C::WTM;                  // rows per wave
     constexpr int YP = 68;                      // exchange-buffer row (fp32 words; 16-byte aligned)
@@ -109,14 +142,13 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
     static_assert(C::NW * RED * 4 <= Y_BYTES, "row partials fit under the exchange buffer");
     const int H = qe.H, KV = qe.KV;
     const bool isq = nb < H, isv = nb >= H + KV;
-    const bf16 *bias = (const bf16 *)qe.bias;
+    const bool bias = qe.bias != nullptr;
     auto row_of = [&](int i, int v) { return i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); };  // in the wave
-    auto col_of = [&](int j) { return wn * 64 + j * 32 + (lane & 31); };                          // in the head
 #pragma unroll
     for (int i = 0; i < C::NI; ++i)
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
-            const float b = bias ? to_f(bias[(size_t)nb * 128 + col_of(j)]) : 0.f;
+            const float b = pre.b[j];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 float a = rho<bf16>(acc[i][j][v]);
@@ -128,7 +160,7 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
     float *ybuf = (float *)smem;                   // [NW][RW][YP]; first the row partials [NW][RW][33]
     float *ssb = (float *)(smem + Y_BYTES);        // [NW][RW] half-row sums of squares
     float *rb = ssb + C::NW * RW;                  // [NW][RW] 1 / rms of the wave's rows
-    const bf16 *nw = isv ? nullptr : (const bf16 *)(isq ? qe.q_norm : qe.k_norm);
+    const bool nw = !isv && (isq ? qe.q_norm : qe.k_norm) != nullptr;
     if (nw) {
         float *red = ybuf + wave * RED;
 #pragma unroll
@@ -149,9 +181,7 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
             const float ss = ssb[wave * RW + lane] + ssb[partner * RW + lane];
             rb[wave * RW + lane] = 1.0f / sqrtf(ss / 128.0f + qe.eps);
         }
-        float w[C::NT];
-#pragma unroll
-        for (int j = 0; j < C::NT; ++j) w[j] = to_f(nw[col_of(j)]);
+        const float *w = pre.nw;
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
 #pragma unroll
@@ -173,7 +203,6 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
             for (int j = 0; j < C::NT; ++j) ybuf[(wave * RW + row_of(i, v)) * YP + j * 32 + (lane & 31)] = acc[i][j][v];
     __syncthreads();
     const int partner = wm * C::WN + (wn ^ 1), c8 = (lane & 7) * 8;
-    const bf16 *cs = (const bf16 *)qe.cos_t, *sn = (const bf16 *)qe.sin_t;
     bf16 *dst = isq ? (bf16 *)qe.q_out
                     : (bf16 *)(isv ? qe.vc : qe.kc) + (size_t)(nb - H - (isv ? KV : 0)) * qe.cap * 128;
 #pragma unroll
@@ -193,9 +222,8 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[C::NI][C::NT], const 
             float yp[8], cv[8], sv[8];
             *(f32x4 *)&yp[0] = yq[0];
             *(f32x4 *)&yp[4] = yq[1];
-            const u32x4 cw = ld16(cs + (size_t)p * 128 + c), sw = ld16(sn + (size_t)p * 128 + c);
-            Vec<bf16>::expand(cw, cv);
-            Vec<bf16>::expand(sw, sv);
+            Vec<bf16>::expand(pre.cw[t], cv);
+            Vec<bf16>::expand(pre.sw[t], sv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = wn == 0 ? y[e] * cv[e] - yp[e] * sv[e] : y[e] * cv[e] + yp[e] * sv[e];
         }
@@ -209,7 +237,7 @@ template <int EPI, class C>
 __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restrict__ A, int M, int K,
                                                           const void *__restrict__ W, const bf16 *__restrict__ scale,
                                                           const bf16 *__restrict__ bias, int N,
-                                                          const bf16 *__restrict__ res, bf16 *__restrict__ out,
+                                                          const bf16 *res, bf16 *out,  // out may alias res
                                                           QkvEpi qe) {
     using namespace g2;
     static_assert(EPI != EPI_SWIGLU || C::NT % 2 == 0, "a SWIGLU wave holds gate and up tiles in pairs");
@@ -276,6 +304,28 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
         }
     }
 
+    // EPI_RESID (bf16 weights): the residual words of this lane's outputs are loaded before the K
+    // loop, so the epilogue does not wait a memory round trip for them (o_proj at T = 2048 33.5 ->
+    // 29.5 us, down 69.7 -> 65.3).  Rows and columns are clamped in bounds; out may alias res (each
+    // word is read and then written by the same lane).
+    QkvPre<C> pre;
+    if constexpr (EPI == EPI_QKV) qkv_prefetch<C>(pre, qe, M, m0, nb, wm, wn, lane);
+    constexpr bool RPF = EPI == EPI_RESID && !C::Q8;
+    uint32_t rv[RPF ? C::NI : 1][RPF ? 16 : 1][RPF ? C::NT : 1];
+    if constexpr (RPF) {
+        const uint16_t *r16 = (const uint16_t *)res;
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = min(m0 + wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), M - 1);
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) {
+                    const int col = min(nb * C::BN + brow[j] + (lane & 31), N - 1);
+                    rv[i][v][j] = r16[(size_t)row * N + col];
+                }
+            }
+    }
 #pragma unroll
     for (int s = 0; s < C::ST - 1; ++s)
         if (s < nk) issue(s);
@@ -380,7 +430,7 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
     }
 
     if constexpr (EPI == EPI_QKV) {
-        qkv_epilogue<C>(acc, qe, smem, M, m0, nb, wm, wn, wave, lane);
+        qkv_epilogue<C>(acc, pre, qe, smem, M, m0, nb, wm, wn, wave, lane);
         return;
     }
     // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
@@ -407,7 +457,10 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
                     if (col >= N) continue;
                     const size_t idx = (size_t)row * N + col;
                     const float a = acc[i][j][v];
-                    out[idx] = from_f<bf16>(EPI == EPI_RESID ? to_f(res[idx]) + rho<bf16>(a) : a);
+                    float r = 0.f;
+                    if constexpr (RPF) r = __uint_as_float(rv[i][v][j] << 16);
+                    else if (EPI == EPI_RESID) r = to_f(res[idx]);
+                    out[idx] = from_f<bf16>(EPI == EPI_RESID ? r + rho<bf16>(a) : a);
                 }
             }
         }
