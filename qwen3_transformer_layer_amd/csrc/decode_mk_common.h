@@ -82,9 +82,13 @@ __device__ __forceinline__ bool spin_out(long s, int *err, unsigned *abt) {
 // the producers' own traffic.  A short pause before the first round (N times 64 clocks) lets that
 // round find nearly every word.  Measured on the 1.7B decode step (ms per step, one box): no pause
 // 0.893; 16 before the q|k|v, pend, h and SwiGLU polls 0.827, 32 0.794, 64 0.827 (longer pauses
-// only add latency); 16 more before the split-partial and merged-output polls 0.791.
+// only add latency); 16 more before the split-partial and merged-output polls 0.791.  Per exchange
+// (same box, interleaved runs, 786 us/step with 32 everywhere): 48 before the pend and q|k|v polls
+// of the dense kernel 779 us (each alone 782 / 781; 64 at both 787); 20 or 48 before the h or
+// SwiGLU polls no better (787-796).
 template <int N> __device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(N); }
-constexpr int PAUSE_VEC = 32;    // before polling a vector every block produces (q|k|v, pend, h, SwiGLU)
+constexpr int PAUSE_VEC = 32;    // before polling a vector every block produces (h, SwiGLU; MoE: all)
+constexpr int PAUSE_LONG = 48;   // dense kernel: before the pend and q|k|v polls
 constexpr int PAUSE_SPLIT = 16;  // before the split partials and the merged attention output
 
 // Wait for words src[t], t < n, to carry `tag`; their bf16 payloads go to dst[t] (LDS).

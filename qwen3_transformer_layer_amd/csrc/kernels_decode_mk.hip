@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         // ---------------- step 1: h = rho(h + pend); y = RMSNorm(h); q|k|v rows
         cbar(&bar, ep, &abt, opaque(A.err), lane);  // every wave is done reading ys (the previous layer's down rows)
         if (l > 0) {
-            poll_pause<PAUSE_VEC>();
+            poll_pause<PAUSE_LONG>();
             poll_bf16<HPT>(opaque(A.x_pend) + (b % NREP) * RSH, HID, ptag, ys, opaque(A.err), &abt, tid);
 #pragma unroll
             for (int k = 0; k < HPT; ++k) {  // a thread's own elements only: no barrier needed
@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             }
         }
 
-        poll_pause<PAUSE_VEC>();
+        poll_pause<PAUSE_LONG>();
         // ---------------- step 2: per-head q/k norm + RoPE + cache write, split-K attention
         if (nK > 0) {
             // the group's q heads, and for the block holding the new key its k and v heads, in
