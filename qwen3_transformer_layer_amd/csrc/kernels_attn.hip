@@ -577,41 +577,54 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
             }
         }
-        // accumulator v of S^T: key kb0 + 8 (v / 4) + 4 hh + v % 4, query qi
+        // accumulator v of S^T: key kb0 + 8 (v / 4) + 4 hh + v % 4, query qi.  Only tiles that cross
+        // the diagonal or the window edge test keys (a uniform branch).
         const bool need_mask = kb0 + 31 > p0 + t0 || (window > 0 && kb0 < kmax - window + 1);
-        float tmax = -INFINITY;
+        if (need_mask) {
+            int qp = qpos;  // passed through the asm so the test cannot be hoisted out of the branch
+            __asm__ volatile("" : "+v"(qp));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float sv = sc[v] * scale_log2;
-            const int key = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (need_mask && (key > qpos || key < qlo)) sv = -INFINITY;
-            sc[v] = sv;
-            tmax = fmaxf(tmax, sv);
+            for (int v = 0; v < 16; ++v) {
+                const int key = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                if (key > qp || key < qlo) sc[v] = -INFINITY;
+            }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // The scale (> 0) is applied after the maximum (fp32 rounding is monotonic, so the rounded
+        // product of the maximum is the maximum of the rounded products) and enters each exponent
+        // through one fma.
+        float tmax = sc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
         const bool up = tmax > m_run + 8.0f;  // also on the first tile with a visible key
         const float m_use = up ? tmax : m_run;
         const float alpha = up ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
-        if (__ballot(up)) {
+        if (__ballot(up)) {  // rare: a real branch, not a multiply by 1 on every tile
+            float a = alpha;
+            __asm__ volatile("" : "+v"(a));
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+                for (int v = 0; v < 16; ++v) o[dt][v] *= a;
         }
         m_run = m_use;
-        const float m_exp = m_use == -INFINITY ? 0.f : m_use;  // no visible key yet: every p is 0
+        const float nm = m_use == -INFINITY ? 0.f : -m_use;  // no visible key yet: every p is 0
         float psum = 0.f;
-        bf16x8 phi[2], plo[2];  // P^T operand of 16-key step cc: values 8 cc .. 8 cc + 7
+        u32x4 hw[2], lw[2];  // P^T operand of 16-key step cc: values 8 cc .. 8 cc + 7, as hi + lo bf16
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(sc[8 * cc + e] - m_exp);
-                psum += pv;
-                const __bf16 hb = (__bf16)pv;
-                phi[cc][e] = hb;
-                plo[cc][e] = (__bf16)(pv - (float)hb);
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[8 * cc + e], scale_log2, nm));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[8 * cc + e + 1], scale_log2, nm));
+                psum += p0;
+                psum += p1;
+                const uint32_t h = pack_bf2(p0, p1);
+                hw[cc][e / 2] = h;
+                lw[cc][e / 2] = pack_bf2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
             }
+        const bf16x8 phi[2] = {__builtin_bit_cast(bf16x8, hw[0]), __builtin_bit_cast(bf16x8, hw[1])};
+        const bf16x8 plo[2] = {__builtin_bit_cast(bf16x8, lw[0]), __builtin_bit_cast(bf16x8, lw[1])};
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
         // V^T operand: group gi reads rows 32 par + 16 cc + 4 (gi / 2) (+ 8) and columns
