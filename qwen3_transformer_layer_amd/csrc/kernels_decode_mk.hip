@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     __shared__ float red[NC * G * D];
     __shared__ float rsum[2][NC];
     __shared__ float pm[NSPLIT_MAX], pl[NSPLIT_MAX];
-    __shared__ float mrow[G], lrow[G];
+    __shared__ float mwv[NC * G], lwv[NC * G];  // each wave's attention max and sum
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), b = blockIdx.x;
     const int H = A.H, KV = A.KV;
@@ -427,10 +427,14 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         if (nK > 0) {
-            // scores; K chunk i holds keys j0 + KPC*i ..; the lane's piece k is key 4k + kslot,
-            // dims sub*8 .. sub*8+7
-            // q and the new key are bf16 values (rounded after RoPE), so packing them is exact and
-            // each 8-dim piece of a score is four v_dot2c_f32_bf16
+            // Each wave takes K chunk i and V chunk i (i = wave, wave + NC, ...): the scores of the
+            // chunk's KPC keys, their exponentials against the wave's running maximum, and p . V,
+            // so the waves need no barrier between scores, softmax and p . V; the waves' (max,
+            // sum, o) are combined once below.  K chunk i holds keys j0 + KPC*i ..; the lane's
+            // piece k is key 4k + kslot, dims sub*8 .. sub*8+7.  q and the new key are bf16 values
+            // (rounded after RoPE), so packing them is exact and each 8-dim piece of a score is
+            // four v_dot2c_f32_bf16.  In p . V lane l owns dims 2l, 2l+1 of every key; the
+            // probabilities go through the wave's own rows of sc (no other wave reads them).
             u32x4 qp[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -441,58 +445,56 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
             const float *kn = kvs + sub * 8;
             const u32x4 knew = {pack_bf2(kn[0], kn[1]), pack_bf2(kn[2], kn[3]), pack_bf2(kn[4], kn[5]),
                                 pack_bf2(kn[6], kn[7])};
+            const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
+            float mw[G], lw[G], o[G][2];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                mw[h] = -INFINITY;
+                lw[h] = 0.f;
+                o[h][0] = o[h][1] = 0.f;
+            }
             for (int i = wave; i < nK; i += NC) {
-                const unsigned g = gb + S.oK() + i;
-                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                const unsigned gk = gb + S.oK() + i;
+                const unsigned char *c = chunk_get<NSL>(ring, ready, gk, &abt, opaque(A.err));
                 u32x4 kr[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) kr[k] = *(const u32x4 *)(c + k * 1024 + lane * 16);
+                float sv[G][4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int j = j0 + i * KPC + 4 * k + kslot;
                     const u32x4 kw = j == jspec ? knew : kr[k];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        float s = dot16<bf16>(qp[h], kw, 0.f);
-                        s = row16_sum(s);  // the key's 16 lanes form one DPP row
-                        if (sub == 0 && j < j1) sc[h * CHUNK_MAX + (j - j0)] = s * A.scale;
+                        const float sdot = row16_sum(dot16<bf16>(qp[h], kw, 0.f));  // the key's 16 lanes form one DPP row
+                        sv[h][k] = j < j1 ? sdot * A.scale : -INFINITY;
                     }
                 }
-                chunk_put<NSL>(done, g, lane);
-            }
-        }
-        cbar(&bar, ep, &abt, opaque(A.err), lane);
-        const int nj = j1 - j0;
-        if (nK > 0 && wave < G) {
-            float m = -INFINITY;
-            for (int j = lane; j < nj; j += 64) m = fmaxf(m, sc[wave * CHUNK_MAX + j]);
-            m = wave_max(m);
-            float ls = 0.f;
-            for (int j = lane; j < nj; j += 64) {
-                const float e = __expf(sc[wave * CHUNK_MAX + j] - m);
-                sc[wave * CHUNK_MAX + j] = e;
-                ls += e;
-            }
-            ls = wave_sum(ls);
-            if (lane == 0) {
-                mrow[wave] = m;
-                lrow[wave] = ls;
-            }
-        }
-        cbar(&bar, ep, &abt, opaque(A.err), lane);
-        if (nK > 0) {
-            // p . V: lane l owns dims 2l, 2l+1 of every key (no cross-lane reduction); the
-            // probabilities are LDS broadcasts
-            float o[G][2];
-#pragma unroll
-            for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
-            const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
-            for (int i = wave; i < nK; i += NC) {
-                const unsigned g = gb + S.oV() + i;
-                const unsigned char *c = chunk_get<NSL>(ring, ready, g, &abt, opaque(A.err));
+                chunk_put<NSL>(done, gk, lane);
                 const int jb = j0 + i * KPC;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float cm = fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3]));
+                    cm = fmaxf(fmaxf(lane_f(cm, 0), lane_f(cm, 16)), fmaxf(lane_f(cm, 32), lane_f(cm, 48)));
+                    const float mn = fmaxf(mw[h], cm);  // finite: key jb is below j1
+                    const float alpha = __expf(mw[h] - mn);
+                    float ps = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float e = __expf(sv[h][k] - mn);
+                        ps += e;
+                        if (sub == 0) sc[h * CHUNK_MAX + (jb + 4 * k + kslot - j0)] = e;
+                    }
+                    ps = (lane_f(ps, 0) + lane_f(ps, 16)) + (lane_f(ps, 32) + lane_f(ps, 48));
+                    lw[h] = lw[h] * alpha + ps;
+                    o[h][0] *= alpha;
+                    o[h][1] *= alpha;
+                    mw[h] = mn;
+                }
+                const unsigned gv = gb + S.oV() + i;
+                c = chunk_get<NSL>(ring, ready, gv, &abt, opaque(A.err));
                 // all KPC rows are read (rows past the split's end hold a copy of its last key
-                // and get probability 0); reads first, then the arithmetic
+                // and have probability 0); reads first, then the arithmetic
                 uint32_t vw[KPC];
                 float pe[G][KPC];
 #pragma unroll
@@ -500,8 +502,7 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int kk = 0; kk < KPC; ++kk)
-                        pe[h][kk] = jb + kk < j1 ? sc[h * CHUNK_MAX + (jb + kk - j0)] : 0.f;
+                    for (int kk = 0; kk < KPC; ++kk) pe[h][kk] = sc[h * CHUNK_MAX + (jb + kk - j0)];
 #pragma unroll
                 for (int kk = 0; kk < KPC; ++kk) {
                     float v0 = bf_lo(vw[kk]), v1 = bf_hi(vw[kk]);
@@ -515,28 +516,41 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
                         o[h][1] += pe[h][kk] * v1;
                     }
                 }
-                chunk_put<NSL>(done, g, lane);
+                chunk_put<NSL>(done, gv, lane);
             }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 red[(wave * G + h) * D + 2 * lane] = o[h][0];
                 red[(wave * G + h) * D + 2 * lane + 1] = o[h][1];
+                if (lane == 0) {
+                    mwv[wave * G + h] = mw[h];
+                    lwv[wave * G + h] = lw[h];
+                }
             }
         }
         cbar(&bar, ep, &abt, opaque(A.err), lane);
         if (nK > 0) {
+            // the split's (max, sum, o) from the waves' (waves without a chunk hold max -inf, sum 0)
             for (int idx = tid; idx < G * D; idx += NCT) {
                 const int i = idx / D, d = idx % D;
+                float m = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NC; ++w) m = fmaxf(m, mwv[w * G + i]);
                 float v = 0.f;
 #pragma unroll
-                for (int w = 0; w < NC; ++w) v += red[(w * G + i) * D + d];
+                for (int w = 0; w < NC; ++w) v += red[(w * G + i) * D + d] * __expf(mwv[w * G + i] - m);
                 xstore64(opaque(A.x_part) + ((size_t)(ag * G + i) * A.nsplit + as) * (D + 2) + 2 + d,
                          ((uint64_t)tag << 32) | __float_as_uint(v));
             }
             if (tid < G) {
+                float m = -INFINITY, ls = 0.f;
+#pragma unroll
+                for (int w = 0; w < NC; ++w) m = fmaxf(m, mwv[w * G + tid]);
+#pragma unroll
+                for (int w = 0; w < NC; ++w) ls += lwv[w * G + tid] * __expf(mwv[w * G + tid] - m);
                 uint64_t *pp = opaque(A.x_part) + ((size_t)(ag * G + tid) * A.nsplit + as) * (D + 2);
-                xstore64(pp, ((uint64_t)tag << 32) | __float_as_uint(mrow[tid]));
-                xstore64(pp + 1, ((uint64_t)tag << 32) | __float_as_uint(lrow[tid]));
+                xstore64(pp, ((uint64_t)tag << 32) | __float_as_uint(m));
+                xstore64(pp + 1, ((uint64_t)tag << 32) | __float_as_uint(ls));
             }
         } else {  // an empty split (fewer keys than splits): max -inf, sum 0
             for (int idx = tid; idx < G * (D + 2); idx += NCT) {
