@@ -524,47 +524,51 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
             const float *kn = kvs + sub * 8;
             const u32x4 knew = {pack_bf2(kn[0], kn[1]), pack_bf2(kn[2], kn[3]), pack_bf2(kn[4], kn[5]),
                                 pack_bf2(kn[6], kn[7])};
+            // per chunk i: the scores of its KPC keys, their exponentials against the wave's running
+            // maximum (earlier chunks rescaled), then p . V with V chunk i; the probabilities go
+            // through the wave's own row of sc.  In p . V lane l owns dims 2l, 2l+1 of every key.
+            float m = -INFINITY, ls = 0.f, o0 = 0.f, o1 = 0.f;
+            const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
             for (int i = 0; i < nK; ++i) {
-                const unsigned g = gb + S.oK() + i;
-                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                const unsigned gk = gb + S.oK() + i;
+                const unsigned char *c = chunk_get<NSM>(ring, ready, gk, &abt, opaque(A.err));
                 u32x4 kr[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) kr[k] = *(const u32x4 *)(c + k * 1024 + lane * 16);
+                float sv[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int j = j0 + i * KPC + 4 * k + kslot;
                     const u32x4 kw = j == jspec ? knew : kr[k];
-                    float s = dot16<bf16>(qp, kw, 0.f);
-                    s = row16_sum(s);  // the key's 16 lanes form one DPP row
-                    if (sub == 0 && j < j1) sc[h * CHM + (j - j0)] = s * A.scale;
+                    const float sdot = row16_sum(dot16<bf16>(qp, kw, 0.f));  // the key's 16 lanes form one DPP row
+                    sv[k] = j < j1 ? sdot * A.scale : -INFINITY;
                 }
-                chunk_put_w<NSM>(done, g, lane, 1u);  // one of the chunk's G readers
-            }
-            // softmax of head h over the split's keys (the wave's own scores)
-            const int nj = j1 - j0;
-            float m = -INFINITY;
-            for (int jj = lane; jj < nj; jj += 64) m = fmaxf(m, sc[h * CHM + jj]);
-            m = wave_max(m);
-            float ls = 0.f;
-            for (int jj = lane; jj < nj; jj += 64) {
-                const float e = __expf(sc[h * CHM + jj] - m);
-                sc[h * CHM + jj] = e;
-                ls += e;
-            }
-            ls = wave_sum(ls);
-            // p . V: lane l owns dims 2l, 2l+1 of every key; the probabilities are LDS broadcasts
-            float o0 = 0.f, o1 = 0.f;
-            const float vs0 = kvs[D + 2 * lane], vs1 = kvs[D + 2 * lane + 1];
-            for (int i = 0; i < nK; ++i) {
-                const unsigned g = gb + S.oV() + i;
-                const unsigned char *c = chunk_get<NSM>(ring, ready, g, &abt, opaque(A.err));
+                chunk_put_w<NSM>(done, gk, lane, 1u);  // one of the chunk's G readers
                 const int jb = j0 + i * KPC;
+                float cm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                cm = fmaxf(fmaxf(lane_f(cm, 0), lane_f(cm, 16)), fmaxf(lane_f(cm, 32), lane_f(cm, 48)));
+                const float mn = fmaxf(m, cm);  // finite: key jb is below j1
+                const float alpha = __expf(m - mn);
+                float ps = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float e = __expf(sv[k] - mn);
+                    ps += e;
+                    if (sub == 0) sc[h * CHM + (jb + 4 * k + kslot - j0)] = e;
+                }
+                ps = (lane_f(ps, 0) + lane_f(ps, 16)) + (lane_f(ps, 32) + lane_f(ps, 48));
+                ls = ls * alpha + ps;
+                o0 *= alpha;
+                o1 *= alpha;
+                m = mn;
+                const unsigned gv = gb + S.oV() + i;
+                c = chunk_get<NSM>(ring, ready, gv, &abt, opaque(A.err));
                 uint32_t vw[KPC];
                 float pe[KPC];
 #pragma unroll
                 for (int kk = 0; kk < KPC; ++kk) vw[kk] = *(const uint32_t *)(c + kk * (D * 2) + lane * 4);
 #pragma unroll
-                for (int kk = 0; kk < KPC; ++kk) pe[kk] = jb + kk < j1 ? sc[h * CHM + (jb + kk - j0)] : 0.f;
+                for (int kk = 0; kk < KPC; ++kk) pe[kk] = sc[h * CHM + (jb + kk - j0)];
 #pragma unroll
                 for (int kk = 0; kk < KPC; ++kk) {
                     float v0 = bf_lo(vw[kk]), v1 = bf_hi(vw[kk]);
@@ -575,7 +579,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
                     o0 += pe[kk] * v0;
                     o1 += pe[kk] * v1;
                 }
-                chunk_put_w<NSM>(done, g, lane, 1u);  // one of the chunk's G readers
+                chunk_put_w<NSM>(done, gv, lane, 1u);  // one of the chunk's G readers
             }
             uint64_t *pp = opaque(A.x_part) + ((size_t)(ag * G + h) * ns + as) * (D + 2);
             xstore64(pp + 2 + 2 * lane, ((uint64_t)tag << 32) | __float_as_uint(o0));
