@@ -329,14 +329,29 @@ __device__ __forceinline__ bool merge_lds(const float *pm, const float *pl, cons
             L += pl[s] * f;
             O += po[s * dpb + d] * f;
         }
-#pragma unroll
-    for (int off = LPD / 2; off > 0; off >>= 1) {
-        const float M2 = __shfl_xor(M, off), L2 = __shfl_xor(L, off), O2 = __shfl_xor(O, off);
+    auto comb = [&](float M2, float L2, float O2) {
         const float Mn = fmaxf(M, M2);
         const float f1 = M == -INFINITY ? 0.f : __expf(M - Mn), f2 = M2 == -INFINITY ? 0.f : __expf(M2 - Mn);
         L = L * f1 + L2 * f2;
         O = O * f1 + O2 * f2;
         M = Mn;
+    };
+    if constexpr (LPD == 8) {
+        // DPP lane moves within each group of 8 (VALU, no LDS crossbar round trip): lane i with
+        // lane 7 - i, then xor 2, then xor 1 pairs every lane of the group with every other; the
+        // combine is symmetric, so all 8 lanes end with the same (M, L, O).  The calling lanes
+        // are whole waves.
+#pragma unroll
+        for (int st = 0; st < 3; ++st) {
+            float M2, L2, O2;
+            if (st == 0) M2 = Q3_DPP(M, 0x141), L2 = Q3_DPP(L, 0x141), O2 = Q3_DPP(O, 0x141);
+            else if (st == 1) M2 = Q3_DPP(M, 0x4e), L2 = Q3_DPP(L, 0x4e), O2 = Q3_DPP(O, 0x4e);
+            else M2 = Q3_DPP(M, 0xb1), L2 = Q3_DPP(L, 0xb1), O2 = Q3_DPP(O, 0xb1);
+            comb(M2, L2, O2);
+        }
+    } else {
+#pragma unroll
+        for (int off = LPD / 2; off > 0; off >>= 1) comb(__shfl_xor(M, off), __shfl_xor(L, off), __shfl_xor(O, off));
     }
     *a = O / L;
     return pt == 0;
