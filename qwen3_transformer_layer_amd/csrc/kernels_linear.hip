@@ -18,6 +18,8 @@
 //    pairs with one activation load (the plain GEMV re-reads all M activation chunks per weight
 //    chunk).  Block = 8 waves on the same 16 outputs (32 weight rows for SWIGLU), each a K/8
 //    slice with 8 loads in flight per lane; the 8 partial tiles are summed in LDS in wave order.
+//  - gemv8_mfma_kernel: the same on 8 outputs per block, where 16-output blocks would leave CUs
+//    idle (2048 outputs: o_proj, down) or need a partial second round (gate|up).
 //  - gemm_f32_kernel: M > 16 in fp32 (strict mode), LDS-tiled FMA.
 #include "common.h"
 #include "kernels.h"
@@ -236,6 +238,59 @@ __global__ void __launch_bounds__(512) gemv_mfma_kernel(const bf16 *__restrict__
     }
 }
 
+// ------------------------------------------------------------ skinny MFMA GEMV, 8 outputs per block
+// The same MFMA and wave layout on 8 outputs per block, for the shapes where 16-output blocks
+// leave CUs idle or need a second round: 2048 outputs give 256 blocks, gate|up's 6144 give 768 (three
+// resident per CU).  The B operand's 16 columns hold, for SWIGLU, the 8 gate rows then the 8 up rows
+// of the same outputs (the up value of column r is column r + 8, lane ^ 8); otherwise the 8 rows
+// twice, and the duplicate columns are not stored.  Each lane issues all U weight and activation
+// loads of its K slice at once (K = NWV * 32 * U).  Same products and summation order as
+// gemv_mfma_kernel with 8 waves.
+template <int EPI, int NWV, int U>
+__global__ void __launch_bounds__(64 * NWV) gemv8_mfma_kernel(const bf16 *__restrict__ x, int M, int K,
+                                                             const bf16 *__restrict__ W, int N, const bf16 *res,
+                                                             bf16 *out) {
+    __shared__ f32x4 part[NWV - 1][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 8, r = lane & 15, h = lane >> 4;
+    const int wrow = EPI == EPI_SWIGLU ? (r < 8 ? min(n0 + r, N - 1) : N + min(n0 + r - 8, N - 1))
+                                       : min(n0 + (r & 7), N - 1);
+    const bf16 *xr = x + (size_t)min(r, M - 1) * K + 8 * h;
+    const bf16 *wr = W + (size_t)wrow * K + 8 * h;
+    const int k0 = wave * 32 * U;
+    u32x4 wv[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        wv[u] = ld_stream(wr + k0 + 32 * u);
+        xv[u] = ld16(xr + k0 + 32 * u);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits for one
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u]), __builtin_bit_cast(bf16x8, wv[u]),
+                                                      acc, 0, 0, 0);
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < NWV - 1; ++w) acc += part[w][lane];
+    // accumulator j of lane i: activation row 4 (i / 16) + j, column i % 16
+    float up[4] = {0.f, 0.f, 0.f, 0.f};
+    if (EPI == EPI_SWIGLU)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[j], 8);
+    const int n = n0 + r;
+    if (r >= 8 || n >= N) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = 4 * h + j;
+        if (m >= M) continue;
+        const size_t idx = (size_t)m * N + n;
+        out[idx] = from_f<bf16>(epi_value<bf16>(EPI, acc[j], up[j], res, idx));
+    }
+}
+
 // ------------------------------------------------------------ fp32 tiled GEMM (strict mode)
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float *__restrict__ A, int M, int K,
@@ -331,6 +386,26 @@ hipError_t launch_linear(int dt, const void *x, int M, int K, const void *W, int
         const dim3 grid((N + 15) / 16);
         const bf16 *a = (const bf16 *)x, *b = (const bf16 *)W, *r = (const bf16 *)res;
         bf16 *o = (bf16 *)out;
+        // 8 outputs per block where 16 would give fewer than 256 blocks or a partial second round
+        // (gate|up); K 2048 / 4096 / 6144 (all loads of a K slice in flight at once)
+        const bool eight = epi == EPI_SWIGLU ? N % 256 != 0 || (N / 16) % 256 != 0 : (N + 15) / 16 < 256;
+        if (eight && (K == 2048 || K == 4096 || K == 6144)) {
+            const dim3 g8((N + 7) / 8);
+            if (epi == EPI_SWIGLU) {
+                if (K == 2048) gemv8_mfma_kernel<EPI_SWIGLU, 8, 8><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else if (K == 4096) gemv8_mfma_kernel<EPI_SWIGLU, 8, 16><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else gemv8_mfma_kernel<EPI_SWIGLU, 8, 24><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+            } else if (epi == EPI_RESID) {
+                if (K == 2048) gemv8_mfma_kernel<EPI_RESID, 8, 8><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else if (K == 4096) gemv8_mfma_kernel<EPI_RESID, 8, 16><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else gemv8_mfma_kernel<EPI_RESID, 8, 24><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+            } else {
+                if (K == 2048) gemv8_mfma_kernel<EPI_STORE, 8, 8><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else if (K == 4096) gemv8_mfma_kernel<EPI_STORE, 8, 16><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+                else gemv8_mfma_kernel<EPI_STORE, 8, 24><<<g8, 512, 0, s>>>(a, M, K, b, N, r, o);
+            }
+            return hipGetLastError();
+        }
         if (epi == EPI_SWIGLU) gemv_mfma_kernel<EPI_SWIGLU><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
         else if (epi == EPI_RESID) gemv_mfma_kernel<EPI_RESID><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
         else gemv_mfma_kernel<EPI_STORE><<<grid, 512, 0, s>>>(a, M, K, b, N, r, o);
