@@ -18,7 +18,11 @@
 //  - Tile shapes, the largest that still gives >= 192 tiles: 128 x 256 with 8 waves for gate|up
 //    (T >= 512; 131 -> 121 us at T = 2048 against 256 x 128), 256 x 128 with 8 waves (q|k|v
 //    at T = 2048), 128 x 128 with 8 waves (o_proj and down at T = 2048), else
-//    128 x 64 (64 x 128 for SWIGLU, whose waves hold gate/up pairs) with 4 waves.  Measured
+//    128 x 64 (64 x 128 for SWIGLU, whose waves hold gate/up pairs) with 4 waves.  The
+//    128 x 128 and 128 x 64 store/residual tiles split each K step between two groups of
+//    64 x 64 waves (K groups, see Cfg), so a wave does twice the MFMAs per fragment read of a
+//    32 x 64 wave and the block still has 8 (4) waves: o_proj at T = 2048 27.8 -> 26.8 us,
+//    down 67.4 -> 61.8; at T = 512 down 44.3 -> 36.8, o_proj 18.4 -> 17.6.  Measured
 //    against one 128 x 256 / 4-wave tiling at T = 2048: gate|up 148 -> 125 us, q|k|v 48 -> 40,
 //    o_proj 40 -> 31; at T = 512 o_proj 54 -> 20 and down 101 -> 38.  8-bit weights: the
 //    per-group fold (2 FMAs per accumulator element) costs about as many cycles as the group's
@@ -44,10 +48,13 @@
 namespace q3 {
 namespace g2 {
 
-template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_> struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, ST = ST_, WM = WM_, WN = WN_;
+// KG > 1: KG groups of WM x WN waves share each K step, group g taking its k-slices
+// [g * 4 / KG, (g + 1) * 4 / KG) of the step's four 16-wide slices; group 0 adds the others'
+// accumulators (through LDS, in group order) after the K loop and runs the epilogue.
+template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_, int KG_ = 1> struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, ST = ST_, WM = WM_, WN = WN_, KG = KG_;
     static constexpr bool Q8 = Q8_;
-    static constexpr int BK = 64, NW = WM * WN, NTH = 64 * NW;
+    static constexpr int BK = 64, NWG = WM * WN, NW = NWG * KG, NTH = 64 * NW;
     static constexpr int RBA = 128, RBB = Q8 ? 64 : 128;  // LDS row bytes of A and of the weights
     static constexpr int A_BYTES = BM * RBA, B_BYTES = BN * RBB, SB_BYTES = Q8 ? BN * 8 : 0;
     static constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;
@@ -62,6 +69,8 @@ template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_> struct Cfg {
     static_assert(ACOP % NW == 0 && NBIG % NW == 0, "row copies split evenly over the waves");
     static_assert(PAD == 0 || Q8, "only the scale/bias copies are padded");
     static_assert(NI >= 1 && NT >= 1, "wave tile at least 32 x 32");
+    static_assert(KG == 1 || (!Q8 && NI == 2 && NT == 2 && 4 % KG == 0), "K groups: bf16 64 x 64 wave tiles");
+    static_assert(KG == 1 || (KG - 1) * NWG * 64 * NI * NT * 16 * 4 <= ST * STAGE, "group partials fit in the stages");
 };
 
 __device__ __forceinline__ int offA(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
@@ -244,8 +253,10 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int kg = wave / C::NWG, wq = wave % C::NWG;  // K group; wave within the group
+    const int wm = wq / C::WN, wn = wq % C::WN;
     const int m0 = blockIdx.y * C::BM, nb = blockIdx.x;
+    static_assert(C::KG == 1 || EPI != EPI_QKV, "the q|k|v epilogue uses every wave");
     const int nk = K / C::BK, ng = K / 64;
     const unsigned lds0 = (unsigned)(uintptr_t)smem;
 
@@ -312,7 +323,7 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
     if constexpr (EPI == EPI_QKV) qkv_prefetch<C>(pre, qe, M, m0, nb, wm, wn, lane);
     constexpr bool RPF = EPI == EPI_RESID && !C::Q8;
     uint32_t rv[RPF ? C::NI : 1][RPF ? 16 : 1][RPF ? C::NT : 1];
-    if constexpr (RPF) {
+    if (RPF && kg == 0) {
         const uint16_t *r16 = (const uint16_t *)res;
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
@@ -344,11 +355,11 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
             // pinned to the reads of k-slice 0, then one MFMA per read of the later slices, so the
             // reads of slice kk+1 overlap the MFMAs of slice kk (left to itself the compiler reuses
             // one fragment set and waits on every read; gate|up at T = 2048 ~130 -> ~118 us)
-            constexpr int NKK = C::BK / 16, RPK = C::NI + C::NT, MPK = C::NI * C::NT;
+            constexpr int NKK = C::BK / 16 / C::KG, RPK = C::NI + C::NT, MPK = C::NI * C::NT;
             bf16x8 af[NKK][C::NI], bfr[NKK][C::NT];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                const int c = 2 * kk + (lane >> 5);
+                const int c = 2 * (kg * NKK + kk) + (lane >> 5);
 #pragma unroll
                 for (int i = 0; i < C::NI; ++i)
                     af[kk][i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), c));
@@ -433,6 +444,34 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
         qkv_epilogue<C>(acc, pre, qe, smem, M, m0, nb, wm, wn, wave, lane);
         return;
     }
+    if constexpr (C::KG > 1) {
+        // the groups' partial sums of the same outputs meet in LDS (the stages are free once every
+        // wave has passed the last K step): group g > 0 stores, group 0 adds them in group order
+        constexpr int E = C::NI * C::NT * 16;
+        float *part = (float *)smem;  // [KG - 1][NWG][E][64]
+        __syncthreads();
+        if (kg > 0) {
+            float *d = part + ((size_t)(kg - 1) * C::NWG + wq) * E * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) d[((i * C::NT + j) * 16 + v) * 64] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < C::KG; ++g) {
+            const float *d = part + ((size_t)(g - 1) * C::NWG + wq) * E * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] += d[((i * C::NT + j) * 16 + v) * 64];
+        }
+    }
     // epilogue: accumulator v of a 32x32 tile sits at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
@@ -471,7 +510,8 @@ namespace {
 typedef g2::Cfg<256, 128, 3, 4, 2, false> Wide;    // 8 waves, 64 x 64 per wave, 144 KB LDS
 typedef g2::Cfg<128, 256, 3, 2, 4, false> WideN;   // 8 waves, 64 x 64 per wave, 144 KB LDS (gate|up)
 typedef g2::Cfg<128, 128, 4, 4, 2, false> Mid;     // 8 waves, 32 x 64 per wave, 128 KB LDS
-typedef g2::Cfg<128, 64, 4, 2, 2, false> SmallN;   // 4 waves, 64 x 32 per wave, 96 KB LDS
+typedef g2::Cfg<128, 128, 4, 2, 2, false, 2> MidK; // 8 waves: 2 K groups of 4 waves, 64 x 64 per wave, 128 KB LDS
+typedef g2::Cfg<128, 64, 4, 2, 1, false, 2> SmallNK;  // 4 waves: 2 K groups of 2 waves, 64 x 64 per wave, 96 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 2, false> SmallM;   // 4 waves, 32 x 64 per wave, 96 KB LDS
 typedef g2::Cfg<128, 128, 4, 2, 2, true> Quant;    // 4 waves, 100 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 2, true> QuantS;    // 4 waves, 68 KB LDS
@@ -527,10 +567,12 @@ hipError_t launch_gemm_dma(const void *x, int M, int K, const void *W, int N, in
     if (epi == EPI_SWIGLU && tiles<WideN>(M, N, epi) >= 192)
         return launch_c<EPI_SWIGLU, WideN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
     if (tiles<Wide>(M, N, epi) >= 192) return launch_e<Wide>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
-    if (tiles<Mid>(M, N, epi) >= 192) return launch_e<Mid>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
-    if (epi == EPI_SWIGLU) return launch_c<EPI_SWIGLU, SmallM>(a, M, K, W, nullptr, nullptr, N, r, o, s);
-    if (epi == EPI_RESID) return launch_c<EPI_RESID, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
-    return launch_c<EPI_STORE, SmallN>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+    if (epi == EPI_SWIGLU) {
+        if (tiles<Mid>(M, N, epi) >= 192) return launch_c<EPI_SWIGLU, Mid>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+        return launch_c<EPI_SWIGLU, SmallM>(a, M, K, W, nullptr, nullptr, N, r, o, s);
+    }
+    if (tiles<MidK>(M, N, epi) >= 192) return launch_sr<MidK>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
+    return launch_sr<SmallNK>(epi, a, M, K, W, nullptr, nullptr, N, r, o, s);
 }
 
 bool gemm_qkv_fused_ok(int M, int K, int H, int KV, int D) {

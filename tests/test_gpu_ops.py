@@ -69,12 +69,14 @@ def test_add_rmsnorm(orc, dtype, n, ops):
 
 # 2 <= M <= 16 in bf16 with K % 256 == 0: the skinny MFMA GEMV, on 8 outputs per block for K 2048 /
 # 4096 / 6144 when 16-output blocks would be too few ((3, 2048, 384), (5, 4096, 1000), (7, 6144, 130),
-# ragged N) and on 16 otherwise ((16, 256, 512)); M = 1 the plain GEMV.  MFMA tilings (the largest with >= 192 tiles): (520, 128, 8200) 256 x 128 for every epilogue;
-# (2000, 128, 1900) 128 x 128 / 8 waves (SWIGLU: 256 x 128); (300, 192, 4100) SWIGLU 128 x 128,
-# the others 128 x 64; the remaining M > 16 cases 128 x 64 (SWIGLU 64 x 128).  Ragged M and N.
+# ragged N) and on 16 otherwise ((16, 256, 512)); M = 1 the plain GEMV.  MFMA tilings (the largest
+# with >= 192 tiles): (520, 128, 8200) 256 x 128 (SWIGLU 128 x 256); (2000, 128, 1900) and
+# (1600, 256, 1800) 128 x 128 in two K groups (SWIGLU 128 x 256); (300, 192, 4100) SWIGLU
+# 128 x 128 with 8 waves, the others 128 x 64 in two K groups; the remaining M > 16 cases
+# 128 x 64 in two K groups (SWIGLU 64 x 128).  Ragged M and N.
 LIN_CASES = [(1, 2048, 4096), (3, 2048, 384), (16, 256, 512), (40, 512, 384), (300, 2048, 640), (130, 6144, 256),
              (520, 128, 8200), (2000, 128, 1900), (300, 192, 4100), (17, 64, 200), (7, 6144, 130),
-             (5, 4096, 1000)]
+             (5, 4096, 1000), (1600, 256, 1800)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
