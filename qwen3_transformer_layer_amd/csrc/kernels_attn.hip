@@ -477,14 +477,22 @@ __global__ void __launch_bounds__(64 * (G >= 8 ? 8 : 4)) attn_prefill_mfma_kerne
     }
 }
 
+// The values of lanes l and l ^ 32 in every lane, as (value of the lower lane, value of the upper
+// lane): one v_permlane32_swap instead of an LDS permute.
+__device__ __forceinline__ f32x2 halves32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // ------------------------------------------------------------ bf16 causal flash prefill, head_dim 128
 // Block: 32 queries x the G heads of one kv head; NP waves per head (NP = 4 for G <= 2, else
 // 2), wave part w takes keys 32 w .. 32 w + 31 of every (32 NP)-key tile, so a block holds
 // 2 waves per SIMD on its own and one wave's softmax arithmetic overlaps another's MFMAs.
 // (With two key halves and two blocks per CU, a CU whose light block finished ran its heavy
 // block at one wave per SIMD, latency-bound: 4 parts, 60 -> 52 us at T = 2048.)  Each wave
-// keeps its own running maximum, sum and O; at the end parts 1..NP-1 hand them over through
-// LDS and part 0 merges (log-sum-exp scaling) and stores.  The running maximum is raised only
+// keeps its own running maximum, sum and O; at the end the parts exchange them through LDS and
+// each part merges (log-sum-exp scaling) and stores its own quarter (half for NP = 2) of the
+// output columns.  The running maximum is raised only
 // when a tile's maximum exceeds it by more than 8 (base 2), so probabilities stay <= 2^8 in
 // fp32 and the O rescale is rare; the normalised result is the same softmax.  Query tiles
 // are dispatched heaviest (most keys) first, so the blocks that start last are the short
@@ -499,8 +507,12 @@ struct FaGeo {
     static constexpr int D = 128, RB = 256, KT = 32 * NP, ST = 2, NW = NP * G;
     static constexpr int TILE = KT * RB, STAGE = 2 * TILE;
     static constexpr int COPIES = STAGE / 1024, PW = COPIES / NW, HALF = PW / 2;
-    static constexpr int MERGE = D * 32 * 4 + 2 * 32 * 4;  // O, then m and l of 32 queries (fp32)
-    static constexpr int LDS = (ST * STAGE > G * (NP - 1) * MERGE) ? ST * STAGE : G * (NP - 1) * MERGE;
+    // merge: part w of a head merges output columns [32 w DP, 32 (w + 1) DP) and hands every other
+    // part its O of those columns (4 KB per 32 columns, fp32), plus its m and l of the 32 queries
+    static constexpr int DP = D / 32 / NP, OSL = D / 32 - DP, OB = 32 * 32 * 4;
+    static constexpr int MERGE_O = G * NP * OSL * OB, MERGE = MERGE_O + G * NP * 2 * 32 * 4;
+    static constexpr int LDS = ST * STAGE > MERGE ? ST * STAGE : MERGE;
+    static_assert(D / 32 % NP == 0, "output column tiles split evenly over the parts");
     static_assert(COPIES % (2 * NW) == 0, "K and V copies split evenly over the waves");
 };
 
@@ -511,6 +523,7 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
                                                                   bf16 *__restrict__ out) {
     using F = FaGeo<G>;
     constexpr int D = F::D, RB = F::RB, KT = F::KT;
+    constexpr bool HOIST = F::NW <= 8;
     extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
     const int ntiles = (T + 31) / 32;
     const int bi = (int)(blockIdx.x / KV), g = blockIdx.x % KV;
@@ -570,11 +583,23 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
 #pragma unroll
         for (int v = 0; v < 16; ++v) sc[v] = 0.f;
         {
+            // with 8 waves (256 registers per lane) every K fragment read is issued before the first
+            // MFMA (pinned: left to itself the compiler waits on each read right before its MFMA;
+            // T = 2048, G = 2: 45.5 -> 42.8 us with the V reads below); 16 waves have half the
+            // registers and keep one read per MFMA
             const int r = 32 * par + qi;
+            bf16x8 kf[HOIST ? D / 16 : 1];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(Ks + r * RB + (((2 * ks + hh) ^ (r & 15)) << 4));
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
+                const bf16x8 k = *(const bf16x8 *)(Ks + r * RB + (((2 * ks + hh) ^ (r & 15)) << 4));
+                if constexpr (HOIST) kf[ks] = k;
+                else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[ks], sc, 0, 0, 0);
+            }
+            if constexpr (HOIST) {
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);  // the DS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);  // then the MFMAs
             }
         }
         // accumulator v of S^T: key kb0 + 8 (v / 4) + 4 hh + v % 4, query qi.  Only tiles that cross
@@ -595,7 +620,8 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
         float tmax = sc[0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+        const f32x2 tm2 = halves32(tmax);
+        tmax = fmaxf(tm2[0], tm2[1]) * scale_log2;
         const bool up = tmax > m_run + 8.0f;  // also on the first tile with a visible key
         const float m_use = up ? tmax : m_run;
         const float alpha = up ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
@@ -625,83 +651,109 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
             }
         const bf16x8 phi[2] = {__builtin_bit_cast(bf16x8, hw[0]), __builtin_bit_cast(bf16x8, hw[1])};
         const bf16x8 plo[2] = {__builtin_bit_cast(bf16x8, lw[0]), __builtin_bit_cast(bf16x8, lw[1])};
-        psum += __shfl_xor(psum, 32, 64);
+        const f32x2 ps2 = halves32(psum);
+        psum = ps2[0] + ps2[1];
         l_run = l_run * alpha + psum;
         // V^T operand: group gi reads rows 32 par + 16 cc + 4 (gi / 2) (+ 8) and columns
         // 32 dt + 16 (gi % 2) + 0..15; lane r of the group receives 4 keys of column 16 (gi % 2) + r
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
+        // with 8 waves every V^T read is issued before the first P.V MFMA (pinned as the K reads)
+        constexpr int NVQ = HOIST ? D / 32 : 1;
+        s16x4 vq[NVQ][2][2];
+        auto vread = [&](int dt, int cc, s16x4 &lo4, s16x4 &hi4) {
             const int d0 = 32 * dt + 16 * (gi & 1) + 4 * (sl & 3);
+            const int r0 = 32 * par + 16 * cc + 4 * (gi >> 1) + (sl >> 2), r1 = r0 + 8;
+            lo4 = lds_tr_b64((const uint16_t *)(Vs + r0 * RB + (((d0 >> 3) ^ (4 * (r0 & 3))) << 4) + ((d0 >> 2) & 1) * 8));
+            hi4 = lds_tr_b64((const uint16_t *)(Vs + r1 * RB + (((d0 >> 3) ^ (4 * (r1 & 3))) << 4) + ((d0 >> 2) & 1) * 8));
+        };
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) vread(dt, cc, vq[HOIST ? dt : 0][cc][0], vq[HOIST ? dt : 0][cc][1]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                const int r0 = 32 * par + 16 * cc + 4 * (gi >> 1) + (sl >> 2), r1 = r0 + 8;
-                const s16x4 lo4 = lds_tr_b64((const uint16_t *)(Vs + r0 * RB + (((d0 >> 3) ^ (4 * (r0 & 3))) << 4) +
-                                                                ((d0 >> 2) & 1) * 8));
-                const s16x4 hi4 = lds_tr_b64((const uint16_t *)(Vs + r1 * RB + (((d0 >> 3) ^ (4 * (r1 & 3))) << 4) +
-                                                                ((d0 >> 2) & 1) * 8));
+                const int qd = HOIST ? dt : 0;
+                if constexpr (!HOIST) vread(dt, cc, vq[0][cc][0], vq[0][cc][1]);
                 bf16x8 vf;
                 short *vs = (short *)&vf;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    vs[e] = lo4[e];
-                    vs[4 + e] = hi4[e];
+                    vs[e] = vq[qd][cc][0][e];
+                    vs[4 + e] = vq[qd][cc][1][e];
                 }
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[cc], o[dt], 0, 0, 0);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[cc], o[dt], 0, 0, 0);
             }
+        if constexpr (HOIST) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);  // the DS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * D / 32, 0);  // then the MFMAs
         }
     }
-    // merge the key parts of each head: parts 1..NP-1 hand over (m, l, O) through LDS
+    // merge the key parts of each head: part w combines the (m, l, O) of every part for its own
+    // output columns; the sums run over the parts in part order
     __syncthreads();  // every wave is done with the K/V tiles
-    // part w's buffer: O as [dt][v / 4][lane][v % 4] (16-byte accesses), then m[32], l[32]
-    auto mbuf = [&](int w) { return (float *)(fa_smem + (hw * (F::NP - 1) + w - 1) * F::MERGE); };
-    if (par > 0) {
-        float *mb = mbuf(par);
+    // O of (head, source part, column tile dt) at slot dt (dt below the part's own tiles) or dt - DP,
+    // as [v / 4][lane][v % 4] (16-byte accesses); then m[32], l[32] of (head, part)
+    auto obuf = [&](int w, int dt) {
+        const int slot = dt < w * F::DP ? dt : dt - F::DP;
+        return (float *)(fa_smem + ((hw * F::NP + w) * F::OSL + slot) * F::OB);
+    };
+    auto mlbuf = [&](int w) { return (float *)(fa_smem + F::MERGE_O + (hw * F::NP + w) * 2 * 32 * 4); };
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt) {
+        if (dt / F::DP == par) continue;  // this part's own columns stay in registers
+        float *mb = obuf(par, dt);
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4)
-                *(f32x4 *)&mb[((dt * 4 + v4) * 64 + lane) * 4] =
-                    f32x4{o[dt][4 * v4], o[dt][4 * v4 + 1], o[dt][4 * v4 + 2], o[dt][4 * v4 + 3]};
-        if (lane < 32) {
-            mb[D * 32 + lane] = m_run;
-            mb[D * 32 + 32 + lane] = l_run;
-        }
+        for (int v4 = 0; v4 < 4; ++v4)
+            *(f32x4 *)&mb[(v4 * 64 + lane) * 4] = f32x4{o[dt][4 * v4], o[dt][4 * v4 + 1], o[dt][4 * v4 + 2], o[dt][4 * v4 + 3]};
+    }
+    if (lane < 32) {
+        mlbuf(par)[lane] = m_run;
+        mlbuf(par)[32 + lane] = l_run;
     }
     __syncthreads();
-    if (par == 0 && t0 + qi < T) {
-        float m = m_run;
-#pragma unroll
-        for (int w = 1; w < F::NP; ++w) m = fmaxf(m, mbuf(w)[D * 32 + qi]);
-        float a[F::NP], lsum = 0.f;
+    if (t0 + qi < T) {
+        float mw[F::NP], lw[F::NP], a[F::NP], m = -INFINITY, lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < F::NP; ++w) {
-            const float mw = w ? mbuf(w)[D * 32 + qi] : m_run, lw = w ? mbuf(w)[D * 32 + 32 + qi] : l_run;
-            a[w] = __builtin_amdgcn_exp2f(mw - m);
-            lsum += lw * a[w];
+            mw[w] = mlbuf(w)[qi];
+            lw[w] = mlbuf(w)[32 + qi];
+            m = fmaxf(m, mw[w]);
+        }
+#pragma unroll
+        for (int w = 0; w < F::NP; ++w) {
+            a[w] = __builtin_amdgcn_exp2f(mw[w] - m);
+            lsum += lw[w] * a[w];
         }
         const float inv = 1.0f / lsum;
         bf16 *dst = out + (size_t)tq * H * D + (size_t)h * D;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt) {
+            if (dt / F::DP != par) continue;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
-                f32x4 part[F::NP - 1];
-#pragma unroll
-                for (int w = 1; w < F::NP; ++w) part[w - 1] = *(const f32x4 *)&mbuf(w)[((dt * 4 + v4) * 64 + lane) * 4];
                 float r[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float t = o[dt][4 * v4 + e] * a[0];
+                for (int e = 0; e < 4; ++e) r[e] = 0.f;
 #pragma unroll
-                    for (int w = 1; w < F::NP; ++w) t += part[w - 1][e] * a[w];
-                    r[e] = t * inv;
+                for (int w = 0; w < F::NP; ++w) {
+                    f32x4 pv;
+                    if (w == par) pv = f32x4{o[dt][4 * v4], o[dt][4 * v4 + 1], o[dt][4 * v4 + 2], o[dt][4 * v4 + 3]};
+                    else pv = *(const f32x4 *)&obuf(w, dt)[(v4 * 64 + lane) * 4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = w ? r[e] + pv[e] * a[w] : pv[e] * a[w];
                 }
-                uint2 w;
-                w.x = pack_bf2(r[0], r[1]);
-                w.y = pack_bf2(r[2], r[3]);
-                *(uint2 *)&dst[32 * dt + 8 * v4 + 4 * hh] = w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] *= inv;
+                uint2 wd;
+                wd.x = pack_bf2(r[0], r[1]);
+                wd.y = pack_bf2(r[2], r[3]);
+                *(uint2 *)&dst[32 * dt + 8 * v4 + 4 * hh] = wd;
             }
+        }
     }
 }
 
