@@ -516,18 +516,15 @@ struct FaGeo {
     static_assert(COPIES % (2 * NW) == 0, "K and V copies split evenly over the waves");
 };
 
+// One query tile qt (32 queries) of kv head g: every wave of the block takes part.
 template <int G>
-__global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
-                                                                  const bf16 *__restrict__ Vc, int T, int H, int KV,
-                                                                  int cap, int p0, int window, float scale_log2,
-                                                                  bf16 *__restrict__ out) {
+__device__ __forceinline__ void fa_query_tile(unsigned char *fa_smem, const bf16 *__restrict__ q,
+                                              const bf16 *__restrict__ Kc, const bf16 *__restrict__ Vc, int T, int H,
+                                              int cap, int p0, int window, float scale_log2, bf16 *__restrict__ out,
+                                              int qt, int g) {
     using F = FaGeo<G>;
     constexpr int D = F::D, RB = F::RB, KT = F::KT;
     constexpr bool HOIST = F::NW <= 8;
-    extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
-    const int ntiles = (T + 31) / 32;
-    const int bi = (int)(blockIdx.x / KV), g = blockIdx.x % KV;
-    const int qt = ntiles - 1 - bi;  // heaviest query tiles first
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = wave / F::NP, par = wave % F::NP;
     const int h = g * G + hw, t0 = qt * 32;
@@ -757,6 +754,25 @@ __global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(cons
     }
 }
 
+// paired: block bi takes query tiles ntiles - 1 - bi and bi (their key-tile counts sum to about the
+// same for every bi), so one wave of blocks covers the causal triangle evenly; otherwise block bi
+// takes tile ntiles - 1 - bi (heaviest first).
+template <int G>
+__global__ void __launch_bounds__(64 * FaGeo<G>::NW) attn_prefill_fa_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ Kc,
+                                                                  const bf16 *__restrict__ Vc, int T, int H, int KV,
+                                                                  int cap, int p0, int window, float scale_log2,
+                                                                  int paired, bf16 *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(1024))) unsigned char fa_smem[];
+    const int ntiles = (T + 31) / 32;
+    const int bi = (int)(blockIdx.x / KV), g = blockIdx.x % KV;
+    const int qa = ntiles - 1 - bi;
+    fa_query_tile<G>(fa_smem, q, Kc, Vc, T, H, cap, p0, window, scale_log2, out, qa, g);
+    if (paired && bi < qa) {
+        __syncthreads();  // every wave is done with the merge buffers before the next tile's copies land
+        fa_query_tile<G>(fa_smem, q, Kc, Vc, T, H, cap, p0, window, scale_log2, out, bi, g);
+    }
+}
+
 template <int G>
 static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T, int H, int KV, int cap, int p0,
                              int window, float sl2, bf16 *out, hipStream_t s) {
@@ -769,8 +785,11 @@ static hipError_t prefill_fa(const bf16 *q, const bf16 *k, const bf16 *v, int T,
         attr = true;
     }
     const int ntiles = (T + 31) / 32;
-    attn_prefill_fa_kernel<G><<<ntiles * KV, 64 * FaGeo<G>::NW, lds, s>>>(q, k, v, T, H, KV, cap, p0, window, sl2,
-                                                                          out);
+    // pairs only when they still give at least one block per CU
+    const int paired = (ntiles + 1) / 2 * KV >= 256;
+    const int nb = paired ? (ntiles + 1) / 2 : ntiles;
+    attn_prefill_fa_kernel<G><<<nb * KV, 64 * FaGeo<G>::NW, lds, s>>>(q, k, v, T, H, KV, cap, p0, window, sl2, paired,
+                                                                      out);
     return hipGetLastError();
 }
 

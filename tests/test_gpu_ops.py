@@ -179,10 +179,11 @@ def test_attention_decode(orc, ops, dtype, H, KV, D, cap, p0):
 
 
 # head_dim 128 takes attn_prefill_fa_kernel (G = 2, 4, 8 and 1 below), head_dim 64 the
-# 16x16x32 kernel
+# 16x16x32 kernel.  (513, 7, 32, 32, ...) has 17 query tiles x 32 kv heads, enough blocks for the
+# flash kernel's paired query tiles (16 and 0, 15 and 1, ..., 8 alone).
 ATT_PREFILL = [(2, 0, 16, 8, 128, 64), (40, 7, 16, 4, 128, 64), (33, 0, 16, 16, 64, 64), (70, 0, 16, 8, 128, 128),
                (64, 5, 4, 2, 64, 128), (200, 100, 32, 4, 128, 512), (130, 0, 8, 8, 64, 256), (16, 48, 4, 2, 64, 64),
-               (97, 30, 8, 8, 128, 160)]
+               (97, 30, 8, 8, 128, 160), (513, 7, 32, 32, 128, 576)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])

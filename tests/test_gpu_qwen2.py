@@ -70,17 +70,17 @@ def test_head_dim64_bf16_window(orc, window, chunks):
     say(f"head_dim 64 bf16 window={window} chunks={chunks}: {e:.2e}")
 
 
-@pytest.mark.parametrize("window", [1, 33, 512, 5000])
-def test_1p7b_prefill_window(orc, window):
-    """The 1.7B shape (head_dim 128, flash prefill), one layer, T = 1024 from an empty cache:
-    a window smaller than a 32-query tile, one spanning tile boundaries, a long one and one
-    wider than the context (causal)."""
+@pytest.mark.parametrize("window,T", [(1, 1024), (33, 1024), (512, 1024), (5000, 1024), (700, 2048)])
+def test_1p7b_prefill_window(orc, window, T):
+    """The 1.7B shape (head_dim 128, flash prefill), one layer from an empty cache: a window
+    smaller than a 32-query tile, one spanning tile boundaries, a long one and one wider than
+    the context (causal); at T = 2048 the flash kernel pairs query tiles (63 and 0, 62 and 1, ...)."""
     from qwen3_transformer_layer_amd.config import QWEN3_1P7B_PREFILL
     cfg = QWEN3_1P7B_PREFILL.replace(n_layers=1, sliding_window=window, capacity=2048)
-    seat, st, got, ref = _run(orc, cfg, [1024])
+    seat, st, got, ref = _run(orc, cfg, [T])
     e = gate(got, ref, "bf16")
-    ek = max_row_rel_l2(np32(seat.k)[0, :, :1024], st.k[0, :, :1024])
-    say(f"1.7B prefill T=1024 window={window}: out {e:.2e}, K {ek:.2e}")
+    ek = max_row_rel_l2(np32(seat.k)[0, :, :T], st.k[0, :, :T])
+    say(f"1.7B prefill T={T} window={window}: out {e:.2e}, K {ek:.2e}")
     assert ek <= BF16_TOL
 
 
