@@ -11,14 +11,15 @@
 //    un-normalised partial sums (max, sum of exp, exp-weighted V) in fp32,
 //    and a combine kernel merges the splits with the usual log-sum-exp scaling.
 //  - attn_prefill_fa_kernel (T > 1, bf16, head_dim 128): causal flash attention on
-//    v_mfma_f32_32x32x16_bf16.  Block = 32 queries x the G heads of one kv head (two waves
-//    per head, each taking one 32-key half of every tile; all waves share one causal key
-//    range); K/V tiles of 64 keys arrive by direct-to-LDS copies in a 2-stage ring.  S^T = K Q^T leaves each lane one query and
-//    32 of the tile's keys, which is exactly the P^T operand layout of O^T += V^T P^T once
-//    the keys of each 16-key MFMA step are taken in the order {4h..4h+3, 8+4h..8+4h+3}
-//    (h = lane / 32); V^T comes from the LDS transpose read.  The grid is 1-D with kv head
-//    b % KV (one kv head per XCD when KV = 8); query tiles run heavy half descending, then
-//    light half ascending.
+//    v_mfma_f32_32x32x16_bf16.  Block = 32 queries x the G heads of one kv head, NP waves
+//    per head (4 for G <= 2, else 2), each taking one 32-key part of every (32 NP)-key tile;
+//    K/V tiles arrive by direct-to-LDS copies in a 2-stage ring.  S^T = K Q^T leaves each lane
+//    one query and 32 of the tile's keys, which is exactly the P^T operand layout of
+//    O^T += V^T P^T once the keys of each 16-key MFMA step are taken in the order
+//    {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); V^T comes from the LDS transpose read.  The
+//    grid is 1-D with kv head b % KV (one kv head per XCD when KV = 8); a block takes the
+//    heaviest and the lightest remaining query tile together when that still gives one block
+//    per CU, else one tile, heaviest first.
 //  - attn_prefill_mfma_kernel (T > 1, bf16, head_dim 64): causal flash attention on MFMA.
 //    Computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (q and k are bf16
 //    values, so the products are exact and the sums fp32), an online fp32
