@@ -511,13 +511,18 @@ def cpu_baseline():
     - the full 28-layer ctx-4096 T=1 decode step at position 4095 (median of 3 with every
       core, plus one run on a single thread): this is `value`, in decode tokens/s;
     - one layer of the 2048-token causal prefill (measured once with every core); the
-      28-layer figure is that time x 28 and is labelled extrapolated.
+      28-layer figure is that time x 28 and is labelled extrapolated;
+    - the full 28-layer 8-bit decode step at position 4095 (the oracle's weights are the
+      dequantised fp32 values s * q + b), median of 3;
+    - two layers of the 48-layer MoE stack decoding at position 2047 (median of 3); the step
+      figure is the per-layer time x 48 and is labelled extrapolated (48 layers of fp32 expert
+      weights would need ~116 GB of host memory).
     Inputs are host copies of the same seeded tensors the GPU legs use."""
     import numpy as np
 
     import oracle
     from qwen3_transformer_layer_amd import synth
-    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE, QWEN3_1P7B_PREFILL
+    from qwen3_transformer_layer_amd.config import QWEN3_1P7B_DECODE, QWEN3_1P7B_PREFILL, QWEN3_1P7B_Q8, QWEN3_MOE
 
     cores = len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
@@ -560,7 +565,42 @@ def cpu_baseline():
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    log(f"cpu baseline: prefill layer {t_pre:.2f} s")
+    log(f"cpu baseline: prefill layer {t_pre:.2f} s; 8-bit decode step")
+    del sp, lp, xp
+
+    def host_layers(cfg, w):  # fp32 host copies; 8-bit weights dequantised by the oracle
+        out = []
+        for lw in w["layers"]:
+            d = {k: v.float().cpu().numpy() for k, v in lw.items() if not k.endswith(("_q", "_s", "_b"))}
+            for name in ("qkv", "o", "gate_up", "down", "router", "exp_gate_up", "exp_down"):
+                if name + "_q" in lw:
+                    q = lw[name + "_q"].cpu().numpy()
+                    g = cfg.quant_group
+                    sc = lw[name + "_s"].float().cpu().numpy().reshape(-1, q.shape[-1] // g)
+                    bi = lw[name + "_b"].float().cpu().numpy().reshape(-1, q.shape[-1] // g)
+                    d[name] = oracle.q8_dequant(q.reshape(-1, q.shape[-1]), sc, bi, g).reshape(q.shape)
+            out.append(d)
+        return out
+
+    def timed_decode(cfg, pos):
+        w = synth.model_weights(cfg, "cuda")
+        K, V = synth.kv_cache(cfg, pos, "cuda")
+        st = oracle.Stack(cfg, host_layers(cfg, w), w["final_norm"].float().cpu().numpy(), "bf16",
+                          kcache=K.float().cpu().numpy(), vcache=V.float().cpu().numpy())
+        del w, K, V
+        xd = synth.hidden_states(cfg, 1, "cuda").float().cpu().numpy()
+        ts = []
+        for _ in range(3):
+            st.length = pos
+            t0 = time.perf_counter()
+            st.forward(xd)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    t_q8 = timed_decode(QWEN3_1P7B_Q8, 4095)
+    log(f"cpu baseline: 8-bit decode step {t_q8 * 1e3:.1f} ms; two MoE layers")
+    t_moe2 = timed_decode(QWEN3_MOE.replace(n_layers=2), 2047)
+    log(f"cpu baseline: two MoE decode layers {t_moe2 * 1e3:.1f} ms")
     return {"value": round(1.0 / t_all, 3), "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
             "sample": f"full 28-layer ctx-4096 T=1 decode step at position 4095, median of 3 "
                       f"({t_all * 1e3:.1f} ms/step); plus one layer of the 2048-token prefill",
@@ -570,7 +610,10 @@ def cpu_baseline():
             "decode_tokens_per_s_1_thread": round(1.0 / t_one, 3),
             "prefill_layer_s_measured": round(t_pre, 3),
             "prefill_layer_gflops": round(layer_flops / t_pre / 1e9, 2),
-            "prefill_28_layers_s_extrapolated": round(t_pre * 28, 2)}
+            "prefill_28_layers_s_extrapolated": round(t_pre * 28, 2),
+            "q8_decode_ms_per_step": round(t_q8 * 1e3, 2),
+            "moe_decode_ms_per_layer_measured": round(t_moe2 / 2 * 1e3, 2),
+            "moe_decode_ms_per_step_extrapolated": round(t_moe2 / 2 * 48 * 1e3, 1)}
 
 
 def main():
