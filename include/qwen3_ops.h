@@ -65,6 +65,14 @@ int qwen3_op_moe(int dtype, const void *x, int T, int hid, const void *router, i
                  const void *exp_gate_up, const void *exp_down, int32_t *idx, void *w, void *out, void *ws,
                  size_t ws_bytes, void *stream);
 
+/* Streaming-read probe, for the measured HBM read peak reported beside the published one
+ * (not part of the layer): reads src[0 .. bytes) with 16-byte non-temporal loads.  Thread t of
+ * the 256 x 256-thread grid reads the 16-byte words t, t + 65536, t + 2 * 65536, ... and
+ * writes to out[t] the XOR of their 32-bit words.  bytes: a positive multiple of 16; src
+ * 16-byte aligned; out: 65536 words (256 KiB), 4-byte aligned.  QWEN3_ERR_ARG otherwise,
+ * before any launch. */
+int qwen3_op_stream_read(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 /* Kernel timing for measurement.  While enabled for a kind (0 q|k|v projection,
  * 1 o_proj, 2 gate|up projection, 3 down projection, 4 attention, 5 the persistent
  * decode kernel of a whole T == 1 step), every launch of

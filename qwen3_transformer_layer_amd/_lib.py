@@ -79,6 +79,7 @@ def load():
         "qwen3_destroy": (None, [H]),
         "qwen3_rope_table": (_I, [_I, _I, ctypes.c_double, _I, _P, _P, _P]),
         "qwen3_op_add_rmsnorm": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P]),
+        "qwen3_op_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
         "qwen3_op_linear": (_I, [_I, _P, _I, _I, _P, _I, _I, _P, _P, _P]),
         "qwen3_op_linear_q8": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P]),
         "qwen3_op_qknorm_rope_kv": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P, _P,

@@ -28,6 +28,8 @@ hipError_t launch_embed(int dt, const int32_t *ids, int T, const void *E, int vo
 
 // Per row t < T: h = res ? rho(h_in + res) : h_in (written to h_out when res and h_out);
 // y = rho(w * rho(h * r)), r = 1/sqrt(mean(h^2) + eps).
+// Streaming read of `bytes` (a multiple of 16) for the measured HBM read peak; out: 256 * 256 words.
+hipError_t launch_stream_read(const void *src, size_t bytes, void *out, hipStream_t s);
 hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const void *w, void *h_out, void *y,
                               int T, int n, float eps, hipStream_t s);
 

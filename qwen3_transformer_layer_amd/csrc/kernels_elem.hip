@@ -155,6 +155,38 @@ hipError_t launch_add_rmsnorm(int dt, const void *h_in, const void *res, const v
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ streaming read probe
+// The measured-peak figure beside the published 8 TB/s: a plain read of n16 16-byte words with
+// non-temporal 16-byte loads, eight in flight per thread per round, consecutive lanes on
+// consecutive words, one block of 4 waves per CU.  Each thread XORs what it read and writes one
+// word (so the loads are not dead); out holds SR_BLOCKS * 256 words.  Over a 4 GiB buffer
+// (one box, graph replays): 256 blocks x 8 loads 7.18 TB/s; 512 x 4 7.05; 1024 x 4 5.73;
+// 8192 x 4 6.45; plain (cached) loads 5.6.
+constexpr int SR_BLOCKS = 256, SR_U = 8;
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4 *__restrict__ src, size_t n16,
+                                                          uint32_t *__restrict__ out) {
+    const size_t stride = (size_t)SR_BLOCKS * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (SR_U - 1) * stride < n16; i += SR_U * stride) {
+        u32x4 v[SR_U];
+#pragma unroll
+        for (int k = 0; k < SR_U; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < SR_U; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void *src, size_t bytes, void *out, hipStream_t s) {
+    stream_read_kernel<<<SR_BLOCKS, 256, 0, s>>>((const u32x4 *)src, bytes / 16, (uint32_t *)out);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ RoPE table
 // inv_j = fp32(theta^(-2j/D)) (rounded to the storage type: the bf16 model holds
 // the inverse frequencies as a bf16 buffer); angle = fp32(p * inv_j);

@@ -20,6 +20,11 @@ int qwen3_op_add_rmsnorm(int dtype, const void *h_in, const void *res, const voi
     return hip_rc(launch_add_rmsnorm(dtype, h_in, res, w, h_out, y, T, n, eps, (hipStream_t)stream));
 }
 
+int qwen3_op_stream_read(const void *src, size_t bytes, uint32_t *out, void *stream) {
+    if (!src || !out || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)out & 3)) return QWEN3_ERR_ARG;
+    return hip_rc(launch_stream_read(src, bytes, out, (hipStream_t)stream));
+}
+
 int qwen3_op_linear(int dtype, const void *x, int M, int K, const void *W, int N, int epilogue, const void *res,
                     void *out, void *stream) {
     if (!dt_ok(dtype)) return QWEN3_ERR_DTYPE;

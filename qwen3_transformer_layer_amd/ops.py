@@ -45,6 +45,15 @@ def add_rmsnorm(h_in, w, eps, res=None, h_out=None):
     return y
 
 
+def stream_read(buf):
+    """Streaming-read probe over a contiguous device tensor (its byte size a multiple of 16):
+    returns the 65536 per-thread XOR words (uint32 values in an int32 tensor)."""
+    _contig(buf)
+    out = torch.empty(256 * 256, dtype=torch.int32, device=buf.device)
+    _lib.check(_lib.load().qwen3_op_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(out), _s()))
+    return out
+
+
 def linear(x, W, epilogue=EPI_STORE, res=None):
     _contig(x, W, res)
     M, K = x.shape

@@ -96,6 +96,9 @@ def test_ops_reject_bad_arguments_before_launch(lib):
     assert lib.qwen3_op_attention(0, fake, fake, fake, 4, 4, 2, 128, 64, 61, fake, fake, 1 << 30, None) == \
         _lib.ERR_ARG                                                                                # p0 + T > cap
     assert lib.qwen3_rope_table(64, 96, 1e6, 0, fake, fake, None) == _lib.ERR_ARG
+    assert lib.qwen3_op_stream_read(fake, 24, fake, None) == _lib.ERR_ARG                        # not 16-byte words
+    assert lib.qwen3_op_stream_read(ctypes.c_void_p((1 << 20) + 8), 64, fake, None) == _lib.ERR_ARG  # misaligned
+    assert lib.qwen3_op_stream_read(None, 64, fake, None) == _lib.ERR_ARG
     assert lib.qwen3_status_string(-3) == b"context exceeds capacity"
 
 

@@ -246,3 +246,21 @@ def test_moe_nan_router_row_gets_valid_experts(orc, ops):
     ref, ridx, _ = orc.moe_block(np32(x)[good], np32(Wr), np32(Wgu), np32(Wd), k, True, False, "bf16")
     assert np.array_equal(gidx[good], ridx)
     assert max_row_rel_l2(np32(out)[good], ref) < BF16_TOL
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 20) * 16 * 9 + 1040])
+def test_stream_read_probe_xor(ops, nbytes):
+    """The streaming-read probe behind the measured HBM peak: thread t XORs the 32-bit words of
+    16-byte words t, t + 65536, ...; checked word for word against numpy on the same bytes
+    (short, ragged and multi-round buffers)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(nbytes)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    got = ops.stream_read(host.to("cuda")).cpu().numpy().view(np.uint32)
+    words = host.numpy().view(np.uint32).reshape(-1, 4)
+    n16, grid = words.shape[0], 256 * 256
+    per16 = np.bitwise_xor.reduce(words, axis=1)
+    pad = np.zeros(((n16 + grid - 1) // grid) * grid, np.uint32)
+    pad[:n16] = per16
+    ref = np.bitwise_xor.reduce(pad.reshape(-1, grid), axis=0)
+    assert np.array_equal(got, ref)
