@@ -14,9 +14,9 @@
 // Roles inside a block.  Waves 0-7 compute; waves 8-10 only stream.  The stream waves copy
 // every weight row (and the K/V rows of the block's attention split) that the block will
 // consume, in consumption order, from HBM straight into a ring of 4 KB LDS slots
-// (global_load_lds_dwordx4, 1 KB per instruction), keeping up to DL chunks in flight each
-// and running up to a full ring ahead of the compute waves, across step and layer
-// boundaries; when the ring is full a stream wave lands and publishes all its chunks in
+// (global_load_lds_dwordx4 with the non-temporal policy, 1 KB per instruction), keeping up to
+// DL chunks in flight each and running up to a full ring ahead of the compute waves, across
+// step and layer boundaries; when the ring is full a stream wave lands and publishes all its chunks in
 // flight before it waits for a slot, so the compute waves always see every landed chunk.
 // The compute waves never issue weight loads: a wave's vector-memory counter retires loads
 // in issue order, so a wave that polls another block's results while its own weight
@@ -216,7 +216,7 @@ __device__ void stream_wave(const Args &A, const Seq<QPB, GPB, DCH, Q8> &S, cons
         unsigned char *dst = ring + (size_t)s * CHB;
         const unsigned dlds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dma16(src[k], dlds + k * 1024);
+        for (int k = 0; k < 4; ++k) dma16_nt(src[k], dlds + k * 1024);
         if constexpr (Q8) dma4(sbsrc, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(sbring + (size_t)s * SBB)));
         ++n;
         if (n - pub >= DL) {

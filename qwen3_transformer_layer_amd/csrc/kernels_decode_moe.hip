@@ -292,7 +292,7 @@ __device__ void stream_wave(const Args &A, const DevLayer *lay, unsigned char *r
         }
         const unsigned dlds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(ring + (size_t)s * CHB));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dma16(src[k], dlds + k * 1024);
+        for (int k = 0; k < 4; ++k) dma16_nt(src[k], dlds + k * 1024);
         if constexpr (Q8) dma4(sbsrc, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(sbring + (size_t)s * SBM)));
         ++n;
         if (n - pub >= DL) {
