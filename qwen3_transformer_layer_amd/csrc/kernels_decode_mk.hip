@@ -52,8 +52,8 @@
 namespace q3 {
 namespace mk {
 
-constexpr int NS = 30;               // ring slots (120 KB)
-constexpr int NSQ = 28;              // ring slots with 8-bit weights (112 KB + 7 KB of scale/bias slots)
+constexpr int NS = 32;               // ring slots (128 KB)
+constexpr int NSQ = 30;              // ring slots with 8-bit weights (120 KB + 7.5 KB of scale/bias slots)
 constexpr int SBB = 256;             // scale/bias bytes per chunk (8-bit weights)
 constexpr int CHUNK_MAX = 256;       // keys per attention split
 static_assert(NSQ >= NL * DL, "the ring holds every stream wave's chunks in flight");
@@ -247,8 +247,11 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
     __shared__ __attribute__((aligned(16))) uint16_t ys[IM];  // current projection input (bf16 bits)
     __shared__ __attribute__((aligned(16))) uint16_t qraw[G * D + 2 * D];
     __shared__ float qs[G * D], kvs[2 * D];
-    __shared__ float sc[G * CHUNK_MAX];
-    __shared__ float red[NC * G * D];
+    // the attention's probabilities and per-wave partial outputs (then the split merge's buffer)
+    // live in ys, which holds nothing between the q|k|v rows and the merged-output poll
+    static_assert((G * CHUNK_MAX + NC * G * D) * 4 <= IM * 2, "attention buffers fit in ys");
+    float *const sc = (float *)ys;
+    float *const red = (float *)ys + G * CHUNK_MAX;
     __shared__ float rsum[2][NC];
     __shared__ float pm[NSPLIT_MAX], pl[NSPLIT_MAX];
     __shared__ float mwv[NC * G], lwv[NC * G];  // each wave's attention max and sum
@@ -599,6 +602,10 @@ __global__ void __launch_bounds__(NTH) decode_mk_kernel(Args A) {
         }
 
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row
+        // the merge has read its buffer (in ys) before ys receives a; the barrier also keeps the other
+        // waves' polls of a from starting while wave 0 still merges (1.7B step ~723 -> ~708 us; with
+        // the ring's two extra slots ~705; a barrier before the q|k|v poll instead cost ~5 us)
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
         poll_pause<PAUSE_SPLIT>();
         poll_bf16<HPT>(opaque(A.x_a) + (b % NREP) * RSH, HID, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
