@@ -598,6 +598,9 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         }
 
         // ---------------- step 3: merge the splits of (head mh, dims md0 .. md0 + dpb)
+        // Barriers before this poll and the merged-output poll keep the block's early waves from
+        // polling while the others still work (MoE step ~1804 -> ~1752 us, 8-bit ~1856 -> ~1803 us).
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
         poll_pause<PAUSE_SPLIT>();
         {
             // the split maxima, sums and this block's dims of every split's output, each word polled
@@ -645,6 +648,7 @@ __global__ void __launch_bounds__(NTH) decode_moe_kernel(Args A) {
         }
 
         // ---------------- step 4: h = rho(h + rho(a . Wo^T)) for this wave's row (two chunks)
+        cbar(&bar, ep, &abt, opaque(A.err), lane);
         poll_pause<PAUSE_SPLIT>();
         poll_bf16<APT>(opaque(A.x_a) + (b % NREP) * RSA, HD, tag, ys, opaque(A.err), &abt, tid);
         cbar(&bar, ep, &abt, opaque(A.err), lane);
