@@ -12,16 +12,19 @@ namespace mk {
 
 constexpr int NB = 256;              // blocks, one per CU
 constexpr int NC = 8;                // compute waves per block
-// 3 stream waves with 3 chunks in flight each beat 2 x 4 (the earlier choice), 3 x 4, 4 x 3 and
-// 4 x 4 on the 1.7B shape (ms per step 0.911 against 0.960, 0.939, 0.965, 0.965 on one box), and
-// 3 x 2, 4 x 2 (0.916 against 0.929, 0.947 on another)
-constexpr int NL = 3;                // stream waves per block
+// Stream waves x chunks in flight per wave.  Before the weight stream carried the non-temporal
+// policy, 3 x 3 beat 2 x 4, 3 x 4, 4 x 3 and 4 x 4 on the 1.7B shape (ms per step 0.911 against
+// 0.960, 0.939, 0.965, 0.965 on one box) and 3 x 2, 4 x 2 (0.916 against 0.929, 0.947 on
+// another).  With it, 4 x 2 edges out 3 x 3 (1.7B 0.703 against 0.707 ms in three interleaved
+// pairs on one box, 8-bit even, MoE 1.745 against 1.758), while 2 x 4, 2 x 5 (0.79 to 0.80)
+// and 4 x 3 (0.747) lose.
+constexpr int NL = 4;                // stream waves per block
 constexpr int NCT = 64 * NC;         // compute threads
 constexpr int NTH = 64 * (NC + NL);  // threads per block
 constexpr int D = 128;               // head dimension
 constexpr int HID = 2048;            // hidden size: one chunk is one weight row of HID bf16
 constexpr int CHB = HID * 2;         // chunk bytes
-constexpr int DL = 3;                // chunks in flight per stream wave while the ring has room
+constexpr int DL = 2;                // chunks in flight per stream wave while the ring has room
 constexpr int KPC = CHB / (D * 2);   // keys per K or V chunk (16)
 constexpr int NSPLIT_MAX = 256;
 constexpr int MAXL = 63;             // layers (tags are call * 64 + layer)

@@ -11,7 +11,7 @@
 // gfx950), more than the 1 - 8 us the steps need at HBM speed.  Here 256 blocks (one per CU,
 // co-resident) run all steps of all layers.
 //
-// Roles inside a block.  Waves 0-7 compute; waves 8-10 only stream.  The stream waves copy
+// Roles inside a block.  Waves 0-7 compute; waves 8-11 only stream.  The stream waves copy
 // every weight row (and the K/V rows of the block's attention split) that the block will
 // consume, in consumption order, from HBM straight into a ring of 4 KB LDS slots
 // (global_load_lds_dwordx4 with the non-temporal policy, 1 KB per instruction), keeping up to

@@ -12,7 +12,7 @@
 //
 // Shape: hidden 2048, head_dim 128, 8 query heads per kv head, n_heads * head_dim = 4096
 // (the attention output, o_proj's input), E <= 128 experts, top 8, expert intermediate 768.
-// Block roles (8 compute waves, 3 stream waves), the LDS ring of 4 KB chunks and the exchange
+// Block roles (8 compute waves, 4 stream waves), the LDS ring of 4 KB chunks and the exchange
 // protocol between blocks are those of kernels_decode_mk.hip.  What differs:
 //  - Attention: a block holds the 8 query heads of its kv head for one split of the keys;
 //    compute wave h takes head h (its scores over every K chunk of the split, its softmax
