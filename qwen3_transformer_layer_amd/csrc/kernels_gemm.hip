@@ -28,9 +28,10 @@
 //    per-group fold (2 FMAs per accumulator element) costs about as many cycles as the group's
 //    MFMAs, so 8 waves per CU let one wave's fold overlap another's MFMAs: 128 x 256 with 8
 //    waves when it gives >= 192 tiles, then 128 x 128 (SwiGLU) or 64 x 128 with 8 waves, else
-//    64 x 64 with 4 waves (3 blocks per CU).  Against the 4-wave 128 x 128 / 64 x 128 tilings
+//    64 x 64 with 2 K groups of 4 waves.  Against the 4-wave 128 x 128 / 64 x 128 tilings
 //    at T = 512: gate|up 96 -> 67 us, down 77 -> 60, o_proj 32 -> 24, q|k|v 32 -> 28.  A
-//    stage's copies are padded with dummies to a multiple of the wave count.
+//    stage's copies are padded with dummies to a multiple of the wave count (a wave's copies of
+//    one round may then be of different kinds).
 //  - 8-bit weights (one K step = one group): the codes (64 B per row) are copied to LDS like
 //    the bf16 operand; the scale and bias words of the group arrive by 4-byte direct copies
 //    (the aligned word holding groups 2i and 2i+1).  K is interleaved per lane so one 16-byte
@@ -66,10 +67,13 @@ template <int BM_, int BN_, int ST_, int WM_, int WN_, bool Q8_, int KG_ = 1> st
     static constexpr int PW = OPS / NW, APW = ACOP / NW, BPW = NBIG / NW;
     static constexpr int JUNK = PAD ? 256 : 0, LDS = ST * STAGE + JUNK;
     static constexpr int WTM = BM / WM, WTN = BN / WN, NI = WTM / 32, NT = WTN / 32;
-    static_assert(ACOP % NW == 0 && NBIG % NW == 0, "row copies split evenly over the waves");
+    // bf16 tilings give every wave the same copies in every round; 8-bit ones may mix kinds in a
+    // round (the kind is then chosen per copy), and their padding copies read the scale array
+    static constexpr bool EVEN = ACOP % NW == 0 && NBIG % NW == 0;
+    static_assert(EVEN || Q8, "bf16 row copies split evenly over the waves");
     static_assert(PAD == 0 || Q8, "only the scale/bias copies are padded");
     static_assert(NI >= 1 && NT >= 1, "wave tile at least 32 x 32");
-    static_assert(KG == 1 || (!Q8 && NI == 2 && NT == 2 && 4 % KG == 0), "K groups: bf16 64 x 64 wave tiles");
+    static_assert(KG == 1 || (4 % KG == 0 && (Q8 || (NI == 2 && NT == 2))), "K groups: bf16 64 x 64 wave tiles");
     static_assert(KG == 1 || (KG - 1) * NWG * 64 * NI * NT * 16 * 4 <= ST * STAGE, "group partials fit in the stages");
 };
 
@@ -267,10 +271,10 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
 #pragma unroll
         for (int i = 0; i < C::PW; ++i) {
             const int d = i * C::NW + wave;
-            if (i < C::APW) {
+            if (C::EVEN ? i < C::APW : d < C::ACOP) {
                 const int r = d * 8 + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
                 dma16(A + (size_t)min(m0 + r, M - 1) * K + k0 + c * 8, __builtin_amdgcn_readfirstlane(st + d * 1024));
-            } else if (i < C::BPW) {
+            } else if (C::EVEN ? i < C::BPW : d < C::NBIG) {
                 const int db = d - C::ACOP;
                 if (C::Q8) {
                     const int r = db * 16 + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
@@ -402,28 +406,33 @@ __global__ void __launch_bounds__(C::NTH) gemm_mfma_kernel(const bf16 *__restric
             const int h = lane >> 5;
             const f32x16 zero = {};
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+            // K groups: group g takes the MFMA steps [g * SPG, (g + 1) * SPG) and folds its own
+            // partial sums with the group's scale and bias (the fold is linear, so the groups' sums add)
+            constexpr int SPG = 4 / C::KG;
+            const int pb = C::KG == 1 ? 0 : (kg * SPG) >> 1;
             f32x16 part[C::NI][C::NT], xs[C::NI];
+            u32x4 cw[C::NT];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                u32x4 cw[C::NT];
+            for (int q = 0; q < SPG; ++q) {
+                const int p = pb + (q >> 1), e = SPG >= 2 ? (q & 1) : (kg & 1);
+                if (SPG == 1 || (q & 1) == 0) {
 #pragma unroll
-                for (int j = 0; j < C::NT; ++j) cw[j] = *(const u32x4 *)(Bs + offB<true>(brow[j] + (lane & 31), 2 * p + h));
+                    for (int j = 0; j < C::NT; ++j)
+                        cw[j] = *(const u32x4 *)(Bs + offB<true>(brow[j] + (lane & 31), 2 * p + h));
+                }
+                bf16x8 af[C::NI], bfr[C::NT];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    bf16x8 af[C::NI], bfr[C::NT];
+                for (int i = 0; i < C::NI; ++i)
+                    af[i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), 2 * (2 * p + h) + e));
 #pragma unroll
-                    for (int i = 0; i < C::NI; ++i)
-                        af[i] = *(const bf16x8 *)(As + offA(wm * C::WTM + i * 32 + (lane & 31), 2 * (2 * p + h) + e));
+                for (int j = 0; j < C::NT; ++j)
+                    bfr[j] = e ? codes8(cw[j][2], cw[j][3]) : codes8(cw[j][0], cw[j][1]);
 #pragma unroll
-                    for (int j = 0; j < C::NT; ++j) bfr[j] = codes8(cw[j][2 * e], cw[j][2 * e + 1]);
+                for (int i = 0; i < C::NI; ++i) {
 #pragma unroll
-                    for (int i = 0; i < C::NI; ++i) {
-#pragma unroll
-                        for (int j = 0; j < C::NT; ++j)
-                            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], (p | e) ? part[i][j] : zero,
-                                                                                 0, 0, 0);
-                        xs[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], ones, (p | e) ? xs[i] : zero, 0, 0, 0);
-                    }
+                    for (int j = 0; j < C::NT; ++j)
+                        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], q ? part[i][j] : zero, 0, 0, 0);
+                    xs[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], ones, q ? xs[i] : zero, 0, 0, 0);
                 }
             }
             const uint32_t *sw = (const uint32_t *)(Bs + C::B_BYTES), *bw = sw + C::BN;
@@ -517,7 +526,11 @@ typedef g2::Cfg<128, 128, 4, 2, 2, true> Quant;    // 4 waves, 100 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 2, true> QuantS;    // 4 waves, 68 KB LDS
 typedef g2::Cfg<128, 256, 3, 2, 4, true> QuantW;   // 8 waves, 64 x 64 per wave, 102 KB LDS
 typedef g2::Cfg<64, 128, 4, 2, 4, true> QuantS8;   // 8 waves, 32 x 32 per wave, 68 KB LDS
-typedef g2::Cfg<64, 64, 4, 2, 2, true> QuantT;     // 4 waves, 32 x 32 per wave, 50 KB LDS (3 blocks per CU)
+// 8 waves: 2 K groups of 4, 32 x 32 per wave, 50 KB LDS.  At T = 512 (one tile per CU) the 8-bit
+// prefill took 5.33 ms with 4 waves (one group), 5.13 with 2 groups, 5.6 with 4 groups; 2 groups of
+// 8 waves for the 64 x 128 tiling (q|k|v) 28 -> 31.5 us; 2-wave groups of 32 x 64 wave tiles 5.6 ms
+// (2 groups) and 6.3 (4), interleaved runs on one box
+typedef g2::Cfg<64, 64, 4, 2, 2, true, 2> QuantTK;
 
 // Output tiles of a BM x BN weight-row tiling (a SWIGLU tile covers BN/2 outputs).
 template <class C> long tiles(int M, int N, int epi) {
@@ -599,7 +612,7 @@ hipError_t launch_gemm_q8_dma(const void *x, int M, int K, const uint8_t *codes,
     }
     if (tiles<QuantW>(M, N, epi) >= 192) return launch_sr<QuantW>(epi, a, M, K, codes, sc, bi, N, r, o, s);
     if (tiles<QuantS8>(M, N, epi) >= 192) return launch_sr<QuantS8>(epi, a, M, K, codes, sc, bi, N, r, o, s);
-    return launch_sr<QuantT>(epi, a, M, K, codes, sc, bi, N, r, o, s);
+    return launch_sr<QuantTK>(epi, a, M, K, codes, sc, bi, N, r, o, s);
 }
 
 }  // namespace q3

@@ -108,7 +108,7 @@ def test_linear(orc, ops, dtype, epi, M, K, N):
 # cases the LDS-DMA one, whose tiling follows the tile count: (1030, 256, 5400) 128 x 256 with
 # 8 waves for every epilogue; (1030, 256, 2800) that tiling for SwiGLU, 64 x 128 with 8 waves
 # (copies padded with dummies) otherwise; (1030, 256, 1400) 128 x 128 for SwiGLU; the smaller
-# ones 64 x 64 (store, residual) and 64 x 128 (SwiGLU) with 4 waves
+# ones 64 x 64 (store, residual: 2 K groups of 4 waves) and 64 x 128 (SwiGLU) with 4 waves
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (5, 6144, 256), (40, 2048, 384), (512, 2048, 640),
                                    (200, 6144, 136), (40, 320, 96), (1030, 256, 2800), (1030, 256, 5400),
                                    (1030, 256, 1400), (17, 128, 72)])
