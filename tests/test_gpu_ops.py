@@ -46,7 +46,7 @@ def test_rope_table_bitwise(orc, dtype, D):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("n", [256, 2048])
+@pytest.mark.parametrize("n", [256, 2048, 4096])
 def test_add_rmsnorm(orc, dtype, n, ops):
     dt = TDT[dtype]
     h = randn((7, n), 1, 1.0, dt)
