@@ -528,7 +528,8 @@ typedef g2::Cfg<128, 256, 3, 2, 4, true> QuantW;   // 8 waves, 64 x 64 per wave,
 typedef g2::Cfg<64, 128, 4, 2, 4, true> QuantS8;   // 8 waves, 32 x 32 per wave, 68 KB LDS
 // 8 waves: 2 K groups of 4, 32 x 32 per wave, 50 KB LDS.  At T = 512 (one tile per CU) the 8-bit
 // prefill took 5.33 ms with 4 waves (one group), 5.13 with 2 groups, 5.6 with 4 groups; 2 groups of
-// 8 waves for the 64 x 128 tiling (q|k|v) 28 -> 31.5 us; 2-wave groups of 32 x 64 wave tiles 5.6 ms
+// 8 waves for the 64 x 128 tiling (q|k|v) 28 -> 31.5 us, of 4 waves of 32 x 64 28 -> 30.6 us; 2-wave
+// groups of 32 x 64 wave tiles for 64 x 64 5.6 ms
 // (2 groups) and 6.3 (4), interleaved runs on one box
 typedef g2::Cfg<64, 64, 4, 2, 2, true, 2> QuantTK;
 
